@@ -1,0 +1,113 @@
+"""Planted mistakes in the oracle (on the CPU only): each plausible slip --
+a dropped factor, a wrong sign placement, a transposed operand, a wrong
+index convention -- must make at least one pin fail."""
+import numpy as np
+import pytest
+
+import oracle.hadamard as H
+import oracle.rtn as R
+import oracle.qwha as Q
+import oracle.harp as P
+import test_oracle_hadamard as th
+import test_oracle_rtn as tr
+import test_oracle_qwha_harp as tq
+
+
+def _fails(fn, *args):
+    with pytest.raises(AssertionError):
+        fn(*args)
+
+
+def test_mutant_unnormalised(monkeypatch):
+    orig = H.wht
+    monkeypatch.setattr(H, "wht", lambda x, normalize=True: orig(x, normalize=False))
+    _fails(th.test_involution_and_norm, 64)
+
+
+def test_mutant_sequency_order(monkeypatch):
+    orig = H.sylvester
+
+    def seq(n):
+        h = orig(n)
+        changes = (np.diff(h, axis=1) != 0).sum(axis=1)
+        return h[np.argsort(changes, kind="stable")]
+    monkeypatch.setattr(H, "sylvester", seq)
+    _fails(th.test_matches_scipy_hadamard, 8)
+    _fails(th.test_golden_h4)
+
+
+def test_mutant_signs_after(monkeypatch):
+    monkeypatch.setattr(H, "rht", lambda x, s: H.wht(x) * s)
+    _fails(th.test_sign_diagonal_orthogonality)
+
+
+def test_mutant_sign_mask_msb_first(monkeypatch):
+    def msb(bits, n):
+        bits = np.asarray(bits, dtype=np.uint32)
+        j = np.arange(n)
+        b = (bits[j >> 5] >> (31 - (j & 31)).astype(np.uint32)) & np.uint32(1)
+        return 1.0 - 2.0 * b.astype(np.float64)
+    monkeypatch.setattr(H, "signs_from_bits", msb)
+    _fails(th.test_sign_mask_golden)
+
+
+def test_mutant_qmax(monkeypatch):
+    monkeypatch.setattr(R, "qmax_of", lambda bits: 1 << (bits - 1))
+    _fails(tr.test_rtn_invariants, 4)
+
+
+def test_mutant_floor_rounding(monkeypatch):
+    monkeypatch.setattr(R.np, "rint", np.floor)
+    try:
+        _fails(tr.test_rtn_bruteforce, 4)
+    finally:
+        monkeypatch.undo()
+
+
+def test_mutant_pack_msb_first(monkeypatch):
+    def pack(q, bits):
+        q = np.asarray(q, dtype=np.int64)
+        rows, n = q.shape
+        u = q & ((1 << bits) - 1)
+        planes = (u[:, :, None] >> np.arange(bits)[::-1]) & 1
+        return np.packbits(planes.reshape(rows, n * bits).astype(np.uint8), axis=1,
+                           bitorder="little")
+    monkeypatch.setattr(R, "pack_codes", pack)
+    _fails(tr.test_packing_golden)
+
+
+def test_mutant_dequant_no_sign_extension(monkeypatch):
+    def unpack(codes, bits, n):
+        planes = np.unpackbits(np.asarray(codes, np.uint8), axis=1, bitorder="little")
+        planes = planes[:, :n * bits].reshape(codes.shape[0], n, bits).astype(np.int64)
+        return (planes << np.arange(bits)).sum(axis=2)
+    monkeypatch.setattr(R, "unpack_codes", unpack)
+    _fails(tr.test_grid_constructed_roundtrip, 4, 128, 1024)
+
+
+def test_mutant_qwha_untransposed(monkeypatch):
+    def fwd(x, row_ptr, col_idx, vals, d_out):
+        f = Q.csr_to_dense(row_ptr, col_idx, vals, d_out, x.shape[1])
+        return H.wht(x) @ f          # F instead of F^T
+    monkeypatch.setattr(Q, "qwha_forward", fwd)
+    _fails(tq.test_qwha_single_nonzero)
+
+
+def test_mutant_harp_block_transposed(monkeypatch):
+    orig = P.stage_matrix
+    monkeypatch.setattr(P, "stage_matrix",
+                        lambda b, t, r: orig(np.transpose(np.asarray(b), (0, 2, 1)), t, r))
+    _fails(tq.test_harp_bruteforce, (4, 4))
+
+
+def test_mutant_harp_digit_order(monkeypatch):
+    orig = P.stage_matrix
+
+    def rev(b, t, r):
+        m = len(r)
+        rr = list(r)[::-1]
+        # act on digit m-1-t instead of t
+        return orig(b, m - 1 - t, rr) if rr == list(r) else orig(b, t, r)[::-1, ::-1]
+    monkeypatch.setattr(P, "stage_matrix", rev)
+    _fails(tq.test_harp_bruteforce, (2, 4, 3))
+    _fails(tq.test_harp_permutation_blocks_at_real_shape)

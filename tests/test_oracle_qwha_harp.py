@@ -1,0 +1,189 @@
+"""Pins of the oracle's QWHA adapter and HARP rotation: special cases that
+reduce to the plain WHT / identity, single-nonzero and permutation cases
+predicted position by position, brute-force loops on tiny shapes, norm
+preservation and exact inversion."""
+import numpy as np
+import pytest
+
+from oracle import hadamard as H, qwha, harp
+from golden_io import rows, ints
+
+
+def brute_wht(x):
+    n = x.shape[-1]
+    out = np.zeros_like(x, dtype=np.float64)
+    for i in range(n):
+        for j in range(n):
+            sgn = -1.0 if bin(i & j).count("1") % 2 else 1.0
+            out[..., i] += sgn * x[..., j]
+    return out / np.sqrt(n)
+
+
+def dense_to_csr(f):
+    r, c = np.nonzero(f)
+    return qwha.coo_to_csr(r, c, f[r, c], f.shape[0])
+
+
+# ------------------------------------------------------------------- QWHA
+
+def test_qwha_identity_and_involution():
+    rng = np.random.default_rng(0)
+    n = 256
+    x = rng.standard_normal((5, n))
+    rp, ci, v = dense_to_csr(np.eye(n))
+    assert np.allclose(qwha.qwha_forward(x, rp, ci, v, n), H.wht(x), atol=1e-12)
+    hn = H.sylvester(n) / np.sqrt(n)
+    rp, ci, v = dense_to_csr(hn)
+    assert np.allclose(qwha.qwha_forward(x, rp, ci, v, n), x, atol=1e-12)
+
+
+def test_qwha_single_nonzero():
+    rng = np.random.default_rng(1)
+    n, o, k, val = 64, 17, 40, -0.375
+    x = rng.standard_normal((3, n))
+    y = qwha.qwha_forward(x, np.r_[np.zeros(o + 1, int), np.ones(n - o, int)],
+                          np.array([k]), np.array([val]), n)
+    want = np.zeros((3, n)); want[:, o] = val * H.wht(x)[:, k]
+    assert np.allclose(y, want, atol=1e-14)
+
+
+@pytest.mark.parametrize("d_in,d_out", [(8, 8), (16, 12), (4, 16)])
+def test_qwha_bruteforce(d_in, d_out):
+    rng = np.random.default_rng(d_in * 100 + d_out)
+    x = rng.standard_normal((4, d_in))
+    nnz = d_out * 3
+    r = rng.integers(0, d_out, nnz)
+    c = rng.integers(0, d_in, nnz)
+    keep = np.unique(r * d_in + c, return_index=True)[1]
+    r, c = r[keep], c[keep]
+    v = rng.standard_normal(r.size)
+    rp, ci, vv = qwha.coo_to_csr(r, c, v, d_out)
+    assert np.all(np.diff(rp) >= 0) and rp[-1] == r.size
+    z = brute_wht(x)
+    want = np.zeros((4, d_out))
+    for o in range(d_out):
+        for e in range(rp[o], rp[o + 1]):
+            want[:, o] += vv[e] * z[:, ci[e]]
+    assert np.allclose(qwha.qwha_forward(x, rp, ci, vv, d_out), want, atol=1e-12)
+
+
+# ------------------------------------------------------------------- HARP
+
+def digits(i, radices):
+    out = []
+    for b in radices:
+        out.append(i % b)
+        i //= b
+    return out
+
+
+def undigits(dg, radices):
+    i, mul = 0, 1
+    for dd, b in zip(dg, radices):
+        i += dd * mul
+        mul *= b
+    return i
+
+
+def brute_stage(z, blocks_t, t, radices):
+    """out[i] = sum_k B_{t,c}[i_t, k] z[i with digit t := k], with c the
+    remaining digits in increasing significance."""
+    d = z.shape[-1]
+    out = np.zeros_like(z)
+    for i in range(d):
+        dg = digits(i, radices)
+        rest = [dd for u, dd in enumerate(dg) if u != t]
+        rad_rest = [b for u, b in enumerate(radices) if u != t]
+        c = undigits(rest, rad_rest)
+        for k in range(radices[t]):
+            j = list(dg); j[t] = k
+            out[..., i] += blocks_t[c, dg[t], k] * z[..., undigits(j, radices)]
+    return out
+
+
+@pytest.mark.parametrize("radices", [(4, 4), (2, 2, 2), (5, 3, 2), (2, 4, 3)])
+def test_harp_bruteforce(radices):
+    rng = np.random.default_rng(sum(radices))
+    d = int(np.prod(radices))
+    blocks = [rng.standard_normal((d // b, b, b)) for b in radices]
+    x = rng.standard_normal((3, d))
+    z = x.copy()
+    for t in range(len(radices)):
+        z = brute_stage(z, blocks[t], t, radices)
+    got = harp.harp_rotate(x, radices, blocks, precondition=False)
+    assert np.allclose(got, z, atol=1e-12)
+
+
+@pytest.mark.parametrize("b,m", [(4, 2), (2, 3), (4, 3), (16, 2), (16, 3)])
+def test_harp_hadamard_blocks_equal_wht(b, m):
+    """Theta = 0: every block is the normalised Sylvester H_b, and the stages
+    compose to exactly the length-d Sylvester WHT under this digit convention."""
+    d = b ** m
+    hb = H.sylvester(b) / np.sqrt(b)
+    blocks = [np.broadcast_to(hb, (d // b, b, b)) for _ in range(m)]
+    rng = np.random.default_rng(b * 10 + m)
+    x = rng.standard_normal((4, d))
+    assert np.allclose(harp.harp_rotate(x, [b] * m, blocks, precondition=False),
+                       H.wht(x), atol=1e-12)
+    s = 1.0 - 2.0 * rng.integers(0, 2, d)
+    eye = [np.broadcast_to(np.eye(b), (d // b, b, b)) for _ in range(m)]
+    assert np.allclose(harp.harp_rotate(x, [b] * m, eye, s=s, precondition=True),
+                       H.rht(x, s), atol=1e-12)
+    assert np.allclose(harp.harp_rotate(x, [b] * m, eye, precondition=False), x)
+
+
+def test_harp_permutation_blocks_at_real_shape():
+    """Identity blocks except one permutation block per stage, d = 4096,
+    radix 16: the output is the predicted permutation of rht(x), checked
+    position by position."""
+    rad = [16, 16, 16]
+    d = 4096
+    rng = np.random.default_rng(42)
+    s = 1.0 - 2.0 * rng.integers(0, 2, d)
+    blocks, perms, which = [], [], []
+    for t in range(3):
+        bl = np.broadcast_to(np.eye(16), (256, 16, 16)).copy()
+        c = int(rng.integers(0, 256))
+        p = rng.permutation(16)
+        bl[c] = np.eye(16)[p]             # out_sub[k] = in_sub[p[k]]
+        blocks.append(bl); perms.append(p); which.append(c)
+    x = rng.standard_normal((2, d))
+    got = harp.harp_rotate(x, rad, blocks, s=s, precondition=True)
+    z = H.rht(x, s)
+    for t in range(3):
+        nz = z.copy()
+        for i in range(d):
+            dg = digits(i, rad)
+            rest = [dd for u, dd in enumerate(dg) if u != t]
+            if undigits(rest, [16, 16]) == which[t]:
+                j = list(dg); j[t] = perms[t][dg[t]]
+                nz[:, i] = z[:, undigits(j, rad)]
+        z = nz
+    assert np.array_equal(got, z)
+
+
+def test_harp_orthogonal_norm_and_inverse():
+    rad = [8, 8, 8, 5, 2]
+    d = 5120
+    rng = np.random.default_rng(3)
+    blocks = []
+    for b in rad:
+        q, r = np.linalg.qr(rng.standard_normal((d // b, b, b)))
+        blocks.append(q)
+    x = rng.standard_normal((3, d))
+    y = harp.harp_rotate(x, rad, blocks, precondition=False)
+    assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-12)
+    z = y
+    for t in reversed(range(len(rad))):
+        z = z @ harp.stage_matrix(np.transpose(blocks[t], (0, 2, 1)), t, rad).T
+    assert np.allclose(z, x, atol=1e-12)
+
+
+def test_harp_schedule_golden():
+    for d, rad, ok in rows("harp_schedule.txt"):
+        d, rad, ok = int(d), ints(rad), bool(int(ok))
+        if ok:
+            harp.check_schedule(rad, d)
+        else:
+            with pytest.raises(ValueError):
+                harp.check_schedule(rad, d)
