@@ -1,0 +1,160 @@
+/*
+ * whtq.h -- C ABI of libwhtq, batched Walsh-Hadamard transforms for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Sources (cited by short key):
+ *   [HARP]  "HARP: Hadamard-Preconditioned Adaptive Rotation Processor for
+ *           Extreme LLM Quantization" (gist.science explainer), technical
+ *           summary: section 1 (randomized Hadamard transform: a fixed random
+ *           sign diagonal followed by the Hadamard transform, exactly
+ *           orthogonal, O(d log d)); 2.1 (mixed-radix schedule, prod b_t = d,
+ *           block-diagonal orthogonal stages on stride-permuted groups); 2.2
+ *           (B_{t,c} = Q_{t,c} G_{b_t}, G the normalised Sylvester Hadamard;
+ *           Theta = 0 gives back the fixed RHT); 2.4 (O(d log d) stages).
+ *   [QWHA]  "QWHA: Quantization-Aware Walsh-Hadamard Adaptation ..."
+ *           (gist.science explainer), section 2.1: Delta W = F H^-1, a single
+ *           transform on the input side, F sparse from values c and indices E,
+ *           +-1 kernel computed with additions and subtractions only.
+ *
+ * Conventions fixed by this library where the pages leave them open:
+ *   - Hn = H / sqrt(n), H the Sylvester matrix H[i][j] = (-1)^popcount(i & j)
+ *     (natural order, not sequency order).
+ *   - Sign diagonal S: bit j (LSB first) of uint32 word j / 32 set means
+ *     s_j = -1; one vector per layer, shared by every row.
+ *   - RHT forward y = Hn (S x); inverse x = S Hn y.
+ *   - Quantiser: per group of g consecutive transformed coordinates,
+ *     s = fp16_rne(max|y| / qmax) with qmax = 2^(b-1) - 1, q = rint(y / s)
+ *     (half to even; s = 0 gives q = 0), codes in [-qmax, qmax].
+ *   - Codes: row-major, each row a little-endian bit stream of n codes of
+ *     b bits (code i in bits [b*i, b*i + b), LSB first, two's complement);
+ *     row stride n*b/8 bytes.  Scales: IEEE fp16 bits, [rows][n/g].
+ *   - QWHA: F is [d_out x d_in] in CSR; Delta W = F Hn; y = (x Hn) F^T.
+ *   - HARP digits: i = sum_t i_t * prod_{u<t} b_u; stage t acts on digit t;
+ *     block index c = i with digit t removed (remaining digits in increasing
+ *     significance); a block maps out_sub[k] = sum_j B[k][j] in_sub[j].
+ *
+ * Common rules for every entry point:
+ *   - All pointers are device pointers owned by the caller, except
+ *     `radices` (host).  The library keeps no pointer after returning and
+ *     allocates no memory.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  WHTQ_OK means
+ *     the work was enqueued; faults surface at the caller's next
+ *     synchronisation.  Nothing is read back to the host.
+ *   - Every argument check runs before any HIP call, so an error status
+ *     means no work was enqueued.
+ *   - Matrices are row-major with the transform along the contiguous last
+ *     dimension; ld* are row strides in elements (>= the row length).
+ *   - Alignment: device base pointers must be 16-byte aligned and
+ *     ld * element_size a multiple of 16 bytes, unless a whole row is
+ *     shorter than 16 bytes (then element alignment suffices).  Violations
+ *     return WHTQ_EALIGN; there is no slower fallback path.
+ */
+#ifndef WHTQ_H
+#define WHTQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WHTQ_ABI_VERSION 1
+
+typedef enum {
+  WHTQ_OK = 0,
+  WHTQ_EINVAL = 1,       /* bad size, null pointer, bits/group/schedule out of rule */
+  WHTQ_EUNSUPPORTED = 2, /* valid request this build has no kernel for            */
+  WHTQ_EALIGN = 3,       /* pointer or row stride not 16-byte aligned              */
+  WHTQ_EHIP = 4          /* HIP runtime / launch failure, including no device      */
+} whtq_status;
+
+typedef enum { WHTQ_F32 = 0, WHTQ_BF16 = 1, WHTQ_F16 = 2 } whtq_dtype;
+
+typedef enum {
+  WHTQ_SIGN_NONE = 0,   /* y = Hn x        */
+  WHTQ_SIGN_BEFORE = 1, /* y = Hn (S x)    (forward RHT) */
+  WHTQ_SIGN_AFTER = 2   /* y = S (Hn x)    (inverse RHT) */
+} whtq_sign_mode;
+
+/*
+ * wht_batched -- orthonormal (or raw) Sylvester WHT of `rows` rows of length
+ * n.  [QWHA] 2.1 (+-1 kernel, add/subtract-only fast transform); [HARP] 1
+ * (RHT = sign diagonal then Hadamard).
+ *   x [rows][ldx] in x_dtype; y [rows][ldy] in y_dtype.  x == y (exact alias,
+ *   equal ld and dtype) is allowed; partial overlap is undefined.
+ *   n: power of two in [2, 8192].
+ *   dtypes: (f32->f32), (bf16->bf16), (f16->f16), (bf16->f32), (f16->f32).
+ *   sign_bits: uint32[ceil(n/32)], required unless sign_mode is NONE.
+ *   normalize: 1 -> Hn = H / sqrt(n); 0 -> the raw +-1 product.
+ * Arithmetic: fp32 throughout; 16-bit outputs are rounded once (nearest even).
+ */
+whtq_status wht_batched(const void* x, whtq_dtype x_dtype, void* y, whtq_dtype y_dtype,
+                        int64_t rows, int64_t n, int64_t ldx, int64_t ldy,
+                        const uint32_t* sign_bits, int sign_mode, int normalize, void* stream);
+
+/*
+ * rht_quantize_rtn -- y = Hn (S w) per row, then per-group absmax RTN to
+ * signed b-bit codes with fp16 scales.  [HARP] 1 (RHT as incoherence
+ * processing before low-bit quantisation, 2-4 bits).
+ *   w [rows][ldw] in w_dtype (bf16, f32 or f16).
+ *   n: power of two in [64, 8192].  bits: 2, 3 or 4.  group: power of two in
+ *   [8, 256] dividing n.  sign_bits: uint32[n/32] or NULL (all +1).
+ *   codes: uint8 [rows][n*bits/8] (written).  scales: uint16 fp16 bits
+ *   [rows][n/group] (written).
+ */
+whtq_status rht_quantize_rtn(const void* w, whtq_dtype w_dtype, int64_t rows, int64_t n, int64_t ldw,
+                             const uint32_t* sign_bits, int bits, int group,
+                             uint8_t* codes, uint16_t* scales, void* stream);
+
+/*
+ * rht_dequantize_inverse -- out = S Hn (q * s): unpack codes, scale by the
+ * group's fp16 scale, inverse RHT.  Inverse of rht_quantize_rtn up to the
+ * quantisation error ([HARP] 1: the transform is exactly orthogonal).
+ *   codes / scales as written by rht_quantize_rtn with the same n, bits,
+ *   group.  out [rows][ldo] in out_dtype (bf16, f32 or f16).
+ */
+whtq_status rht_dequantize_inverse(const uint8_t* codes, const uint16_t* scales, int64_t rows, int64_t n,
+                                   const uint32_t* sign_bits, int bits, int group,
+                                   void* out, whtq_dtype out_dtype, int64_t ldo, void* stream);
+
+/*
+ * qwha_adapter_forward -- y[t][o] = sum_{k in row o of F} F[o][k] * (Hn x_t)[k],
+ * the QWHA adapter output x Delta W^T with Delta W = F Hn ([QWHA] 2.1).
+ *   x [tokens][ldx] bf16; y [tokens][ldy] bf16; d_in = 4096 in this build.
+ *   F: CSR [d_out x d_in]: row_ptr int32[d_out + 1] (row_ptr[0] = 0,
+ *   row_ptr[d_out] = nnz, non-decreasing), col_idx int32[nnz] in [0, d_in),
+ *   vals[nnz] in val_dtype (bf16 or f32).  The library does not read the CSR
+ *   on the host: a malformed CSR gives undefined results.
+ *   d_out in [1, 4096].  Accumulation in fp32; Hn x is kept on chip in fp16
+ *   with a per-token power-of-two scale.
+ */
+whtq_status qwha_adapter_forward(const void* x, whtq_dtype x_dtype, int64_t tokens, int64_t d_in,
+                                 int64_t ldx, const int32_t* row_ptr, const int32_t* col_idx,
+                                 const void* vals, whtq_dtype val_dtype, int64_t d_out, int64_t nnz,
+                                 void* y, whtq_dtype y_dtype, int64_t ldy, void* stream);
+
+/*
+ * harp_rotate -- y = Stage_{m-1}( ... Stage_0( P x ) ), P = Hn S if
+ * precondition else I; stage t applies d / b_t independent b_t x b_t blocks
+ * along digit t ([HARP] 2.1, 2.2).
+ *   x, y [tokens][ld] in dtype (bf16 or f32); x == y not allowed.
+ *   radices: HOST int32[n_stages], each >= 2, product == d.  This build runs
+ *   d = 4096 with radices (16, 16, 16).
+ *   blocks: device fp32, stage-major, stage t as [d / b_t][b_t][b_t]
+ *   row-major (B[k][j] at k * b_t + j).  Block stages multiply bf16-rounded
+ *   operands with fp32 accumulation (MFMA).
+ *   sign_bits: uint32[d/32] or NULL (all +1); used when precondition != 0.
+ */
+whtq_status harp_rotate(const void* x, void* y, whtq_dtype dtype, int64_t tokens, int64_t d,
+                        int64_t ldx, int64_t ldy, const uint32_t* sign_bits, int precondition,
+                        const int32_t* radices, int n_stages, const float* blocks, void* stream);
+
+const char* whtq_status_string(whtq_status s);
+int whtq_last_hip_error(void); /* hipError_t behind this thread's last WHTQ_EHIP */
+int whtq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WHTQ_H */

@@ -1,0 +1,139 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry
+point include/whtq.h declares, and rejects bad arguments with the documented
+status before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "whtq.h")
+
+OK, EINVAL, EUNSUP, EALIGN, EHIP = 0, 1, 2, 3, 4
+P = ctypes.c_void_p(0x10000)       # 16-byte aligned stand-in, never dereferenced
+P_MIS = ctypes.c_void_p(0x10004)   # misaligned stand-in
+NULL = ctypes.c_void_p(0)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from wht_adapters_amd import whtq
+    return whtq.raw()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:whtq_status|const char\*|int)\s+(\w+)\s*\(", text, flags=re.M)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) >= {"wht_batched", "rht_quantize_rtn", "rht_dequantize_inverse",
+                          "qwha_adapter_forward", "harp_rotate", "whtq_status_string",
+                          "whtq_last_hip_error", "whtq_abi_version"}
+    for nm in names:
+        assert hasattr(lib, nm), nm
+
+
+def test_version_and_strings(lib):
+    assert lib.whtq_abi_version() == 1
+    for s in range(5):
+        assert lib.whtq_status_string(s)
+    assert b"unknown" in lib.whtq_status_string(99)
+
+
+def wht(lib, x=P, xd=0, y=P, yd=0, rows=4, n=64, ldx=64, ldy=64, sb=NULL, mode=0, norm=1):
+    return lib.wht_batched(x, xd, y, yd, rows, n, ldx, ldy, sb, mode, norm, NULL)
+
+
+def test_wht_validation(lib):
+    assert wht(lib, n=12, ldx=12, ldy=12) == EUNSUP           # not a power of two
+    assert wht(lib, n=16384, ldx=16384, ldy=16384) == EUNSUP   # beyond 8192
+    assert wht(lib, ldx=32) == EINVAL                          # ld < n
+    assert wht(lib, rows=-1) == EINVAL
+    assert wht(lib, xd=7) == EINVAL                            # bad dtype
+    assert wht(lib, xd=0, yd=1) == EUNSUP                      # f32 -> bf16 not offered
+    assert wht(lib, mode=1) == EINVAL                          # signs required
+    assert wht(lib, mode=3, sb=P) == EINVAL
+    assert wht(lib, norm=2) == EINVAL
+    assert wht(lib, x=NULL) == EINVAL
+    assert wht(lib, x=P_MIS) == EALIGN
+    assert wht(lib, ldx=65, ldy=64, y=ctypes.c_void_p(0x20000)) == EALIGN  # 65*4 B rows
+    assert wht(lib, ldx=64, ldy=72) == EINVAL                  # exact alias needs equal ld
+    assert wht(lib, xd=1, yd=0, x=P, y=P) == EINVAL            # alias with different dtypes
+    assert wht(lib, rows=0) == OK                              # empty batch: nothing to do
+
+
+def q(lib, w=P, wd=1, rows=4, n=256, ldw=256, sb=NULL, bits=4, g=64, c=P, s=P):
+    return lib.rht_quantize_rtn(w, wd, rows, n, ldw, sb, bits, g, c, s, NULL)
+
+
+def dq(lib, c=P, s=P, rows=4, n=256, sb=NULL, bits=4, g=64, o=P, od=1, ldo=256):
+    return lib.rht_dequantize_inverse(c, s, rows, n, sb, bits, g, o, od, ldo, NULL)
+
+
+def test_quant_validation(lib):
+    for f in (q, dq):
+        assert f(lib, bits=5) == EINVAL
+        assert f(lib, bits=1) == EINVAL
+        assert f(lib, g=48) == EINVAL          # does not divide 256
+        assert f(lib, g=4) == EINVAL           # below 8
+        assert f(lib, g=512, n=1024) == EUNSUP if f is q else True
+        assert f(lib, n=32, g=8) == EUNSUP     # n < 64
+        assert f(lib, n=384, g=128) == EUNSUP  # not a power of two
+        assert f(lib, rows=-2) == EINVAL
+        assert f(lib, rows=0) == OK
+    assert q(lib, ldw=128) == EINVAL
+    assert q(lib, w=P_MIS) == EALIGN
+    assert q(lib, c=P_MIS) == EALIGN
+    assert q(lib, sb=ctypes.c_void_p(0x10002)) == EALIGN
+    assert q(lib, c=NULL) == EINVAL
+    assert dq(lib, o=NULL) == EINVAL
+    assert dq(lib, ldo=100) == EINVAL
+
+
+def qw(lib, x=P, xd=1, tokens=8, d_in=4096, ldx=4096, rp=P, ci=P, v=P, vd=1, d_out=4096, nnz=100,
+       y=P, yd=1, ldy=4096):
+    return lib.qwha_adapter_forward(x, xd, tokens, d_in, ldx, rp, ci, v, vd, d_out, nnz, y, yd, ldy, NULL)
+
+
+def test_qwha_validation(lib):
+    assert qw(lib, ldx=100) == EINVAL
+    assert qw(lib, rp=NULL) == EINVAL
+    assert qw(lib, nnz=4096 * 4096 + 1) == EINVAL
+    assert qw(lib, d_in=3000, ldx=3000) == EUNSUP
+    assert qw(lib, d_in=2048, ldx=2048) == EUNSUP
+    assert qw(lib, xd=0) == EUNSUP
+    assert qw(lib, vd=2) == EUNSUP
+    assert qw(lib, x=P_MIS) == EALIGN
+    assert qw(lib, tokens=0) == OK
+
+
+def hp(lib, x=P, y=ctypes.c_void_p(0x20000), dt=1, tokens=8, d=4096, ldx=4096, ldy=4096, sb=NULL,
+       pre=1, rad=(16, 16, 16), blocks=P):
+    arr = (ctypes.c_int32 * len(rad))(*rad)
+    return lib.harp_rotate(x, y, dt, tokens, d, ldx, ldy, sb, pre, arr, len(rad), blocks, NULL)
+
+
+def test_harp_validation(lib):
+    assert hp(lib, rad=(16, 16, 8)) == EINVAL              # product != d
+    assert hp(lib, rad=(16, 16, 16, 1)) == EINVAL          # radix < 2
+    assert hp(lib, d=5120, ldx=5120, ldy=5120, rad=(8, 8, 8, 5, 2)) == EUNSUP  # valid schedule, no kernel
+    assert hp(lib, rad=(64, 64)) == EUNSUP
+    assert hp(lib, y=P) == EINVAL                          # in place not allowed
+    assert hp(lib, pre=3) == EINVAL
+    assert hp(lib, blocks=NULL) == EINVAL
+    assert hp(lib, dt=2) == EUNSUP
+    assert hp(lib, x=P_MIS) == EALIGN
+    assert hp(lib, tokens=0) == OK
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="needs a host without a GPU")
+def test_valid_call_without_device_is_ehip(lib):
+    assert wht(lib) == EHIP
+    assert lib.whtq_last_hip_error() != 0
+    assert q(lib) == EHIP and dq(lib) == EHIP
+    assert qw(lib) == EHIP and hp(lib) == EHIP

@@ -1,0 +1,142 @@
+"""GPU parity of rht_quantize_rtn / rht_dequantize_inverse against the
+oracle: codes bit-exact up to the boundary exemption, scales bit-exact up to
+the fp16-midpoint exemption, dequantised floats within tolerance."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import hadamard as H, rtn, compare
+from wht_adapters_amd import synth
+from gpu_util import dev, mask_dev, host64, codes_host, scales_host
+
+pytestmark = pytest.mark.gpu
+
+
+def W():
+    from wht_adapters_amd import whtq
+    return whtq
+
+
+def check_quant(w_dev, mask, bits, g, rows_sel=None):
+    """Quantise on the GPU and compare (optionally only rows_sel) with the oracle."""
+    n = w_dev.shape[1]
+    codes, scales = W().rht_quantize_rtn(w_dev, mask_dev(mask), bits, g)
+    torch.cuda.synchronize()
+    w64 = host64(w_dev if rows_sel is None else w_dev[rows_sel])
+    c = codes_host(codes if rows_sel is None else codes[rows_sel])
+    sc = scales_host(scales if rows_sel is None else scales[rows_sel])
+    s = H.signs_from_bits(mask, n)
+    y = H.rht(w64, s)
+    q_or, s16, v, s_pre = rtn.quantize_rtn(y, bits, g)
+    q_dev = rtn.unpack_codes(c, bits, n)
+    rep = compare.compare_quant(q_dev, sc, y, s16, q_or, v, s_pre, bits, g)
+    assert rep["ok"], rep
+    return codes, scales, rep
+
+
+@pytest.mark.parametrize("logn", range(6, 14))
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_quant_all_sizes(logn, bits):
+    n = 1 << logn
+    rng = np.random.default_rng(logn * 10 + bits)
+    w = dev(0.02 * rng.standard_t(3, size=(21, n)), torch.bfloat16)
+    mask = synth.sign_bits_to_mask(rng.integers(0, 2, n))
+    for g in sorted({8, 32, 64, min(128, n), min(256, n)}):
+        check_quant(w, mask, bits, g)
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.float16])
+def test_quant_other_input_dtypes(dt):
+    rng = np.random.default_rng(5)
+    n = 1024
+    w = dev(rng.standard_normal((33, n)), dt)
+    mask = synth.sign_bits_to_mask(rng.integers(0, 2, n))
+    check_quant(w, mask, 4, 128)
+    check_quant(w, mask, 2, 64)
+
+
+def test_quant_no_signs_and_zero_rows():
+    n = 512
+    w = torch.zeros((4, n), dtype=torch.bfloat16, device="cuda:0")
+    w[1] = torch.linspace(-1, 1, n)
+    codes, scales = W().rht_quantize_rtn(w, None, 4, 64)
+    torch.cuda.synchronize()
+    assert torch.all(codes[0] == 0) and torch.all(scales[0] == 0)
+    q_or, s16, v, s_pre = rtn.quantize_rtn(H.wht(host64(w)), 4, 64)
+    rep = compare.compare_quant(rtn.unpack_codes(codes_host(codes), 4, n), scales_host(scales),
+                                H.wht(host64(w)), s16, q_or, v, s_pre, 4, 64)
+    assert rep["ok"], rep
+
+
+@pytest.mark.parametrize("bits,g,n", [(4, 128, 4096), (2, 64, 8192), (3, 32, 1024), (4, 8, 256)])
+def test_grid_constructed_roundtrip(bits, g, n):
+    """Codes and scales fixed first; x = irht(q*s) in fp64 rounded to fp32.
+    The GPU must return exactly q, s (up to the scale exemption), and its
+    dequant-inverse must give back x."""
+    rng = np.random.default_rng(100 + bits + n)
+    rows = 16
+    qm = (1 << (bits - 1)) - 1
+    q = rng.integers(-qm, qm + 1, size=(rows, n // g, g))
+    pos = rng.integers(0, g, size=(rows, n // g))
+    np.put_along_axis(q, pos[:, :, None], (rng.choice([-1, 1], (rows, n // g)) * qm)[:, :, None], 2)
+    s16 = np.exp(rng.uniform(-5, 0, size=(rows, n // g))).astype(np.float16)
+    mask = synth.sign_bits_to_mask(rng.integers(0, 2, n))
+    sgn = H.signs_from_bits(mask, n)
+    x = H.irht((q * s16.astype(np.float64)[:, :, None]).reshape(rows, n), sgn).astype(np.float32)
+    codes, scales = W().rht_quantize_rtn(dev(x), mask_dev(mask), bits, g)
+    torch.cuda.synchronize()
+    q_dev = rtn.unpack_codes(codes_host(codes), bits, n)
+    assert np.array_equal(q_dev, q.reshape(rows, n))
+    assert np.array_equal(scales_host(scales).view(np.uint16), s16.view(np.uint16))
+    back = W().rht_dequantize_inverse(codes, scales, mask_dev(mask), bits, g, n, out_dtype=torch.float32)
+    assert compare.float_err(host64(back), x.astype(np.float64))[0] <= 1e-5
+
+
+@pytest.mark.parametrize("logn", range(6, 14))
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("odt", [torch.float32, torch.bfloat16])
+def test_dequant_inverse_parity(logn, bits, odt):
+    n = 1 << logn
+    rng = np.random.default_rng(logn + 50 * bits)
+    w = dev(0.02 * rng.standard_t(3, size=(11, n)), torch.bfloat16)
+    mask = synth.sign_bits_to_mask(rng.integers(0, 2, n))
+    g = min(128, n)
+    codes, scales = W().rht_quantize_rtn(w, mask_dev(mask), bits, g)
+    out = W().rht_dequantize_inverse(codes, scales, mask_dev(mask), bits, g, n, out_dtype=odt)
+    want = rtn.dequantize_inverse(codes_host(codes), scales_host(scales), H.signs_from_bits(mask, n),
+                                  bits, g, n)
+    tol = 1e-5 if odt == torch.float32 else 2e-2
+    assert compare.float_err(host64(out), want)[0] <= tol
+
+
+def test_full_config_int4_g128_4096():
+    """4096 x 4096 Student-t weights with outlier columns, INT4, g = 128."""
+    d = synth.rht_int4_g128()
+    w = dev(d["w"])
+    codes, scales, rep = check_quant(w, d["signs"], 4, 128)
+    print("int4 g128 4096x4096:", rep)
+    out = W().rht_dequantize_inverse(codes, scales, mask_dev(d["signs"]), 4, 128, 4096)
+    sel = np.arange(0, 4096, 16)
+    want = rtn.dequantize_inverse(codes_host(codes[sel]), scales_host(scales[sel]),
+                                  H.signs_from_bits(d["signs"], 4096), 4, 128, 4096)
+    assert compare.float_err(host64(out[sel]), want)[0] <= 2e-2
+
+
+def test_full_config_int2_g64_28672x8192_sampled():
+    """28672 x 8192 at full size on the GPU; the oracle checks 192 sampled rows
+    (first, last, ragged middle) for codes, scales and the inverse."""
+    d = synth.rht_int2_g64()
+    w = dev(d["w"])
+    sel = np.r_[0:64, 14000:14064, 28608:28672]
+    codes, scales, rep = check_quant(w, d["signs"], 2, 64, rows_sel=sel)
+    print("int2 g64 28672x8192 (sampled):", rep)
+    out = W().rht_dequantize_inverse(codes, scales, mask_dev(d["signs"]), 2, 64, 8192)
+    want = rtn.dequantize_inverse(codes_host(codes[sel]), scales_host(scales[sel]),
+                                  H.signs_from_bits(d["signs"], 8192), 2, 64, 8192)
+    assert compare.float_err(host64(out[sel]), want)[0] <= 2e-2
+    # whole-matrix property: the RTN error bound |y - q s| <= s/2 holds through the
+    # orthogonal inverse as ||w - w_hat|| <= sqrt(sum_g g * s_g^2 / 4)
+    w32 = w.float()
+    err = (w32 - out.float()).pow(2).sum(dim=1)
+    bound = (scales.float().pow(2) * 64 / 4).sum(dim=1)
+    assert torch.all(err <= bound * (1 + 1e-2) + 1e-6)

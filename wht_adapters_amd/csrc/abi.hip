@@ -1,0 +1,231 @@
+// C ABI of libwhtq: argument validation, then dispatch to the kernels.
+// Every check runs before the first HIP call, so an error status means
+// nothing was enqueued.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+#include <mutex>
+
+#include "../../include/whtq.h"
+
+namespace whtq {
+
+hipError_t launch_wht(int logn, int din, int dout, const void* x, void* y, int64_t rows, int64_t ldx,
+                      int64_t ldy, const uint32_t* sbits, int sign_mode, float scale, hipStream_t s);
+hipError_t launch_rht_quant(int logn, int din, int bits, int logg, const void* w, int64_t rows,
+                            int64_t ldw, const uint32_t* sb, uint8_t* codes, uint16_t* scales,
+                            hipStream_t s);
+hipError_t launch_rht_dequant(int logn, int dout, int bits, int logg, const uint8_t* codes,
+                              const uint16_t* scales, int64_t rows, const uint32_t* sb, void* out,
+                              int64_t ldo, hipStream_t s);
+hipError_t launch_qwha(const void* x, int64_t tokens, int64_t ldx, const int32_t* row_ptr,
+                       const int32_t* col_idx, const void* vals, int val_dt, int64_t d_out,
+                       void* y, int64_t ldy, hipStream_t s);
+hipError_t launch_harp(const void* x, void* y, int dt, int64_t tokens, int64_t ldx, int64_t ldy,
+                       const uint32_t* sbits, int precondition, const float* blocks, hipStream_t s);
+
+static thread_local int g_last_hip = 0;
+
+static constexpr int kMaxDevices = 64;
+static int g_cu[kMaxDevices];
+static std::once_flag g_cu_once[kMaxDevices];
+
+int device_cu_count(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return 256;
+  std::call_once(g_cu_once[dev], [dev] {
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu < 1)
+      cu = 256;
+    g_cu[dev] = cu;
+  });
+  return g_cu[dev];
+}
+
+}  // namespace whtq
+
+using namespace whtq;
+
+static whtq_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return WHTQ_OK;
+  g_last_hip = (int)e;
+  return WHTQ_EHIP;
+}
+
+// A device must be present and current before anything is launched.
+static whtq_status need_device() {
+  int n = 0;
+  hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess) return hip_status(e);
+  if (n < 1) return hip_status(hipErrorNoDevice);
+  return WHTQ_OK;
+}
+
+static int ilog2_pow2(int64_t n) {
+  if (n < 1 || (n & (n - 1))) return -1;
+  int l = 0;
+  while ((int64_t(1) << l) < n) ++l;
+  return l;
+}
+
+static int dt_bytes(int dt) { return dt == WHTQ_F32 ? 4 : 2; }
+static bool dt_valid(int dt) { return dt == WHTQ_F32 || dt == WHTQ_BF16 || dt == WHTQ_F16; }
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Row-matrix alignment rule: 16-byte base and row stride unless a row is
+// shorter than 16 bytes, then element alignment.
+static bool rows_aligned(const void* p, int64_t n, int64_t ld, int esz) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  if (n * esz >= 16) return (a & 15u) == 0 && ((ld * esz) & 15) == 0;
+  return (a % (uintptr_t)esz) == 0;
+}
+
+extern "C" {
+
+int whtq_abi_version(void) { return WHTQ_ABI_VERSION; }
+
+int whtq_last_hip_error(void) { return g_last_hip; }
+
+const char* whtq_status_string(whtq_status s) {
+  switch (s) {
+    case WHTQ_OK: return "ok";
+    case WHTQ_EINVAL: return "invalid argument";
+    case WHTQ_EUNSUPPORTED: return "unsupported configuration";
+    case WHTQ_EALIGN: return "misaligned pointer or row stride";
+    case WHTQ_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+whtq_status wht_batched(const void* x, whtq_dtype x_dtype, void* y, whtq_dtype y_dtype, int64_t rows,
+                        int64_t n, int64_t ldx, int64_t ldy, const uint32_t* sign_bits, int sign_mode,
+                        int normalize, void* stream) {
+  if (!dt_valid(x_dtype) || !dt_valid(y_dtype)) return WHTQ_EINVAL;
+  if (rows < 0 || n < 1 || ldx < n || ldy < n) return WHTQ_EINVAL;
+  if (sign_mode < WHTQ_SIGN_NONE || sign_mode > WHTQ_SIGN_AFTER) return WHTQ_EINVAL;
+  if (sign_mode != WHTQ_SIGN_NONE && !sign_bits) return WHTQ_EINVAL;
+  if (normalize != 0 && normalize != 1) return WHTQ_EINVAL;
+  if (rows > 0 && (!x || !y)) return WHTQ_EINVAL;
+  const int logn = ilog2_pow2(n);
+  if (logn < 1 || logn > 13) return WHTQ_EUNSUPPORTED;
+  const bool same = x_dtype == y_dtype;
+  const bool widen = y_dtype == WHTQ_F32 && x_dtype != WHTQ_F32;
+  if (!same && !widen) return WHTQ_EUNSUPPORTED;
+  if (x == y && (!same || ldx != ldy)) return WHTQ_EINVAL;
+  if (!rows_aligned(x, n, ldx, dt_bytes(x_dtype)) || !rows_aligned(y, n, ldy, dt_bytes(y_dtype)))
+    return WHTQ_EALIGN;
+  if (sign_bits && (reinterpret_cast<uintptr_t>(sign_bits) & 3u)) return WHTQ_EALIGN;
+  if (rows == 0) return WHTQ_OK;
+  whtq_status st = need_device();
+  if (st != WHTQ_OK) return st;
+  const float scale = normalize ? (float)(1.0 / std::sqrt((double)n)) : 1.0f;
+  return hip_status(launch_wht(logn, x_dtype, y_dtype, x, y, rows, ldx, ldy, sign_bits, sign_mode, scale,
+                               (hipStream_t)stream));
+}
+
+static whtq_status check_quant_shape(int64_t rows, int64_t n, int bits, int group, int* logn, int* logg) {
+  if (rows < 0 || n < 1) return WHTQ_EINVAL;
+  if (bits < 2 || bits > 4) return WHTQ_EINVAL;
+  if (group < 1 || n % group) return WHTQ_EINVAL;
+  *logn = ilog2_pow2(n);
+  if (*logn < 0) return WHTQ_EUNSUPPORTED;
+  *logg = ilog2_pow2(group);
+  if (*logg < 3) return WHTQ_EINVAL;  // group must be a power of two >= 8 (it divides n)
+  if (*logn < 6 || *logn > 13 || *logg > 8) return WHTQ_EUNSUPPORTED;
+  return WHTQ_OK;
+}
+
+whtq_status rht_quantize_rtn(const void* w, whtq_dtype w_dtype, int64_t rows, int64_t n, int64_t ldw,
+                             const uint32_t* sign_bits, int bits, int group, uint8_t* codes,
+                             uint16_t* scales, void* stream) {
+  if (!dt_valid(w_dtype)) return WHTQ_EINVAL;
+  int logn = 0, logg = 0;
+  whtq_status st = check_quant_shape(rows, n, bits, group, &logn, &logg);
+  if (st != WHTQ_OK) return st;
+  if (ldw < n) return WHTQ_EINVAL;
+  if (rows > 0 && (!w || !codes || !scales)) return WHTQ_EINVAL;
+  if (!rows_aligned(w, n, ldw, dt_bytes(w_dtype)) || !aligned16(codes) || !aligned16(scales))
+    return WHTQ_EALIGN;
+  if (sign_bits && (reinterpret_cast<uintptr_t>(sign_bits) & 3u)) return WHTQ_EALIGN;
+  if (rows == 0) return WHTQ_OK;
+  st = need_device();
+  if (st != WHTQ_OK) return st;
+  return hip_status(launch_rht_quant(logn, w_dtype, bits, logg, w, rows, ldw, sign_bits, codes, scales,
+                                     (hipStream_t)stream));
+}
+
+whtq_status rht_dequantize_inverse(const uint8_t* codes, const uint16_t* scales, int64_t rows, int64_t n,
+                                   const uint32_t* sign_bits, int bits, int group, void* out,
+                                   whtq_dtype out_dtype, int64_t ldo, void* stream) {
+  if (!dt_valid(out_dtype)) return WHTQ_EINVAL;
+  int logn = 0, logg = 0;
+  whtq_status st = check_quant_shape(rows, n, bits, group, &logn, &logg);
+  if (st != WHTQ_OK) return st;
+  if (ldo < n) return WHTQ_EINVAL;
+  if (rows > 0 && (!codes || !scales || !out)) return WHTQ_EINVAL;
+  if (!rows_aligned(out, n, ldo, dt_bytes(out_dtype)) || !aligned16(codes) || !aligned16(scales))
+    return WHTQ_EALIGN;
+  if (sign_bits && (reinterpret_cast<uintptr_t>(sign_bits) & 3u)) return WHTQ_EALIGN;
+  if (rows == 0) return WHTQ_OK;
+  st = need_device();
+  if (st != WHTQ_OK) return st;
+  return hip_status(launch_rht_dequant(logn, out_dtype, bits, logg, codes, scales, rows, sign_bits, out, ldo,
+                                       (hipStream_t)stream));
+}
+
+whtq_status qwha_adapter_forward(const void* x, whtq_dtype x_dtype, int64_t tokens, int64_t d_in,
+                                 int64_t ldx, const int32_t* row_ptr, const int32_t* col_idx,
+                                 const void* vals, whtq_dtype val_dtype, int64_t d_out, int64_t nnz,
+                                 void* y, whtq_dtype y_dtype, int64_t ldy, void* stream) {
+  if (!dt_valid(x_dtype) || !dt_valid(val_dtype) || !dt_valid(y_dtype)) return WHTQ_EINVAL;
+  if (tokens < 0 || d_in < 1 || d_out < 1 || nnz < 0 || ldx < d_in || ldy < d_out) return WHTQ_EINVAL;
+  if (nnz > d_in * d_out) return WHTQ_EINVAL;
+  if (!row_ptr || (nnz > 0 && (!col_idx || !vals))) return WHTQ_EINVAL;
+  if (tokens > 0 && (!x || !y)) return WHTQ_EINVAL;
+  if (ilog2_pow2(d_in) < 0) return WHTQ_EUNSUPPORTED;
+  if (d_in != 4096 || d_out > 4096) return WHTQ_EUNSUPPORTED;
+  if (x_dtype != WHTQ_BF16 || y_dtype != WHTQ_BF16) return WHTQ_EUNSUPPORTED;
+  if (val_dtype != WHTQ_BF16 && val_dtype != WHTQ_F32) return WHTQ_EUNSUPPORTED;
+  if (!rows_aligned(x, d_in, ldx, 2) || !rows_aligned(y, d_out, ldy, 2)) return WHTQ_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(row_ptr) & 3u) || (reinterpret_cast<uintptr_t>(col_idx) & 3u) ||
+      (reinterpret_cast<uintptr_t>(vals) % (uintptr_t)dt_bytes(val_dtype)))
+    return WHTQ_EALIGN;
+  if (d_out % 8) return WHTQ_EUNSUPPORTED;
+  if (tokens == 0) return WHTQ_OK;
+  whtq_status st = need_device();
+  if (st != WHTQ_OK) return st;
+  return hip_status(launch_qwha(x, tokens, ldx, row_ptr, col_idx, vals, val_dtype, d_out, y, ldy,
+                                (hipStream_t)stream));
+}
+
+whtq_status harp_rotate(const void* x, void* y, whtq_dtype dtype, int64_t tokens, int64_t d, int64_t ldx,
+                        int64_t ldy, const uint32_t* sign_bits, int precondition, const int32_t* radices,
+                        int n_stages, const float* blocks, void* stream) {
+  if (!dt_valid(dtype)) return WHTQ_EINVAL;
+  if (tokens < 0 || d < 1 || ldx < d || ldy < d) return WHTQ_EINVAL;
+  if (!radices || n_stages < 1 || n_stages > 64 || !blocks) return WHTQ_EINVAL;
+  if (precondition != 0 && precondition != 1) return WHTQ_EINVAL;
+  int64_t prod = 1;
+  for (int t = 0; t < n_stages; ++t) {
+    if (radices[t] < 2) return WHTQ_EINVAL;
+    prod *= radices[t];
+    if (prod > d) return WHTQ_EINVAL;
+  }
+  if (prod != d) return WHTQ_EINVAL;
+  if (tokens > 0 && (!x || !y)) return WHTQ_EINVAL;
+  if (tokens > 0 && x == y) return WHTQ_EINVAL;
+  if (d != 4096 || n_stages != 3 || radices[0] != 16 || radices[1] != 16 || radices[2] != 16)
+    return WHTQ_EUNSUPPORTED;
+  if (dtype != WHTQ_BF16 && dtype != WHTQ_F32) return WHTQ_EUNSUPPORTED;
+  const int esz = dt_bytes(dtype);
+  if (!rows_aligned(x, d, ldx, esz) || !rows_aligned(y, d, ldy, esz) || !aligned16(blocks)) return WHTQ_EALIGN;
+  if (sign_bits && (reinterpret_cast<uintptr_t>(sign_bits) & 3u)) return WHTQ_EALIGN;
+  if (tokens == 0) return WHTQ_OK;
+  whtq_status st = need_device();
+  if (st != WHTQ_OK) return st;
+  return hip_status(launch_harp(x, y, dtype, tokens, ldx, ldy, sign_bits, precondition, blocks,
+                                (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,201 @@
+"""ctypes binding over libwhtq.so (C ABI in include/whtq.h).
+
+Argument marshalling only: tensors are checked for device, dtype, layout and
+shape, their pointers and the current HIP stream are handed to the library,
+and every step of the computation runs in the library's HIP kernels.  There
+is no CPU fallback: importing this module fails if the library is missing.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.environ.get("WHTQ_LIB", os.path.join(_HERE, "libwhtq.so"))
+
+if not os.path.exists(lib_path):
+    raise ImportError(
+        f"libwhtq.so not found at {lib_path}; build it with `python -m wht_adapters_amd.build`")
+_lib = ctypes.CDLL(lib_path)
+
+_i64, _int, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+
+_SIG = {
+    "wht_batched": [_vp, _int, _vp, _int, _i64, _i64, _i64, _i64, _vp, _int, _int, _vp],
+    "rht_quantize_rtn": [_vp, _int, _i64, _i64, _i64, _vp, _int, _int, _vp, _vp, _vp],
+    "rht_dequantize_inverse": [_vp, _vp, _i64, _i64, _vp, _int, _int, _vp, _int, _i64, _vp],
+    "qwha_adapter_forward": [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _int, _i64, _i64, _vp, _int,
+                             _i64, _vp],
+    "harp_rotate": [_vp, _vp, _int, _i64, _i64, _i64, _i64, _vp, _int, _vp, _int, _vp, _vp],
+}
+for _name, _args in _SIG.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = _int
+_lib.whtq_status_string.argtypes = [_int]
+_lib.whtq_status_string.restype = ctypes.c_char_p
+_lib.whtq_last_hip_error.restype = _int
+_lib.whtq_abi_version.restype = _int
+
+F32, BF16, F16 = 0, 1, 2
+_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+SIGN_NONE, SIGN_BEFORE, SIGN_AFTER = 0, 1, 2
+_SIGN_MODES = {"none": SIGN_NONE, "before": SIGN_BEFORE, "after": SIGN_AFTER}
+
+
+class WhtqError(RuntimeError):
+    def __init__(self, fn, status):
+        msg = _lib.whtq_status_string(status).decode()
+        if status == 4:
+            msg += f" (hipError {_lib.whtq_last_hip_error()})"
+        super().__init__(f"{fn}: {msg} [status {status}]")
+        self.status = status
+
+
+def abi_version():
+    return _lib.whtq_abi_version()
+
+
+def raw():
+    """The ctypes library handle (for callers that marshal pointers themselves)."""
+    return _lib
+
+
+def _check(fn, status):
+    if status != 0:
+        raise WhtqError(fn, status)
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need_cuda(name, t):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def _rows_ld(name, t):
+    """(rows, n, ld) of a 2-D tensor with unit stride along the last dim."""
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with a contiguous last dimension")
+    rows, n = t.shape
+    # a single row's stride is meaningless (torch may report 0 or 1 for it)
+    return rows, n, (t.stride(0) if rows > 1 else n)
+
+
+def _sign_ptr(signs, n, device):
+    if signs is None:
+        return ctypes.c_void_p(0)
+    _need_cuda("signs", signs)
+    if signs.dtype not in (torch.int32, torch.uint32) or signs.numel() * 32 < n or not signs.is_contiguous():
+        raise ValueError("signs must be a contiguous int32/uint32 bitmask of ceil(n/32) words")
+    if signs.device != device:
+        raise ValueError("signs must be on the same device")
+    return _ptr(signs)
+
+
+def wht_batched(x, out=None, *, signs=None, sign_mode="none", normalize=True, out_dtype=None):
+    """y = Hn(S x) ('before'), Hn x ('none') or S Hn x ('after') along the last dim."""
+    _need_cuda("x", x)
+    rows, n, ldx = _rows_ld("x", x)
+    if out is None:
+        out = torch.empty((rows, n), dtype=out_dtype or x.dtype, device=x.device)
+    _need_cuda("out", out)
+    r2, n2, ldy = _rows_ld("out", out)
+    if (r2, n2) != (rows, n):
+        raise ValueError("out shape mismatch")
+    mode = _SIGN_MODES[sign_mode]
+    with torch.cuda.device(x.device):
+        _check("wht_batched", _lib.wht_batched(
+            _ptr(x), _DT[x.dtype], _ptr(out), _DT[out.dtype], rows, n, ldx, ldy,
+            _sign_ptr(signs, n, x.device), mode, int(bool(normalize)), _stream(x)))
+    return out
+
+
+def rht_quantize_rtn(w, signs, bits, group, codes=None, scales=None):
+    """Returns (codes uint8 [rows, n*bits/8], scales float16 [rows, n/group])."""
+    _need_cuda("w", w)
+    rows, n, ldw = _rows_ld("w", w)
+    if codes is None:
+        codes = torch.empty((rows, n * bits // 8), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty((rows, max(1, n // group)), dtype=torch.float16, device=w.device)
+    if not (codes.is_contiguous() and scales.is_contiguous()):
+        raise ValueError("codes and scales must be contiguous")
+    with torch.cuda.device(w.device):
+        _check("rht_quantize_rtn", _lib.rht_quantize_rtn(
+            _ptr(w), _DT[w.dtype], rows, n, ldw, _sign_ptr(signs, n, w.device), bits, group,
+            _ptr(codes), _ptr(scales), _stream(w)))
+    return codes, scales
+
+
+def rht_dequantize_inverse(codes, scales, signs, bits, group, n, out=None, out_dtype=torch.bfloat16):
+    """out = S Hn (q * s) for codes/scales written by rht_quantize_rtn."""
+    _need_cuda("codes", codes)
+    rows = codes.shape[0]
+    if codes.dtype != torch.uint8 or scales.dtype != torch.float16:
+        raise ValueError("codes must be uint8 and scales float16")
+    if codes.shape != (rows, n * bits // 8) or scales.shape != (rows, n // group):
+        raise ValueError("codes / scales shape mismatch")
+    if out is None:
+        out = torch.empty((rows, n), dtype=out_dtype, device=codes.device)
+    r2, n2, ldo = _rows_ld("out", out)
+    if (r2, n2) != (rows, n):
+        raise ValueError("out shape mismatch")
+    with torch.cuda.device(codes.device):
+        _check("rht_dequantize_inverse", _lib.rht_dequantize_inverse(
+            _ptr(codes), _ptr(scales), rows, n, _sign_ptr(signs, n, codes.device), bits, group,
+            _ptr(out), _DT[out.dtype], ldo, _stream(codes)))
+    return out
+
+
+def qwha_adapter_forward(x, row_ptr, col_idx, vals, d_out, out=None):
+    """y = (x Hn) F^T with F [d_out x d_in] in CSR (int32 row_ptr / col_idx)."""
+    _need_cuda("x", x)
+    tokens, d_in, ldx = _rows_ld("x", x)
+    for nm, t in (("row_ptr", row_ptr), ("col_idx", col_idx), ("vals", vals)):
+        _need_cuda(nm, t)
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    if row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+        raise ValueError("row_ptr and col_idx must be int32")
+    if row_ptr.numel() != d_out + 1:
+        raise ValueError("row_ptr must have d_out + 1 entries")
+    nnz = col_idx.numel()
+    if vals.numel() != nnz:
+        raise ValueError("vals and col_idx must have the same length")
+    if out is None:
+        out = torch.empty((tokens, d_out), dtype=x.dtype, device=x.device)
+    r2, n2, ldy = _rows_ld("out", out)
+    if (r2, n2) != (tokens, d_out):
+        raise ValueError("out shape mismatch")
+    with torch.cuda.device(x.device):
+        _check("qwha_adapter_forward", _lib.qwha_adapter_forward(
+            _ptr(x), _DT[x.dtype], tokens, d_in, ldx, _ptr(row_ptr), _ptr(col_idx), _ptr(vals),
+            _DT[vals.dtype], d_out, nnz, _ptr(out), _DT[out.dtype], ldy, _stream(x)))
+    return out
+
+
+def harp_rotate(x, blocks, radices=(16, 16, 16), signs=None, precondition=True, out=None):
+    """y = stages(Hn S x) (precondition) or stages(x); blocks fp32, stage-major."""
+    _need_cuda("x", x)
+    _need_cuda("blocks", blocks)
+    tokens, d, ldx = _rows_ld("x", x)
+    if blocks.dtype != torch.float32 or not blocks.is_contiguous():
+        raise ValueError("blocks must be contiguous float32")
+    rad = (ctypes.c_int32 * len(radices))(*[int(b) for b in radices])
+    if out is None:
+        out = torch.empty_like(x)
+    r2, d2, ldy = _rows_ld("out", out)
+    if (r2, d2) != (tokens, d):
+        raise ValueError("out shape mismatch")
+    with torch.cuda.device(x.device):
+        _check("harp_rotate", _lib.harp_rotate(
+            _ptr(x), _ptr(out), _DT[x.dtype], tokens, d, ldx, ldy, _sign_ptr(signs, d, x.device),
+            int(bool(precondition)), rad, len(radices), _ptr(blocks), _stream(x)))
+    return out
