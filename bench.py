@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Throughput of the MI355X Walsh-Hadamard hot path on one GPU.
+
+Main workload (the one `value` is quoted on): RHT + INT4 round-to-nearest
+quantisation, bf16 weight matrix 4096 x 4096, group 128 along d_in, fp16
+scales, signed int4 codes -- one `rht_quantize_rtn` launch per step.  The
+other workloads (orthonormal FWHT 256 x 4096 fp32, the inverse of the INT4
+path, QWHA adapter forward, HARP rotation, 28672 x 8192 RHT + INT2) are
+timed the same way and reported under "workloads".
+
+Timing: each step processes a different copy of the input, rotating over
+copies totalling >= 1 GiB so that inputs come from HBM rather than the
+256 MB last-level cache; the K launches are captured once in a HIP graph
+(no host launch overhead) and replayed inside a HIP-event pair on the
+launch stream.  Data are synthetic (seeded generators in
+wht_adapters_amd.synth) with the shapes and value structure of the
+workloads; see the design doc for the recipes.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+GIB = 1 << 30
+
+# algorithmic HBM bytes per launch: inputs read once + outputs written once
+ALGO_BYTES = {
+    "fwht_f32_256x4096": 2 * 256 * 4096 * 4,
+    "rht_int4_g128_4096x4096": 4096 * 4096 * 2 + 512 + 4096 * 2048 + 4096 * 32 * 2,
+    "rht_int4_g128_4096x4096_inverse": 4096 * 4096 * 2 + 512 + 4096 * 2048 + 4096 * 32 * 2,
+    "qwha_2048x4096_nnz262144": 2 * 2048 * 4096 * 2 + 4097 * 4 + 262144 * 4 + 262144 * 2,
+    "harp_8192x4096_r16x3": 2 * 8192 * 4096 * 2 + 3 * 256 * 16 * 16 * 4 + 512,
+    "rht_int2_g64_28672x8192": 28672 * 8192 * 2 + 1024 + 28672 * 2048 + 28672 * 128 * 2,
+    "rht_int2_g64_28672x8192_inverse": 28672 * 8192 * 2 + 1024 + 28672 * 2048 + 28672 * 128 * 2,
+}
+ROWS = {
+    "fwht_f32_256x4096": 256, "rht_int4_g128_4096x4096": 4096,
+    "rht_int4_g128_4096x4096_inverse": 4096, "qwha_2048x4096_nnz262144": 2048,
+    "harp_8192x4096_r16x3": 8192, "rht_int2_g64_28672x8192": 28672,
+    "rht_int2_g64_28672x8192_inverse": 28672,
+}
+MAIN = "rht_int4_g128_4096x4096"
+KERNEL_SOURCES = {  # sources a workload's kernel is built from (traffic counters go stale with them)
+    MAIN: ["rht_quant.hpp", "rq_fwd_b4.hip", "engine.hpp", "io.hpp", "common.hpp"],
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def src_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "wht_adapters_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(name, launches_bytes):
+    """HBM bytes per launch from committed rocprofv3 PMC counters, if they
+    were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if name not in KERNEL_SOURCES or not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        tr = json.load(fh).get(name)
+    if not tr or tr.get("src_sha") != src_hash(KERNEL_SOURCES[name]):
+        return None
+    return tr["bytes_per_launch"]
+
+
+class Timed:
+    """K launches of `launch(i)` captured in one HIP graph, replayed between
+    two HIP events on the capture stream."""
+
+    def __init__(self, torch, launch, steps, warmup):
+        self.torch = torch
+        for i in range(warmup):
+            launch(i)
+        torch.cuda.synchronize()
+        self.stream = torch.cuda.Stream()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(self.stream):
+            launch(0)                      # first call on this stream outside the capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(self.graph, stream=self.stream):
+            for i in range(steps):
+                launch(i)
+        torch.cuda.synchronize()
+        self.steps = steps
+
+    def run(self):
+        torch = self.torch
+        with torch.cuda.stream(self.stream):
+            self.graph.replay()            # untimed replay: pages in the graph
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(self.stream):
+            e0.record(self.stream)
+            self.graph.replay()
+            e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3   # seconds for self.steps launches
+
+
+def copies(torch, t, total_bytes=GIB, cap=64):
+    k = max(2, min(cap, math.ceil(total_bytes / max(1, t.numel() * t.element_size()))))
+    return [t.clone() for _ in range(k)]
+
+
+def result(name, secs, steps):
+    per = secs / steps
+    gbs = ALGO_BYTES[name] / per / 1e9
+    return {"ms_per_launch": per * 1e3, "rows_per_s": ROWS[name] / per, "GBps": gbs,
+            "frac_hbm_peak": gbs / PEAK_HBM_GBS, "algo_bytes": ALGO_BYTES[name]}
+
+
+def bench_quant(torch, W, mask_dev, cfg, name, bits, g, steps, warmup):
+    w0 = cfg["w"].to("cuda:0")
+    rows, n = w0.shape
+    ws = copies(torch, w0)
+    sg = mask_dev(cfg["signs"])
+    cs = [torch.empty((rows, n * bits // 8), dtype=torch.uint8, device="cuda:0") for _ in ws]
+    ss = [torch.empty((rows, n // g), dtype=torch.float16, device="cuda:0") for _ in ws]
+    del w0
+    fwd = Timed(torch, lambda i: W.rht_quantize_rtn(ws[i % len(ws)], sg, bits, g, cs[i % len(ws)],
+                                                    ss[i % len(ws)]), steps, warmup)
+    outs = [torch.empty((rows, n), dtype=torch.bfloat16, device="cuda:0") for _ in ws]
+    inv = Timed(torch, lambda i: W.rht_dequantize_inverse(cs[i % len(ws)], ss[i % len(ws)], sg, bits, g, n,
+                                                          out=outs[i % len(ws)]), steps, warmup)
+    r = {name: result(name, fwd.run(), steps)}
+    r[name + "_inverse"] = result(name + "_inverse", inv.run(), steps)
+    del ws, cs, ss, outs
+    torch.cuda.empty_cache()
+    return r
+
+
+def cpu_baseline(cfg, budget_s=12.0):
+    """The oracle as it stands, timed on this host on a bounded row sample of
+    the main workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import hadamard as H, rtn
+    from wht_adapters_amd import synth
+    w = synth.bf16_to_f64(cfg["w"])
+    s = H.signs_from_bits(cfg["signs"], w.shape[1])
+    rows_done, t0 = 0, time.perf_counter()
+    chunk = 256
+    while rows_done < w.shape[0] and time.perf_counter() - t0 < budget_s:
+        rtn.rht_quantize(w[rows_done:rows_done + chunk], s, 4, 128)
+        rows_done += chunk
+    secs = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": rows_done / secs, "unit": "rows/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows_done} of 4096 rows of the 4096x4096 INT4 g128 workload "
+                      f"(dense fp64 Sylvester product + naive RTN), {secs:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workloads", default="all", help="all | main | int2")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB device copy (PMC calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards rows "
+              f"with no communication, so N GPUs would each run this same kernel on rows/N.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from wht_adapters_amd import synth, whtq as W
+
+    def mask_dev(m):
+        return torch.from_numpy(np.asarray(m, dtype=np.uint32).view(np.int32).copy()).to("cuda:0")
+
+    torch.cuda.init()
+    K, Wm = args.steps, args.warmup
+    log(f"[bench] device {torch.cuda.get_device_name(0)}, steps {K}, warmup {Wm}")
+
+    if args.copy_probe:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda:0")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+        log("[bench] copy probe: 3 x 256 MiB device copy done")
+
+    cfg_main = synth.rht_int4_g128()
+    res = bench_quant(torch, W, mask_dev, cfg_main, MAIN, 4, 128, K, Wm)
+    log(f"[bench] {MAIN}: {res[MAIN]}")
+    if args.workloads == "int2":
+        cfg5 = synth.rht_int2_g64()
+        res.update(bench_quant(torch, W, mask_dev, cfg5, "rht_int2_g64_28672x8192", 2, 64, K, Wm))
+        log(f"[bench] rht_int2_g64_28672x8192: {res['rht_int2_g64_28672x8192']}")
+
+    if args.workloads == "all":
+        x = torch.from_numpy(synth.fwht_f32()["x"]).to("cuda:0")
+        xs = copies(torch, x, cap=256)
+        ys = [torch.empty_like(x) for _ in xs]
+        t = Timed(torch, lambda i: W.wht_batched(xs[i % len(xs)], out=ys[i % len(xs)]), K, Wm)
+        res["fwht_f32_256x4096"] = result("fwht_f32_256x4096", t.run(), K)
+        log(f"[bench] fwht_f32_256x4096: {res['fwht_f32_256x4096']}")
+        del xs, ys
+        for fn, nm in (("qwha", "qwha_2048x4096_nnz262144"), ("harp", "harp_8192x4096_r16x3")):
+            try:
+                res[nm] = bench_other(torch, W, mask_dev, synth, fn, nm, K, Wm)
+                log(f"[bench] {nm}: {res[nm]}")
+            except W.WhtqError as e:
+                log(f"[bench] {nm}: not available ({e})")
+        cfg5 = synth.rht_int2_g64()
+        res.update(bench_quant(torch, W, mask_dev, cfg5, "rht_int2_g64_28672x8192", 2, 64, K, Wm))
+        log(f"[bench] rht_int2_g64_28672x8192: {res['rht_int2_g64_28672x8192']}")
+
+    main_r = res[MAIN]
+    per_launch = main_r["ms_per_launch"] / 1e3
+    traffic = traffic_for(MAIN, ALGO_BYTES[MAIN])
+    line = {
+        "metric": "rows/s and HBM GB/s (% of peak) for RHT+quant at d=4096/8192",
+        "value": main_r["rows_per_s"],
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": main_r["ms_per_launch"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "rht_int4_g128_4096x4096", "rows": 4096, "d": 4096, "bits": 4,
+                   "group": 128, "input": "bf16 Student-t(3)*0.02, 0.1% outlier columns x20",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": main_r["GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": main_r["GBps"] / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel": "k_rht_quant<12,bf16,4,7>", "algo_bytes_per_launch": ALGO_BYTES[MAIN],
+                     "avg_launch_us": per_launch * 1e6},
+        "workloads": res,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        line["cpu_baseline"] = cpu_baseline(cfg_main)
+    print(json.dumps(line), flush=True)
+
+
+def bench_other(torch, W, mask_dev, synth, fn, name, K, Wm):
+    if fn == "qwha":
+        d = synth.qwha()
+        x0 = d["x"].to("cuda:0")
+        rp = torch.from_numpy(d["row_ptr"]).to("cuda:0")
+        ci = torch.from_numpy(d["col_idx"]).to("cuda:0")
+        v = d["vals"].to("cuda:0")
+        xs = copies(torch, x0)
+        ys = [torch.empty((x0.shape[0], d["d_out"]), dtype=torch.bfloat16, device="cuda:0") for _ in xs]
+        t = Timed(torch, lambda i: W.qwha_adapter_forward(xs[i % len(xs)], rp, ci, v, d["d_out"],
+                                                          out=ys[i % len(xs)]), K, Wm)
+    else:
+        d = synth.harp()
+        x0 = d["x"].to("cuda:0")
+        blocks = torch.from_numpy(np.concatenate([b.reshape(-1) for b in d["blocks"]])).to("cuda:0")
+        sg = mask_dev(d["signs"])
+        xs = copies(torch, x0)
+        ys = [torch.empty_like(x0) for _ in xs]
+        t = Timed(torch, lambda i: W.harp_rotate(xs[i % len(xs)], blocks, d["radices"], sg, True,
+                                                 out=ys[i % len(xs)]), K, Wm)
+    r = result(name, t.run(), K)
+    torch.cuda.empty_cache()
+    return r
+
+
+if __name__ == "__main__":
+    main()

@@ -40,6 +40,26 @@ __device__ __forceinline__ void bfly(float& a, float& b) {
 #define WHTQ_DPP_Q0 "quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
 #define WHTQ_DPP_Q1 "quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
 
+#define WHTQ_DPP8(CTRL)                                   \
+  asm volatile("s_nop 1\n\t"                              \
+               "v_fmac_f32_dpp %0, %0, %8 " CTRL "\n\t"   \
+               "v_fmac_f32_dpp %1, %1, %8 " CTRL "\n\t"   \
+               "v_fmac_f32_dpp %2, %2, %8 " CTRL "\n\t"   \
+               "v_fmac_f32_dpp %3, %3, %8 " CTRL "\n\t"   \
+               "v_fmac_f32_dpp %4, %4, %8 " CTRL "\n\t"   \
+               "v_fmac_f32_dpp %5, %5, %8 " CTRL "\n\t"   \
+               "v_fmac_f32_dpp %6, %6, %8 " CTRL "\n\t"   \
+               "v_fmac_f32_dpp %7, %7, %8 " CTRL           \
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), \
+                 "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])  \
+               : "v"(k))
+
+template <int LANEBIT>
+__device__ __forceinline__ void dpp_bfly8(float* v, float k) {
+  if constexpr (LANEBIT == 0) WHTQ_DPP8(WHTQ_DPP_Q0);
+  else WHTQ_DPP8(WHTQ_DPP_Q1);
+}
+
 template <int LANEBIT>
 __device__ __forceinline__ void dpp_bfly4(float& a, float& b, float& c, float& d, float k) {
   if constexpr (LANEBIT == 0) {
@@ -72,9 +92,19 @@ __device__ __forceinline__ float quad_max(float x, int lanes) {
   return x;
 }
 
-// |a| max over three values in one v_max3_f32.
+// acc <- max(acc, |a|, |b|) in one v_max3_f32 with abs source modifiers
+// (the compiler otherwise splits it into two or three v_max_f32).
 __device__ __forceinline__ float max3abs(float acc, float a, float b) {
-  return __builtin_fmaxf(acc, __builtin_fmaxf(__builtin_fabsf(a), __builtin_fabsf(b)));
+  asm("v_max3_f32 %0, |%1|, |%2|, %0" : "+v"(acc) : "v"(a), "v"(b));
+  return acc;
+}
+
+// acc <- (acc << S) + x in one v_lshl_add_u32 (keeps the packing chain from
+// being re-associated into separate shifts and adds).
+template <int S>
+__device__ __forceinline__ uint32_t shl_add(uint32_t acc, uint32_t x) {
+  asm("v_lshl_add_u32 %0, %0, %2, %1" : "+v"(acc) : "v"(x), "i"(S));
+  return acc;
 }
 
 // bf16 pair <-> fp32 (exact widening; the pair's low half is the lower index).
@@ -91,17 +121,47 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, p);
 }
 
-// Sum and difference of a bf16 / fp16 pair straight into fp32: the products
-// with +-1 are exact, so each result is the correctly rounded lo +- hi.
-__device__ __forceinline__ void pair_sumdiff_bf16(uint32_t w, float& s, float& d) {
-  const bf16x2_t x = __builtin_bit_cast(bf16x2_t, w);
-  s = __builtin_amdgcn_fdot2_f32_bf16(x, __builtin_bit_cast(bf16x2_t, 0x3f803f80u), 0.0f, false);
-  d = __builtin_amdgcn_fdot2_f32_bf16(x, __builtin_bit_cast(bf16x2_t, 0xbf803f80u), 0.0f, false);
-}
-__device__ __forceinline__ void pair_sumdiff_f16(uint32_t w, float& s, float& d) {
-  const f16x2_t x = __builtin_bit_cast(f16x2_t, w);
-  s = __builtin_amdgcn_fdot2(x, __builtin_bit_cast(f16x2_t, 0x3c003c00u), 0.0f, false);
-  d = __builtin_amdgcn_fdot2(x, __builtin_bit_cast(f16x2_t, 0xbc003c00u), 0.0f, false);
+// Eight 16-bit values (packed words x0 = (v0, v1), x1 = (v2, v3), x2, x3)
+// to fp32 with the butterflies on index bits 0 and 1 applied, per quad:
+//   y0 = v0+v1+v2+v3, y1 = v0-v1+v2-v3, y2 = v0+v1-v2-v3, y3 = v0-v1-v2+v3.
+// VOP3P v_dot2_f32_{bf16,f16} with a +-1 pair k (low half = lower index):
+// d = x.lo * k.lo + x.hi * k.hi + acc; the products with +-1 are exact.
+// gfx950 does not interlock a dot2 result against its next readers, so the
+// block spaces dependent dot2s by at least three instructions and ends with
+// three wait states before anything else may read its outputs.
+template <bool BF16> struct PM {
+  static constexpr uint32_t PP = BF16 ? 0x3f803f80u : 0x3c003c00u;  // (+1, +1)
+  static constexpr uint32_t PN = BF16 ? 0xbf803f80u : 0xbc003c00u;  // (+1, -1)
+  static constexpr uint32_t NN = BF16 ? 0xbf80bf80u : 0xbc00bc00u;  // (-1, -1)
+  static constexpr uint32_t NP = BF16 ? 0x3f80bf80u : 0x3c00bc00u;  // (-1, +1)
+};
+
+#define WHTQ_QUAD8(OP)                                                        \
+  asm(OP " %8, %12, %16, 0\n\t"   /* s0 = x0 . (+,+)            */          \
+      OP " %9, %12, %17, 0\n\t"   /* d0 = x0 . (+,-)            */          \
+      OP " %10, %14, %16, 0\n\t"  /* s1 = x2 . (+,+)            */          \
+      OP " %11, %14, %17, 0\n\t"  /* d1 = x2 . (+,-)            */          \
+      "s_nop 0\n\t"                                                           \
+      OP " %0, %13, %16, %8\n\t"  /* y0 = s0 + x1 . (+,+)       */          \
+      OP " %2, %13, %18, %8\n\t"  /* y2 = s0 + x1 . (-,-)       */          \
+      OP " %1, %13, %17, %9\n\t"  /* y1 = d0 + x1 . (+,-)       */          \
+      OP " %3, %13, %19, %9\n\t"  /* y3 = d0 + x1 . (-,+)       */          \
+      OP " %4, %15, %16, %10\n\t"                                             \
+      OP " %6, %15, %18, %10\n\t"                                             \
+      OP " %5, %15, %17, %11\n\t"                                             \
+      OP " %7, %15, %19, %11\n\t"                                             \
+      "s_nop 2"                                                               \
+      : "=&v"(y[0]), "=&v"(y[1]), "=&v"(y[2]), "=&v"(y[3]),                   \
+        "=&v"(y[4]), "=&v"(y[5]), "=&v"(y[6]), "=&v"(y[7]),                   \
+        "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)                            \
+      : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]),                           \
+        "s"(PM<BF16>::PP), "s"(PM<BF16>::PN), "s"(PM<BF16>::NN), "s"(PM<BF16>::NP))
+
+template <bool BF16>
+__device__ __forceinline__ void oct_bfly16(const uint32_t* x, float* y) {
+  float t0, t1, t2, t3;
+  if constexpr (BF16) WHTQ_QUAD8("v_dot2_f32_bf16");
+  else WHTQ_QUAD8("v_dot2_f32_f16");
 }
 
 // Global loads / stores with explicit widths.

@@ -14,8 +14,7 @@
 //
 // Layout A covers index bit 0 and every index bit >= 8, layout B the bits
 // 0..7, so one LDS transpose between them completes the transform (13 bits
-// at n = 8192: 5 in A, 8 in B).  The LDS image of a row is padded by 4 floats
-// per 64 so that the 16-byte reads of layout B are bank-conflict free.
+// at n = 8192: 5 in A, 8 in B).
 //
 // DPP butterflies leave the upper lane of each pair holding the negated
 // result; the sign accumulated by an element is (-1)^popcount(i & RHO_MASK)
@@ -35,7 +34,7 @@ struct Geo {
   static constexpr int LOGT = LOGN - LOGR;
   static constexpr int T = 1 << LOGT;
   static constexpr bool TWO = LOGT >= 3;
-  static constexpr int LDS_ROW = TWO ? N + N / 16 : 0;  // floats per row slot
+  static constexpr int LDS_ROW = TWO ? N / 2 + N / 16 : 0;  // floats per row slot (half row, padded)
 
   // index bits whose butterfly runs over DPP (so carry the rho sign)
   static constexpr unsigned RHO_MASK =
@@ -54,8 +53,24 @@ struct Geo {
   // layout B
   __device__ static __forceinline__ int idxB(int t, int r) { return t * R + r; }
 
-  __device__ static __forceinline__ int phys(int i) { return i + ((i >> 6) << 2); }
+  // Work-group shape: one wave per block while a row fits in a wave
+  // (rows never straddle waves, so the LDS hand-off needs no block
+  // barrier), else one row per block.
+  static constexpr int THREADS = T >= 64 ? T : 64;
+  static constexpr int RPB = THREADS / T;  // rows per block
 };
+
+// Hand-off point of the LDS transpose.  Within one wave the LDS executes a
+// wave's instructions in issue order, so waiting for its own LDS traffic is
+// enough; a multi-wave block needs the barrier.
+template <int THREADS>
+__device__ __forceinline__ void row_sync() {
+  if constexpr (THREADS == 64) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  } else {
+    __syncthreads();
+  }
+}
 
 // ---------------------------------------------------------------- butterflies
 
@@ -69,8 +84,13 @@ __device__ __forceinline__ void reg_stage(float (&v)[R]) {
 template <int R, int K>
 __device__ __forceinline__ void lane_stage(float (&v)[R], int t) {
   const float c = ((t >> K) & 1) ? -1.0f : 1.0f;
+  if constexpr (R % 8 == 0) {
 #pragma unroll
-  for (int r = 0; r < R; r += 4) dpp_bfly4<K>(v[r], v[r + 1], v[r + 2], v[r + 3], c);
+    for (int r = 0; r < R; r += 8) dpp_bfly8<K>(v + r, c);
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; r += 4) dpp_bfly4<K>(v[r], v[r + 1], v[r + 2], v[r + 3], c);
+  }
 }
 
 // Layout B stages on index bits [lo, 8) (register bits lo..5, quad bits 6, 7).
@@ -88,11 +108,14 @@ __device__ __forceinline__ void stages_B(float (&v)[Geo<LOGN>::R], int t) {
   if constexpr (G::LOGT >= 2) lane_stage<R, 1>(v, t);
 }
 
-// Layout A stages on index bits >= 8 (and bit 0 when WITH_BIT0).
-template <int LOGN, bool WITH_BIT0>
+// Layout A stages on index bits >= 8 (and bits 0, 1 when WITH_LOW01).
+template <int LOGN, bool WITH_LOW01>
 __device__ __forceinline__ void stages_A(float (&v)[64], int t) {
   static_assert(Geo<LOGN>::TWO, "layout A only exists for n >= 512");
-  if constexpr (WITH_BIT0) reg_stage<64, 0>(v);
+  if constexpr (WITH_LOW01) {
+    reg_stage<64, 0>(v);
+    reg_stage<64, 1>(v);
+  }
   if constexpr (LOGN - 3 >= 8) reg_stage<64, 3>(v);
   if constexpr (LOGN - 2 >= 8) reg_stage<64, 4>(v);
   if constexpr (LOGN - 1 >= 8) reg_stage<64, 5>(v);
@@ -101,46 +124,58 @@ __device__ __forceinline__ void stages_A(float (&v)[64], int t) {
 }
 
 // ------------------------------------------------------------- LDS transposes
+//
+// The A <-> B exchange runs in two halves split on index bit 2, which is a
+// register bit in both layouts: each half moves one 16-byte float4 out of
+// every 8-value chunk, so the LDS image holds half a row (index bit 2
+// removed: c(i) = (i & 3) | ((i >> 3) << 2)) and the registers a half reads
+// into are exactly those its write has just freed.  Padding: 4 floats per 32.
 
 template <int LOGN>
-__device__ __forceinline__ void lds_write_A(float* row, const float (&v)[64], int t) {
+__device__ __forceinline__ int hphys(int ci) { return ci + ((ci >> 5) << 2); }
+
+template <int LOGN, int THREADS>
+__device__ __forceinline__ void transpose_AB(float* row, float (&v)[64], int t) {
   using G = Geo<LOGN>;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    float* p = row + G::phys(G::idxA(t, c * 8));
-    *reinterpret_cast<f32x4*>(p) = f32x4{v[c * 8 + 0], v[c * 8 + 1], v[c * 8 + 2], v[c * 8 + 3]};
-    *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[c * 8 + 4], v[c * 8 + 5], v[c * 8 + 6], v[c * 8 + 7]};
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int ci = G::idxA(t, c * 8) >> 1;
+      *reinterpret_cast<f32x4*>(row + hphys<LOGN>(ci)) =
+          f32x4{v[c * 8 + 4 * h], v[c * 8 + 4 * h + 1], v[c * 8 + 4 * h + 2], v[c * 8 + 4 * h + 3]};
+    }
+    row_sync<THREADS>();
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int q = 2 * k + h;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(row + hphys<LOGN>(t * 32 + 4 * k));
+      v[4 * q] = a[0]; v[4 * q + 1] = a[1]; v[4 * q + 2] = a[2]; v[4 * q + 3] = a[3];
+    }
+    row_sync<THREADS>();
   }
 }
 
-template <int LOGN>
-__device__ __forceinline__ void lds_read_A(const float* row, float (&v)[64], int t) {
+template <int LOGN, int THREADS>
+__device__ __forceinline__ void transpose_BA(float* row, float (&v)[64], int t) {
   using G = Geo<LOGN>;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const float* p = row + G::phys(G::idxA(t, c * 8));
-    f32x4 a = *reinterpret_cast<const f32x4*>(p);
-    f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-    v[c * 8 + 0] = a[0]; v[c * 8 + 1] = a[1]; v[c * 8 + 2] = a[2]; v[c * 8 + 3] = a[3];
-    v[c * 8 + 4] = b[0]; v[c * 8 + 5] = b[1]; v[c * 8 + 6] = b[2]; v[c * 8 + 7] = b[3];
-  }
-}
-
-template <int LOGN>
-__device__ __forceinline__ void lds_write_B(float* row, const float (&v)[64], int t) {
-  float* p = row + t * 68;
+  for (int h = 0; h < 2; ++h) {
 #pragma unroll
-  for (int q = 0; q < 16; ++q)
-    *reinterpret_cast<f32x4*>(p + 4 * q) = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
-}
-
-template <int LOGN>
-__device__ __forceinline__ void lds_read_B(const float* row, float (&v)[64], int t) {
-  const float* p = row + t * 68;
+    for (int k = 0; k < 8; ++k) {
+      const int q = 2 * k + h;
+      *reinterpret_cast<f32x4*>(row + hphys<LOGN>(t * 32 + 4 * k)) =
+          f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+    }
+    row_sync<THREADS>();
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    f32x4 a = *reinterpret_cast<const f32x4*>(p + 4 * q);
-    v[4 * q] = a[0]; v[4 * q + 1] = a[1]; v[4 * q + 2] = a[2]; v[4 * q + 3] = a[3];
+    for (int c = 0; c < 8; ++c) {
+      const int ci = G::idxA(t, c * 8) >> 1;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(row + hphys<LOGN>(ci));
+      v[c * 8 + 4 * h] = a[0]; v[c * 8 + 4 * h + 1] = a[1];
+      v[c * 8 + 4 * h + 2] = a[2]; v[c * 8 + 4 * h + 3] = a[3];
+    }
+    row_sync<THREADS>();
   }
 }
 

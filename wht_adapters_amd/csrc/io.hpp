@@ -18,34 +18,54 @@ __device__ __forceinline__ float widen16(uint32_t w, bool hi, int dt) {
   return hi ? (float)h[1] : (float)h[0];
 }
 
-// Load 8 contiguous values starting at element `i` of `row` into v[0..7].
-// 16-bit inputs come in with the index-bit-0 butterfly already applied
-// (v[2p] = x[2p] + x[2p+1], v[2p+1] = x[2p] - x[2p+1]); fp32 inputs come in
-// raw.  `m` holds per-pair sign-flip masks (16-bit) or is ignored (fp32; the
-// caller passes the sign byte in `sb` instead).
-template <int DT, bool SIGNS>
-__device__ __forceinline__ void load8(const void* rowp, int i, float* v, const uint32_t* m, uint32_t sb) {
+// Raw bytes of 8 contiguous values (one 16-byte vector for 16-bit types, two
+// for fp32), fetched ahead of use so that the next row's loads overlap the
+// current row's arithmetic.
+struct Raw8 {
+  u32x4 a, b;
+};
+
+template <int DT>
+__device__ __forceinline__ void fetch8(const void* rowp, int i, Raw8& r) {
   if constexpr (DT == DT_F32) {
     const float* p = reinterpret_cast<const float*>(rowp) + i;
-    f32x4 a = ldg<f32x4>(p), b = ldg<f32x4>(p + 4);
-    uint32_t u[8] = {as_u(a[0]), as_u(a[1]), as_u(a[2]), as_u(a[3]),
-                     as_u(b[0]), as_u(b[1]), as_u(b[2]), as_u(b[3])};
+    r.a = ldg<u32x4>(p);
+    r.b = ldg<u32x4>(p + 4);
+  } else {
+    r.a = ldg<u32x4>(reinterpret_cast<const uint16_t*>(rowp) + i);
+  }
+}
+
+// Widen fetched raw values into v[0..7].  16-bit inputs come out with the
+// butterflies on index bits 0 and 1 already applied (oct_bfly16); fp32
+// inputs come out raw.  Signs: `m` holds per-pair sign-flip masks (16-bit),
+// `sb` the sign byte (fp32).
+template <int DT> struct Fused { static constexpr int LO = DT == DT_F32 ? 0 : 2; };
+
+template <int DT, bool SIGNS>
+__device__ __forceinline__ void widen8(const Raw8& r, float* v, const uint32_t* m, uint32_t sb) {
+  if constexpr (DT == DT_F32) {
+    uint32_t u[8] = {r.a[0], r.a[1], r.a[2], r.a[3], r.b[0], r.b[1], r.b[2], r.b[3]};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       if constexpr (SIGNS) u[e] ^= ((sb >> e) & 1u) << 31;
       v[e] = as_f(u[e]);
     }
   } else {
-    const uint16_t* p = reinterpret_cast<const uint16_t*>(rowp) + i;
-    u32x4 w = ldg<u32x4>(p);
+    uint32_t x[4] = {r.a[0], r.a[1], r.a[2], r.a[3]};
+    if constexpr (SIGNS) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t x = w[q];
-      if constexpr (SIGNS) x ^= m[q];
-      if constexpr (DT == DT_BF16) pair_sumdiff_bf16(x, v[2 * q], v[2 * q + 1]);
-      else pair_sumdiff_f16(x, v[2 * q], v[2 * q + 1]);
+      for (int q = 0; q < 4; ++q) x[q] ^= m[q];
     }
+    oct_bfly16<DT == DT_BF16>(x, v);
   }
+}
+
+template <int DT, bool SIGNS>
+__device__ __forceinline__ void load8(const void* rowp, int i, float* v, const uint32_t* m, uint32_t sb) {
+  Raw8 r;
+  fetch8<DT>(rowp, i, r);
+  widen8<DT, SIGNS>(r, v, m, sb);
 }
 
 // Store 8 contiguous fp32 values at element `i` of `row` in dtype DT.

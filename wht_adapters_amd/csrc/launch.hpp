@@ -21,11 +21,11 @@ int blocks_per_cu(K kernel, int block, size_t dyn_lds) {
 }
 
 // Grid of min(groups, CUs * resident blocks) for a grid-stride kernel.
-template <typename K>
-unsigned persistent_grid(K kernel, int64_t groups, int block, size_t dyn_lds) {
+// `nb` is the kernel's resident blocks per CU (callers cache it per instance).
+inline unsigned persistent_grid(int64_t groups, int nb) {
   int dev = 0;
   (void)hipGetDevice(&dev);
-  const int64_t cap = (int64_t)device_cu_count(dev) * blocks_per_cu(kernel, block, dyn_lds);
+  const int64_t cap = (int64_t)device_cu_count(dev) * nb;
   return (unsigned)std::max<int64_t>(1, std::min<int64_t>(groups, cap));
 }
 

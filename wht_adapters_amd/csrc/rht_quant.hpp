@@ -1,0 +1,384 @@
+// rht_quantize_rtn / rht_dequantize_inverse.
+//
+// Forward: y = Hn(S w) (randomized Hadamard transform, HARP explainer
+// section 1: fixed random sign diagonal then Hadamard, exactly orthogonal),
+// then per group of g consecutive transformed coordinates a symmetric absmax
+// scale, stored as fp16 (round to nearest even), and signed b-bit codes
+// q = rint(y / s) in [-qmax, qmax], qmax = 2^(b-1) - 1, packed LSB-first
+// into a little-endian bit stream (the pages leave the quantiser to other
+// systems; these are this library's fixed conventions).
+//
+// Inverse: unpack, y_hat = q * s, x_hat = S Hn(y_hat): both factors are
+// involutions, so the inverse exists and is the same transform.
+//
+// Quantiser epilogue, per element:
+//   f = fma(y_raw, m_g, 1.5*2^23 + 2^(b-1)),  m_g = rho * n^-1/2 / s16_g
+// The fma rounds the exact product once, to an integer (the ulp at 2^23 is
+// 1, round half to even), so the low bits of f hold q + 2^(b-1); codes are
+// packed with a shift-add chain and the constant high bits removed at the end.
+#pragma once
+
+#include "io.hpp"
+#include "launch.hpp"
+
+
+namespace whtq {
+
+template <int BITS>
+struct QPack {
+  static constexpr int QMAX = (1 << (BITS - 1)) - 1;
+  static constexpr float MAGIC = 12582912.0f + (float)(1 << (BITS - 1));
+  static constexpr uint32_t MAGIC_BITS = 0x4b400000u + (1u << (BITS - 1));
+  static constexpr int PER_WORD = 32 / BITS;  // BITS 2 or 4
+  static constexpr uint32_t ones() {
+    uint32_t s = 0;
+    for (int k = 0; k < PER_WORD; ++k) s += 1u << (BITS * k);
+    return s;
+  }
+  // sum_k MAGIC_BITS << (BITS k)  mod 2^32, where the code field holds 2^(b-1)
+  static constexpr uint32_t K = 0x4b400000u * ones();
+  static constexpr uint32_t BIAS = (1u << (BITS - 1)) * ones();
+};
+
+// ------------------------------------------------------------------ forward
+
+template <int LOGN, int DIN, int BITS, int LOGG>
+__global__ __launch_bounds__(Geo<LOGN>::THREADS) void k_rht_quant(
+    const uint8_t* __restrict__ w, int64_t rows, int64_t ldw_b, const uint32_t* __restrict__ sbits,
+    uint8_t* __restrict__ codes, uint16_t* __restrict__ scales, float inv_sqrt_n) {
+  using G = Geo<LOGN>;
+  static_assert(G::R == 64, "quantiser needs n >= 64");
+  constexpr int T = G::T, RPB = G::RPB;
+  constexpr int GS = 1 << LOGG;
+  constexpr int GL = GS <= 64 ? GS : 64;           // group length inside one lane
+  constexpr int NG = 64 / GL;                      // groups per lane
+  constexpr int SPAN = GS <= 64 ? 1 : GS / 64;     // lanes per group
+  constexpr int ROW_CODE_B = (G::N * BITS) / 8;
+  constexpr int LANE_CODE_B = 8 * BITS;            // 64 codes
+  constexpr int NSC = G::N / GS;                   // scales per row
+  constexpr float QM = (float)QPack<BITS>::QMAX;
+  using QP = QPack<BITS>;
+
+  const int tid = threadIdx.x, slot = tid / T, t = tid % T;
+  const int64_t ngroups = (rows + RPB - 1) / RPB;
+  const bool rho = rho_B<LOGN>(t);
+
+  __shared__ float lds[G::TWO ? RPB * G::LDS_ROW : 1];
+  float* myrow = lds + slot * G::LDS_ROW;
+
+  // per-lane sign masks for the load layout (A when two-phase, else B)
+  int col[8];
+  uint32_t sb[8], m[8][4];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    col[c] = G::TWO ? G::idxA(t, c * 8) : t * 64 + c * 8;
+    sb[c] = sbits ? sign_byte(sbits, col[c]) : 0u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) m[c][q] = pair_mask16(sb[c] >> (2 * q));
+  }
+
+  for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
+    const int64_t row = g * RPB + slot;
+    const bool valid = row < rows;
+    // rows past the end (last block only) transform a copy of the last row
+    // and store nothing, so every lane runs the same code without branches
+    const uint8_t* wr = w + (valid ? row : rows - 1) * ldw_b;
+    float v[64];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      Raw8 raw;
+      fetch8<DIN>(wr, col[c], raw);
+      widen8<DIN, true>(raw, v + 8 * c, m[c], sb[c]);
+    }
+    // 16-bit loads arrive with the index-bit 0 and 1 butterflies applied
+    if constexpr (G::TWO) {
+      stages_A<LOGN, DIN == DT_F32>(v, t);
+      transpose_AB<LOGN, G::THREADS>(myrow, v, t);
+      stages_B<LOGN, 2>(v, t);
+    } else {
+      stages_B<LOGN, Fused<DIN>::LO>(v, t);
+    }
+
+    // ---- epilogue: group absmax -> fp16 scale -> codes
+    float mult[NG];
+    uint16_t s16b[NG];
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {
+      // four independent max3 chains, then combined (short dependency chains)
+      float a4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e + 1 < GL; e += 2) a4[(e >> 1) & 3] = max3abs(a4[(e >> 1) & 3], v[k * GL + e], v[k * GL + e + 1]);
+      float a = __builtin_fmaxf(__builtin_fmaxf(a4[0], a4[1]), __builtin_fmaxf(a4[2], a4[3]));
+      a = quad_max(a, SPAN);
+      const float s_pre = (a * inv_sqrt_n) / QM;
+      const _Float16 h = (_Float16)s_pre;
+      const float sf = (float)h;
+      const float mm = sf > 0.f ? inv_sqrt_n / sf : 0.f;
+      mult[k] = rho ? -mm : mm;
+      s16b[k] = __builtin_bit_cast(uint16_t, h);
+    }
+    uint32_t cw[LANE_CODE_B / 4];
+    if constexpr (BITS == 3) {
+#pragma unroll
+      for (int j = 0; j < 6; ++j) cw[j] = 0u;
+#pragma unroll
+      for (int r = 0; r < 64; ++r) {
+        const float f = __builtin_fmaf(v[r], mult[r / GL], QP::MAGIC);
+        const uint32_t c = (as_u(f) & 7u) ^ 4u;
+        const int bit = 3 * r, wi = bit >> 5, off = bit & 31;
+        cw[wi] |= c << off;
+        if (off > 29) cw[wi + 1] |= c >> (32 - off);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < LANE_CODE_B / 4; ++j) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int k = QP::PER_WORD - 1; k >= 0; --k) {
+          const int r = j * QP::PER_WORD + k;
+          const float f = __builtin_fmaf(v[r], mult[r / GL], QP::MAGIC);
+          acc = shl_add<BITS>(acc, as_u(f));
+        }
+        cw[j] = (acc - QP::K) ^ QP::BIAS;
+      }
+    }
+    if (valid) {
+      uint8_t* cr = codes + row * (int64_t)ROW_CODE_B + t * LANE_CODE_B;
+      if constexpr (BITS == 4) {
+        stg<u32x4>(cr, u32x4{cw[0], cw[1], cw[2], cw[3]});
+        stg<u32x4>(cr + 16, u32x4{cw[4], cw[5], cw[6], cw[7]});
+      } else if constexpr (BITS == 2) {
+        stg<u32x4>(cr, u32x4{cw[0], cw[1], cw[2], cw[3]});
+      } else {
+        stg<u32x2>(cr, u32x2{cw[0], cw[1]});
+        stg<u32x2>(cr + 8, u32x2{cw[2], cw[3]});
+        stg<u32x2>(cr + 16, u32x2{cw[4], cw[5]});
+      }
+      uint16_t* sr = scales + row * (int64_t)NSC;
+      if constexpr (SPAN == 1) {
+#pragma unroll
+        for (int k = 0; k < NG; ++k) sr[t * NG + k] = s16b[k];
+      } else {
+        if (t % SPAN == 0) sr[t / SPAN] = s16b[0];
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ inverse
+
+template <int BITS>
+__device__ __forceinline__ int code_at(const uint32_t* cw, int r) {
+  if constexpr (BITS == 3) {
+    const int bit = 3 * r, wi = bit >> 5, off = bit & 31;
+    uint32_t u = cw[wi] >> off;
+    if (off > 29) u |= cw[wi + 1] << (32 - off);
+    return ((int)(u << 29)) >> 29;
+  } else {
+    constexpr int PW = 32 / BITS;
+    return __builtin_amdgcn_sbfe((int)cw[r / PW], (r % PW) * BITS, BITS);
+  }
+}
+
+// The 64 codes (8*BITS bytes) of one lane.
+template <int BITS>
+__device__ __forceinline__ void fetch_codes(const uint8_t* cr, uint32_t* cw) {
+  if constexpr (BITS == 4) {
+    u32x4 a = ldg<u32x4>(cr), b = ldg<u32x4>(cr + 16);
+    cw[0] = a[0]; cw[1] = a[1]; cw[2] = a[2]; cw[3] = a[3];
+    cw[4] = b[0]; cw[5] = b[1]; cw[6] = b[2]; cw[7] = b[3];
+  } else if constexpr (BITS == 2) {
+    u32x4 a = ldg<u32x4>(cr);
+    cw[0] = a[0]; cw[1] = a[1]; cw[2] = a[2]; cw[3] = a[3];
+  } else {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      u32x2 a = ldg<u32x2>(cr + 8 * j);
+      cw[2 * j] = a[0]; cw[2 * j + 1] = a[1];
+    }
+  }
+}
+
+template <int LOGN, int BITS, int LOGG, int DOUT>
+__global__ __launch_bounds__(Geo<LOGN>::THREADS) void k_rht_dequant(
+    const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int64_t rows,
+    const uint32_t* __restrict__ sbits, uint8_t* __restrict__ out, int64_t ldo_b, float inv_sqrt_n) {
+  using G = Geo<LOGN>;
+  static_assert(G::R == 64, "dequantiser needs n >= 64");
+  constexpr int T = G::T, RPB = G::RPB;
+  constexpr int GS = 1 << LOGG;
+  constexpr int GL = GS <= 64 ? GS : 64;
+  constexpr int NG = 64 / GL;
+  constexpr int SPAN = GS <= 64 ? 1 : GS / 64;
+  constexpr int ROW_CODE_B = (G::N * BITS) / 8;
+  constexpr int LANE_CODE_B = 8 * BITS;
+  constexpr int NSC = G::N / GS;
+
+  const int tid = threadIdx.x, slot = tid / T, t = tid % T;
+  const int64_t ngroups = (rows + RPB - 1) / RPB;
+
+  __shared__ float lds[G::TWO ? RPB * G::LDS_ROW : 1];
+  float* myrow = lds + slot * G::LDS_ROW;
+
+  // output sign masks (S and the rho of the DPP butterflies) for the store layout
+  uint32_t sb[8], m[8][4];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    if constexpr (G::TWO) {
+      const bool rl = rho_A_lane<LOGN>(t);
+      sb[c] = sbits ? sign_byte(sbits, G::idxA(t, c * 8)) : 0u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (rl ^ rho_A_reg<LOGN>(c * 8 + e)) sb[c] ^= 1u << e;
+    } else {
+      sb[c] = sbits ? sign_byte(sbits, t * 64 + c * 8) : 0u;
+      if (rho_B<LOGN>(t)) sb[c] ^= 0xffu;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) m[c][q] = pair_mask16(sb[c] >> (2 * q));
+  }
+
+  for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
+    const int64_t row = g * RPB + slot;
+    const bool valid = row < rows;
+    const int64_t rl = valid ? row : rows - 1;  // past-the-end rows: recompute the last, store nothing
+    uint32_t cw[LANE_CODE_B / 4];
+    fetch_codes<BITS>(codes + rl * (int64_t)ROW_CODE_B + t * LANE_CODE_B, cw);
+    const uint16_t* sr = scales + rl * (int64_t)NSC;
+    float ms[NG];
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {
+      const uint16_t hb = SPAN == 1 ? sr[t * NG + k] : sr[t / SPAN];
+      ms[k] = (float)__builtin_bit_cast(_Float16, hb) * inv_sqrt_n;
+    }
+    float v[64];
+#pragma unroll
+    for (int r = 0; r < 64; ++r) v[r] = (float)code_at<BITS>(cw, r) * ms[r / GL];
+    stages_B<LOGN, 0>(v, t);
+    if constexpr (G::TWO) {
+      transpose_BA<LOGN, G::THREADS>(myrow, v, t);
+      stages_A<LOGN, false>(v, t);
+    }
+    if (valid) {
+      uint8_t* orow = out + row * ldo_b;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int i = G::TWO ? G::idxA(t, c * 8) : t * 64 + c * 8;
+        if constexpr (DOUT == DT_F32) {
+          float o[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = as_f(as_u(v[c * 8 + e]) ^ (((sb[c] >> e) & 1u) << 31));
+          store8<DT_F32>(orow, i, o);
+        } else {
+          u32x4 wv;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t p = DOUT == DT_BF16 ? pack_bf16(v[c * 8 + 2 * q], v[c * 8 + 2 * q + 1])
+                                               : pack_f16(v[c * 8 + 2 * q], v[c * 8 + 2 * q + 1]);
+            wv[q] = p ^ m[c][q];
+          }
+          stg<u32x4>(reinterpret_cast<uint16_t*>(orow) + i, wv);
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ dispatch
+
+template <int LOGN, int DIN, int BITS, int LOGG>
+static hipError_t run_q(const void* w, int64_t rows, int64_t ldw, const uint32_t* sb, uint8_t* codes,
+                        uint16_t* scales, hipStream_t s) {
+  using G = Geo<LOGN>;
+  auto k = k_rht_quant<LOGN, DIN, BITS, LOGG>;
+  static const int nb = blocks_per_cu(k, G::THREADS, 0);
+  const unsigned grid = persistent_grid((rows + G::RPB - 1) / G::RPB, nb);
+  hipLaunchKernelGGL(k, dim3(grid), dim3(G::THREADS), 0, s, (const uint8_t*)w, rows,
+                     ldw * DtInfo<DIN>::BYTES, sb, codes, scales, (float)(1.0 / __builtin_sqrt((double)(1 << LOGN))));
+  return hipGetLastError();
+}
+
+template <int LOGN, int BITS, int LOGG, int DOUT>
+static hipError_t run_dq(const uint8_t* codes, const uint16_t* scales, int64_t rows, const uint32_t* sb,
+                         void* out, int64_t ldo, hipStream_t s) {
+  using G = Geo<LOGN>;
+  auto k = k_rht_dequant<LOGN, BITS, LOGG, DOUT>;
+  static const int nb = blocks_per_cu(k, G::THREADS, 0);
+  const unsigned grid = persistent_grid((rows + G::RPB - 1) / G::RPB, nb);
+  hipLaunchKernelGGL(k, dim3(grid), dim3(G::THREADS), 0, s, codes, scales, rows, sb, (uint8_t*)out,
+                     ldo * DtInfo<DOUT>::BYTES, (float)(1.0 / __builtin_sqrt((double)(1 << LOGN))));
+  return hipGetLastError();
+}
+
+// Supported instances: n = 2^6 .. 2^13, bits 2/3/4, g = 2^3 .. 2^8 (g <= n).
+#define WHTQ_G_CASES(MACRO, L, ...) \
+  switch (logg) {                   \
+    case 3: MACRO(L, 3, __VA_ARGS__) \
+    case 4: MACRO(L, 4, __VA_ARGS__) \
+    case 5: MACRO(L, 5, __VA_ARGS__) \
+    case 6: MACRO(L, 6, __VA_ARGS__) \
+    case 7: if constexpr (L >= 7) { MACRO(L, 7, __VA_ARGS__) } break; \
+    case 8: if constexpr (L >= 8) { MACRO(L, 8, __VA_ARGS__) } break; \
+    default: break;                 \
+  }
+
+template <int L, int DIN, int BITS>
+static hipError_t q_logg(int logg, const void* w, int64_t rows, int64_t ldw, const uint32_t* sb,
+                         uint8_t* codes, uint16_t* scales, hipStream_t s) {
+#define Q_CALL(LL, GG, ...) return run_q<LL, DIN, BITS, GG>(w, rows, ldw, sb, codes, scales, s);
+  WHTQ_G_CASES(Q_CALL, L, 0)
+#undef Q_CALL
+  return hipErrorInvalidValue;
+}
+
+template <int L, int DOUT, int BITS>
+static hipError_t dq_logg(int logg, const uint8_t* codes, const uint16_t* scales, int64_t rows,
+                          const uint32_t* sb, void* out, int64_t ldo, hipStream_t s) {
+#define DQ_CALL(LL, GG, ...) return run_dq<LL, BITS, GG, DOUT>(codes, scales, rows, sb, out, ldo, s);
+  WHTQ_G_CASES(DQ_CALL, L, 0)
+#undef DQ_CALL
+  return hipErrorInvalidValue;
+}
+
+template <int BITS, int DIN>
+static hipError_t q_n(int logn, int logg, const void* w, int64_t rows, int64_t ldw,
+                      const uint32_t* sb, uint8_t* codes, uint16_t* scales, hipStream_t s) {
+  switch (logn) {
+#define QN(L) case L: return q_logg<L, DIN, BITS>(logg, w, rows, ldw, sb, codes, scales, s);
+    QN(6) QN(7) QN(8) QN(9) QN(10) QN(11) QN(12) QN(13)
+#undef QN
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int BITS, int DOUT>
+static hipError_t dq_n(int logn, int logg, const uint8_t* codes, const uint16_t* scales,
+                       int64_t rows, const uint32_t* sb, void* out, int64_t ldo, hipStream_t s) {
+  switch (logn) {
+#define DQN(L) case L: return dq_logg<L, DOUT, BITS>(logg, codes, scales, rows, sb, out, ldo, s);
+    DQN(6) DQN(7) DQN(8) DQN(9) DQN(10) DQN(11) DQN(12) DQN(13)
+#undef DQN
+  }
+  return hipErrorInvalidValue;
+}
+
+// One translation unit per (direction, bits) instantiates these.
+template <int BITS>
+hipError_t launch_rht_quant_bits(int logn, int din, int logg, const void* w, int64_t rows, int64_t ldw,
+                                 const uint32_t* sb, uint8_t* codes, uint16_t* scales, hipStream_t s) {
+  if (din == DT_BF16) return q_n<BITS, DT_BF16>(logn, logg, w, rows, ldw, sb, codes, scales, s);
+  if (din == DT_F32) return q_n<BITS, DT_F32>(logn, logg, w, rows, ldw, sb, codes, scales, s);
+  if (din == DT_F16) return q_n<BITS, DT_F16>(logn, logg, w, rows, ldw, sb, codes, scales, s);
+  return hipErrorInvalidValue;
+}
+
+template <int BITS>
+hipError_t launch_rht_dequant_bits(int logn, int dout, int logg, const uint8_t* codes, const uint16_t* scales,
+                                   int64_t rows, const uint32_t* sb, void* out, int64_t ldo, hipStream_t s) {
+  if (dout == DT_BF16) return dq_n<BITS, DT_BF16>(logn, logg, codes, scales, rows, sb, out, ldo, s);
+  if (dout == DT_F32) return dq_n<BITS, DT_F32>(logn, logg, codes, scales, rows, sb, out, ldo, s);
+  if (dout == DT_F16) return dq_n<BITS, DT_F16>(logn, logg, codes, scales, rows, sb, out, ldo, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace whtq

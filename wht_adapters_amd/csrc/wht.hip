@@ -13,52 +13,47 @@ namespace whtq {
 enum SignMode : int { SIGN_NONE = 0, SIGN_BEFORE = 1, SIGN_AFTER = 2 };
 
 template <int LOGN, int DIN, int DOUT>
-__global__ __launch_bounds__(256) void k_wht(const uint8_t* x, uint8_t* y,
-                                             int64_t rows, int64_t ldx_b, int64_t ldy_b,
-                                             const uint32_t* __restrict__ sbits, int sign_mode,
-                                             float scale) {
+__global__ __launch_bounds__(Geo<LOGN>::THREADS) void k_wht(const uint8_t* x, uint8_t* y, int64_t rows,
+                                                           int64_t ldx_b, int64_t ldy_b,
+                                                           const uint32_t* __restrict__ sbits,
+                                                           int sign_mode, float scale) {
   using G = Geo<LOGN>;
-  constexpr int T = G::T, R = G::R, RPW = 256 / T;
+  constexpr int T = G::T, R = G::R, RPB = G::RPB;
   const int tid = threadIdx.x, slot = tid / T, t = tid % T;
-  const int64_t ngroups = (rows + RPW - 1) / RPW;
+  const int64_t ngroups = (rows + RPB - 1) / RPB;
+  const float cs = rho_B<LOGN>(t) ? -scale : scale;
 
   if constexpr (G::TWO) {
-    __shared__ float lds[RPW * G::LDS_ROW];
+    __shared__ float lds[RPB * G::LDS_ROW];
     float* myrow = lds + slot * G::LDS_ROW;
+    int col[8];
     uint32_t sb[8], m[8][4];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      sb[c] = sign_mode == SIGN_BEFORE ? sign_byte(sbits, G::idxA(t, c * 8)) : 0u;
+      col[c] = G::idxA(t, c * 8);
+      sb[c] = sign_mode == SIGN_BEFORE ? sign_byte(sbits, col[c]) : 0u;
 #pragma unroll
       for (int q = 0; q < 4; ++q) m[c][q] = pair_mask16(sb[c] >> (2 * q));
     }
     uint32_t sa0 = 0, sa1 = 0;
     if (sign_mode == SIGN_AFTER) { sa0 = sbits[2 * t]; sa1 = sbits[2 * t + 1]; }
-    const float cs = rho_B<LOGN>(t) ? -scale : scale;
 
     for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
-      const int64_t row = g * RPW + slot;
+      const int64_t row = g * RPB + slot;
       const bool valid = row < rows;
+      // rows past the end (last block only) transform a copy of the last row
+      // and store nothing
+      const uint8_t* xr = x + (valid ? row : rows - 1) * ldx_b;
       float v[64];
-      if (valid) {
-        const uint8_t* xr = x + row * ldx_b;
-        if (sign_mode == SIGN_BEFORE) {
 #pragma unroll
-          for (int c = 0; c < 8; ++c) load8<DIN, true>(xr, G::idxA(t, c * 8), v + 8 * c, m[c], sb[c]);
-        } else {
-#pragma unroll
-          for (int c = 0; c < 8; ++c) load8<DIN, false>(xr, G::idxA(t, c * 8), v + 8 * c, m[c], 0u);
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 64; ++r) v[r] = 0.f;
+      for (int c = 0; c < 8; ++c) {
+        Raw8 raw;
+        fetch8<DIN>(xr, col[c], raw);
+        widen8<DIN, true>(raw, v + 8 * c, m[c], sb[c]);   // (masks are zero unless SIGN_BEFORE)
       }
       stages_A<LOGN, DIN == DT_F32>(v, t);
-      lds_write_A<LOGN>(myrow, v, t);
-      __syncthreads();
-      lds_read_B<LOGN>(myrow, v, t);
-      __syncthreads();
-      stages_B<LOGN, 1>(v, t);
+      transpose_AB<LOGN, G::THREADS>(myrow, v, t);
+      stages_B<LOGN, 2>(v, t);
 #pragma unroll
       for (int r = 0; r < 64; ++r) v[r] *= cs;
       if (sign_mode == SIGN_AFTER) {
@@ -74,15 +69,14 @@ __global__ __launch_bounds__(256) void k_wht(const uint8_t* x, uint8_t* y,
     }
   } else {
     // Single layout (n <= 256): R contiguous values per lane, T <= 4 lanes per row.
-    const float cs = rho_B<LOGN>(t) ? -scale : scale;
     for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
-      const int64_t row = g * RPW + slot;
+      const int64_t row = g * RPB + slot;
       const bool valid = row < rows;
       const int base = t * R;
       float v[R];
-      constexpr bool FUSED = (R >= 8) && (DIN != DT_F32);
-      if (valid) {
-        const uint8_t* xr = x + row * ldx_b;
+      constexpr int LO = R >= 8 ? Fused<DIN>::LO : 0;
+      {
+        const uint8_t* xr = x + (valid ? row : rows - 1) * ldx_b;
         if constexpr (R >= 8) {
 #pragma unroll
           for (int q = 0; q < R / 8; ++q) {
@@ -101,11 +95,8 @@ __global__ __launch_bounds__(256) void k_wht(const uint8_t* x, uint8_t* y,
               if ((sbits[(base + e) >> 5] >> ((base + e) & 31)) & 1u) v[e] = -v[e];
           }
         }
-      } else {
-#pragma unroll
-        for (int r = 0; r < R; ++r) v[r] = 0.f;
       }
-      stages_B<LOGN, FUSED ? 1 : 0>(v, t);
+      stages_B<LOGN, LO>(v, t);
 #pragma unroll
       for (int r = 0; r < R; ++r) v[r] *= cs;
       if (sign_mode == SIGN_AFTER) {
@@ -130,11 +121,11 @@ template <int LOGN, int DIN, int DOUT>
 static hipError_t run_wht(const void* x, void* y, int64_t rows, int64_t ldx, int64_t ldy,
                           const uint32_t* sbits, int sign_mode, float scale, hipStream_t s) {
   using G = Geo<LOGN>;
-  constexpr int RPW = 256 / G::T;
-  const int64_t groups = (rows + RPW - 1) / RPW;
+  const int64_t groups = (rows + G::RPB - 1) / G::RPB;
   auto k = k_wht<LOGN, DIN, DOUT>;
-  const unsigned grid = persistent_grid(k, groups, 256, 0);
-  hipLaunchKernelGGL(k, dim3(grid), dim3(256), 0, s, (const uint8_t*)x, (uint8_t*)y, rows,
+  static const int nb = blocks_per_cu(k, G::THREADS, 0);
+  const unsigned grid = persistent_grid(groups, nb);
+  hipLaunchKernelGGL(k, dim3(grid), dim3(G::THREADS), 0, s, (const uint8_t*)x, (uint8_t*)y, rows,
                      ldx * DtInfo<DIN>::BYTES, ldy * DtInfo<DOUT>::BYTES, sbits, sign_mode, scale);
   return hipGetLastError();
 }
