@@ -137,12 +137,13 @@ whtq_status qwha_adapter_forward(const void* x, whtq_dtype x_dtype, int64_t toke
  * harp_rotate -- y = Stage_{m-1}( ... Stage_0( P x ) ), P = Hn S if
  * precondition else I; stage t applies d / b_t independent b_t x b_t blocks
  * along digit t ([HARP] 2.1, 2.2).
- *   x, y [tokens][ld] in dtype (bf16 or f32); x == y not allowed.
+ *   x, y [tokens][ld] in dtype (bf16 in this build); x == y not allowed.
  *   radices: HOST int32[n_stages], each >= 2, product == d.  This build runs
  *   d = 4096 with radices (16, 16, 16).
  *   blocks: device fp32, stage-major, stage t as [d / b_t][b_t][b_t]
- *   row-major (B[k][j] at k * b_t + j).  Block stages multiply bf16-rounded
- *   operands with fp32 accumulation (MFMA).
+ *   row-major (B[k][j] at k * b_t + j).  The preconditioning runs in fp32;
+ *   the block stages multiply bf16-rounded operands with fp32 accumulation
+ *   (MFMA) and round each stage's output to bf16.
  *   sign_bits: uint32[d/32] or NULL (all +1); used when precondition != 0.
  */
 whtq_status harp_rotate(const void* x, void* y, whtq_dtype dtype, int64_t tokens, int64_t d,

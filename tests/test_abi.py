@@ -127,6 +127,7 @@ def test_harp_validation(lib):
     assert hp(lib, pre=3) == EINVAL
     assert hp(lib, blocks=NULL) == EINVAL
     assert hp(lib, dt=2) == EUNSUP
+    assert hp(lib, dt=0) == EUNSUP
     assert hp(lib, x=P_MIS) == EALIGN
     assert hp(lib, tokens=0) == OK
 

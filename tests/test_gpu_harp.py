@@ -1,0 +1,95 @@
+"""GPU parity of harp_rotate against the dense-stage oracle."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import hadamard as H, harp, compare
+from wht_adapters_amd import synth
+from gpu_util import dev, mask_dev, host64
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+RAD = [16, 16, 16]
+
+
+def W():
+    from wht_adapters_amd import whtq
+    return whtq
+
+
+def flat(blocks):
+    return torch.from_numpy(np.concatenate([np.asarray(b, np.float32).reshape(-1) for b in blocks]))
+
+
+def run(x, blocks, mask=None, pre=True):
+    return W().harp_rotate(dev(x), dev(flat(blocks)), RAD, mask_dev(mask) if mask is not None else None, pre)
+
+
+def digits(i):
+    return [i % 16, (i // 16) % 16, i // 256]
+
+
+def test_permutation_blocks_exact():
+    """Identity blocks except one permutation block per stage, no
+    preconditioning: every output is one input value, so the result must be
+    the predicted permutation bit for bit (checks the MFMA operand layouts
+    and the digit / block-index convention at the real shape)."""
+    rng = np.random.default_rng(5)
+    x = synth.to_bf16(rng.standard_normal((37, 4096)))
+    blocks = []
+    for t in range(3):
+        bl = np.broadcast_to(np.eye(16, dtype=np.float32), (256, 16, 16)).copy()
+        for _ in range(5):
+            bl[int(rng.integers(0, 256))] = np.eye(16, dtype=np.float32)[rng.permutation(16)]
+        blocks.append(bl)
+    y = run(x, blocks, pre=False)
+    want = synth.bf16_to_f64(x)
+    for t in range(3):
+        z = want.copy()
+        bl = blocks[t]
+        for i in range(4096):
+            dg = digits(i)
+            rest = [dd for u, dd in enumerate(dg) if u != t]
+            c = rest[0] + 16 * rest[1]
+            k = int(np.argmax(bl[c][dg[t]]))
+            j = list(dg); j[t] = k
+            z[:, i] = want[:, j[0] + 16 * j[1] + 256 * j[2]]
+        want = z
+    assert np.array_equal(host64(y), want)
+
+
+def test_hadamard_blocks_equal_wht():
+    """Theta = 0: blocks H16/4 compose to the Sylvester WHT (H16/4 is exact in bf16)."""
+    rng = np.random.default_rng(6)
+    x = synth.to_bf16(rng.standard_normal((20, 4096)))
+    h = (H.sylvester(16) / 4.0).astype(np.float32)
+    blocks = [np.broadcast_to(h, (256, 16, 16)) for _ in range(3)]
+    y = run(x, blocks, pre=False)
+    assert compare.float_err(host64(y), H.wht(synth.bf16_to_f64(x)))[0] <= TOL
+    eye = [np.broadcast_to(np.eye(16, dtype=np.float32), (256, 16, 16)) for _ in range(3)]
+    mask = synth.sign_bits_to_mask(rng.integers(0, 2, 4096))
+    y = run(x, eye, mask=mask, pre=True)
+    want = H.rht(synth.bf16_to_f64(x), H.signs_from_bits(mask, 4096))
+    assert compare.float_err(host64(y), want)[0] <= TOL
+
+
+@pytest.mark.parametrize("tokens", [1, 15, 16, 31, 100])
+def test_random_orthogonal(tokens):
+    rng = np.random.default_rng(tokens)
+    x = synth.to_bf16(rng.standard_normal((tokens, 4096)))
+    blocks = [synth.orthogonal_blocks(rng, 256, 16) for _ in range(3)]
+    mask = synth.sign_bits_to_mask(rng.integers(0, 2, 4096))
+    y = run(x, blocks, mask=mask)
+    want = harp.harp_rotate(synth.bf16_to_f64(x), RAD, blocks, s=H.signs_from_bits(mask, 4096))
+    assert compare.float_err(host64(y), want)[0] <= TOL
+
+
+def test_full_config_8192x4096_sampled():
+    d = synth.harp()
+    y = W().harp_rotate(dev(d["x"]), dev(flat(d["blocks"])), d["radices"], mask_dev(d["signs"]), True)
+    sel = np.r_[0:40, 4090:4110, 8150:8192]
+    want = harp.harp_rotate(synth.bf16_to_f64(d["x"][sel]), RAD, d["blocks"],
+                            s=H.signs_from_bits(d["signs"], 4096))
+    err, roww = compare.float_err(host64(y[sel]), want)
+    print("harp 8192x4096 sampled: max scaled err", err, "max row rel err", roww)
+    assert err <= TOL

@@ -1,0 +1,85 @@
+"""GPU parity of qwha_adapter_forward against the dense oracle."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import hadamard as H, qwha, compare
+from wht_adapters_amd import synth
+from gpu_util import dev, host64
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+def W():
+    from wht_adapters_amd import whtq
+    return whtq
+
+
+def run(x, rp, ci, vals, d_out):
+    return W().qwha_adapter_forward(dev(x), dev(rp), dev(ci), dev(vals), d_out)
+
+
+def random_csr(rng, d_out, d_in, nnz, empty_rows=()):
+    rows = rng.integers(0, d_out, nnz)
+    rows = np.array([r for r in rows if r not in set(empty_rows)])
+    cols = rng.integers(0, d_in, rows.size)
+    key = np.unique(rows * d_in + cols)
+    rows, cols = key // d_in, key % d_in
+    vals = synth.to_bf16(0.1 * rng.standard_normal(rows.size))
+    rp, ci, _ = qwha.coo_to_csr(rows, cols, np.arange(rows.size), d_out)
+    order = np.lexsort((cols, rows))
+    return rp, ci, vals[torch.from_numpy(order)]
+
+
+@pytest.mark.parametrize("tokens,d_out,nnz", [(37, 64, 1000), (8, 4096, 20000), (1, 8, 50), (130, 512, 9000)])
+def test_random_csr(tokens, d_out, nnz):
+    rng = np.random.default_rng(tokens + d_out)
+    x = synth.to_bf16(rng.standard_normal((tokens, 4096)))
+    rp, ci, v = random_csr(rng, d_out, 4096, nnz, empty_rows=(0, 5))
+    y = run(x, rp, ci, v, d_out)
+    want = qwha.qwha_forward(synth.bf16_to_f64(x), rp, ci, synth.bf16_to_f64(v), d_out)
+    err, _ = compare.float_err(host64(y), want)
+    assert err <= TOL, err
+    assert torch.all(y[:, 0] == 0) and torch.all(y[:, 5] == 0)
+
+
+def test_identity_and_single_nonzero():
+    rng = np.random.default_rng(1)
+    x = synth.to_bf16(rng.standard_normal((16, 4096)))
+    n = 4096
+    rp = np.arange(n + 1, dtype=np.int32)
+    ci = np.arange(n, dtype=np.int32)
+    y = run(x, rp, ci, synth.to_bf16(np.ones(n)), n)
+    assert compare.float_err(host64(y), H.wht(synth.bf16_to_f64(x)))[0] <= TOL
+    # single nonzero F[o, k] = v  ->  y[:, o] = v * (Hn x)[:, k], everything else 0
+    o, k, val = 77, 1234, -0.375
+    rp = np.r_[np.zeros(o + 1, np.int32), np.ones(n - o, np.int32)]
+    y = run(x, rp, np.array([k], np.int32), synth.to_bf16(np.array([val])), n)
+    z = H.wht(synth.bf16_to_f64(x))[:, k] * val
+    yy = host64(y)
+    assert np.allclose(yy[:, o], z, rtol=8e-3, atol=0)
+    yy[:, o] = 0
+    assert not yy.any()
+
+
+def test_f32_values_and_determinism():
+    rng = np.random.default_rng(2)
+    x = synth.to_bf16(rng.standard_normal((24, 4096)))
+    rp, ci, v = random_csr(rng, 256, 4096, 5000)
+    vf = v.to(torch.float32)
+    y1 = run(x, rp, ci, vf, 256)
+    y2 = run(x, rp, ci, vf, 256)
+    assert torch.equal(y1, y2)
+    want = qwha.qwha_forward(synth.bf16_to_f64(x), rp, ci, vf.double().numpy(), 256)
+    assert compare.float_err(host64(y1), want)[0] <= TOL
+
+
+def test_full_config_2048x4096_nnz262144():
+    d = synth.qwha()
+    y = run(d["x"], d["row_ptr"], d["col_idx"], d["vals"], d["d_out"])
+    want = qwha.qwha_forward(synth.bf16_to_f64(d["x"]), d["row_ptr"], d["col_idx"],
+                             synth.bf16_to_f64(d["vals"]), d["d_out"])
+    err, roww = compare.float_err(host64(y), want)
+    print("qwha 2048x4096 nnz 262144: max scaled err", err, "max row rel err", roww)
+    assert err <= TOL

@@ -217,7 +217,7 @@ whtq_status harp_rotate(const void* x, void* y, whtq_dtype dtype, int64_t tokens
   if (tokens > 0 && x == y) return WHTQ_EINVAL;
   if (d != 4096 || n_stages != 3 || radices[0] != 16 || radices[1] != 16 || radices[2] != 16)
     return WHTQ_EUNSUPPORTED;
-  if (dtype != WHTQ_BF16 && dtype != WHTQ_F32) return WHTQ_EUNSUPPORTED;
+  if (dtype != WHTQ_BF16) return WHTQ_EUNSUPPORTED;
   const int esz = dt_bytes(dtype);
   if (!rows_aligned(x, d, ldx, esz) || !rows_aligned(y, d, ldy, esz) || !aligned16(blocks)) return WHTQ_EALIGN;
   if (sign_bits && (reinterpret_cast<uintptr_t>(sign_bits) & 3u)) return WHTQ_EALIGN;

@@ -164,6 +164,15 @@ __device__ __forceinline__ void oct_bfly16(const uint32_t* x, float* y) {
   else WHTQ_QUAD8("v_dot2_f32_f16");
 }
 
+// acc += a * h (h an fp16 value in the low / high half of `w`), one
+// v_fma_mix_f32 with the fp16 operand widened exactly inside the FMA.
+__device__ __forceinline__ void fma_mix_lo(float& acc, float a, uint32_t w) {
+  asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel_hi:[0,1,0]" : "+v"(acc) : "v"(a), "v"(w));
+}
+__device__ __forceinline__ void fma_mix_hi(float& acc, float a, uint32_t w) {
+  asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(acc) : "v"(a), "v"(w));
+}
+
 // Global loads / stores with explicit widths.
 template <typename V>
 __device__ __forceinline__ V ldg(const void* p) { return *reinterpret_cast<const V*>(p); }
