@@ -29,7 +29,8 @@ namespace hp {
 constexpr int LOGN = 12;
 constexpr int N = 1 << LOGN;
 constexpr int TT = 15;        // tokens per tile (the 16th MFMA column is a duplicate)
-constexpr int THREADS = 256;  // 4 waves
+constexpr int THREADS = 512;  // 8 waves (4 run the preconditioning transforms)
+constexpr int FWAVES = 4;
 constexpr int TILE_BYTES = TT * N * 2;
 constexpr int SCRATCH_BYTES = 4 * Geo<LOGN>::LDS_ROW * 4;
 constexpr int LDS_BYTES = TILE_BYTES + SCRATCH_BYTES + 4 * 16;  // + per-token exponents
@@ -51,6 +52,13 @@ __device__ __forceinline__ float wave_sum(float a) {
   for (int s = 1; s < 64; s <<= 1) a += __shfl_xor(a, s);
   return a;
 }
+
+// Tile layout: token row r at r * 4096 halves, element i stored at
+// i ^ (r << 3): whole 16-byte chunks are permuted per row, so row-contiguous
+// 16-byte accesses stay contiguous while the 64 lanes of a stage access
+// (16 tokens x 4 digit groups, same offset in every row) spread over the LDS
+// banks instead of all hitting one.
+__device__ __forceinline__ int tsw(int row, int i) { return i ^ (row << 3); }
 
 // element index of digit value k in block c of stage t (stride 16^t)
 __device__ __forceinline__ int harp_idx(int t, int c, int k) {
@@ -88,7 +96,7 @@ __global__ __launch_bounds__(hp::THREADS) void k_harp(const uint16_t* __restrict
     const int ntok = (int)min<int64_t>(hp::TT, tokens - tok0);
 
     // ---- 1. preconditioning (or plain copy) into the fp16 tile
-    for (int k = wave; k < hp::TT; k += 4) {
+    for (int k = wave; wave < hp::FWAVES && k < hp::TT; k += hp::FWAVES) {
       const uint16_t* xr = x + (tok0 + min(k, ntok - 1)) * ldx;
       uint16_t* trow = tile + k * hp::N;
       float v[64];
@@ -127,7 +135,7 @@ __global__ __launch_bounds__(hp::THREADS) void k_harp(const uint16_t* __restrict
         uint32_t w[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) w[p] = pack_f16(v[8 * q + 2 * p] * sc, v[8 * q + 2 * p + 1] * sc);
-        *reinterpret_cast<u32x4*>(trow + lane * 64 + 8 * q) = u32x4{w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<u32x4*>(trow + tsw(k, lane * 64 + 8 * q)) = u32x4{w[0], w[1], w[2], w[3]};
       }
     }
     __syncthreads();
@@ -135,19 +143,22 @@ __global__ __launch_bounds__(hp::THREADS) void k_harp(const uint16_t* __restrict
     // ---- 2. three radix-16 stages on MFMA
     // lane l: token l % 16 (column 15 duplicates row 14), k-group l / 16
     const int tcol = lane & 15, kg = lane >> 4;
-    const uint16_t* trd = tile + min(tcol, hp::TT - 1) * hp::N;
+    const int rrd = min(tcol, hp::TT - 1);
+    const uint16_t* trd = tile + rrd * hp::N;
     uint16_t* twr = tile + tcol * hp::N;
+    constexpr int NW = hp::THREADS / 64;
     for (int t = 0; t < 3; ++t) {
-      const float* bt = blocks + (size_t)t * 256 * 256;
-      for (int c = wave; c < 256; c += 4) {
-        // A operand: B_{t,c}[n = l % 16][k = 4 kg .. 4 kg + 3]
-        float bw[4];
-        __builtin_memcpy(bw, bt + c * 256 + tcol * 16 + 4 * kg, 16);
+      const float* bt = blocks + (size_t)t * 256 * 256 + tcol * 16 + 4 * kg;
+      // A operand of block c: B_{t,c}[n = l % 16][k = 4 kg .. 4 kg + 3], fetched one block ahead
+      float bw[4];
+      __builtin_memcpy(bw, bt + wave * 256, 16);
+      for (int c = wave; c < 256; c += NW) {
         const f16x4_t a = {(_Float16)bw[0], (_Float16)bw[1], (_Float16)bw[2], (_Float16)bw[3]};
+        if (c + NW < 256) __builtin_memcpy(bw, bt + (c + NW) * 256, 16);
         // B operand: X[tok][idx(c, k)], k = 4 kg .. 4 kg + 3
         uint16_t bh[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bh[i] = trd[harp_idx(t, c, 4 * kg + i)];
+        for (int i = 0; i < 4; ++i) bh[i] = trd[tsw(rrd, harp_idx(t, c, 4 * kg + i))];
         f16x4_t b;
         __builtin_memcpy(&b, bh, 8);
         f32x4_t d = {0.f, 0.f, 0.f, 0.f};
@@ -158,7 +169,7 @@ __global__ __launch_bounds__(hp::THREADS) void k_harp(const uint16_t* __restrict
         if (tcol < hp::TT) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            twr[harp_idx(t, c, 4 * kg + i)] = (uint16_t)(pack_f16(dd[i], 0.f) & 0xffffu);
+            twr[tsw(tcol, harp_idx(t, c, 4 * kg + i))] = (uint16_t)(pack_f16(dd[i], 0.f) & 0xffffu);
         }
       }
       __syncthreads();
@@ -169,7 +180,7 @@ __global__ __launch_bounds__(hp::THREADS) void k_harp(const uint16_t* __restrict
       const int k = i / (hp::N / 8), q = i - k * (hp::N / 8);
       const float us = ldexpf(1.0f, texp[k] - 14);
       uint32_t w[4];
-      __builtin_memcpy(w, tile + k * hp::N + 8 * q, 16);
+      __builtin_memcpy(w, tile + k * hp::N + tsw(k, 8 * q), 16);
       uint32_t o[4];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {

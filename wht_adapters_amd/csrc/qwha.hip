@@ -13,10 +13,10 @@
 //      column), so one ds_read_b128 returns a column for all 8 tokens;
 //   3. rows of F are bucketed by their nnz (ceil(nnz / 8)) so that the 8 rows
 //      a wave handles together need about the same number of iterations;
-//   4. CSR gather SpMM: 8 lanes per row, one nonzero per lane per iteration,
-//      8 fp32 accumulators per lane (v_fma_mix with the fp16 column), a DPP
-//      reduction over the 8 lanes, and the bf16 result staged in LDS;
-//   5. the 8 x d_out tile is written with 16-byte stores.
+//   4. CSR gather SpMM: 8 lanes per row, up to 8 nonzeros per lane per step
+//      with the next row group's first step fetched ahead, 8 fp32
+//      accumulators per lane (v_fma_mix with the fp16 column), a DPP
+//      reduction over the 8 lanes; each lane stores one token's bf16 output.
 #include "io.hpp"
 #include "launch.hpp"
 
@@ -26,20 +26,24 @@ namespace qw {
 constexpr int LOGN = 12;
 constexpr int N = 1 << LOGN;
 constexpr int TT = 8;                     // tokens per block
-constexpr int THREADS = 256;              // 4 waves
+constexpr int THREADS = 1024;             // 16 waves (4 transform token rows)
 constexpr int NBKT = 512;                 // nnz buckets: ceil(nnz / 8), capped
+constexpr int FWAVES = 4;                 // waves that run the token transforms
+constexpr int UNROLL = 8;                 // nonzeros per lane per step
 }  // namespace qw
 
 // LDS map (bytes):
 //   [0, 64K)        Z[k][tok] fp16, 16 B per column      (FWHT scratch before step 2)
-//   [64K, 128K)     staging Zt[tok][k] fp16 in steps 1-2, then Y[tok][o] bf16
-//   [128K, +8K)     sorted row ids (uint16)
-//   [+8K, +2K)      bucket counters (uint32)
+//   [64K, 128K)     staging Zt[tok][k] fp16 in steps 1-2; afterwards the
+//                   length-sorted row list: id (u16), start (i32), length (u16)
+//   [128K, +2K)     bucket counters (uint32)
 //   [+2K, +32)      per-token exponent
 constexpr int QW_LDS_Z = 0;
 constexpr int QW_LDS_Y = 65536;
-constexpr int QW_LDS_ORDER = 131072;
-constexpr int QW_LDS_BKT = QW_LDS_ORDER + 8192;
+constexpr int QW_LDS_RID = QW_LDS_Y;
+constexpr int QW_LDS_RBEG = QW_LDS_Y + 8192;
+constexpr int QW_LDS_RLEN = QW_LDS_Y + 8192 + 16384;
+constexpr int QW_LDS_BKT = 131072;
 constexpr int QW_LDS_EXP = QW_LDS_BKT + 4 * qw::NBKT;
 constexpr int QW_LDS_BYTES = QW_LDS_EXP + 4 * qw::TT;
 
@@ -63,7 +67,9 @@ __global__ __launch_bounds__(qw::THREADS) void k_qwha(const uint16_t* __restrict
   const int64_t tok0 = (int64_t)blockIdx.x * qw::TT;
   const int ntok = (int)min<int64_t>(qw::TT, tokens - tok0);
 
-  uint16_t* order = reinterpret_cast<uint16_t*>(smem + QW_LDS_ORDER);
+  uint16_t* rid = reinterpret_cast<uint16_t*>(smem + QW_LDS_RID);
+  int* rbeg = reinterpret_cast<int*>(smem + QW_LDS_RBEG);
+  uint16_t* rlen = reinterpret_cast<uint16_t*>(smem + QW_LDS_RLEN);
   uint32_t* bkt = reinterpret_cast<uint32_t*>(smem + QW_LDS_BKT);
   int* texp = reinterpret_cast<int*>(smem + QW_LDS_EXP);
 
@@ -77,7 +83,7 @@ __global__ __launch_bounds__(qw::THREADS) void k_qwha(const uint16_t* __restrict
   }
 
   // ---- 1. FWHT of the token rows, staged as fp16 token-major
-  {
+  if (wave < qw::FWAVES) {
     float* scratch = reinterpret_cast<float*>(smem + QW_LDS_Z) + wave * G::LDS_ROW;
     uint16_t* zt = reinterpret_cast<uint16_t*>(smem + QW_LDS_Y);
     const int t = lane;
@@ -86,7 +92,7 @@ __global__ __launch_bounds__(qw::THREADS) void k_qwha(const uint16_t* __restrict
 #pragma unroll
     for (int c = 0; c < 8; ++c) col[c] = G::idxA(t, c * 8);
     const uint32_t nomask[4] = {0u, 0u, 0u, 0u};
-    for (int k = wave; k < qw::TT; k += qw::THREADS / 64) {
+    for (int k = wave; k < qw::TT; k += qw::FWAVES) {
       const int64_t tok = tok0 + min(k, ntok - 1);  // tail tokens recompute the last one
       const uint16_t* xr = x + tok * ldx;
       float v[64];
@@ -150,70 +156,91 @@ __global__ __launch_bounds__(qw::THREADS) void k_qwha(const uint16_t* __restrict
   }
   __syncthreads();
   for (int o = tid; o < d_out; o += qw::THREADS) {
-    const int len = row_ptr[o + 1] - row_ptr[o];
+    const int beg = row_ptr[o];
+    const int len = row_ptr[o + 1] - beg;
     const int b = min((len + 7) >> 3, qw::NBKT - 1);
     const uint32_t pos = atomicAdd(&bkt[qw::NBKT - 1 - b], 1u);
-    order[pos] = (uint16_t)o;
+    rid[pos] = (uint16_t)o;
+    rbeg[pos] = beg;
+    rlen[pos] = (uint16_t)min(len, 65535);
   }
   __syncthreads();
 
-  // ---- 4. gather SpMM: lane octet j of a wave handles row order[8*grp + j]
+  // ---- 4. gather SpMM: lane octet j of a wave handles sorted row 8*grp + j
   {
     const u32x4* z = reinterpret_cast<const u32x4*>(smem + QW_LDS_Z);
-    uint16_t* yl = reinterpret_cast<uint16_t*>(smem + QW_LDS_Y);
     const int oct = lane >> 3, slot = lane & 7;
-    float osc[qw::TT];
+    const float osc = ldexpf(1.0f, texp[min(slot, qw::TT - 1)] - 20);  // 2^(e-14) / 64 of token `slot`
+    constexpr int NW = qw::THREADS / 64;
+    const int ngrp = d_out >> 3;
+
+    // one step = up to UNROLL nonzeros per lane: j = start + slot + 8 u
+    struct Step { int c[qw::UNROLL]; float fv[qw::UNROLL]; };
+    auto fetch = [&](Step& st, int start, int end) {
 #pragma unroll
-    for (int k = 0; k < qw::TT; ++k) osc[k] = ldexpf(1.0f, texp[k] - 20);  // 2^(e-14) / 64
-    const int ngrp = (d_out + 7) >> 3;
-    for (int grp = wave; grp < ngrp; grp += qw::THREADS / 64) {
-      const int oi = grp * 8 + oct;
-      const bool live = oi < d_out;
-      const int o = live ? order[oi] : 0;
-      const int beg = live ? row_ptr[o] : 0;
-      const int end = live ? row_ptr[o + 1] : 0;
-      float acc[qw::TT];
+      for (int u = 0; u < qw::UNROLL; ++u) {
+        const int j = start + slot + 8 * u;
+        const bool ok = j < end;
+        st.c[u] = ok ? col_idx[j] : -1;
+        if constexpr (VALDT == DT_BF16)
+          st.fv[u] = ok ? bf16lo((uint32_t)reinterpret_cast<const uint16_t*>(vals)[j]) : 0.f;
+        else
+          st.fv[u] = ok ? reinterpret_cast<const float*>(vals)[j] : 0.f;
+      }
+    };
+    auto consume = [&](const Step& st, float* acc) {
 #pragma unroll
-      for (int k = 0; k < qw::TT; ++k) acc[k] = 0.f;
-      for (int j = beg + slot; __builtin_amdgcn_ballot_w64(j < end); j += 8) {
-        if (j < end) {
-          const int c = col_idx[j];
-          float fv;
-          if constexpr (VALDT == DT_BF16) fv = bf16lo((uint32_t)reinterpret_cast<const uint16_t*>(vals)[j]);
-          else fv = reinterpret_cast<const float*>(vals)[j];
+      for (int u = 0; u < qw::UNROLL; ++u) {
+        if (st.c[u] >= 0) {
           // (copied out as words: subscripting the loaded vector with the
           // unrolled loop index was miscompiled into a single 4-byte read)
           uint32_t zc[4];
-          __builtin_memcpy(zc, &z[c], 16);
+          __builtin_memcpy(zc, &z[st.c[u]], 16);
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
-            fma_mix_lo(acc[2 * p], fv, zc[p]);
-            fma_mix_hi(acc[2 * p + 1], fv, zc[p]);
+            fma_mix_lo(acc[2 * p], st.fv[u], zc[p]);
+            fma_mix_hi(acc[2 * p + 1], st.fv[u], zc[p]);
           }
         }
+      }
+    };
+
+    Step cur, nxt;
+    int g = wave;
+    int pos = g * 8 + oct;
+    int beg = g < ngrp ? rbeg[pos] : 0;
+    int end = g < ngrp ? beg + rlen[pos] : 0;
+    fetch(cur, beg, end);
+    for (; g < ngrp; g += NW) {
+      const int o = rid[pos];
+      // fetch the next group's first step before working on this one
+      const int gn = g + NW;
+      const int posn = gn * 8 + oct;
+      const int begn = gn < ngrp ? rbeg[posn] : 0;
+      const int endn = gn < ngrp ? begn + rlen[posn] : 0;
+      fetch(nxt, begn, endn);
+      float acc[qw::TT];
+#pragma unroll
+      for (int k = 0; k < qw::TT; ++k) acc[k] = 0.f;
+      consume(cur, acc);
+      // rows longer than 8 * UNROLL (few after sorting) take more steps
+      for (int j0 = beg + 8 * qw::UNROLL; __builtin_amdgcn_ballot_w64(j0 < end); j0 += 8 * qw::UNROLL) {
+        Step more;
+        fetch(more, j0, end);
+        consume(more, acc);
       }
       float mine = 0.f;
 #pragma unroll
       for (int k = 0; k < qw::TT; ++k) {
-        const float s = dpp_sum8(acc[k]);
-        mine = slot == k ? s : mine;
+        const float sum = dpp_sum8(acc[k]);
+        mine = slot == k ? sum : mine;
       }
-      if (live && slot < ntok) {
-        const float yv = mine * osc[slot];
-        yl[slot * qw::N + o] = (uint16_t)(pack_bf16(yv, 0.f) & 0xffffu);
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- 5. write the tile
-  {
-    const uint16_t* yl = reinterpret_cast<const uint16_t*>(smem + QW_LDS_Y);
-    const int per_row = d_out >> 3;  // 16-byte chunks per token row (d_out % 8 == 0)
-    for (int i = tid; i < ntok * per_row; i += qw::THREADS) {
-      const int k = i / per_row, q = i - k * per_row;
-      *reinterpret_cast<u32x4*>(y + (tok0 + k) * ldy + 8 * q) =
-          *reinterpret_cast<const u32x4*>(yl + k * qw::N + 8 * q);
+      if (slot < ntok)
+        y[(tok0 + slot) * ldy + o] = (uint16_t)(pack_bf16(mine * osc, 0.f) & 0xffffu);
+      cur = nxt;
+      pos = posn;
+      beg = begn;
+      end = endn;
     }
   }
 }
