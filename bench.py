@@ -106,6 +106,10 @@ class Timed:
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(self.stream):
+            # a ~2 ms device-side spin ahead of the start event: the host has queued
+            # the whole graph before the GPU reaches e0, so submission latency stays
+            # outside the timed region and the per-launch average is kernel time
+            torch.cuda._sleep(5_000_000)
             e0.record(self.stream)
             self.graph.replay()
             e1.record(self.stream)
