@@ -65,12 +65,16 @@ def test_hadamard_blocks_equal_wht():
     h = (H.sylvester(16) / 4.0).astype(np.float32)
     blocks = [np.broadcast_to(h, (256, 16, 16)) for _ in range(3)]
     y = run(x, blocks, pre=False)
-    assert compare.float_err(host64(y), H.wht(synth.bf16_to_f64(x)))[0] <= TOL
+    err = compare.float_err(host64(y), H.wht(synth.bf16_to_f64(x)))[0]
+    print(f"hadamard blocks: max scaled error {err:.3e}")
+    assert err <= TOL
     eye = [np.broadcast_to(np.eye(16, dtype=np.float32), (256, 16, 16)) for _ in range(3)]
     mask = synth.sign_bits_to_mask(rng.integers(0, 2, 4096))
     y = run(x, eye, mask=mask, pre=True)
     want = H.rht(synth.bf16_to_f64(x), H.signs_from_bits(mask, 4096))
-    assert compare.float_err(host64(y), want)[0] <= TOL
+    err = compare.float_err(host64(y), want)[0]
+    print(f"max scaled error {err:.3e}")
+    assert err <= TOL
 
 
 @pytest.mark.parametrize("tokens", [1, 15, 16, 31, 100])
@@ -81,7 +85,9 @@ def test_random_orthogonal(tokens):
     mask = synth.sign_bits_to_mask(rng.integers(0, 2, 4096))
     y = run(x, blocks, mask=mask)
     want = harp.harp_rotate(synth.bf16_to_f64(x), RAD, blocks, s=H.signs_from_bits(mask, 4096))
-    assert compare.float_err(host64(y), want)[0] <= TOL
+    err = compare.float_err(host64(y), want)[0]
+    print(f"max scaled error {err:.3e}")
+    assert err <= TOL
 
 
 def test_full_config_8192x4096_sampled():
@@ -91,5 +97,6 @@ def test_full_config_8192x4096_sampled():
     want = harp.harp_rotate(synth.bf16_to_f64(d["x"][sel]), RAD, d["blocks"],
                             s=H.signs_from_bits(d["signs"], 4096))
     err, roww = compare.float_err(host64(y[sel]), want)
+    print(f"full config, sampled rows: max scaled error {err:.3e}, max row relative error {roww:.3e}")
     print("harp 8192x4096 sampled: max scaled err", err, "max row rel err", roww)
     assert err <= TOL

@@ -3,44 +3,54 @@
 // HARP explainer, 2.1: a mixed-radix schedule with prod b_t = d, each stage a
 // block-diagonal orthogonal matrix acting on coordinate groups separated by a
 // stride permutation; 2.2: blocks B_{t,c} = Q_{t,c} G (G the normalised
-// Sylvester Hadamard), and the random-sign Hadamard preconditioning P = Hn S
-// in front; 2.4: the stages cost O(d log d) and are applied by fused kernels
-// without materialising the permutations.
+// Sylvester Hadamard), with Theta = 0 (Q = I) giving back the fixed
+// randomized Hadamard transform P = Hn S; 2.4: the stages cost O(d log d) and
+// are applied by fused kernels without materialising the permutations.
 //
 // Digit convention: index i = i0 + 16 i1 + 256 i2; stage t acts on digit t;
 // its block c is i with digit t removed (remaining digits in increasing
 // significance); out_sub[k] = sum_j B[k][j] in_sub[j].
 //
-// One block per tile of 15 tokens, all of it kept on chip:
-//   1. P x: each wave transforms one token row at a time with the fp32
-//      register / LDS FWHT engine; the row is scaled by an exact power of two
-//      that puts its L2 norm in [2^13, 2^14) (every later value is bounded by
-//      that norm, the stages being orthogonal) and stored to the fp16 tile;
-//   2. each stage: for every 16 x 16 block, one MFMA
-//      D[n][tok] = sum_k B[n][k] X[tok][idx(c, k)] (fp16 operands, fp32
-//      accumulation), read from and written back to the tile in place;
-//   3. the tile is unscaled, rounded to bf16 and written with 16-byte stores.
+// The preconditioning is itself three radix-16 stages: the Sylvester matrix
+// factors over the digits, Hn = (G (x) G (x) G) with G = H16 / 4, so P x is
+// G applied along each digit after the sign flips.  Every radix-16 stage,
+// fixed (G) or learned (B_{t,c}), runs the same way: one 16 x 16 x 16 MFMA
+// per block and per tile of 16 tokens, D[k][tok] = sum_j Blk[k][j] X[tok][j].
+//
+// One workgroup (8 waves) per CU, looping over tiles of 16 tokens kept in
+// LDS as fp16 (140 KB with padding):
+//   load   each wave converts two token rows: sign flips, an exact power-of-
+//          two scale that puts the row's L2 norm in [2^13, 2^14) (every later
+//          value is bounded by that norm, all stages being orthogonal), fp16;
+//          the next tile's rows are fetched meanwhile;
+//   passes G along digit 1, G along digit 2, G then B_0 along digit 0
+//          (chained MFMAs, G and B_0 act on the same digit), B_1 along digit
+//          1, B_2 along digit 2, each reading and writing the tile in place
+//          with 8-byte LDS accesses; the last pass unscales and rounds to bf16;
+//   store  each wave writes its two rows with 16-byte stores.
+// Without preconditioning the G passes and the sign flips are skipped.
 #include "io.hpp"
 #include "launch.hpp"
 
 namespace whtq {
 
 namespace hp {
-constexpr int LOGN = 12;
-constexpr int N = 1 << LOGN;
-constexpr int TT = 15;        // tokens per tile (the 16th MFMA column is a duplicate)
-constexpr int THREADS = 512;  // 8 waves (4 run the preconditioning transforms)
-constexpr int FWAVES = 4;
-constexpr int TILE_BYTES = TT * N * 2;
-constexpr int SCRATCH_BYTES = 4 * Geo<LOGN>::LDS_ROW * 4;
-constexpr int LDS_BYTES = TILE_BYTES + SCRATCH_BYTES + 4 * 16;  // + per-token exponents
-static_assert(LDS_BYTES <= 160 * 1024, "tile + scratch must fit in LDS");
+constexpr int N = 4096;
+constexpr int TT = 16;        // tokens per tile = MFMA N
+constexpr int NW = 8;         // waves per workgroup; wave w owns tile rows 2w, 2w+1 for load / store
+constexpr int THREADS = NW * 64;
+constexpr int RS = 4488;      // row stride in halfwords: >= lay(4095) + 1, RS / 2 = 4 (mod 64)
+constexpr int TILE_BYTES = TT * RS * 2;
+constexpr int LDS_BYTES = TILE_BYTES + TT * 4;  // + per-token exponents
+static_assert(LDS_BYTES <= 160 * 1024, "tile must fit in LDS");
+static_assert(TT == 2 * NW, "two rows per wave");
+static_assert(RS >= 4096 + 4 * 64 + 4 * 4 && (RS / 2) % 64 == 4, "row stride");
 }  // namespace hp
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 
-// power-of-two scale for a row with squared norm `ss` (wave-uniform)
+// power-of-two exponent of a row with squared norm `ss` (wave-uniform)
 __device__ __forceinline__ int row_exponent(float ss) {
   int e = 0;
   if (ss > 0.f) (void)frexpf(__builtin_sqrtf(ss), &e);  // ||z|| = m 2^e, m in [0.5, 1)
@@ -53,143 +63,258 @@ __device__ __forceinline__ float wave_sum(float a) {
   return a;
 }
 
-// Tile layout: token row r at r * 4096 halves, element i stored at
-// i ^ (r << 3): whole 16-byte chunks are permuted per row, so row-contiguous
-// 16-byte accesses stay contiguous while the 64 lanes of a stage access
-// (16 tokens x 4 digit groups, same offset in every row) spread over the LDS
-// banks instead of all hitting one.
-__device__ __forceinline__ int tsw(int row, int i) { return i ^ (row << 3); }
+// Tile layout (halfwords): row n at n * RS; element i at lay(i), which pads
+// 4 halfwords (8 bytes) after every 64 elements and 4 more after every 1024.
+// Units of 4 consecutive elements stay contiguous, and lay() is additive over
+// disjoint bit fields (lay(a | b) = lay(a) + lay(b) when a & b == 0), so an
+// address splits into a lane part and a compile-time group part.  With RS =
+// 4 (mod 64) banks per row, the 64 lanes of one 8-byte MFMA operand access
+// (16 rows x the 4-element group along the stage's digit, index bits 2-3,
+// 6-7 or 10-11) fall on distinct banks in each half-wave for all three digits.
+__device__ __forceinline__ constexpr int lay(int i) { return i + 4 * (i >> 6) + 4 * (i >> 10); }
 
-// element index of digit value k in block c of stage t (stride 16^t)
-__device__ __forceinline__ int harp_idx(int t, int c, int k) {
-  const int st = 1 << (4 * t);
-  return (c & (st - 1)) + k * st + (c >> (4 * t)) * (st << 4);
+__device__ __forceinline__ u32x2 lds_rd8(const uint16_t* tile, int off) {
+  return *reinterpret_cast<const u32x2*>(tile + off);
+}
+__device__ __forceinline__ void lds_wr8(uint16_t* tile, int off, u32x2 v) {
+  *reinterpret_cast<u32x2*>(tile + off) = v;
+}
+
+__device__ __forceinline__ f16x4_t as_h4(u32x2 v) { return __builtin_bit_cast(f16x4_t, v); }
+__device__ __forceinline__ f16x4_t f4_to_h4(f32x4_t a) {
+  return f16x4_t{(_Float16)a[0], (_Float16)a[1], (_Float16)a[2], (_Float16)a[3]};
+}
+__device__ __forceinline__ u32x2 h4_bits(f32x4_t d) {
+  return u32x2{pack_f16(d[0], d[1]), pack_f16(d[2], d[3])};
+}
+
+__device__ __forceinline__ f32x4_t mfma16(f16x4_t a, f16x4_t b) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+}
+
+// 4 x 4 transpose of 16-bit values held as four 8-byte rows r[j] = (v[j][0..3]):
+// o[a] = (v[0][a], v[1][a], v[2][a], v[3][a]).
+__device__ __forceinline__ void tr4x4(const u32x2* r, u32x2* o) {
+  constexpr uint32_t LO = 0x05040100u, HI = 0x07060302u;  // v_perm selectors: low / high halves of (s1, s0)
+  o[0] = u32x2{__builtin_amdgcn_perm(r[1].x, r[0].x, LO), __builtin_amdgcn_perm(r[3].x, r[2].x, LO)};
+  o[1] = u32x2{__builtin_amdgcn_perm(r[1].x, r[0].x, HI), __builtin_amdgcn_perm(r[3].x, r[2].x, HI)};
+  o[2] = u32x2{__builtin_amdgcn_perm(r[1].y, r[0].y, LO), __builtin_amdgcn_perm(r[3].y, r[2].y, LO)};
+  o[3] = u32x2{__builtin_amdgcn_perm(r[1].y, r[0].y, HI), __builtin_amdgcn_perm(r[3].y, r[2].y, HI)};
+}
+
+// A operand of block c of one stage: Blk[m = lane % 16][k = 4 kg .. 4 kg + 3]
+__device__ __forceinline__ f32x4_t blk_row(const float* stage, int c, int n, int kg) {
+  return ldg<f32x4_t>(stage + c * 256 + n * 16 + 4 * kg);
+}
+
+enum PassA : int { A_G = 0, A_BLK = 1, A_BLK_LAST = 2 };
+
+// Stage along digit D (1 or 2), in place.  Block c = i0 + 16 v, v the other
+// digit; a group is 4 blocks with consecutive i0 = 4e .. 4e + 3, so the
+// operand reads are 8-byte rows along i0 transposed in registers.  Wave w
+// takes groups 8w .. 8w + 7.
+template <int D, int MODE>
+__device__ __forceinline__ void pass_dd(uint16_t* tile, const float* stage, f16x4_t g, float us, int w, int n,
+                                        int kg) {
+  constexpr int ST = D == 1 ? 16 : 256;  // stride of the stage's digit
+  constexpr int SV = D == 1 ? 256 : 16;  // stride of the other digit
+  // element index = ST (4 kg + j) + 4 e + SV v with v = 2w + gi / 4, e = gi % 4;
+  // lane part ST 4 kg and wave part SV 2w occupy bit fields disjoint from the rest
+  const int wb = n * hp::RS + lay(ST * 4 * kg) + lay(SV * 2 * w);
+  f32x4_t an[4];
+  if constexpr (MODE != A_G) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) an[a] = blk_row(stage, a + 32 * w, n, kg);
+  }
+#pragma unroll
+  for (int gi = 0; gi < 8; ++gi) {
+    const int grp = 8 * w + gi;
+    f32x4_t ac[4];
+    if constexpr (MODE != A_G) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) ac[a] = an[a];
+      if (gi + 1 < 8) {
+        const int g2 = grp + 1;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) an[a] = blk_row(stage, 4 * (g2 & 3) + a + 16 * (g2 >> 2), n, kg);
+      }
+    }
+    int off[4];
+    u32x2 r[4], b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      off[j] = wb + lay(4 * (gi & 3) + SV * (gi >> 2) + ST * j);
+      r[j] = lds_rd8(tile, off[j]);
+    }
+    tr4x4(r, b);
+    u32x2 o[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const f16x4_t A = MODE == A_G ? g : f4_to_h4(ac[a]);
+      f32x4_t d = mfma16(A, as_h4(b[a]));
+      if constexpr (MODE == A_BLK_LAST)
+        o[a] = u32x2{pack_bf16(d[0] * us, d[1] * us), pack_bf16(d[2] * us, d[3] * us)};
+      else
+        o[a] = h4_bits(d);
+    }
+    tr4x4(o, r);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lds_wr8(tile, off[j], r[j]);
+    __builtin_amdgcn_sched_barrier(0);  // keep groups in order: bounds the registers in flight
+  }
+}
+
+// Stage along digit 0, in place: block c = i1 + 16 i2 reads one 8-byte row
+// per lane.  CHAIN applies G first (the last preconditioning factor) and then
+// the stage's block, both along digit 0.  Wave w takes blocks 32w .. 32w + 31.
+template <bool CHAIN>
+__device__ __forceinline__ void pass_d0(uint16_t* tile, const float* stage, f16x4_t g, int w, int n, int kg) {
+  // element index = 4 kg + 16 c with c = 32 w + 4 gi + a: lane, wave and group bit fields are disjoint
+  const int wb = n * hp::RS + lay(4 * kg) + lay(512 * w);
+  f32x4_t an[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) an[a] = blk_row(stage, 32 * w + a, n, kg);
+#pragma unroll
+  for (int gi = 0; gi < 8; ++gi) {
+    const int c0 = 32 * w + 4 * gi;
+    f32x4_t ac[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) ac[a] = an[a];
+    if (gi + 1 < 8) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) an[a] = blk_row(stage, c0 + 4 + a, n, kg);
+    }
+    int off[4];
+    u32x2 r[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      off[a] = wb + lay(64 * gi + 16 * a);
+      r[a] = lds_rd8(tile, off[a]);
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      f16x4_t bx = as_h4(r[a]);
+      if constexpr (CHAIN) bx = f4_to_h4(mfma16(g, bx));
+      r[a] = h4_bits(mfma16(f4_to_h4(ac[a]), bx));
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) lds_wr8(tile, off[a], r[a]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 __global__ __launch_bounds__(hp::THREADS) void k_harp(const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
                                                       int64_t tokens, int64_t ldx, int64_t ldy,
                                                       const uint32_t* __restrict__ sbits, int precondition,
                                                       const float* __restrict__ blocks) {
-  using G = Geo<hp::LOGN>;
   extern __shared__ __align__(16) uint8_t smem[];
   uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
-  float* scratch = reinterpret_cast<float*>(smem + hp::TILE_BYTES);
-  int* texp = reinterpret_cast<int*>(smem + hp::TILE_BYTES + hp::SCRATCH_BYTES);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int* texp = reinterpret_cast<int*>(smem + hp::TILE_BYTES);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n = lane & 15, kg = lane >> 4;
   const int64_t ntiles = (tokens + hp::TT - 1) / hp::TT;
+  const bool pre = precondition != 0;
 
-  // per-lane sign masks for the engine's load layout
-  int col[8];
-  uint32_t sb[8], m[8][4];
+  // sign-flip masks for the lane's load columns 8 (lane + 64 r) .. + 7
+  uint32_t msk[8][4];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    col[c] = G::idxA(lane, c * 8);
-    sb[c] = sbits ? sign_byte(sbits, col[c]) : 0u;
+  for (int r = 0; r < 8; ++r) {
+    const uint32_t sb = (pre && sbits) ? sign_byte(sbits, 8 * (lane + 64 * r)) : 0u;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) m[c][q] = pair_mask16(sb[c] >> (2 * q));
+    for (int q = 0; q < 4; ++q) msk[r][q] = pair_mask16(sb >> (2 * q));
   }
-  const float cs = rho_B<hp::LOGN>(lane) ? -1.0f / 64.0f : 1.0f / 64.0f;
-  float* myscr = scratch + wave * G::LDS_ROW;
+  // G = H16 / 4 as the A operand: G[m = n][k = 4 kg + i]
+  f16x4_t g;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) g[i] = (__builtin_popcount(n & (4 * kg + i)) & 1) ? (_Float16)-0.25f : (_Float16)0.25f;
+
+  u32x4 raw[2][8];
+  auto fetch = [&](int64_t tl) {
+    const int64_t t0 = tl * hp::TT;
+    const int nt = (int)min<int64_t>(hp::TT, tokens - t0);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const uint16_t* xr = x + (t0 + min(2 * w + s, nt - 1)) * ldx;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) raw[s][r] = ldg<u32x4>(xr + 8 * (lane + 64 * r));
+    }
+  };
+  if ((int64_t)blockIdx.x < ntiles) fetch(blockIdx.x);
 
   for (int64_t tl = blockIdx.x; tl < ntiles; tl += gridDim.x) {
     const int64_t tok0 = tl * hp::TT;
     const int ntok = (int)min<int64_t>(hp::TT, tokens - tok0);
 
-    // ---- 1. preconditioning (or plain copy) into the fp16 tile
-    for (int k = wave; wave < hp::FWAVES && k < hp::TT; k += hp::FWAVES) {
-      const uint16_t* xr = x + (tok0 + min(k, ntok - 1)) * ldx;
-      uint16_t* trow = tile + k * hp::N;
-      float v[64];
-      if (precondition) {
+    // ---- load: signs, per-row power-of-two scale, fp16 into the tile
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          Raw8 raw;
-          fetch8<DT_BF16>(xr, col[c], raw);
-          widen8<DT_BF16, true>(raw, v + 8 * c, m[c], sb[c]);
-        }
-        stages_A<hp::LOGN, false>(v, lane);
-        transpose_AB<hp::LOGN, 64>(myscr, v, lane);
-        stages_B<hp::LOGN, 2>(v, lane);
-#pragma unroll
-        for (int r = 0; r < 64; ++r) v[r] *= cs;
-      } else {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const u32x4 w = *reinterpret_cast<const u32x4*>(xr + lane * 64 + 8 * q);
-          const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            v[8 * q + 2 * p] = bf16lo(wv[p]);
-            v[8 * q + 2 * p + 1] = bf16hi(wv[p]);
-          }
-        }
-      }
+    for (int s = 0; s < 2; ++s) {
+      const int row = 2 * w + s;
       float ss = 0.f;
 #pragma unroll
-      for (int r = 0; r < 64; ++r) ss = __builtin_fmaf(v[r], v[r], ss);
+      for (int r = 0; r < 8; ++r) {
+        u32x4 v = raw[s][r];
+        v.x ^= msk[r][0];
+        v.y ^= msk[r][1];
+        v.z ^= msk[r][2];
+        v.w ^= msk[r][3];
+        raw[s][r] = v;
+        ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v.x), __builtin_bit_cast(bf16x2_t, v.x), ss, false);
+        ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v.y), __builtin_bit_cast(bf16x2_t, v.y), ss, false);
+        ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v.z), __builtin_bit_cast(bf16x2_t, v.z), ss, false);
+        ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v.w), __builtin_bit_cast(bf16x2_t, v.w), ss, false);
+      }
       const int e = row_exponent(wave_sum(ss));
       const float sc = ldexpf(1.0f, 14 - e);
-      if (lane == 0) texp[k] = e;
+      if (lane == 0) texp[row] = e;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        uint32_t w[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) w[p] = pack_f16(v[8 * q + 2 * p] * sc, v[8 * q + 2 * p + 1] * sc);
-        *reinterpret_cast<u32x4*>(trow + tsw(k, lane * 64 + 8 * q)) = u32x4{w[0], w[1], w[2], w[3]};
+      for (int r = 0; r < 8; ++r) {
+        const u32x4 v = raw[s][r];
+        const int o = row * hp::RS + lay(8 * lane) + lay(512 * r);
+        lds_wr8(tile, o, u32x2{pack_f16(bf16lo(v.x) * sc, bf16hi(v.x) * sc),
+                               pack_f16(bf16lo(v.y) * sc, bf16hi(v.y) * sc)});
+        lds_wr8(tile, o + 4, u32x2{pack_f16(bf16lo(v.z) * sc, bf16hi(v.z) * sc),
+                                   pack_f16(bf16lo(v.w) * sc, bf16hi(v.w) * sc)});
       }
     }
+    if (tl + gridDim.x < ntiles) fetch(tl + gridDim.x);
     __syncthreads();
 
-    // ---- 2. three radix-16 stages on MFMA
-    // lane l: token l % 16 (column 15 duplicates row 14), k-group l / 16
-    const int tcol = lane & 15, kg = lane >> 4;
-    const int rrd = min(tcol, hp::TT - 1);
-    const uint16_t* trd = tile + rrd * hp::N;
-    uint16_t* twr = tile + tcol * hp::N;
-    constexpr int NW = hp::THREADS / 64;
-    for (int t = 0; t < 3; ++t) {
-      const float* bt = blocks + (size_t)t * 256 * 256 + tcol * 16 + 4 * kg;
-      // A operand of block c: B_{t,c}[n = l % 16][k = 4 kg .. 4 kg + 3], fetched one block ahead
-      float bw[4];
-      __builtin_memcpy(bw, bt + wave * 256, 16);
-      for (int c = wave; c < 256; c += NW) {
-        const f16x4_t a = {(_Float16)bw[0], (_Float16)bw[1], (_Float16)bw[2], (_Float16)bw[3]};
-        if (c + NW < 256) __builtin_memcpy(bw, bt + (c + NW) * 256, 16);
-        // B operand: X[tok][idx(c, k)], k = 4 kg .. 4 kg + 3
-        uint16_t bh[4];
+    // ---- radix-16 stages on MFMA
+    // the block operands are re-read from L2 per tile; an opaque copy of the
+    // pointer keeps the compiler from hoisting (and spilling) them across tiles
+    const float* bl = blocks;
+    asm volatile("" : "+s"(bl));
+    if (pre) {
+      pass_dd<1, A_G>(tile, nullptr, g, 1.f, w, n, kg);
+      __syncthreads();
+      pass_dd<2, A_G>(tile, nullptr, g, 1.f, w, n, kg);
+      __syncthreads();
+      pass_d0<true>(tile, bl, g, w, n, kg);
+    } else {
+      pass_d0<false>(tile, bl, g, w, n, kg);
+    }
+    __syncthreads();
+    pass_dd<1, A_BLK>(tile, bl + 65536, g, 1.f, w, n, kg);
+    __syncthreads();
+    const float us = ldexpf(1.0f, texp[n] - 14);
+    pass_dd<2, A_BLK_LAST>(tile, bl + 2 * 65536, g, us, w, n, kg);
+    __syncthreads();
+
+    // ---- store: bf16 rows 2w, 2w + 1
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bh[i] = trd[tsw(rrd, harp_idx(t, c, 4 * kg + i))];
-        f16x4_t b;
-        __builtin_memcpy(&b, bh, 8);
-        f32x4_t d = {0.f, 0.f, 0.f, 0.f};
-        d = __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, d, 0, 0, 0);
-        float dd[4];
-        __builtin_memcpy(dd, &d, 16);
-        // D[n = 4 kg + i][tok = l % 16]
-        if (tcol < hp::TT) {
+    for (int s = 0; s < 2; ++s) {
+      const int row = 2 * w + s;
+      if (row < ntok) {
+        uint16_t* yr = y + (tok0 + row) * ldy;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            twr[tsw(tcol, harp_idx(t, c, 4 * kg + i))] = (uint16_t)(pack_f16(dd[i], 0.f) & 0xffffu);
+        for (int r = 0; r < 8; ++r) {
+          const int o = row * hp::RS + lay(8 * lane) + lay(512 * r);
+          const u32x2 lo = lds_rd8(tile, o), hi = lds_rd8(tile, o + 4);
+          stg(yr + 8 * (lane + 64 * r), u32x4{lo.x, lo.y, hi.x, hi.y});
         }
       }
-      __syncthreads();
     }
-
-    // ---- 3. unscale, round to bf16, write the tile
-    for (int i = tid; i < ntok * (hp::N / 8); i += hp::THREADS) {
-      const int k = i / (hp::N / 8), q = i - k * (hp::N / 8);
-      const float us = ldexpf(1.0f, texp[k] - 14);
-      uint32_t w[4];
-      __builtin_memcpy(w, tile + k * hp::N + tsw(k, 8 * q), 16);
-      uint32_t o[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const f16x2_t h = __builtin_bit_cast(f16x2_t, w[p]);
-        o[p] = pack_bf16((float)h[0] * us, (float)h[1] * us);
-      }
-      *reinterpret_cast<u32x4*>(y + (tok0 + k) * ldy + 8 * q) = u32x4{o[0], o[1], o[2], o[3]};
-    }
-    __syncthreads();
+    // the next tile's load writes only rows 2w, 2w + 1, which this wave alone reads here
   }
 }
 
@@ -200,9 +325,7 @@ hipError_t launch_harp(const void* x, void* y, int dt, int64_t tokens, int64_t l
                                                hp::LDS_BYTES) == hipSuccess;
   (void)attr;
   const int64_t ntiles = (tokens + hp::TT - 1) / hp::TT;
-  int dev = 0;
-  (void)hipGetDevice(&dev);
-  const unsigned grid = (unsigned)std::min<int64_t>(ntiles, (int64_t)device_cu_count(dev));
+  const unsigned grid = persistent_grid(ntiles, 1);
   hipLaunchKernelGGL(k_harp, dim3(grid), dim3(hp::THREADS), hp::LDS_BYTES, s, (const uint16_t*)x,
                      (uint16_t*)y, tokens, ldx, ldy, sbits, precondition, blocks);
   return hipGetLastError();
