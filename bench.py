@@ -38,7 +38,7 @@ ALGO_BYTES = {
     "rht_int4_g128_4096x4096": 4096 * 4096 * 2 + 512 + 4096 * 2048 + 4096 * 32 * 2,
     "rht_int4_g128_4096x4096_inverse": 4096 * 4096 * 2 + 512 + 4096 * 2048 + 4096 * 32 * 2,
     "qwha_2048x4096_nnz262144": 2 * 2048 * 4096 * 2 + 4097 * 4 + 262144 * 4 + 262144 * 2,
-    "harp_8192x4096_r16x3": 2 * 8192 * 4096 * 2 + 3 * 256 * 16 * 16 * 4 + 512,
+    "harp_8192x4096_r16x3": 2 * 8192 * 4096 * 2 + 3 * 256 * 16 * 16 * 2 + 512,  # fp16 blocks
     "rht_int2_g64_28672x8192": 28672 * 8192 * 2 + 1024 + 28672 * 2048 + 28672 * 128 * 2,
     "rht_int2_g64_28672x8192_inverse": 28672 * 8192 * 2 + 1024 + 28672 * 2048 + 28672 * 128 * 2,
 }
@@ -175,7 +175,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workloads", default="all", help="all | main | int2")
+    ap.add_argument("--workloads", default="all",
+                    help="all | main | comma list of fwht, qwha, harp, int2 (the main workload always runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (PMC calibration)")
@@ -205,15 +206,13 @@ def main():
         del a, b
         log("[bench] copy probe: 3 x 256 MiB device copy done")
 
+    sel = {"all": {"main", "fwht", "qwha", "harp", "int2"}, "main": {"main"}}.get(
+        args.workloads, set(args.workloads.split(",")))
+    sel.add("main")  # `value` is always quoted on the main workload
     cfg_main = synth.rht_int4_g128()
     res = bench_quant(torch, W, mask_dev, cfg_main, MAIN, 4, 128, K, Wm)
     log(f"[bench] {MAIN}: {res[MAIN]}")
-    if args.workloads == "int2":
-        cfg5 = synth.rht_int2_g64()
-        res.update(bench_quant(torch, W, mask_dev, cfg5, "rht_int2_g64_28672x8192", 2, 64, K, Wm))
-        log(f"[bench] rht_int2_g64_28672x8192: {res['rht_int2_g64_28672x8192']}")
-
-    if args.workloads == "all":
+    if "fwht" in sel:
         x = torch.from_numpy(synth.fwht_f32()["x"]).to("cuda:0")
         xs = copies(torch, x, cap=256)
         ys = [torch.empty_like(x) for _ in xs]
@@ -221,12 +220,11 @@ def main():
         res["fwht_f32_256x4096"] = result("fwht_f32_256x4096", t.run(), K)
         log(f"[bench] fwht_f32_256x4096: {res['fwht_f32_256x4096']}")
         del xs, ys
-        for fn, nm in (("qwha", "qwha_2048x4096_nnz262144"), ("harp", "harp_8192x4096_r16x3")):
-            try:
-                res[nm] = bench_other(torch, W, mask_dev, synth, fn, nm, K, Wm)
-                log(f"[bench] {nm}: {res[nm]}")
-            except W.WhtqError as e:
-                log(f"[bench] {nm}: not available ({e})")
+    for fn, nm in (("qwha", "qwha_2048x4096_nnz262144"), ("harp", "harp_8192x4096_r16x3")):
+        if fn in sel:
+            res[nm] = bench_other(torch, W, mask_dev, synth, fn, nm, K, Wm)
+            log(f"[bench] {nm}: {res[nm]}")
+    if "int2" in sel:
         cfg5 = synth.rht_int2_g64()
         res.update(bench_quant(torch, W, mask_dev, cfg5, "rht_int2_g64_28672x8192", 2, 64, K, Wm))
         log(f"[bench] rht_int2_g64_28672x8192: {res['rht_int2_g64_28672x8192']}")
@@ -276,7 +274,8 @@ def bench_other(torch, W, mask_dev, synth, fn, name, K, Wm):
     else:
         d = synth.harp()
         x0 = d["x"].to("cuda:0")
-        blocks = torch.from_numpy(np.concatenate([b.reshape(-1) for b in d["blocks"]])).to("cuda:0")
+        # the blocks are parameters: handed over in fp16, the precision the stages multiply in
+        blocks = torch.from_numpy(np.concatenate([b.reshape(-1) for b in d["blocks"]])).to("cuda:0").half()
         sg = mask_dev(d["signs"])
         xs = copies(torch, x0)
         ys = [torch.empty_like(x0) for _ in xs]

@@ -140,15 +140,22 @@ whtq_status qwha_adapter_forward(const void* x, whtq_dtype x_dtype, int64_t toke
  *   x, y [tokens][ld] in dtype (bf16 in this build); x == y not allowed.
  *   radices: HOST int32[n_stages], each >= 2, product == d.  This build runs
  *   d = 4096 with radices (16, 16, 16).
- *   blocks: device fp32, stage-major, stage t as [d / b_t][b_t][b_t]
- *   row-major (B[k][j] at k * b_t + j).  The preconditioning runs in fp32;
- *   the block stages multiply bf16-rounded operands with fp32 accumulation
- *   (MFMA) and round each stage's output to bf16.
+ *   blocks: device, stage-major, stage t as [d / b_t][b_t][b_t] row-major
+ *   (B[k][j] at k * b_t + j), in blocks_dtype: WHTQ_F32, or WHTQ_F16 (half
+ *   the bytes read per call; the kernel rounds fp32 blocks to fp16 itself,
+ *   so both give the same result for the same fp16-representable values).
+ *   Arithmetic: each token row is scaled by an exact power of two that puts
+ *   its L2 norm in [2^13, 2^14) and kept on chip in fp16; the
+ *   preconditioning Hn = (H16 / 4) (x) (H16 / 4) (x) (H16 / 4) and every
+ *   block stage run as 16 x 16 x 16 MFMAs with fp16 operands and fp32
+ *   accumulation, the result of each rounded to fp16; the output is
+ *   unscaled and rounded once to bf16 (nearest even).
  *   sign_bits: uint32[d/32] or NULL (all +1); used when precondition != 0.
  */
 whtq_status harp_rotate(const void* x, void* y, whtq_dtype dtype, int64_t tokens, int64_t d,
                         int64_t ldx, int64_t ldy, const uint32_t* sign_bits, int precondition,
-                        const int32_t* radices, int n_stages, const float* blocks, void* stream);
+                        const int32_t* radices, int n_stages, const void* blocks,
+                        whtq_dtype blocks_dtype, void* stream);
 
 const char* whtq_status_string(whtq_status s);
 int whtq_last_hip_error(void); /* hipError_t behind this thread's last WHTQ_EHIP */

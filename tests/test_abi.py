@@ -113,9 +113,9 @@ def test_qwha_validation(lib):
 
 
 def hp(lib, x=P, y=ctypes.c_void_p(0x20000), dt=1, tokens=8, d=4096, ldx=4096, ldy=4096, sb=NULL,
-       pre=1, rad=(16, 16, 16), blocks=P):
+       pre=1, rad=(16, 16, 16), blocks=P, bd=0):
     arr = (ctypes.c_int32 * len(rad))(*rad)
-    return lib.harp_rotate(x, y, dt, tokens, d, ldx, ldy, sb, pre, arr, len(rad), blocks, NULL)
+    return lib.harp_rotate(x, y, dt, tokens, d, ldx, ldy, sb, pre, arr, len(rad), blocks, bd, NULL)
 
 
 def test_harp_validation(lib):
@@ -128,6 +128,9 @@ def test_harp_validation(lib):
     assert hp(lib, blocks=NULL) == EINVAL
     assert hp(lib, dt=2) == EUNSUP
     assert hp(lib, dt=0) == EUNSUP
+    assert hp(lib, bd=7) == EINVAL                         # not a dtype
+    assert hp(lib, bd=1) == EUNSUP                         # bf16 blocks: no kernel
+    assert hp(lib, bd=2, tokens=0) == OK                   # fp16 blocks accepted
     assert hp(lib, x=P_MIS) == EALIGN
     assert hp(lib, tokens=0) == OK
 

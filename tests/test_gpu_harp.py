@@ -17,12 +17,12 @@ def W():
     return whtq
 
 
-def flat(blocks):
-    return torch.from_numpy(np.concatenate([np.asarray(b, np.float32).reshape(-1) for b in blocks]))
+def flat(blocks, dtype=torch.float32):
+    return torch.from_numpy(np.concatenate([np.asarray(b, np.float32).reshape(-1) for b in blocks])).to(dtype)
 
 
-def run(x, blocks, mask=None, pre=True):
-    return W().harp_rotate(dev(x), dev(flat(blocks)), RAD, mask_dev(mask) if mask is not None else None, pre)
+def run(x, blocks, mask=None, pre=True, bdt=torch.float32):
+    return W().harp_rotate(dev(x), dev(flat(blocks, bdt)), RAD, mask_dev(mask) if mask is not None else None, pre)
 
 
 def digits(i):
@@ -77,26 +77,40 @@ def test_hadamard_blocks_equal_wht():
     assert err <= TOL
 
 
+@pytest.mark.parametrize("bdt", [torch.float32, torch.float16])
 @pytest.mark.parametrize("tokens", [1, 15, 16, 31, 100])
-def test_random_orthogonal(tokens):
+def test_random_orthogonal(tokens, bdt):
     rng = np.random.default_rng(tokens)
     x = synth.to_bf16(rng.standard_normal((tokens, 4096)))
     blocks = [synth.orthogonal_blocks(rng, 256, 16) for _ in range(3)]
     mask = synth.sign_bits_to_mask(rng.integers(0, 2, 4096))
-    y = run(x, blocks, mask=mask)
+    y = run(x, blocks, mask=mask, bdt=bdt)
     want = harp.harp_rotate(synth.bf16_to_f64(x), RAD, blocks, s=H.signs_from_bits(mask, 4096))
     err = compare.float_err(host64(y), want)[0]
     print(f"max scaled error {err:.3e}")
     assert err <= TOL
 
 
-def test_full_config_8192x4096_sampled():
+def test_fp16_blocks_match_fp32_blocks():
+    """The kernel rounds fp32 blocks to fp16 (nearest even) before its MFMAs,
+    so blocks handed over already rounded the same way give the same bits."""
+    rng = np.random.default_rng(77)
+    x = synth.to_bf16(rng.standard_normal((48, 4096)))
+    blocks = [synth.orthogonal_blocks(rng, 256, 16) for _ in range(3)]
+    mask = synth.sign_bits_to_mask(rng.integers(0, 2, 4096))
+    y32 = run(x, blocks, mask=mask, bdt=torch.float32)
+    y16 = run(x, blocks, mask=mask, bdt=torch.float16)
+    assert torch.equal(y32.cpu(), y16.cpu())
+
+
+@pytest.mark.parametrize("bdt", [torch.float16, torch.float32])
+def test_full_config_8192x4096_sampled(bdt):
+    """At the full size, with fp16 blocks as bench.py times them and fp32 blocks."""
     d = synth.harp()
-    y = W().harp_rotate(dev(d["x"]), dev(flat(d["blocks"])), d["radices"], mask_dev(d["signs"]), True)
+    y = W().harp_rotate(dev(d["x"]), dev(flat(d["blocks"], bdt)), d["radices"], mask_dev(d["signs"]), True)
     sel = np.r_[0:40, 4090:4110, 8150:8192]
     want = harp.harp_rotate(synth.bf16_to_f64(d["x"][sel]), RAD, d["blocks"],
                             s=H.signs_from_bits(d["signs"], 4096))
     err, roww = compare.float_err(host64(y[sel]), want)
     print(f"full config, sampled rows: max scaled error {err:.3e}, max row relative error {roww:.3e}")
-    print("harp 8192x4096 sampled: max scaled err", err, "max row rel err", roww)
     assert err <= TOL

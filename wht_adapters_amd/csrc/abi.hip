@@ -23,7 +23,7 @@ hipError_t launch_qwha(const void* x, int64_t tokens, int64_t ldx, const int32_t
                        const int32_t* col_idx, const void* vals, int val_dt, int64_t d_out,
                        void* y, int64_t ldy, hipStream_t s);
 hipError_t launch_harp(const void* x, void* y, int dt, int64_t tokens, int64_t ldx, int64_t ldy,
-                       const uint32_t* sbits, int precondition, const float* blocks, hipStream_t s);
+                       const uint32_t* sbits, int precondition, const void* blocks, int bdt, hipStream_t s);
 
 static thread_local int g_last_hip = 0;
 
@@ -201,8 +201,8 @@ whtq_status qwha_adapter_forward(const void* x, whtq_dtype x_dtype, int64_t toke
 
 whtq_status harp_rotate(const void* x, void* y, whtq_dtype dtype, int64_t tokens, int64_t d, int64_t ldx,
                         int64_t ldy, const uint32_t* sign_bits, int precondition, const int32_t* radices,
-                        int n_stages, const float* blocks, void* stream) {
-  if (!dt_valid(dtype)) return WHTQ_EINVAL;
+                        int n_stages, const void* blocks, whtq_dtype blocks_dtype, void* stream) {
+  if (!dt_valid(dtype) || !dt_valid(blocks_dtype)) return WHTQ_EINVAL;
   if (tokens < 0 || d < 1 || ldx < d || ldy < d) return WHTQ_EINVAL;
   if (!radices || n_stages < 1 || n_stages > 64 || !blocks) return WHTQ_EINVAL;
   if (precondition != 0 && precondition != 1) return WHTQ_EINVAL;
@@ -217,14 +217,14 @@ whtq_status harp_rotate(const void* x, void* y, whtq_dtype dtype, int64_t tokens
   if (tokens > 0 && x == y) return WHTQ_EINVAL;
   if (d != 4096 || n_stages != 3 || radices[0] != 16 || radices[1] != 16 || radices[2] != 16)
     return WHTQ_EUNSUPPORTED;
-  if (dtype != WHTQ_BF16) return WHTQ_EUNSUPPORTED;
+  if (dtype != WHTQ_BF16 || blocks_dtype == WHTQ_BF16) return WHTQ_EUNSUPPORTED;
   const int esz = dt_bytes(dtype);
   if (!rows_aligned(x, d, ldx, esz) || !rows_aligned(y, d, ldy, esz) || !aligned16(blocks)) return WHTQ_EALIGN;
   if (sign_bits && (reinterpret_cast<uintptr_t>(sign_bits) & 3u)) return WHTQ_EALIGN;
   if (tokens == 0) return WHTQ_OK;
   whtq_status st = need_device();
   if (st != WHTQ_OK) return st;
-  return hip_status(launch_harp(x, y, dtype, tokens, ldx, ldy, sign_bits, precondition, blocks,
+  return hip_status(launch_harp(x, y, dtype, tokens, ldx, ldy, sign_bits, precondition, blocks, blocks_dtype,
                                 (hipStream_t)stream));
 }
 

@@ -26,7 +26,7 @@ _SIG = {
     "rht_dequantize_inverse": [_vp, _vp, _i64, _i64, _vp, _int, _int, _vp, _int, _i64, _vp],
     "qwha_adapter_forward": [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _int, _i64, _i64, _vp, _int,
                              _i64, _vp],
-    "harp_rotate": [_vp, _vp, _int, _i64, _i64, _i64, _i64, _vp, _int, _vp, _int, _vp, _vp],
+    "harp_rotate": [_vp, _vp, _int, _i64, _i64, _i64, _i64, _vp, _int, _vp, _int, _vp, _int, _vp],
 }
 for _name, _args in _SIG.items():
     _f = getattr(_lib, _name)
@@ -182,12 +182,12 @@ def qwha_adapter_forward(x, row_ptr, col_idx, vals, d_out, out=None):
 
 
 def harp_rotate(x, blocks, radices=(16, 16, 16), signs=None, precondition=True, out=None):
-    """y = stages(Hn S x) (precondition) or stages(x); blocks fp32, stage-major."""
+    """y = stages(Hn S x) (precondition) or stages(x); blocks float32 or float16, stage-major."""
     _need_cuda("x", x)
     _need_cuda("blocks", blocks)
     tokens, d, ldx = _rows_ld("x", x)
-    if blocks.dtype != torch.float32 or not blocks.is_contiguous():
-        raise ValueError("blocks must be contiguous float32")
+    if blocks.dtype not in (torch.float32, torch.float16) or not blocks.is_contiguous():
+        raise ValueError("blocks must be contiguous float32 or float16")
     rad = (ctypes.c_int32 * len(radices))(*[int(b) for b in radices])
     if out is None:
         out = torch.empty_like(x)
@@ -197,5 +197,5 @@ def harp_rotate(x, blocks, radices=(16, 16, 16), signs=None, precondition=True, 
     with torch.cuda.device(x.device):
         _check("harp_rotate", _lib.harp_rotate(
             _ptr(x), _ptr(out), _DT[x.dtype], tokens, d, ldx, ldy, _sign_ptr(signs, d, x.device),
-            int(bool(precondition)), rad, len(radices), _ptr(blocks), _stream(x)))
+            int(bool(precondition)), rad, len(radices), _ptr(blocks), _DT[blocks.dtype], _stream(x)))
     return out
