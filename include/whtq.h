@@ -125,8 +125,9 @@ whtq_status rht_dequantize_inverse(const uint8_t* codes, const uint16_t* scales,
  *   row_ptr[d_out] = nnz, non-decreasing), col_idx int32[nnz] in [0, d_in),
  *   vals[nnz] in val_dtype (bf16 or f32).  The library does not read the CSR
  *   on the host: a malformed CSR gives undefined results.
- *   d_out in [1, 4096].  Accumulation in fp32; Hn x is kept on chip in fp16
- *   with a per-token power-of-two scale.
+ *   d_out in [1, 4096] (any value); col_idx and vals 16-byte aligned (the
+ *   common rule).  Accumulation in fp32; Hn x is kept on chip in fp16 with a
+ *   per-token power-of-two scale; each output is rounded once to bf16.
  */
 whtq_status qwha_adapter_forward(const void* x, whtq_dtype x_dtype, int64_t tokens, int64_t d_in,
                                  int64_t ldx, const int32_t* row_ptr, const int32_t* col_idx,

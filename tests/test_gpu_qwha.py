@@ -16,8 +16,8 @@ def W():
     return whtq
 
 
-def run(x, rp, ci, vals, d_out):
-    return W().qwha_adapter_forward(dev(x), dev(rp), dev(ci), dev(vals), d_out)
+def run(x, rp, ci, vals, d_out, out=None):
+    return W().qwha_adapter_forward(dev(x), dev(rp), dev(ci), dev(vals), d_out, out=out)
 
 
 def random_csr(rng, d_out, d_in, nnz, empty_rows=()):
@@ -32,7 +32,8 @@ def random_csr(rng, d_out, d_in, nnz, empty_rows=()):
     return rp, ci, vals[torch.from_numpy(order)]
 
 
-@pytest.mark.parametrize("tokens,d_out,nnz", [(37, 64, 1000), (8, 4096, 20000), (1, 8, 50), (130, 512, 9000)])
+@pytest.mark.parametrize("tokens,d_out,nnz", [(37, 64, 1000), (8, 4096, 20000), (1, 8, 50), (130, 512, 9000),
+                                             (13, 37, 800), (20, 2500, 30000), (9, 2049, 7000)])
 def test_random_csr(tokens, d_out, nnz):
     rng = np.random.default_rng(tokens + d_out)
     x = synth.to_bf16(rng.standard_normal((tokens, 4096)))
@@ -42,6 +43,36 @@ def test_random_csr(tokens, d_out, nnz):
     err, _ = compare.float_err(host64(y), want)
     assert err <= TOL, err
     assert torch.all(y[:, 0] == 0) and torch.all(y[:, 5] == 0)
+
+
+def test_short_rows_unaligned_output():
+    """d_out = 5: output rows of 10 bytes, stored with element stores."""
+    rng = np.random.default_rng(3)
+    x = synth.to_bf16(rng.standard_normal((9, 4096)))
+    rp, ci, v = random_csr(rng, 5, 4096, 300)
+    out = torch.empty((9, 5), dtype=torch.bfloat16, device="cuda")
+    y = run(x, rp, ci, v, 5, out=out)
+    want = qwha.qwha_forward(synth.bf16_to_f64(x), rp, ci, synth.bf16_to_f64(v), 5)
+    assert compare.float_err(host64(y), want)[0] <= TOL
+
+
+def test_dense_and_long_rows():
+    """Rows longer than the bucket cap (a full 4096-entry row), next to
+    single-entry rows and empty rows, in one chunk."""
+    rng = np.random.default_rng(4)
+    x = synth.to_bf16(rng.standard_normal((11, 4096)))
+    d_out = 300
+    lens = rng.integers(0, 3, d_out)
+    lens[7] = 4096
+    lens[150] = 4001
+    rows = np.repeat(np.arange(d_out), lens)
+    cols = np.concatenate([np.sort(rng.choice(4096, int(l), replace=False)) for l in lens])
+    rp = np.r_[0, np.cumsum(lens)].astype(np.int32)
+    v = synth.to_bf16(0.02 * rng.standard_normal(rows.size))
+    y = run(x, rp, cols.astype(np.int32), v, d_out)
+    want = qwha.qwha_forward(synth.bf16_to_f64(x), rp, cols.astype(np.int32), synth.bf16_to_f64(v), d_out)
+    err, _ = compare.float_err(host64(y), want)
+    assert err <= TOL, err
 
 
 def test_identity_and_single_nonzero():
@@ -81,5 +112,5 @@ def test_full_config_2048x4096_nnz262144():
     want = qwha.qwha_forward(synth.bf16_to_f64(d["x"]), d["row_ptr"], d["col_idx"],
                              synth.bf16_to_f64(d["vals"]), d["d_out"])
     err, roww = compare.float_err(host64(y), want)
-    print("qwha 2048x4096 nnz 262144: max scaled err", err, "max row rel err", roww)
+    print(f"qwha 2048x4096 nnz 262144: max scaled error {err:.3e}, max row relative error {roww:.3e}")
     assert err <= TOL

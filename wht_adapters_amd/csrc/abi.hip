@@ -20,7 +20,7 @@ hipError_t launch_rht_dequant(int logn, int dout, int bits, int logg, const uint
                               const uint16_t* scales, int64_t rows, const uint32_t* sb, void* out,
                               int64_t ldo, hipStream_t s);
 hipError_t launch_qwha(const void* x, int64_t tokens, int64_t ldx, const int32_t* row_ptr,
-                       const int32_t* col_idx, const void* vals, int val_dt, int64_t d_out,
+                       const int32_t* col_idx, const void* vals, int val_dt, int64_t d_out, int64_t nnz,
                        void* y, int64_t ldy, hipStream_t s);
 hipError_t launch_harp(const void* x, void* y, int dt, int64_t tokens, int64_t ldx, int64_t ldy,
                        const uint32_t* sbits, int precondition, const void* blocks, int bdt, hipStream_t s);
@@ -188,14 +188,11 @@ whtq_status qwha_adapter_forward(const void* x, whtq_dtype x_dtype, int64_t toke
   if (x_dtype != WHTQ_BF16 || y_dtype != WHTQ_BF16) return WHTQ_EUNSUPPORTED;
   if (val_dtype != WHTQ_BF16 && val_dtype != WHTQ_F32) return WHTQ_EUNSUPPORTED;
   if (!rows_aligned(x, d_in, ldx, 2) || !rows_aligned(y, d_out, ldy, 2)) return WHTQ_EALIGN;
-  if ((reinterpret_cast<uintptr_t>(row_ptr) & 3u) || (reinterpret_cast<uintptr_t>(col_idx) & 3u) ||
-      (reinterpret_cast<uintptr_t>(vals) % (uintptr_t)dt_bytes(val_dtype)))
-    return WHTQ_EALIGN;
-  if (d_out % 8) return WHTQ_EUNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(row_ptr) & 3u) || !aligned16(col_idx) || !aligned16(vals)) return WHTQ_EALIGN;
   if (tokens == 0) return WHTQ_OK;
   whtq_status st = need_device();
   if (st != WHTQ_OK) return st;
-  return hip_status(launch_qwha(x, tokens, ldx, row_ptr, col_idx, vals, val_dtype, d_out, y, ldy,
+  return hip_status(launch_qwha(x, tokens, ldx, row_ptr, col_idx, vals, val_dtype, d_out, nnz, y, ldy,
                                 (hipStream_t)stream));
 }
 

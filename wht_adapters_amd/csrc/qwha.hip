@@ -6,17 +6,21 @@
 // y = x Delta W^T = (x Hn) F^T.
 //
 // One block per tile of 8 tokens:
-//   1. each wave transforms one token row at a time with the register / LDS
-//      FWHT engine (fp32); the row is scaled by an exact power of two so its
-//      largest entry sits near 2^14, rounded to fp16 and staged token-major;
+//   1. each of 4 waves transforms token rows with the register / LDS FWHT
+//      engine (fp32); a row is scaled by an exact power of two so its largest
+//      entry sits in [2^13, 2^14), rounded to fp16 and staged token-major;
 //   2. the staged tile is re-laid out to Z[k][8 tokens] (16 bytes per
 //      column), so one ds_read_b128 returns a column for all 8 tokens;
-//   3. rows of F are bucketed by their nnz (ceil(nnz / 8)) so that the 8 rows
-//      a wave handles together need about the same number of iterations;
-//   4. CSR gather SpMM: 8 lanes per row, up to 8 nonzeros per lane per step
-//      with the next row group's first step fetched ahead, 8 fp32
-//      accumulators per lane (v_fma_mix with the fp16 column), a DPP
-//      reduction over the 8 lanes; each lane stores one token's bf16 output.
+//   3. the rows of F are taken in chunks of 2048 consecutive rows; within a
+//      chunk they are bucketed by the number of 16-entry steps they need
+//      (longest first), so the 16 rows a wave handles together finish at
+//      about the same time;
+//   4. CSR gather SpMM: a quad of lanes per row, each lane taking 4
+//      consecutive entries per step with 16-byte index loads (the quad reads
+//      64 contiguous bytes of col_idx), 8 fp32 accumulators per lane
+//      (v_fma_mix with the fp16 column), a quad DPP reduction per row; the
+//      results go to a token-major bf16 buffer in LDS;
+//   5. the chunk's outputs leave with 16-byte row-contiguous stores.
 #include "io.hpp"
 #include "launch.hpp"
 
@@ -25,43 +29,64 @@ namespace whtq {
 namespace qw {
 constexpr int LOGN = 12;
 constexpr int N = 1 << LOGN;
-constexpr int TT = 8;                     // tokens per block
-constexpr int THREADS = 1024;             // 16 waves (4 transform token rows)
-constexpr int NBKT = 512;                 // nnz buckets: ceil(nnz / 8), capped
-constexpr int FWAVES = 4;                 // waves that run the token transforms
-constexpr int UNROLL = 8;                 // nonzeros per lane per step
+constexpr int TT = 8;          // tokens per block
+constexpr int THREADS = 1024;  // 16 waves (4 transform token rows)
+constexpr int NW = THREADS / 64;
+constexpr int FWAVES = 4;      // waves that run the token transforms
+constexpr int CHUNK = 2048;    // rows per output chunk
+constexpr int NBKT = 256;      // buckets: 16-entry steps per row, capped
 }  // namespace qw
 
 // LDS map (bytes):
-//   [0, 64K)        Z[k][tok] fp16, 16 B per column      (FWHT scratch before step 2)
-//   [64K, 128K)     staging Zt[tok][k] fp16 in steps 1-2; afterwards the
-//                   length-sorted row list: id (u16), start (i32), length (u16)
-//   [128K, +2K)     bucket counters (uint32)
-//   [+2K, +32)      per-token exponent
+//   [0, 64K)      Z[k][tok] fp16, 16 B per column     (FWHT scratch before step 2)
+//   [64K, 128K)   staging Zt[tok][k] fp16 in steps 1-2; afterwards, per chunk,
+//                 the sorted row list (row u16, start i32, end i32) and the
+//                 output buffer O[tok][row] bf16
+//   [128K, +1K)   bucket counters (uint32)
+//   [+1K, +32)    per-token exponent
 constexpr int QW_LDS_Z = 0;
-constexpr int QW_LDS_Y = 65536;
-constexpr int QW_LDS_RID = QW_LDS_Y;
-constexpr int QW_LDS_RBEG = QW_LDS_Y + 8192;
-constexpr int QW_LDS_RLEN = QW_LDS_Y + 8192 + 16384;
+constexpr int QW_LDS_ZT = 65536;
+constexpr int QW_LDS_RID = 65536;
+constexpr int QW_LDS_RBEG = QW_LDS_RID + 2 * qw::CHUNK;
+constexpr int QW_LDS_REND = QW_LDS_RBEG + 4 * qw::CHUNK;
+constexpr int QW_LDS_OUT = QW_LDS_REND + 4 * qw::CHUNK;
 constexpr int QW_LDS_BKT = 131072;
 constexpr int QW_LDS_EXP = QW_LDS_BKT + 4 * qw::NBKT;
 constexpr int QW_LDS_BYTES = QW_LDS_EXP + 4 * qw::TT;
+static_assert(QW_LDS_OUT % 16 == 0 && QW_LDS_OUT + 2 * qw::TT * qw::CHUNK <= QW_LDS_BKT,
+              "row list + output buffer fit the staging area");
 
-__device__ __forceinline__ float dpp_sum8(float x) {
-  // sum over the 8 lanes of an aligned lane octet; every lane gets the total
-  x += as_f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u(x), 0xB1, 0xF, 0xF, true));   // ^1
-  x += as_f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u(x), 0x4E, 0xF, 0xF, true));   // ^2
-  x += as_f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u(x), 0x141, 0xF, 0xF, true));  // row_half_mirror
-  return x;
-}
+// 16-entry steps of a row [beg, end) whose steps start at beg rounded down to a multiple of 4
+__device__ __forceinline__ int qw_steps(int beg, int end) { return end > beg ? (end - (beg & ~3) + 15) >> 4 : 0; }
+
+// four consecutive values of F, from an index that is a multiple of 4
+template <int VALDT> struct ValQuad;
+template <> struct ValQuad<DT_BF16> {  // 8 bytes
+  typedef u32x2 raw;
+  static __device__ __forceinline__ raw load(const void* v, int j) {
+    return ldg<u32x2>(reinterpret_cast<const uint8_t*>(v) + 2u * (uint32_t)j);
+  }
+  static __device__ __forceinline__ float get(const raw& r, int q) {
+    const uint32_t w = q < 2 ? r.x : r.y;
+    return (q & 1) ? bf16hi(w) : bf16lo(w);
+  }
+};
+template <> struct ValQuad<DT_F32> {  // 16 bytes
+  typedef f32x4 raw;
+  static __device__ __forceinline__ raw load(const void* v, int j) {
+    return ldg<f32x4>(reinterpret_cast<const uint8_t*>(v) + 4u * (uint32_t)j);
+  }
+  static __device__ __forceinline__ float get(const raw& r, int q) { return r[q]; }
+};
 
 template <int VALDT>
 __global__ __launch_bounds__(qw::THREADS) void k_qwha(const uint16_t* __restrict__ x, int64_t tokens,
                                                       int64_t ldx, const int32_t* __restrict__ row_ptr,
                                                       const int32_t* __restrict__ col_idx,
-                                                      const void* __restrict__ vals, int d_out,
-                                                      uint16_t* __restrict__ y, int64_t ldy) {
+                                                      const void* __restrict__ vals, int d_out, int nnz,
+                                                      uint16_t* __restrict__ y, int64_t ldy, int vec_out) {
   using G = Geo<qw::LOGN>;
+  using V = ValQuad<VALDT>;
   extern __shared__ __align__(16) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t tok0 = (int64_t)blockIdx.x * qw::TT;
@@ -69,23 +94,27 @@ __global__ __launch_bounds__(qw::THREADS) void k_qwha(const uint16_t* __restrict
 
   uint16_t* rid = reinterpret_cast<uint16_t*>(smem + QW_LDS_RID);
   int* rbeg = reinterpret_cast<int*>(smem + QW_LDS_RBEG);
-  uint16_t* rlen = reinterpret_cast<uint16_t*>(smem + QW_LDS_RLEN);
+  int* rend = reinterpret_cast<int*>(smem + QW_LDS_REND);
+  uint16_t* obuf = reinterpret_cast<uint16_t*>(smem + QW_LDS_OUT);
   uint32_t* bkt = reinterpret_cast<uint32_t*>(smem + QW_LDS_BKT);
   int* texp = reinterpret_cast<int*>(smem + QW_LDS_EXP);
 
-  // ---- 3a. bucket histogram of row lengths (overlaps with the transforms)
+  auto histogram = [&](int base, int cn) {
+    for (int r = tid; r < cn; r += qw::THREADS) {
+      const int st = qw_steps(row_ptr[base + r], row_ptr[base + r + 1]);
+      atomicAdd(&bkt[qw::NBKT - 1 - min(st, qw::NBKT - 1)], 1u);  // longest rows first
+    }
+  };
+
+  // ---- bucket histogram of the first chunk (overlaps with the transforms)
   for (int i = tid; i < qw::NBKT; i += qw::THREADS) bkt[i] = 0;
   __syncthreads();
-  for (int o = tid; o < d_out; o += qw::THREADS) {
-    const int len = row_ptr[o + 1] - row_ptr[o];
-    const int b = min((len + 7) >> 3, qw::NBKT - 1);
-    atomicAdd(&bkt[qw::NBKT - 1 - b], 1u);  // longest rows first
-  }
+  histogram(0, min(qw::CHUNK, d_out));
 
   // ---- 1. FWHT of the token rows, staged as fp16 token-major
   if (wave < qw::FWAVES) {
     float* scratch = reinterpret_cast<float*>(smem + QW_LDS_Z) + wave * G::LDS_ROW;
-    uint16_t* zt = reinterpret_cast<uint16_t*>(smem + QW_LDS_Y);
+    uint16_t* zt = reinterpret_cast<uint16_t*>(smem + QW_LDS_ZT);
     const int t = lane;
     const bool rho = rho_B<qw::LOGN>(t);
     int col[8];
@@ -130,7 +159,7 @@ __global__ __launch_bounds__(qw::THREADS) void k_qwha(const uint16_t* __restrict
 
   // ---- 2. Zt[tok][k] -> Z[k][tok]
   {
-    const uint16_t* zt = reinterpret_cast<const uint16_t*>(smem + QW_LDS_Y);
+    const uint16_t* zt = reinterpret_cast<const uint16_t*>(smem + QW_LDS_ZT);
     u32x4* z = reinterpret_cast<u32x4*>(smem + QW_LDS_Z);
     for (int kk = tid; kk < qw::N; kk += qw::THREADS) {
       uint32_t h[qw::TT];
@@ -139,132 +168,194 @@ __global__ __launch_bounds__(qw::THREADS) void k_qwha(const uint16_t* __restrict
       z[kk] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
     }
   }
-  // ---- 3b. bucket offsets (one wave), then scatter row ids
-  if (wave == 0) {
-    uint32_t run = 0;
-    for (int base = 0; base < qw::NBKT; base += 64) {
-      const uint32_t c = bkt[base + lane];
-      uint32_t incl = c;
-#pragma unroll
-      for (int s = 1; s < 64; s <<= 1) {
-        const uint32_t o = __shfl_up(incl, s);
-        if (lane >= s) incl += o;
-      }
-      bkt[base + lane] = run + incl - c;
-      run += __shfl(incl, 63);
+  __syncthreads();  // the staging area becomes the row list / output buffer
+
+  const int slot = lane & 3;  // lane within the row's quad
+  // tokens 2 slot, 2 slot + 1: undo the staging scale 2^(14-e) and normalise by 1/sqrt(4096)
+  const float osc0 = ldexpf(1.0f, texp[2 * slot] - 20), osc1 = ldexpf(1.0f, texp[2 * slot + 1] - 20);
+
+  for (int base = 0; base < d_out; base += qw::CHUNK) {
+    const int cn = min(qw::CHUNK, d_out - base);
+    if (base > 0) {
+      for (int i = tid; i < qw::NBKT; i += qw::THREADS) bkt[i] = 0;
+      __syncthreads();
+      histogram(base, cn);
     }
-  }
-  __syncthreads();
-  for (int o = tid; o < d_out; o += qw::THREADS) {
-    const int beg = row_ptr[o];
-    const int len = row_ptr[o + 1] - beg;
-    const int b = min((len + 7) >> 3, qw::NBKT - 1);
-    const uint32_t pos = atomicAdd(&bkt[qw::NBKT - 1 - b], 1u);
-    rid[pos] = (uint16_t)o;
-    rbeg[pos] = beg;
-    rlen[pos] = (uint16_t)min(len, 65535);
-  }
-  __syncthreads();
-
-  // ---- 4. gather SpMM: lane octet j of a wave handles sorted row 8*grp + j
-  {
-    const u32x4* z = reinterpret_cast<const u32x4*>(smem + QW_LDS_Z);
-    const int oct = lane >> 3, slot = lane & 7;
-    const float osc = ldexpf(1.0f, texp[min(slot, qw::TT - 1)] - 20);  // 2^(e-14) / 64 of token `slot`
-    constexpr int NW = qw::THREADS / 64;
-    const int ngrp = d_out >> 3;
-
-    // one step = up to UNROLL nonzeros per lane: j = start + slot + 8 u
-    struct Step { int c[qw::UNROLL]; float fv[qw::UNROLL]; };
-    auto fetch = [&](Step& st, int start, int end) {
+    __syncthreads();
+    // ---- 3. bucket offsets (one wave), then scatter the chunk's rows
+    if (wave == 0) {
+      uint32_t run = 0;
+      for (int b0 = 0; b0 < qw::NBKT; b0 += 64) {
+        const uint32_t c = bkt[b0 + lane];
+        uint32_t incl = c;
 #pragma unroll
-      for (int u = 0; u < qw::UNROLL; ++u) {
-        const int j = start + slot + 8 * u;
-        const bool ok = j < end;
-        st.c[u] = ok ? col_idx[j] : -1;
-        if constexpr (VALDT == DT_BF16)
-          st.fv[u] = ok ? bf16lo((uint32_t)reinterpret_cast<const uint16_t*>(vals)[j]) : 0.f;
-        else
-          st.fv[u] = ok ? reinterpret_cast<const float*>(vals)[j] : 0.f;
+        for (int s = 1; s < 64; s <<= 1) {
+          const uint32_t o = __shfl_up(incl, s);
+          if (lane >= s) incl += o;
+        }
+        bkt[b0 + lane] = run + incl - c;
+        run += __shfl(incl, 63);
       }
+    }
+    __syncthreads();
+    for (int r = tid; r < cn; r += qw::THREADS) {
+      const int beg = row_ptr[base + r], end = row_ptr[base + r + 1];
+      const uint32_t pos = atomicAdd(&bkt[qw::NBKT - 1 - min(qw_steps(beg, end), qw::NBKT - 1)], 1u);
+      rid[pos] = (uint16_t)r;
+      rbeg[pos] = beg;
+      rend[pos] = end;
+    }
+    __syncthreads();
+
+    // ---- 4. gather SpMM: group g = 16 sorted rows, one quad of lanes per
+    // row; a wave takes groups rr NW + (wave, or NW - 1 - wave on odd rr):
+    // snake order, so that long and short groups mix.  The index / value
+    // loads run one step ahead, across group boundaries.
+    const int ng = nnz > 0 ? (cn + 15) >> 4 : 0;
+    if (nnz == 0)  // F = 0: every output is zero
+      for (int i = tid; i < qw::TT * cn; i += qw::THREADS) obuf[(i / cn) * qw::CHUNK + i % cn] = 0;
+    struct Row {
+      int r, beg, end, nst;
     };
-    auto consume = [&](const Step& st, float* acc) {
+    auto row_of = [&](int rr) {
+      const int g = rr * qw::NW + ((rr & 1) ? qw::NW - 1 - wave : wave);
+      const int p = 16 * g + (lane >> 2);
+      Row w{0, 0, 0, 0};
+      if (g < ng && p < cn) {
+        w.r = rid[p];
+        w.beg = rbeg[p];
+        w.end = rend[p];
+        w.nst = qw_steps(w.beg, w.end);
+      }
+      return w;
+    };
+    // index / value loads of one step, kept in two alternating buffers (even
+    // steps in A, odd in B) so that a load is never copied while in flight
+    struct Buf {
+      u32x4 cw;
+      typename V::raw vw;
+    };
+    // this lane's entries of step s of a row: [(beg & ~3) + 16 s + 4 slot, + 4)
+    // The whole aligned 16-byte index block (8 or 16 bytes of values) holding
+    // entry jj is read even where the arrays end inside it: an aligned block
+    // never straddles a page, and entries outside the row are masked below.
+    // Every step issues the same two loads (a step with nothing to do reads
+    // block 0) so that the outstanding-load count is the same on every path
+    // and a use waits only for its own buffer.
+    auto load_step = [&](const Row& w, int s, Buf& b) {
+      int jj = (w.beg & ~3) + 16 * s + 4 * slot;
+      jj = (s < w.nst && jj < w.end) ? jj : 0;
+      b.cw = ldg<u32x4>(reinterpret_cast<const uint8_t*>(col_idx) + 4u * (uint32_t)jj);
+      b.vw = V::load(vals, jj);
+    };
+    auto run_step = [&](const Row& w, int s, const Buf& b, float* acc) {
+      const int jc = (w.beg & ~3) + 16 * s + 4 * slot;
+      if (s >= w.nst || jc >= w.end) return;
+      // the four Z columns first, then their 32 FMAs
+      u32x4 cw = b.cw;
+      float v[4];
 #pragma unroll
-      for (int u = 0; u < qw::UNROLL; ++u) {
-        if (st.c[u] >= 0) {
-          // (copied out as words: subscripting the loaded vector with the
-          // unrolled loop index was miscompiled into a single 4-byte read)
-          uint32_t zc[4];
-          __builtin_memcpy(zc, &z[st.c[u]], 16);
+      for (int q = 0; q < 4; ++q) v[q] = V::get(b.vw, q);
+      if (jc < w.beg || jc + 4 > w.end) {  // the row's first or last quad: drop other entries
 #pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            fma_mix_lo(acc[2 * p], st.fv[u], zc[p]);
-            fma_mix_hi(acc[2 * p + 1], st.fv[u], zc[p]);
-          }
+        for (int q = 0; q < 4; ++q) {
+          v[q] = (jc + q >= w.beg && jc + q < w.end) ? v[q] : 0.f;
+          cw[q] &= (uint32_t)(qw::N - 1);  // past the arrays' end the index is arbitrary
+        }
+      }
+      u32x4 zv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) zv[q] = *reinterpret_cast<const u32x4*>(smem + QW_LDS_Z + (cw[q] << 4));
+      // (copied out as words: subscripting the loaded vectors with the
+      // unrolled loop index was miscompiled into a single 4-byte read)
+      uint32_t zc[4][4];
+      __builtin_memcpy(zc, zv, 64);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+          fma_mix_lo(acc[2 * w2], v[q], zc[q][w2]);
+          fma_mix_hi(acc[2 * w2 + 1], v[q], zc[q][w2]);
         }
       }
     };
-
-    Step cur, nxt;
-    int g = wave;
-    int pos = g * 8 + oct;
-    int beg = g < ngrp ? rbeg[pos] : 0;
-    int end = g < ngrp ? beg + rlen[pos] : 0;
-    fetch(cur, beg, end);
-    for (; g < ngrp; g += NW) {
-      const int o = rid[pos];
-      // fetch the next group's first step before working on this one
-      const int gn = g + NW;
-      const int posn = gn * 8 + oct;
-      const int begn = gn < ngrp ? rbeg[posn] : 0;
-      const int endn = gn < ngrp ? begn + rlen[posn] : 0;
-      fetch(nxt, begn, endn);
+    Buf A{}, B{};
+    Row cur = row_of(0);
+    load_step(cur, 0, A);
+    for (int rr = 0; rr * qw::NW < ng; ++rr) {
+      const Row nxt = row_of(rr + 1);
       float acc[qw::TT];
 #pragma unroll
       for (int k = 0; k < qw::TT; ++k) acc[k] = 0.f;
-      consume(cur, acc);
-      // rows longer than 8 * UNROLL (few after sorting) take more steps
-      for (int j0 = beg + 8 * qw::UNROLL; __builtin_amdgcn_ballot_w64(j0 < end); j0 += 8 * qw::UNROLL) {
-        Step more;
-        fetch(more, j0, end);
-        consume(more, acc);
+      // steps in pairs (an odd count gets an empty last step); the group after
+      // this one starts in buffer A again
+      for (int s = 0; s < cur.nst || s == 0; s += 2) {
+        load_step(cur, s + 1, B);
+        run_step(cur, s, A, acc);
+        if (s + 2 < cur.nst) load_step(cur, s + 2, A);
+        else load_step(nxt, 0, A);
+        run_step(cur, s + 1, B, acc);
       }
-      float mine = 0.f;
+      // quad all-reduce: every lane of the quad gets the row's 8 sums
 #pragma unroll
       for (int k = 0; k < qw::TT; ++k) {
-        const float sum = dpp_sum8(acc[k]);
-        mine = slot == k ? sum : mine;
+        acc[k] += as_f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u(acc[k]), 0xB1, 0xF, 0xF, true));  // ^1
+        acc[k] += as_f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u(acc[k]), 0x4E, 0xF, 0xF, true));  // ^2
       }
-      if (slot < ntok)
-        y[(tok0 + slot) * ldy + o] = (uint16_t)(pack_bf16(mine * osc, 0.f) & 0xffffu);
+      const int g = rr * qw::NW + ((rr & 1) ? qw::NW - 1 - wave : wave);
+      if (g < ng && 16 * g + (lane >> 2) < cn) {  // lane `slot` writes tokens 2 slot, 2 slot + 1
+        float a = acc[0], b = acc[1];
+#pragma unroll
+        for (int k = 1; k < 4; ++k) {
+          a = slot == k ? acc[2 * k] : a;
+          b = slot == k ? acc[2 * k + 1] : b;
+        }
+        const uint32_t ab = pack_bf16(a * osc0, b * osc1);
+        obuf[(2 * slot) * qw::CHUNK + cur.r] = (uint16_t)(ab & 0xffffu);
+        obuf[(2 * slot + 1) * qw::CHUNK + cur.r] = (uint16_t)(ab >> 16);
+      }
       cur = nxt;
-      pos = posn;
-      beg = begn;
-      end = endn;
     }
+    __syncthreads();
+
+    // ---- 5. the chunk's outputs, row-contiguous
+    const int cq = (cn + 7) >> 3;
+    for (int i = tid; i < ntok * cq; i += qw::THREADS) {
+      const int t = i / cq, q = i - t * cq;
+      const uint16_t* src = obuf + t * qw::CHUNK + 8 * q;
+      uint16_t* dst = y + (tok0 + t) * ldy + base + 8 * q;
+      if (vec_out && 8 * q + 8 <= cn) {
+        stg(dst, *reinterpret_cast<const u32x4*>(src));
+      } else {
+        for (int e = 0; e < 8 && 8 * q + e < cn; ++e) dst[e] = src[e];
+      }
+    }
+    __syncthreads();  // the next chunk reuses the row list and the output buffer
   }
 }
 
 hipError_t launch_qwha(const void* x, int64_t tokens, int64_t ldx, const int32_t* row_ptr,
-                       const int32_t* col_idx, const void* vals, int val_dt, int64_t d_out, void* y,
-                       int64_t ldy, hipStream_t s) {
+                       const int32_t* col_idx, const void* vals, int val_dt, int64_t d_out, int64_t nnz,
+                       void* y, int64_t ldy, hipStream_t s) {
   const unsigned grid = (unsigned)((tokens + qw::TT - 1) / qw::TT);
+  // 16-byte output stores need a 16-byte aligned base and row stride
+  const int vec_out = ((reinterpret_cast<uintptr_t>(y) & 15u) == 0 && (ldy * 2) % 16 == 0) ? 1 : 0;
   if (val_dt == DT_BF16) {
     static const bool attr = hipFuncSetAttribute((const void*)k_qwha<DT_BF16>,
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
                                                  QW_LDS_BYTES) == hipSuccess;
     (void)attr;
     hipLaunchKernelGGL(k_qwha<DT_BF16>, dim3(grid), dim3(qw::THREADS), QW_LDS_BYTES, s,
-                       (const uint16_t*)x, tokens, ldx, row_ptr, col_idx, vals, (int)d_out,
-                       (uint16_t*)y, ldy);
+                       (const uint16_t*)x, tokens, ldx, row_ptr, col_idx, vals, (int)d_out, (int)nnz,
+                       (uint16_t*)y, ldy, vec_out);
   } else {
     static const bool attr = hipFuncSetAttribute((const void*)k_qwha<DT_F32>,
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
                                                  QW_LDS_BYTES) == hipSuccess;
     (void)attr;
     hipLaunchKernelGGL(k_qwha<DT_F32>, dim3(grid), dim3(qw::THREADS), QW_LDS_BYTES, s,
-                       (const uint16_t*)x, tokens, ldx, row_ptr, col_idx, vals, (int)d_out,
-                       (uint16_t*)y, ldy);
+                       (const uint16_t*)x, tokens, ldx, row_ptr, col_idx, vals, (int)d_out, (int)nnz,
+                       (uint16_t*)y, ldy, vec_out);
   }
   return hipGetLastError();
 }

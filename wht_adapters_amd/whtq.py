@@ -170,7 +170,9 @@ def qwha_adapter_forward(x, row_ptr, col_idx, vals, d_out, out=None):
     if vals.numel() != nnz:
         raise ValueError("vals and col_idx must have the same length")
     if out is None:
-        out = torch.empty((tokens, d_out), dtype=x.dtype, device=x.device)
+        # rows of 16 bytes or more need a 16-byte row stride: pad the storage to a multiple of 8
+        width = d_out if d_out < 8 else -(-d_out // 8) * 8
+        out = torch.empty((tokens, width), dtype=x.dtype, device=x.device)[:, :d_out]
     r2, n2, ldy = _rows_ld("out", out)
     if (r2, n2) != (tokens, d_out):
         raise ValueError("out shape mismatch")
