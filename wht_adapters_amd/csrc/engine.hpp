@@ -201,6 +201,23 @@ constexpr bool rho_A_reg(int r) {
 __device__ __forceinline__ uint32_t sign_byte(const uint32_t* bits, int base) {
   return (bits[base >> 5] >> (base & 31)) & 0xffu;
 }
+// All +1 signs for the largest row (8192 bits): read in place of a sign
+// vector when none applies, so that sign loads need no branch.
+__device__ uint32_t kNoSigns[256];  // zero-initialised, never written
+
+// Sign bytes at bases base[0..NC) (multiples of 8) of a uint32 bitmask, or
+// zeros when `on` is false (`on` must be uniform).  The loads are
+// unconditional (kNoSigns stands in), so they go out back to back and the
+// compiler can put independent loads ahead of their first use.
+template <int NC>
+__device__ __forceinline__ void sign_bytes(const uint32_t* bits, bool on, const int* base, uint32_t* sb) {
+  const uint32_t* p = on ? bits : kNoSigns;
+  uint32_t wv[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) wv[c] = p[base[c] >> 5];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) sb[c] = (wv[c] >> (base[c] & 31)) & 0xffu;
+}
 // XOR mask flipping the sign bits of a 16-bit pair from two sign bits.
 __device__ __forceinline__ uint32_t pair_mask16(uint32_t b2) {
   return ((b2 & 1u) << 15) | ((b2 & 2u) << 30);

@@ -252,13 +252,15 @@ __global__ __launch_bounds__(hp::THREADS) void k_harp(const uint16_t* __restrict
   const bool pre = precondition != 0;
 
   // sign-flip masks for the lane's load columns 8 (lane + 64 r) .. + 7
-  uint32_t msk[8][4];
+  uint32_t msk[8][4], sb[8];
+  int sbase[8];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const uint32_t sb = (pre && sbits) ? sign_byte(sbits, 8 * (lane + 64 * r)) : 0u;
+  for (int r = 0; r < 8; ++r) sbase[r] = 8 * (lane + 64 * r);
+  sign_bytes<8>(sbits, pre && sbits != nullptr, sbase, sb);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) msk[r][q] = pair_mask16(sb >> (2 * q));
-  }
+  for (int r = 0; r < 8; ++r)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) msk[r][q] = pair_mask16(sb[r] >> (2 * q));
   // G = H16 / 4 as the A operand: G[m = n][k = 4 kg + i]
   f16x4_t g;
   uint32_t gbh[4];

@@ -66,30 +66,42 @@ __global__ __launch_bounds__(Geo<LOGN>::THREADS) void k_rht_quant(
   __shared__ float lds[G::TWO ? RPB * G::LDS_ROW : 1];
   float* myrow = lds + slot * G::LDS_ROW;
 
-  // per-lane sign masks for the load layout (A when two-phase, else B)
+  // per-lane sign bytes for the load layout (A when two-phase, else B)
   int col[8];
   uint32_t sb[8], m[8][4];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    col[c] = G::TWO ? G::idxA(t, c * 8) : t * 64 + c * 8;
-    sb[c] = sbits ? sign_byte(sbits, col[c]) : 0u;
+  for (int c = 0; c < 8; ++c) col[c] = G::TWO ? G::idxA(t, c * 8) : t * 64 + c * 8;
+  sign_bytes<8>(sbits, sbits != nullptr, col, sb);
+  // rows past the end (last block only) transform a copy of the last row
+  // and store nothing, so every lane runs the same code without branches
+  auto row_ptr = [&](int64_t g) {
+    const int64_t row = g * RPB + slot;
+    return w + (row < rows ? row : rows - 1) * ldw_b;
+  };
+  // One-wave blocks (n <= 4096, a row or two per wave at typical sizes) peel
+  // the first row: its loads go out right behind the sign-byte loads, before
+  // the masks are built, so the mask arithmetic overlaps the row's HBM
+  // latency (loads complete in order: the masks wait for the sign bytes
+  // only).  The grid never exceeds the row groups, so the row exists.  Wider
+  // rows run many rows per block and keep the plain loop (the peeled copy
+  // would cost them occupancy).
+  constexpr bool PEEL = G::THREADS == 64;
+  Raw8 raw[8];
+  if constexpr (PEEL) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) fetch8<DIN>(row_ptr(blockIdx.x), col[c], raw[c]);
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
 #pragma unroll
     for (int q = 0; q < 4; ++q) m[c][q] = pair_mask16(sb[c] >> (2 * q));
-  }
 
-  for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
+  auto do_row = [&](int64_t g) {
     const int64_t row = g * RPB + slot;
     const bool valid = row < rows;
-    // rows past the end (last block only) transform a copy of the last row
-    // and store nothing, so every lane runs the same code without branches
-    const uint8_t* wr = w + (valid ? row : rows - 1) * ldw_b;
     float v[64];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      Raw8 raw;
-      fetch8<DIN>(wr, col[c], raw);
-      widen8<DIN, true>(raw, v + 8 * c, m[c], sb[c]);
-    }
+    for (int c = 0; c < 8; ++c) widen8<DIN, true>(raw[c], v + 8 * c, m[c], sb[c]);
     // 16-bit loads arrive with the index-bit 0 and 1 butterflies applied
     if constexpr (G::TWO) {
       stages_A<LOGN, DIN == DT_F32>(v, t);
@@ -162,6 +174,12 @@ __global__ __launch_bounds__(Geo<LOGN>::THREADS) void k_rht_quant(
         if (t % SPAN == 0) sr[t / SPAN] = s16b[0];
       }
     }
+  };
+  if constexpr (PEEL) do_row(blockIdx.x);
+  for (int64_t g = blockIdx.x + (PEEL ? gridDim.x : 0); g < ngroups; g += gridDim.x) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) fetch8<DIN>(row_ptr(g), col[c], raw[c]);
+    do_row(g);
   }
 }
 
@@ -222,16 +240,18 @@ __global__ __launch_bounds__(Geo<LOGN>::THREADS) void k_rht_dequant(
 
   // output sign masks (S and the rho of the DPP butterflies) for the store layout
   uint32_t sb[8], m[8][4];
+  int obase[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) obase[c] = G::TWO ? G::idxA(t, c * 8) : t * 64 + c * 8;
+  sign_bytes<8>(sbits, sbits != nullptr, obase, sb);
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     if constexpr (G::TWO) {
       const bool rl = rho_A_lane<LOGN>(t);
-      sb[c] = sbits ? sign_byte(sbits, G::idxA(t, c * 8)) : 0u;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (rl ^ rho_A_reg<LOGN>(c * 8 + e)) sb[c] ^= 1u << e;
     } else {
-      sb[c] = sbits ? sign_byte(sbits, t * 64 + c * 8) : 0u;
       if (rho_B<LOGN>(t)) sb[c] ^= 0xffu;
     }
 #pragma unroll

@@ -29,12 +29,12 @@ __global__ __launch_bounds__(Geo<LOGN>::THREADS) void k_wht(const uint8_t* x, ui
     int col[8];
     uint32_t sb[8], m[8][4];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      col[c] = G::idxA(t, c * 8);
-      sb[c] = sign_mode == SIGN_BEFORE ? sign_byte(sbits, col[c]) : 0u;
+    for (int c = 0; c < 8; ++c) col[c] = G::idxA(t, c * 8);
+    sign_bytes<8>(sbits, sign_mode == SIGN_BEFORE, col, sb);
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
 #pragma unroll
       for (int q = 0; q < 4; ++q) m[c][q] = pair_mask16(sb[c] >> (2 * q));
-    }
     uint32_t sa0 = 0, sa1 = 0;
     if (sign_mode == SIGN_AFTER) { sa0 = sbits[2 * t]; sa1 = sbits[2 * t + 1]; }
 
@@ -69,6 +69,14 @@ __global__ __launch_bounds__(Geo<LOGN>::THREADS) void k_wht(const uint8_t* x, ui
     }
   } else {
     // Single layout (n <= 256): R contiguous values per lane, T <= 4 lanes per row.
+    constexpr int NSB = R >= 8 ? R / 8 : 1;
+    uint32_t s8v[NSB];
+    {
+      int sbase[NSB];
+#pragma unroll
+      for (int q = 0; q < NSB; ++q) sbase[q] = t * R + 8 * q;
+      sign_bytes<NSB>(sbits, R >= 8 && sign_mode == SIGN_BEFORE, sbase, s8v);
+    }
     for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
       const int64_t row = g * RPB + slot;
       const bool valid = row < rows;
@@ -81,7 +89,7 @@ __global__ __launch_bounds__(Geo<LOGN>::THREADS) void k_wht(const uint8_t* x, ui
 #pragma unroll
           for (int q = 0; q < R / 8; ++q) {
             const int i = base + 8 * q;
-            uint32_t s8 = sign_mode == SIGN_BEFORE ? sign_byte(sbits, i) : 0u;
+            const uint32_t s8 = s8v[q];
             uint32_t mm[4];
 #pragma unroll
             for (int p = 0; p < 4; ++p) mm[p] = pair_mask16(s8 >> (2 * p));
