@@ -173,6 +173,14 @@ __device__ __forceinline__ void fma_mix_hi(float& acc, float a, uint32_t w) {
   asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(acc) : "v"(a), "v"(w));
 }
 
+// Load from a pointer known to be in global memory, whatever the compiler can
+// still infer about it (keeps global_load rather than flat_load, whose
+// completion also counts against the LDS wait counter).
+template <typename V>
+__device__ __forceinline__ V ldg_global(const void* p) {
+  return *reinterpret_cast<const __attribute__((address_space(1))) V*>(reinterpret_cast<uintptr_t>(p));
+}
+
 // Global loads / stores with explicit widths.
 template <typename V>
 __device__ __forceinline__ V ldg(const void* p) { return *reinterpret_cast<const V*>(p); }

@@ -118,7 +118,7 @@ template <> struct Blk<false> {
   typedef f32x4_t raw;
   static constexpr int STAGE = 65536 * 4;  // bytes per stage
   static __device__ __forceinline__ raw load(const uint8_t* stage, int c, int n, int kg) {
-    return ldg<f32x4_t>(reinterpret_cast<const float*>(stage) + c * 256 + n * 16 + 4 * kg);
+    return ldg_global<f32x4_t>(reinterpret_cast<const float*>(stage) + c * 256 + n * 16 + 4 * kg);
   }
   static __device__ __forceinline__ f16x4_t op(raw r) { return f4_to_h4(r); }
 };
@@ -126,7 +126,7 @@ template <> struct Blk<true> {
   typedef u32x2 raw;
   static constexpr int STAGE = 65536 * 2;
   static __device__ __forceinline__ raw load(const uint8_t* stage, int c, int n, int kg) {
-    return ldg<u32x2>(reinterpret_cast<const uint16_t*>(stage) + c * 256 + n * 16 + 4 * kg);
+    return ldg_global<u32x2>(reinterpret_cast<const uint16_t*>(stage) + c * 256 + n * 16 + 4 * kg);
   }
   static __device__ __forceinline__ f16x4_t op(raw r) { return as_h4(r); }
 };
@@ -155,6 +155,12 @@ __device__ __forceinline__ void pass_dd(uint16_t* tile, const uint8_t* stage, f1
 #pragma unroll
     for (int a = 0; a < 4; ++a) an[a] = B::load(stage, a + 32 * w, n, kg);
   }
+  // group gi's four 8-byte rows; the next group's rows are read before this
+  // group's MFMAs (groups touch disjoint addresses)
+  auto off = [&](int gi, int j) { return wb + lay(4 * (gi & 3) + SV * (gi >> 2) + ST * j); };
+  u32x2 rn[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) rn[j] = lds_rd8(tile, off(0, j));
 #pragma unroll
   for (int gi = 0; gi < 8; ++gi) {
     const int grp = 8 * w + gi;
@@ -168,12 +174,12 @@ __device__ __forceinline__ void pass_dd(uint16_t* tile, const uint8_t* stage, f1
         for (int a = 0; a < 4; ++a) an[a] = B::load(stage, 4 * (g2 & 3) + a + 16 * (g2 >> 2), n, kg);
       }
     }
-    int off[4];
     u32x2 r[4], b[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      off[j] = wb + lay(4 * (gi & 3) + SV * (gi >> 2) + ST * j);
-      r[j] = lds_rd8(tile, off[j]);
+    for (int j = 0; j < 4; ++j) r[j] = rn[j];
+    if (gi + 1 < 8) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rn[j] = lds_rd8(tile, off(gi + 1, j));
     }
     tr4x4(r, b);
     u32x2 o[4];
@@ -194,7 +200,7 @@ __device__ __forceinline__ void pass_dd(uint16_t* tile, const uint8_t* stage, f1
     }
     tr4x4(o, r);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) lds_wr8(tile, off[j], r[j]);
+    for (int j = 0; j < 4; ++j) lds_wr8(tile, off(gi, j), r[j]);
   }
 }
 
@@ -209,6 +215,10 @@ __device__ __forceinline__ void pass_d0(uint16_t* tile, const uint8_t* stage, f1
   typename B::raw an[4];
 #pragma unroll
   for (int a = 0; a < 4; ++a) an[a] = B::load(stage, 32 * w + a, n, kg);
+  auto off = [&](int gi, int a) { return wb + lay(64 * gi + 16 * a); };
+  u32x2 rn[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) rn[a] = lds_rd8(tile, off(0, a));
 #pragma unroll
   for (int gi = 0; gi < 8; ++gi) {
     const int c0 = 32 * w + 4 * gi;
@@ -219,12 +229,12 @@ __device__ __forceinline__ void pass_d0(uint16_t* tile, const uint8_t* stage, f1
 #pragma unroll
       for (int a = 0; a < 4; ++a) an[a] = B::load(stage, c0 + 4 + a, n, kg);
     }
-    int off[4];
     u32x2 r[4];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      off[a] = wb + lay(64 * gi + 16 * a);
-      r[a] = lds_rd8(tile, off[a]);
+    for (int a = 0; a < 4; ++a) r[a] = rn[a];
+    if (gi + 1 < 8) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) rn[a] = lds_rd8(tile, off(gi + 1, a));
     }
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
@@ -233,7 +243,7 @@ __device__ __forceinline__ void pass_d0(uint16_t* tile, const uint8_t* stage, f1
       r[a] = h4_bits(mfma16(B::op(ac[a]), bx));
     }
 #pragma unroll
-    for (int a = 0; a < 4; ++a) lds_wr8(tile, off[a], r[a]);
+    for (int a = 0; a < 4; ++a) lds_wr8(tile, off(gi, a), r[a]);
   }
 }
 
