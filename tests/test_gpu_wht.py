@@ -76,6 +76,43 @@ def test_16bit_inputs(logn, dt):
     assert compare.float_err(host64(y32), want)[0] <= TOL32
 
 
+@pytest.mark.parametrize("logn", [10, 11, 12, 13])
+@pytest.mark.parametrize("mode", ["none", "before", "after"])
+@pytest.mark.parametrize("rows", [1, 255, 1023, 1024, 1500])
+def test_batch_sizes_both_kernels(logn, mode, rows):
+    """Below 1024 rows each row is spread over a block of threads, from 1024
+    rows on one wave takes a row: both kernels, every sign mode, checked
+    against the oracle on sampled rows (first, last and a spread)."""
+    n = 1 << logn
+    rng = np.random.default_rng(logn * 7 + rows)
+    x = rng.standard_normal((rows, n)).astype(np.float32)
+    mask = synth.sign_bits_to_mask(rng.integers(0, 2, n))
+    s = H.signs_from_bits(mask, n)
+    y = host64(W().wht_batched(dev(x), signs=mask_dev(mask), sign_mode=mode))
+    sel = np.unique(np.r_[0:min(rows, 8), np.linspace(0, rows - 1, 16).astype(int), rows - 1])
+    xs = x[sel].astype(np.float64)
+    want = {"none": H.wht(xs), "before": H.rht(xs, s), "after": H.irht(xs, s)}[mode]
+    err, _ = compare.float_err(y[sel], want)
+    assert err <= TOL32, err
+
+
+@pytest.mark.parametrize("logn", [10, 12, 13])
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("rows", [100, 1100])
+def test_16bit_both_kernels(logn, dt, rows):
+    n = 1 << logn
+    rng = np.random.default_rng(logn + rows)
+    x = dev(rng.standard_normal((rows, n)), dt)
+    mask = synth.sign_bits_to_mask(rng.integers(0, 2, n))
+    s = H.signs_from_bits(mask, n)
+    sel = np.linspace(0, rows - 1, 12).astype(int)
+    want = H.rht(host64(x[sel]), s)
+    y16 = W().wht_batched(x, signs=mask_dev(mask), sign_mode="before")
+    y32 = W().wht_batched(x, signs=mask_dev(mask), sign_mode="before", out_dtype=torch.float32)
+    assert compare.float_err(host64(y16[sel]), want)[0] <= TOL16
+    assert compare.float_err(host64(y32[sel]), want)[0] <= TOL32
+
+
 def test_pair_sum_rounding():
     """bf16 pairs whose sum / difference needs rounding in fp32: the fused
     first butterfly must round exactly like an fp32 add."""

@@ -125,9 +125,134 @@ __global__ __launch_bounds__(Geo<LOGN>::THREADS) void k_wht(const uint8_t* x, ui
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Small batches (fewer rows than the chip has SIMDs to give one wave each):
+// one block of N/E threads per row, E = 16 values per thread (32 at n = 8192),
+// so a row is spread over up to four waves.  The log2 n butterfly stages run
+// in three register phases; between phases the row passes through LDS in
+// place (each thread reads back exactly the values its next phase needs).
+// Phase p holds the E values whose index bits [a_p, a_p + e) vary (a_0 = 0,
+// a_1 = e, a_2 = L - e) and applies the stages on bits [b_p, b_p+1) with
+// b = (0, e, 2e, L); the other index bits are the thread id in order.
+namespace wsm {
+template <int LOGN> struct Cfg {
+  static constexpr int N = 1 << LOGN;
+  static constexpr int LOGE = LOGN >= 13 ? 5 : 4;
+  static constexpr int E = 1 << LOGE;
+  static constexpr int THREADS = N / E;
+  static constexpr int A[3] = {0, LOGE, LOGN - LOGE};
+  static constexpr int B[4] = {0, LOGE, 2 * LOGE, LOGN};
+  static_assert(3 * LOGE >= LOGN && LOGN >= 2 * LOGE, "three phases cover the index");
+};
+// index of value r of thread t in phase p (r's bits at [a, a + LOGE))
+template <int LOGE>
+__device__ __forceinline__ int at(int t, int r, int a) {
+  return (t & ((1 << a) - 1)) | (r << a) | ((t >> a) << (a + LOGE));
+}
+__device__ __forceinline__ int pad(int i) { return i + (i >> 4); }  // one float per 16: spreads banks
+// eight consecutive values widened to fp32, nothing else applied
+template <int DT>
+__device__ __forceinline__ void load8_plain(const uint8_t* rowp, int i, float* v) {
+  if constexpr (DT == DT_F32) {
+    const f32x4 a = ldg<f32x4>(reinterpret_cast<const float*>(rowp) + i);
+    const f32x4 b = ldg<f32x4>(reinterpret_cast<const float*>(rowp) + i + 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[q] = a[q];
+      v[4 + q] = b[q];
+    }
+  } else {
+    const u32x4 w = ldg<u32x4>(reinterpret_cast<const uint16_t*>(rowp) + i);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = widen16(w[q], false, DT);
+      v[2 * q + 1] = widen16(w[q], true, DT);
+    }
+  }
+}
+}  // namespace wsm
+
+template <int LOGN, int DIN, int DOUT>
+__global__ __launch_bounds__(wsm::Cfg<LOGN>::THREADS) void k_wht_blk(const uint8_t* x, uint8_t* y, int64_t rows,
+                                                                   int64_t ldx_b, int64_t ldy_b,
+                                                                   const uint32_t* __restrict__ sbits,
+                                                                   int sign_mode, float scale) {
+  using C = wsm::Cfg<LOGN>;
+  constexpr int E = C::E, LE = C::LOGE;
+  __shared__ float lds[C::N + C::N / 16];
+  const int t = threadIdx.x;
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    float v[E];
+    // ---- phase 0: E contiguous values, sign before, stages on bits [0, e)
+    {
+      const uint8_t* xr = x + row * ldx_b;
+      const int i0 = t * E;
+#pragma unroll
+      for (int q = 0; q < E / 8; ++q) wsm::load8_plain<DIN>(xr, i0 + 8 * q, v + 8 * q);
+      if (sign_mode == SIGN_BEFORE) {
+        const uint32_t sw = sbits[i0 >> 5] >> (i0 & 31);
+#pragma unroll
+        for (int r = 0; r < E; ++r) v[r] = as_f(as_u(v[r]) ^ (((sw >> r) & 1u) << 31));
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      if (p > 0) {
+        __syncthreads();  // the previous phase's values are all in LDS
+#pragma unroll
+        for (int r = 0; r < E; ++r) v[r] = lds[wsm::pad(wsm::at<LE>(t, r, C::A[p]))];
+      }
+#pragma unroll
+      for (int bit = C::B[p]; bit < C::B[p + 1]; ++bit) {
+        const int m = 1 << (bit - C::A[p]);
+#pragma unroll
+        for (int r = 0; r < E; ++r)
+          if (!(r & m)) {
+            const float a = v[r], b = v[r | m];
+            v[r] = a + b;
+            v[r | m] = a - b;
+          }
+      }
+      if (p < 2) {
+        if (p > 0) __syncthreads();  // everyone has read this phase's values
+#pragma unroll
+        for (int r = 0; r < E; ++r) lds[wsm::pad(wsm::at<LE>(t, r, C::A[p]))] = v[r];
+      }
+    }
+    // ---- scale, sign after, store (lane-consecutive indices: coalesced)
+    uint8_t* yr = y + row * ldy_b;
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+      const int i = wsm::at<LE>(t, r, C::A[2]);
+      float o = v[r] * scale;
+      if (sign_mode == SIGN_AFTER) o = as_f(as_u(o) ^ (((sbits[i >> 5] >> (i & 31)) & 1u) << 31));
+      if constexpr (DOUT == DT_F32) reinterpret_cast<float*>(yr)[i] = o;
+      else if constexpr (DOUT == DT_BF16) reinterpret_cast<uint16_t*>(yr)[i] = (uint16_t)(pack_bf16(o, 0.f) & 0xffffu);
+      else reinterpret_cast<uint16_t*>(yr)[i] = (uint16_t)(pack_f16(o, 0.f) & 0xffffu);
+    }
+    __syncthreads();  // the next row reuses LDS
+  }
+}
+
+// Rows below this use the block-per-row kernel (n >= 1024): with one wave
+// per row they would leave most of the chip's 1024 SIMDs idle.
+constexpr int64_t SMALL_BATCH_ROWS = 1024;
+
 template <int LOGN, int DIN, int DOUT>
 static hipError_t run_wht(const void* x, void* y, int64_t rows, int64_t ldx, int64_t ldy,
                           const uint32_t* sbits, int sign_mode, float scale, hipStream_t s) {
+  if constexpr (LOGN >= 10) {
+    if (rows < SMALL_BATCH_ROWS) {
+      using C = wsm::Cfg<LOGN>;
+      auto kb = k_wht_blk<LOGN, DIN, DOUT>;
+      static const int nbb = blocks_per_cu(kb, C::THREADS, 0);
+      hipLaunchKernelGGL(kb, dim3(persistent_grid(rows, nbb)), dim3(C::THREADS), 0, s, (const uint8_t*)x,
+                         (uint8_t*)y, rows, ldx * DtInfo<DIN>::BYTES, ldy * DtInfo<DOUT>::BYTES, sbits, sign_mode,
+                         scale);
+      return hipGetLastError();
+    }
+  }
   using G = Geo<LOGN>;
   const int64_t groups = (rows + G::RPB - 1) / G::RPB;
   auto k = k_wht<LOGN, DIN, DOUT>;
