@@ -13,8 +13,8 @@ copies totalling >= 1 GiB so that inputs come from HBM rather than the
 256 MB last-level cache; the K launches are captured once in a HIP graph
 (no host launch overhead) and replayed inside a HIP-event pair on the
 launch stream.  Data are synthetic (seeded generators in
-wht_adapters_amd.synth) with the shapes and value structure of the
-workloads; see the design doc for the recipes.
+wht_adapters_amd.synth, whose docstrings give each recipe) with the shapes
+and value structure of the workloads.
 """
 import argparse
 import hashlib
@@ -50,7 +50,7 @@ ROWS = {
 }
 MAIN = "rht_int4_g128_4096x4096"
 KERNEL_SOURCES = {  # sources a workload's kernel is built from (traffic counters go stale with them)
-    MAIN: ["rht_quant.hpp", "rq_fwd_b4.hip", "engine.hpp", "io.hpp", "common.hpp"],
+    MAIN: ["rht_quant.hpp", "rq_fwd_b4.hip", "engine.hpp", "io.hpp", "common.hpp", "launch.hpp"],
 }
 
 
