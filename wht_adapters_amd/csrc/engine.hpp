@@ -209,14 +209,24 @@ __device__ uint32_t kNoSigns[256];  // zero-initialised, never written
 // zeros when `on` is false (`on` must be uniform).  The loads are
 // unconditional (kNoSigns stands in), so they go out back to back and the
 // compiler can put independent loads ahead of their first use.
+// sign_words issues the loads, sign_bytes_of extracts the bytes (split so a
+// caller can put other loads between the two).
 template <int NC>
-__device__ __forceinline__ void sign_bytes(const uint32_t* bits, bool on, const int* base, uint32_t* sb) {
+__device__ __forceinline__ void sign_words(const uint32_t* bits, bool on, const int* base, uint32_t* wv) {
   const uint32_t* p = on ? bits : kNoSigns;
-  uint32_t wv[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) wv[c] = p[base[c] >> 5];
+}
+template <int NC>
+__device__ __forceinline__ void sign_bytes_of(const uint32_t* wv, const int* base, uint32_t* sb) {
 #pragma unroll
   for (int c = 0; c < NC; ++c) sb[c] = (wv[c] >> (base[c] & 31)) & 0xffu;
+}
+template <int NC>
+__device__ __forceinline__ void sign_bytes(const uint32_t* bits, bool on, const int* base, uint32_t* sb) {
+  uint32_t wv[NC];
+  sign_words<NC>(bits, on, base, wv);
+  sign_bytes_of<NC>(wv, base, sb);
 }
 // XOR mask flipping the sign bits of a 16-bit pair from two sign bits.
 __device__ __forceinline__ uint32_t pair_mask16(uint32_t b2) {

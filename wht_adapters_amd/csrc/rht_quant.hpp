@@ -68,35 +68,24 @@ __global__ __launch_bounds__(Geo<LOGN>::THREADS) void k_rht_quant(
 
   // per-lane sign bytes for the load layout (A when two-phase, else B)
   int col[8];
-  uint32_t sb[8], m[8][4];
+  uint32_t sw[8], sb[8], m[8][4];
 #pragma unroll
   for (int c = 0; c < 8; ++c) col[c] = G::TWO ? G::idxA(t, c * 8) : t * 64 + c * 8;
-  sign_bytes<8>(sbits, sbits != nullptr, col, sb);
-  // rows past the end (last block only) transform a copy of the last row
-  // and store nothing, so every lane runs the same code without branches
+  // slots past the end (last block only) transform a copy of the last row
+  // and store the same bytes there, so every lane runs the same code
+  // without branches
   auto row_ptr = [&](int64_t g) {
     const int64_t row = g * RPB + slot;
     return w + (row < rows ? row : rows - 1) * ldw_b;
   };
-  // One-wave blocks (n <= 4096, a row or two per wave at typical sizes) peel
-  // the first row: its loads go out right behind the sign-byte loads, before
-  // the masks are built, so the mask arithmetic overlaps the row's HBM
-  // latency (loads complete in order: the masks wait for the sign bytes
-  // only).  The grid never exceeds the row groups, so the row exists.  Wider
-  // rows run many rows per block and keep the plain loop (the peeled copy
-  // would cost them occupancy).
-  constexpr bool PEEL = G::THREADS == 64;
-  Raw8 raw[8];
-  if constexpr (PEEL) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) fetch8<DIN>(row_ptr(blockIdx.x), col[c], raw[c]);
-  }
+  sign_words<8>(sbits, sbits != nullptr, col, sw);
+  sign_bytes_of<8>(sw, col, sb);
 #pragma unroll
   for (int c = 0; c < 8; ++c)
 #pragma unroll
     for (int q = 0; q < 4; ++q) m[c][q] = pair_mask16(sb[c] >> (2 * q));
 
-  auto do_row = [&](int64_t g) {
+  auto do_row = [&](Raw8 (&raw)[8], int64_t g) {
     const int64_t row = g * RPB + slot;
     const bool valid = row < rows;
     float v[64];
@@ -125,7 +114,10 @@ __global__ __launch_bounds__(Geo<LOGN>::THREADS) void k_rht_quant(
       const float s_pre = (a * inv_sqrt_n) / QM;
       const _Float16 h = (_Float16)s_pre;
       const float sf = (float)h;
-      const float mm = sf > 0.f ? inv_sqrt_n / sf : 0.f;
+      // an fp16 scale > 0 is >= 2^-24, so the max() only changes the
+      // all-zero group, whose multiplier is 0; no branch around the divide
+      const float dv = inv_sqrt_n / __builtin_fmaxf(sf, 1.17549435e-38f);
+      const float mm = sf > 0.f ? dv : 0.f;
       mult[k] = rho ? -mm : mm;
       s16b[k] = __builtin_bit_cast(uint16_t, h);
     }
@@ -154,32 +146,37 @@ __global__ __launch_bounds__(Geo<LOGN>::THREADS) void k_rht_quant(
         cw[j] = (acc - QP::K) ^ QP::BIAS;
       }
     }
-    if (valid) {
-      uint8_t* cr = codes + row * (int64_t)ROW_CODE_B + t * LANE_CODE_B;
-      if constexpr (BITS == 4) {
-        stg<u32x4>(cr, u32x4{cw[0], cw[1], cw[2], cw[3]});
-        stg<u32x4>(cr + 16, u32x4{cw[4], cw[5], cw[6], cw[7]});
-      } else if constexpr (BITS == 2) {
-        stg<u32x4>(cr, u32x4{cw[0], cw[1], cw[2], cw[3]});
-      } else {
-        stg<u32x2>(cr, u32x2{cw[0], cw[1]});
-        stg<u32x2>(cr + 8, u32x2{cw[2], cw[3]});
-        stg<u32x2>(cr + 16, u32x2{cw[4], cw[5]});
-      }
-      uint16_t* sr = scales + row * (int64_t)NSC;
-      if constexpr (SPAN == 1) {
+    // Stores are unconditional (no branch, so no conservative wait at a
+    // join): a slot past the last row has recomputed the last row and writes
+    // the same bytes there.  Lanes sharing a group write the same scale.
+    const int64_t srow = valid ? row : rows - 1;
+    uint8_t* cr = codes + srow * (int64_t)ROW_CODE_B + t * LANE_CODE_B;
+    if constexpr (BITS == 4) {
+      stg<u32x4>(cr, u32x4{cw[0], cw[1], cw[2], cw[3]});
+      stg<u32x4>(cr + 16, u32x4{cw[4], cw[5], cw[6], cw[7]});
+    } else if constexpr (BITS == 2) {
+      stg<u32x4>(cr, u32x4{cw[0], cw[1], cw[2], cw[3]});
+    } else {
+      stg<u32x2>(cr, u32x2{cw[0], cw[1]});
+      stg<u32x2>(cr + 8, u32x2{cw[2], cw[3]});
+      stg<u32x2>(cr + 16, u32x2{cw[4], cw[5]});
+    }
+    uint16_t* sr = scales + srow * (int64_t)NSC;
+    if constexpr (SPAN == 1) {
 #pragma unroll
-        for (int k = 0; k < NG; ++k) sr[t * NG + k] = s16b[k];
-      } else {
-        if (t % SPAN == 0) sr[t / SPAN] = s16b[0];
-      }
+      for (int k = 0; k < NG; ++k) sr[t * NG + k] = s16b[k];
+    } else {
+      sr[t / SPAN] = s16b[0];
     }
   };
-  if constexpr (PEEL) do_row(blockIdx.x);
-  for (int64_t g = blockIdx.x + (PEEL ? gridDim.x : 0); g < ngroups; g += gridDim.x) {
+  auto fetch_row = [&](Raw8 (&raw)[8], int64_t g) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) fetch8<DIN>(row_ptr(g), col[c], raw[c]);
-    do_row(g);
+  };
+  for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
+    Raw8 ra[8];
+    fetch_row(ra, g);
+    do_row(ra, g);
   }
 }
 
@@ -239,11 +236,27 @@ __global__ __launch_bounds__(Geo<LOGN>::THREADS) void k_rht_dequant(
   float* myrow = lds + slot * G::LDS_ROW;
 
   // output sign masks (S and the rho of the DPP butterflies) for the store layout
-  uint32_t sb[8], m[8][4];
+  uint32_t sw[8], sb[8], m[8][4];
   int obase[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) obase[c] = G::TWO ? G::idxA(t, c * 8) : t * 64 + c * 8;
-  sign_bytes<8>(sbits, sbits != nullptr, obase, sb);
+  sign_words<8>(sbits, sbits != nullptr, obase, sw);
+
+  // A row's inputs: its codes and the raw fp16 scales of this lane's groups.
+  struct In {
+    uint32_t cw[LANE_CODE_B / 4];
+    uint16_t hb[NG];
+  };
+  // rows past the end (last block only) recompute the last row
+  auto fetch_row = [&](In& in, int64_t g) {
+    const int64_t row = g * RPB + slot;
+    const int64_t rl = row < rows ? row : rows - 1;
+    fetch_codes<BITS>(codes + rl * (int64_t)ROW_CODE_B + t * LANE_CODE_B, in.cw);
+    const uint16_t* sr = scales + rl * (int64_t)NSC;
+#pragma unroll
+    for (int k = 0; k < NG; ++k) in.hb[k] = SPAN == 1 ? sr[t * NG + k] : sr[t / SPAN];
+  };
+  sign_bytes_of<8>(sw, obase, sb);
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     if constexpr (G::TWO) {
@@ -258,49 +271,46 @@ __global__ __launch_bounds__(Geo<LOGN>::THREADS) void k_rht_dequant(
     for (int q = 0; q < 4; ++q) m[c][q] = pair_mask16(sb[c] >> (2 * q));
   }
 
-  for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
+  auto do_row = [&](const In& in, int64_t g) {
     const int64_t row = g * RPB + slot;
-    const bool valid = row < rows;
-    const int64_t rl = valid ? row : rows - 1;  // past-the-end rows: recompute the last, store nothing
-    uint32_t cw[LANE_CODE_B / 4];
-    fetch_codes<BITS>(codes + rl * (int64_t)ROW_CODE_B + t * LANE_CODE_B, cw);
-    const uint16_t* sr = scales + rl * (int64_t)NSC;
     float ms[NG];
 #pragma unroll
-    for (int k = 0; k < NG; ++k) {
-      const uint16_t hb = SPAN == 1 ? sr[t * NG + k] : sr[t / SPAN];
-      ms[k] = (float)__builtin_bit_cast(_Float16, hb) * inv_sqrt_n;
-    }
+    for (int k = 0; k < NG; ++k) ms[k] = (float)__builtin_bit_cast(_Float16, in.hb[k]) * inv_sqrt_n;
     float v[64];
 #pragma unroll
-    for (int r = 0; r < 64; ++r) v[r] = (float)code_at<BITS>(cw, r) * ms[r / GL];
+    for (int r = 0; r < 64; ++r) v[r] = (float)code_at<BITS>(in.cw, r) * ms[r / GL];
     stages_B<LOGN, 0>(v, t);
     if constexpr (G::TWO) {
       transpose_BA<LOGN, G::THREADS>(myrow, v, t);
       stages_A<LOGN, false>(v, t);
     }
-    if (valid) {
-      uint8_t* orow = out + row * ldo_b;
+    // unconditional stores: a slot past the last row writes the last row's
+    // bytes again
+    uint8_t* orow = out + (row < rows ? row : rows - 1) * ldo_b;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int i = G::TWO ? G::idxA(t, c * 8) : t * 64 + c * 8;
-        if constexpr (DOUT == DT_F32) {
-          float o[8];
+    for (int c = 0; c < 8; ++c) {
+      const int i = G::TWO ? G::idxA(t, c * 8) : t * 64 + c * 8;
+      if constexpr (DOUT == DT_F32) {
+        float o[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] = as_f(as_u(v[c * 8 + e]) ^ (((sb[c] >> e) & 1u) << 31));
-          store8<DT_F32>(orow, i, o);
-        } else {
-          u32x4 wv;
+        for (int e = 0; e < 8; ++e) o[e] = as_f(as_u(v[c * 8 + e]) ^ (((sb[c] >> e) & 1u) << 31));
+        store8<DT_F32>(orow, i, o);
+      } else {
+        u32x4 wv;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t p = DOUT == DT_BF16 ? pack_bf16(v[c * 8 + 2 * q], v[c * 8 + 2 * q + 1])
-                                               : pack_f16(v[c * 8 + 2 * q], v[c * 8 + 2 * q + 1]);
-            wv[q] = p ^ m[c][q];
-          }
-          stg<u32x4>(reinterpret_cast<uint16_t*>(orow) + i, wv);
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t p = DOUT == DT_BF16 ? pack_bf16(v[c * 8 + 2 * q], v[c * 8 + 2 * q + 1])
+                                             : pack_f16(v[c * 8 + 2 * q], v[c * 8 + 2 * q + 1]);
+          wv[q] = p ^ m[c][q];
         }
+        stg<u32x4>(reinterpret_cast<uint16_t*>(orow) + i, wv);
       }
     }
+  };
+  for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
+    In ia;
+    fetch_row(ia, g);
+    do_row(ia, g);
   }
 }
 
