@@ -34,7 +34,8 @@ struct Geo {
   static constexpr int LOGT = LOGN - LOGR;
   static constexpr int T = 1 << LOGT;
   static constexpr bool TWO = LOGT >= 3;
-  static constexpr int LDS_ROW = TWO ? N / 2 + N / 16 : 0;  // floats per row slot (half row, padded)
+  // floats per row slot (half row, padded: see hphys)
+  static constexpr int LDS_ROW = TWO ? N / 2 + N / 16 + (LOGN >= 13 ? N / 64 : 0) : 0;
 
   // index bits whose butterfly runs over DPP (so carry the rho sign)
   static constexpr unsigned RHO_MASK =
@@ -129,10 +130,19 @@ __device__ __forceinline__ void stages_A(float (&v)[64], int t) {
 // register bit in both layouts: each half moves one 16-byte float4 out of
 // every 8-value chunk, so the LDS image holds half a row (index bit 2
 // removed: c(i) = (i & 3) | ((i >> 3) << 2)) and the registers a half reads
-// into are exactly those its write has just freed.  Padding: 4 floats per 32.
+// into are exactly those its write has just freed.
+//
+// Padding, for 16-byte LDS accesses served 8 lanes at a time over 32 banks
+// (the model that reproduces the measured conflict counts): 4 floats per 32
+// keeps the layout-B side (lane t at 32 t + 4 k) conflict-free, and at
+// n >= 8192 another 8 floats per 256 separate the four quad lanes of the
+// layout-A side, whose half-row offsets are 128 floats apart there (with
+// the first term alone they fall 16 banks apart, two to a bank group).
 
 template <int LOGN>
-__device__ __forceinline__ int hphys(int ci) { return ci + ((ci >> 5) << 2); }
+__device__ __forceinline__ int hphys(int ci) {
+  return ci + ((ci >> 5) << 2) + (LOGN >= 13 ? (ci >> 8) << 3 : 0);
+}
 
 template <int LOGN, int THREADS>
 __device__ __forceinline__ void transpose_AB(float* row, float (&v)[64], int t) {
