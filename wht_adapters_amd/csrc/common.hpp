@@ -164,6 +164,45 @@ __device__ __forceinline__ void oct_bfly16(const uint32_t* x, float* y) {
   else WHTQ_QUAD8("v_dot2_f32_f16");
 }
 
+// The same butterflies with a +-1 sign per input folded into the products:
+// k[q] is the pair (s_2q, s_2q+1) of +-1 (low half = lower index) for word
+// x[q], and the VOP3P neg_lo / neg_hi modifiers on the coefficient operand
+// give the other three sign patterns, so no separate sign flip is needed.
+#define WHTQ_QUAD8K(OP)                                                       \
+  asm(OP " %8, %12, %16, 0\n\t"                         /* s0 = x0 . k0      */ \
+      OP " %9, %12, %16, 0 neg_hi:[0,1,0]\n\t"          /* d0 = x0 . k0(+,-) */ \
+      OP " %10, %14, %18, 0\n\t"                                               \
+      OP " %11, %14, %18, 0 neg_hi:[0,1,0]\n\t"                                \
+      "s_nop 0\n\t"                                                            \
+      OP " %0, %13, %17, %8\n\t"                        /* y0 = s0 + x1 . k1 */ \
+      OP " %2, %13, %17, %8 neg_lo:[0,1,0] neg_hi:[0,1,0]\n\t" /* y2 = s0 - x1 . k1 */ \
+      OP " %1, %13, %17, %9 neg_hi:[0,1,0]\n\t"         /* y1 = d0 + x1 . k1(+,-) */ \
+      OP " %3, %13, %17, %9 neg_lo:[0,1,0]\n\t"         /* y3 = d0 + x1 . k1(-,+) */ \
+      OP " %4, %15, %19, %10\n\t"                                              \
+      OP " %6, %15, %19, %10 neg_lo:[0,1,0] neg_hi:[0,1,0]\n\t"                \
+      OP " %5, %15, %19, %11 neg_hi:[0,1,0]\n\t"                               \
+      OP " %7, %15, %19, %11 neg_lo:[0,1,0]\n\t"                               \
+      "s_nop 2"                                                               \
+      : "=&v"(y[0]), "=&v"(y[1]), "=&v"(y[2]), "=&v"(y[3]),                   \
+        "=&v"(y[4]), "=&v"(y[5]), "=&v"(y[6]), "=&v"(y[7]),                   \
+        "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)                            \
+      : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]),                           \
+        "v"(k[0]), "v"(k[1]), "v"(k[2]), "v"(k[3]))
+
+template <bool BF16>
+__device__ __forceinline__ void oct_bfly16_signed(const uint32_t* x, const uint32_t* k, float* y) {
+  float t0, t1, t2, t3;
+  if constexpr (BF16) WHTQ_QUAD8K("v_dot2_f32_bf16");
+  else WHTQ_QUAD8K("v_dot2_f32_f16");
+}
+
+// +-1 coefficient pair of oct_bfly16_signed from two sign bits (bit 0: the
+// lower index; a set bit means -1)
+template <bool BF16>
+__device__ __forceinline__ uint32_t sign_coef16(uint32_t b2) {
+  return PM<BF16>::PP ^ (((b2 & 1u) << 15) | ((b2 & 2u) << 30));
+}
+
 // acc += a * h (h an fp16 value in the low / high half of `w`), one
 // v_fma_mix_f32 with the fp16 operand widened exactly inside the FMA.
 __device__ __forceinline__ void fma_mix_lo(float& acc, float a, uint32_t w) {

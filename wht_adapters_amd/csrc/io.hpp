@@ -38,8 +38,9 @@ __device__ __forceinline__ void fetch8(const void* rowp, int i, Raw8& r) {
 
 // Widen fetched raw values into v[0..7].  16-bit inputs come out with the
 // butterflies on index bits 0 and 1 already applied (oct_bfly16); fp32
-// inputs come out raw.  Signs: `m` holds per-pair sign-flip masks (16-bit),
-// `sb` the sign byte (fp32).
+// inputs come out raw.  Signs: for 16-bit inputs `m` holds the four +-1
+// coefficient pairs (sign_coef16) the butterflies fold the signs into, for
+// fp32 `sb` holds the sign byte.
 template <int DT> struct Fused { static constexpr int LO = DT == DT_F32 ? 0 : 2; };
 
 template <int DT, bool SIGNS>
@@ -52,12 +53,9 @@ __device__ __forceinline__ void widen8(const Raw8& r, float* v, const uint32_t* 
       v[e] = as_f(u[e]);
     }
   } else {
-    uint32_t x[4] = {r.a[0], r.a[1], r.a[2], r.a[3]};
-    if constexpr (SIGNS) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) x[q] ^= m[q];
-    }
-    oct_bfly16<DT == DT_BF16>(x, v);
+    const uint32_t x[4] = {r.a[0], r.a[1], r.a[2], r.a[3]};
+    if constexpr (SIGNS) oct_bfly16_signed<DT == DT_BF16>(x, m, v);
+    else oct_bfly16<DT == DT_BF16>(x, v);
   }
 }
 

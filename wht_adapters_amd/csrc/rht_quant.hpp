@@ -80,10 +80,12 @@ __global__ __launch_bounds__(Geo<LOGN>::THREADS) void k_rht_quant(
   };
   sign_words<8>(sbits, sbits != nullptr, col, sw);
   sign_bytes_of<8>(sw, col, sb);
+  // 16-bit rows: the signs ride on the +-1 coefficients of the first
+  // butterflies (fp32 rows flip sign bits with sb instead)
 #pragma unroll
   for (int c = 0; c < 8; ++c)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) m[c][q] = pair_mask16(sb[c] >> (2 * q));
+    for (int q = 0; q < 4; ++q) m[c][q] = sign_coef16<DIN == DT_BF16>(sb[c] >> (2 * q));
 
   auto do_row = [&](Raw8 (&raw)[8], int64_t g) {
     const int64_t row = g * RPB + slot;

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(Geo<LOGN>::THREADS) void k_wht(const uint8_t* x, ui
 #pragma unroll
     for (int c = 0; c < 8; ++c)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) m[c][q] = pair_mask16(sb[c] >> (2 * q));
+      for (int q = 0; q < 4; ++q) m[c][q] = sign_coef16<DIN == DT_BF16>(sb[c] >> (2 * q));
     uint32_t sa0 = 0, sa1 = 0;
     if (sign_mode == SIGN_AFTER) { sa0 = sbits[2 * t]; sa1 = sbits[2 * t + 1]; }
 
@@ -49,7 +49,7 @@ __global__ __launch_bounds__(Geo<LOGN>::THREADS) void k_wht(const uint8_t* x, ui
       for (int c = 0; c < 8; ++c) {
         Raw8 raw;
         fetch8<DIN>(xr, col[c], raw);
-        widen8<DIN, true>(raw, v + 8 * c, m[c], sb[c]);   // (masks are zero unless SIGN_BEFORE)
+        widen8<DIN, true>(raw, v + 8 * c, m[c], sb[c]);   // (coefficients are +1 unless SIGN_BEFORE)
       }
       stages_A<LOGN, DIN == DT_F32>(v, t);
       transpose_AB<LOGN, G::THREADS>(myrow, v, t);
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(Geo<LOGN>::THREADS) void k_wht(const uint8_t* x, ui
             const uint32_t s8 = s8v[q];
             uint32_t mm[4];
 #pragma unroll
-            for (int p = 0; p < 4; ++p) mm[p] = pair_mask16(s8 >> (2 * p));
+            for (int p = 0; p < 4; ++p) mm[p] = sign_coef16<DIN == DT_BF16>(s8 >> (2 * p));
             load8<DIN, true>(xr, i, v + 8 * q, mm, s8);
           }
         } else {
