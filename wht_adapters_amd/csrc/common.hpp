@@ -212,6 +212,25 @@ __device__ __forceinline__ void fma_mix_hi(float& acc, float a, uint32_t w) {
   asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(acc) : "v"(a), "v"(w));
 }
 
+// s * h for the fp16 value h in the low / high half of `w` (exact widening
+// inside the mixed-precision FMA, one rounding of the product).
+__device__ __forceinline__ float f16_mul_lo(float s, uint32_t w) {
+  float d;
+  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=v"(d) : "v"(s), "v"(w));
+  return d;
+}
+__device__ __forceinline__ float f16_mul_hi(float s, uint32_t w) {
+  float d;
+  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(d) : "v"(s), "v"(w));
+  return d;
+}
+// (lo, hi) -> (lo + hi, lo - hi) on an fp16 pair, one packed add.
+__device__ __forceinline__ f16x2_t f16_pair_bfly(f16x2_t a) {
+  f16x2_t d;
+  asm("v_pk_add_f16 %0, %1, %1 op_sel:[0,1] op_sel_hi:[0,1] neg_hi:[0,1]" : "=v"(d) : "v"(a));
+  return d;
+}
+
 // Load from a pointer known to be in global memory, whatever the compiler can
 // still infer about it (keeps global_load rather than flat_load, whose
 // completion also counts against the LDS wait counter).

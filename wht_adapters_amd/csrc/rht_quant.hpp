@@ -197,6 +197,75 @@ __device__ __forceinline__ int code_at(const uint32_t* cw, int r) {
   }
 }
 
+// Dequantise a lane's 64 codes (BITS 2 or 4, one scale for all of them) and
+// apply the butterflies on index bits 0..5 (the lane's own) on the way.
+// Those six stages only add and subtract codes, so they run on the exact
+// integers in packed fp16 (|sum| <= 64 * 2^(b-1) <= 512, exact there): two
+// values per VALU op instead of one.  A register pair holds codes k and
+// k + CPW/2 of a 32-bit code word, which sit 16 bits apart, so one shift
+// and one and-or turn a word into fp16 pairs 1024 + q + 2^(b-1) (offset
+// binary after flipping the code's sign bit; 0x6400 is 1024.0, whose ulp
+// is 1).  Each result is then widened and scaled in one mixed FMA:
+// v = s * (H_64 q), one rounding instead of a rounding per stage.
+template <int BITS>
+__device__ __forceinline__ void dequant_lane_h64(const uint32_t* cw, float s, float* v) {
+  static_assert(BITS == 2 || BITS == 4, "codes must tile 16-bit halves");
+  constexpr int CPW = 32 / BITS, HALF = CPW / 2, NW = 64 / CPW;
+  constexpr uint32_t FIELD = (1u << BITS) - 1, MASK = FIELD | (FIELD << 16);
+  constexpr uint32_t FLIP = BITS == 2 ? 0xaaaaaaaau : 0x88888888u;
+  constexpr _Float16 BIAS = (_Float16)(1024 + (1 << (BITS - 1)));
+  // the magic in a VGPR: with the mask in an SGPR the and-or is one VOP3
+  // (gfx9 reads one scalar operand per VALU instruction)
+  uint32_t magic = 0x64006400u;
+  asm volatile("" : "+v"(magic));
+  f16x2_t R[NW][HALF];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t u = cw[w] ^ FLIP;
+#pragma unroll
+    for (int k = 0; k < HALF; ++k) {
+      const uint32_t b = ((u >> (BITS * k)) & MASK) | magic;
+      R[w][k] = __builtin_bit_cast(f16x2_t, b) - f16x2_t{BIAS, BIAS};
+    }
+  }
+  // element index r = CPW w + HALF h + k: the pair bit h is a stage inside
+  // each register, the bits of k and w pair registers
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+#pragma unroll
+    for (int k = 0; k < HALF; ++k) R[w][k] = f16_pair_bfly(R[w][k]);
+#pragma unroll
+  for (int kb = 1; kb < HALF; kb <<= 1)
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+#pragma unroll
+      for (int k = 0; k < HALF; ++k)
+        if (!(k & kb)) {
+          const f16x2_t a = R[w][k], b = R[w][k | kb];
+          R[w][k] = a + b;
+          R[w][k | kb] = a - b;
+        }
+#pragma unroll
+  for (int wb = 1; wb < NW; wb <<= 1)
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      if (!(w & wb))
+#pragma unroll
+        for (int k = 0; k < HALF; ++k) {
+          const f16x2_t a = R[w][k], b = R[w | wb][k];
+          R[w][k] = a + b;
+          R[w | wb][k] = a - b;
+        }
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+#pragma unroll
+    for (int k = 0; k < HALF; ++k) {
+      const uint32_t b = __builtin_bit_cast(uint32_t, R[w][k]);
+      v[CPW * w + k] = f16_mul_lo(s, b);
+      v[CPW * w + HALF + k] = f16_mul_hi(s, b);
+    }
+}
+
 // The 64 codes (8*BITS bytes) of one lane.
 template <int BITS>
 __device__ __forceinline__ void fetch_codes(const uint8_t* cr, uint32_t* cw) {
@@ -279,9 +348,14 @@ __global__ __launch_bounds__(Geo<LOGN>::THREADS) void k_rht_dequant(
 #pragma unroll
     for (int k = 0; k < NG; ++k) ms[k] = (float)__builtin_bit_cast(_Float16, in.hb[k]) * inv_sqrt_n;
     float v[64];
+    if constexpr (BITS != 3 && NG == 1) {
+      dequant_lane_h64<BITS>(in.cw, ms[0], v);  // index bits 0..5 done
+      stages_B<LOGN, 6>(v, t);
+    } else {
 #pragma unroll
-    for (int r = 0; r < 64; ++r) v[r] = (float)code_at<BITS>(in.cw, r) * ms[r / GL];
-    stages_B<LOGN, 0>(v, t);
+      for (int r = 0; r < 64; ++r) v[r] = (float)code_at<BITS>(in.cw, r) * ms[r / GL];
+      stages_B<LOGN, 0>(v, t);
+    }
     if constexpr (G::TWO) {
       transpose_BA<LOGN, G::THREADS>(myrow, v, t);
       stages_A<LOGN, false>(v, t);
