@@ -109,6 +109,22 @@ def test_dequant_inverse_parity(logn, bits, odt):
     assert compare.float_err(host64(out), want)[0] <= tol
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("logn,g", [(6, 64), (10, 32), (12, 64), (12, 128), (13, 64), (13, 256), (11, 8)])
+def test_dequant_arbitrary_codes(logn, g, bits):
+    # every code value, including -2^(b-1), which the quantiser never emits
+    n = 1 << logn
+    rng = np.random.default_rng(7 * logn + bits + g)
+    rows = 13
+    codes = torch.from_numpy(rng.integers(0, 256, size=(rows, n * bits // 8), dtype=np.uint8)).to("cuda:0")
+    sc = rng.uniform(1e-3, 2.0, size=(rows, n // g)).astype(np.float16)
+    scales = torch.from_numpy(sc).to("cuda:0")
+    mask = synth.sign_bits_to_mask(rng.integers(0, 2, n))
+    out = W().rht_dequantize_inverse(codes, scales, mask_dev(mask), bits, g, n, out_dtype=torch.float32)
+    want = rtn.dequantize_inverse(codes_host(codes), sc, H.signs_from_bits(mask, n), bits, g, n)
+    assert compare.float_err(host64(out), want)[0] <= 1e-5
+
+
 def test_full_config_int4_g128_4096():
     """4096 x 4096 Student-t weights with outlier columns, INT4, g = 128."""
     d = synth.rht_int4_g128()
