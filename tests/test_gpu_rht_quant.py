@@ -109,6 +109,22 @@ def test_dequant_inverse_parity(logn, bits, odt):
     assert compare.float_err(host64(out), want)[0] <= tol
 
 
+@pytest.mark.parametrize("bits,g,logn", [(4, 128, 12), (4, 64, 13), (3, 32, 10), (4, 16, 8)])  # (INT2 cannot overflow)
+def test_quant_subnormal_scales_clip(bits, g, logn):
+    # rows so small that the fp16 scales are subnormal: rounding can shrink
+    # a scale enough that the group maximum maps past qmax + 1/2, where the
+    # codes must be clipped to +-qmax
+    n = 1 << logn
+    rng = np.random.default_rng(90 + bits)
+    sig = np.exp(rng.uniform(np.log(2e-8), np.log(2e-6), size=(24, 1)))
+    w = dev(sig * rng.standard_normal((24, n)), torch.bfloat16)
+    mask = synth.sign_bits_to_mask(rng.integers(0, 2, n))
+    y = H.rht(host64(w), H.signs_from_bits(mask, n))
+    _, _, v, _ = rtn.quantize_rtn(y, bits, g)
+    assert (np.rint(np.abs(v)) > rtn.qmax_of(bits)).sum() > 0  # the case occurs
+    check_quant(w, mask, bits, g)
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("logn,g", [(6, 64), (10, 32), (12, 64), (12, 128), (13, 64), (13, 256), (11, 8)])
 def test_dequant_arbitrary_codes(logn, g, bits):

@@ -99,14 +99,6 @@ __device__ __forceinline__ float max3abs(float acc, float a, float b) {
   return acc;
 }
 
-// acc <- (acc << S) + x in one v_lshl_add_u32 (keeps the packing chain from
-// being re-associated into separate shifts and adds).
-template <int S>
-__device__ __forceinline__ uint32_t shl_add(uint32_t acc, uint32_t x) {
-  asm("v_lshl_add_u32 %0, %0, %2, %1" : "+v"(acc) : "v"(x), "i"(S));
-  return acc;
-}
-
 // bf16 pair <-> fp32 (exact widening; the pair's low half is the lower index).
 __device__ __forceinline__ float bf16lo(uint32_t w) { return as_f(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return as_f(w & 0xffff0000u); }

@@ -12,11 +12,14 @@
 // involutions, so the inverse exists and is the same transform.
 //
 // Quantiser epilogue, per element:
-//   f = fma(y_raw, m_g, 1.5*2^23 + 2^(b-1)),  m_g = rho * n^-1/2 / s16_g
+//   f = fma(y_raw, m_g, 1.5*2^23),  m_g = rho * n^-1/2 / s16_g
 // The fma rounds the exact product once, to an integer (the ulp at 2^23 is
-// 1, round half to even), so the low bits of f hold q + 2^(b-1); codes are
-// packed with a shift-add chain and the constant high bits removed at the end.
+// 1, round half to even), and |q| <= 2^(b-1) keeps f in [2^23, 2^24), so the
+// low b bits of f are q in two's complement.  Codes are packed with a
+// funnel shift (v_alignbit_b32) that moves just those bits into the word.
 #pragma once
+
+#include <type_traits>
 
 #include "io.hpp"
 #include "launch.hpp"
@@ -27,17 +30,8 @@ namespace whtq {
 template <int BITS>
 struct QPack {
   static constexpr int QMAX = (1 << (BITS - 1)) - 1;
-  static constexpr float MAGIC = 12582912.0f + (float)(1 << (BITS - 1));
-  static constexpr uint32_t MAGIC_BITS = 0x4b400000u + (1u << (BITS - 1));
-  static constexpr int PER_WORD = 32 / BITS;  // BITS 2 or 4
-  static constexpr uint32_t ones() {
-    uint32_t s = 0;
-    for (int k = 0; k < PER_WORD; ++k) s += 1u << (BITS * k);
-    return s;
-  }
-  // sum_k MAGIC_BITS << (BITS k)  mod 2^32, where the code field holds 2^(b-1)
-  static constexpr uint32_t K = 0x4b400000u * ones();
-  static constexpr uint32_t BIAS = (1u << (BITS - 1)) * ones();
+  static constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
+  static constexpr int PER_WORD = 32 / BITS;   // BITS 2 or 4
 };
 
 // ------------------------------------------------------------------ forward
@@ -105,6 +99,7 @@ __global__ __launch_bounds__(Geo<LOGN>::THREADS) void k_rht_quant(
     // ---- epilogue: group absmax -> fp16 scale -> codes
     float mult[NG];
     uint16_t s16b[NG];
+    bool ovf = false;
 #pragma unroll
     for (int k = 0; k < NG; ++k) {
       // four independent max3 chains, then combined (short dependency chains)
@@ -122,32 +117,43 @@ __global__ __launch_bounds__(Geo<LOGN>::THREADS) void k_rht_quant(
       const float mm = sf > 0.f ? dv : 0.f;
       mult[k] = rho ? -mm : mm;
       s16b[k] = __builtin_bit_cast(uint16_t, h);
+      // fp16 rounding can shrink the scale enough (only where it is
+      // subnormal) that the group maximum lands past qmax + 1/2: then q
+      // must be clipped to +-qmax
+      ovf |= a * mm > QM + 0.25f;
     }
     uint32_t cw[LANE_CODE_B / 4];
-    if constexpr (BITS == 3) {
+    auto codes_of = [&](auto clip) {
+      auto q_of = [&](int r) {
+        float f = __builtin_fmaf(v[r], mult[r / GL], QP::MAGIC);
+        if constexpr (decltype(clip)::value) f = __builtin_amdgcn_fmed3f(f, QP::MAGIC - QM, QP::MAGIC + QM);
+        return as_u(f);
+      };
+      if constexpr (BITS == 3) {
 #pragma unroll
-      for (int j = 0; j < 6; ++j) cw[j] = 0u;
+        for (int j = 0; j < 6; ++j) cw[j] = 0u;
 #pragma unroll
-      for (int r = 0; r < 64; ++r) {
-        const float f = __builtin_fmaf(v[r], mult[r / GL], QP::MAGIC);
-        const uint32_t c = (as_u(f) & 7u) ^ 4u;
-        const int bit = 3 * r, wi = bit >> 5, off = bit & 31;
-        cw[wi] |= c << off;
-        if (off > 29) cw[wi + 1] |= c >> (32 - off);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < LANE_CODE_B / 4; ++j) {
-        uint32_t acc = 0;
-#pragma unroll
-        for (int k = QP::PER_WORD - 1; k >= 0; --k) {
-          const int r = j * QP::PER_WORD + k;
-          const float f = __builtin_fmaf(v[r], mult[r / GL], QP::MAGIC);
-          acc = shl_add<BITS>(acc, as_u(f));
+        for (int r = 0; r < 64; ++r) {
+          const uint32_t c = q_of(r) & 7u;
+          const int bit = 3 * r, wi = bit >> 5, off = bit & 31;
+          cw[wi] |= c << off;
+          if (off > 29) cw[wi + 1] |= c >> (32 - off);
         }
-        cw[j] = (acc - QP::K) ^ QP::BIAS;
+      } else {
+#pragma unroll
+        for (int j = 0; j < LANE_CODE_B / 4; ++j) {
+          // each step shifts the word down by BITS and puts the next code's
+          // bits on top: the first code ends in the lowest field
+          uint32_t acc = 0;
+#pragma unroll
+          for (int k = 0; k < QP::PER_WORD; ++k) acc = __builtin_amdgcn_alignbit(q_of(j * QP::PER_WORD + k), acc, BITS);
+          cw[j] = acc;
+        }
       }
-    }
+    };
+    // the clipping copy runs only for a wave that needs it
+    if (__builtin_amdgcn_ballot_w64(ovf)) codes_of(std::true_type{});
+    else codes_of(std::false_type{});
     // Stores are unconditional (no branch, so no conservative wait at a
     // join): a slot past the last row has recomputed the last row and writes
     // the same bytes there.  Lanes sharing a group write the same scale.
