@@ -34,8 +34,7 @@ struct Geo {
   static constexpr int LOGT = LOGN - LOGR;
   static constexpr int T = 1 << LOGT;
   static constexpr bool TWO = LOGT >= 3;
-  // floats per row slot (half row, padded: see hphys)
-  static constexpr int LDS_ROW = TWO ? N / 2 + N / 16 + (LOGN >= 13 ? N / 64 : 0) : 0;
+  static constexpr int LDS_ROW = TWO ? N / 2 + N / 16 : 0;  // floats per row slot (half row, padded)
 
   // index bits whose butterfly runs over DPP (so carry the rho sign)
   static constexpr unsigned RHO_MASK =
@@ -132,17 +131,17 @@ __device__ __forceinline__ void stages_A(float (&v)[64], int t) {
 // removed: c(i) = (i & 3) | ((i >> 3) << 2)) and the registers a half reads
 // into are exactly those its write has just freed.
 //
-// Padding, for 16-byte LDS accesses served 8 lanes at a time over 32 banks
-// (the model that reproduces the measured conflict counts): 4 floats per 32
-// keeps the layout-B side (lane t at 32 t + 4 k) conflict-free, and at
-// n >= 8192 another 8 floats per 256 separate the four quad lanes of the
-// layout-A side, whose half-row offsets are 128 floats apart there (with
-// the first term alone they fall 16 banks apart, two to a bank group).
+// Padding: 4 floats per 32.  Measured on gfx950 with the bank-conflict
+// counter: 16-byte LDS writes are served 8 consecutive lanes at a time over
+// 32 four-byte banks, 16-byte reads 16 lanes at a time over 64 banks.  With
+// this padding the layout-B side (lane t at 32 t + 4 k) is conflict-free both
+// ways; the layout-A side is conflict-free for n = 4096 writes and n = 8192
+// reads and 2-way for n = 8192 writes and n = 4096 reads.  A search over
+// paddings that add multiples of 4 floats per power-of-two block found none
+// better over both directions; the kernels that pay it are VALU-bound.
 
 template <int LOGN>
-__device__ __forceinline__ int hphys(int ci) {
-  return ci + ((ci >> 5) << 2) + (LOGN >= 13 ? (ci >> 8) << 3 : 0);
-}
+__device__ __forceinline__ int hphys(int ci) { return ci + ((ci >> 5) << 2); }
 
 template <int LOGN, int THREADS>
 __device__ __forceinline__ void transpose_AB(float* row, float (&v)[64], int t) {
