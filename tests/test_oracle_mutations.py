@@ -111,3 +111,19 @@ def test_mutant_harp_digit_order(monkeypatch):
     monkeypatch.setattr(P, "stage_matrix", rev)
     _fails(tq.test_harp_bruteforce, (2, 4, 3))
     _fails(tq.test_harp_permutation_blocks_at_real_shape)
+
+
+def test_mutant_qwha_backward_no_transform(monkeypatch):
+    def bwd(dy, row_ptr, col_idx, vals, d_in):
+        f = Q.csr_to_dense(row_ptr, col_idx, vals, dy.shape[1], d_in)
+        return np.asarray(dy, dtype=np.float64) @ f   # the Hn factor dropped
+    monkeypatch.setattr(Q, "qwha_backward_input", bwd)
+    _fails(tq.test_qwha_backward_input_is_the_adjoint, 64, 48)
+
+
+def test_mutant_qwha_grad_values_untransformed_x(monkeypatch):
+    def gv(x, dy, row_ptr, col_idx):
+        rows = np.repeat(np.arange(len(row_ptr) - 1), np.diff(row_ptr))
+        return np.einsum("te,te->e", np.asarray(dy)[:, rows], np.asarray(x)[:, col_idx])  # x, not x Hn
+    monkeypatch.setattr(Q, "qwha_grad_values", gv)
+    _fails(tq.test_qwha_grad_values_finite_differences)

@@ -67,6 +67,76 @@ def test_qwha_bruteforce(d_in, d_out):
     assert np.allclose(qwha.qwha_forward(x, rp, ci, vv, d_out), want, atol=1e-12)
 
 
+def random_csr(rng, d_out, d_in, per_row):
+    r = np.repeat(np.arange(d_out), per_row)
+    c = np.concatenate([rng.choice(d_in, per_row, replace=False) for _ in range(d_out)])
+    return qwha.coo_to_csr(r, c, rng.standard_normal(r.size), d_out)
+
+
+@pytest.mark.parametrize("d_in,d_out", [(64, 48), (256, 256), (16, 40)])
+def test_qwha_backward_input_is_the_adjoint(d_in, d_out):
+    # <y(x), dy> = <x, dx(dy)> for the linear map x -> y: pins the backward
+    # to the forward without restating either
+    rng = np.random.default_rng(d_in + d_out)
+    rp, ci, v = random_csr(rng, d_out, d_in, min(5, d_in))
+    x = rng.standard_normal((7, d_in))
+    dy = rng.standard_normal((7, d_out))
+    y = qwha.qwha_forward(x, rp, ci, v, d_out)
+    dx = qwha.qwha_backward_input(dy, rp, ci, v, d_in)
+    assert np.isclose(np.sum(y * dy), np.sum(x * dx), rtol=1e-12, atol=1e-12)
+
+
+def test_qwha_grad_values_finite_differences():
+    # the forward is linear in each value: moving c_e by 1 changes <y, dy> by dc_e
+    rng = np.random.default_rng(5)
+    d_in, d_out = 32, 24
+    rp, ci, v = random_csr(rng, d_out, d_in, 4)
+    x = rng.standard_normal((6, d_in))
+    dy = rng.standard_normal((6, d_out))
+    base = np.sum(qwha.qwha_forward(x, rp, ci, v, d_out) * dy)
+    dc = qwha.qwha_grad_values(x, dy, rp, ci)
+    for e in range(len(v)):
+        v2 = v.copy(); v2[e] += 1.0
+        assert np.isclose(np.sum(qwha.qwha_forward(x, rp, ci, v2, d_out) * dy) - base, dc[e], atol=1e-11)
+
+
+@pytest.mark.parametrize("d_in,d_out", [(8, 8), (16, 12)])
+def test_qwha_backward_bruteforce(d_in, d_out):
+    rng = np.random.default_rng(d_in * 7 + d_out)
+    rp, ci, v = random_csr(rng, d_out, d_in, 3)
+    x = rng.standard_normal((3, d_in))
+    dy = rng.standard_normal((3, d_out))
+    dz = np.zeros((3, d_in))
+    dc = np.zeros(len(v))
+    z = brute_wht(x)
+    for o in range(d_out):
+        for e in range(rp[o], rp[o + 1]):
+            dz[:, ci[e]] += v[e] * dy[:, o]
+            dc[e] = np.dot(dy[:, o], z[:, ci[e]])
+    assert np.allclose(qwha.qwha_backward_input(dy, rp, ci, v, d_in), brute_wht(dz), atol=1e-12)
+    assert np.allclose(qwha.qwha_grad_values(x, dy, rp, ci), dc, atol=1e-12)
+
+
+def test_qwha_backward_identity_f():
+    rng = np.random.default_rng(9)
+    n = 128
+    rp, ci, v = dense_to_csr(np.eye(n))
+    x = rng.standard_normal((4, n)); dy = rng.standard_normal((4, n))
+    assert np.allclose(qwha.qwha_backward_input(dy, rp, ci, v, n), H.wht(dy), atol=1e-12)
+    assert np.allclose(qwha.qwha_grad_values(x, dy, rp, ci), np.sum(dy * H.wht(x), axis=0), atol=1e-12)
+
+
+def test_csr_transpose():
+    rng = np.random.default_rng(11)
+    d_out, d_in = 20, 12
+    rp, ci, v = random_csr(rng, d_out, d_in, 3)
+    trp, tci, tv, perm = qwha.csr_transpose(rp, ci, v, d_in)
+    assert np.array_equal(qwha.csr_to_dense(trp, tci, tv, d_in, d_out), qwha.csr_to_dense(rp, ci, v, d_out, d_in).T)
+    assert np.array_equal(tv, np.asarray(v)[perm])
+    for k in range(d_in):  # rows of F^T hold increasing rows of F
+        assert np.all(np.diff(tci[trp[k]:trp[k + 1]]) > 0)
+
+
 # ------------------------------------------------------------------- HARP
 
 def digits(i, radices):
