@@ -35,8 +35,10 @@
  *
  * Common rules for every entry point:
  *   - All pointers are device pointers owned by the caller, except
- *     `radices` (host).  The library keeps no pointer after returning and
- *     allocates no memory.
+ *     `radices` (host) and those of the host helper qwha_csr_transpose.
+ *     The library keeps no pointer after returning and allocates no memory
+ *     (scratch space, where an operation needs it, is a caller-provided
+ *     workspace argument).
  *   - `stream` is a hipStream_t (NULL = the default stream).  WHTQ_OK means
  *     the work was enqueued; faults surface at the caller's next
  *     synchronisation.  Nothing is read back to the host.
@@ -58,7 +60,7 @@
 extern "C" {
 #endif
 
-#define WHTQ_ABI_VERSION 1
+#define WHTQ_ABI_VERSION 2
 
 typedef enum {
   WHTQ_OK = 0,
@@ -133,6 +135,86 @@ whtq_status qwha_adapter_forward(const void* x, whtq_dtype x_dtype, int64_t toke
                                  int64_t ldx, const int32_t* row_ptr, const int32_t* col_idx,
                                  const void* vals, whtq_dtype val_dtype, int64_t d_out, int64_t nnz,
                                  void* y, whtq_dtype y_dtype, int64_t ldy, void* stream);
+
+/*
+ * ---- QWHA adapter backward (training).  [QWHA] 2.1 makes the adapter linear
+ * in its input x and in the value vector c placed at the index list E, so
+ * its gradients for an upstream dy = dL/dy are the adjoint products:
+ *   dx   = dy Delta W = (dy F) Hn                  (Hn is symmetric)
+ *   dc_e = sum_t dy[t][o_e] (Hn x_t)[k_e]          (entry e at row o_e, column k_e of F)
+ */
+
+/*
+ * qwha_csr_transpose -- HOST helper: the CSR of F^T from the CSR of F.
+ *   All pointers are HOST pointers (caller-owned).  Inputs: row_ptr
+ *   int32[d_out + 1], col_idx int32[nnz] (the CSR of F, d_out x d_in).
+ *   Outputs: t_row_ptr int32[d_in + 1], t_col_idx int32[nnz] (the rows o of F
+ *   holding each entry, ascending within a column), t_perm int32[nnz] (entry j
+ *   of F^T is entry t_perm[j] of F).  The support E is fixed during training,
+ *   so this runs once; the values are re-permuted per step by
+ *   qwha_permute_values.  Unlike the device entry points this one reads the
+ *   CSR and returns WHTQ_EINVAL if it is malformed (row_ptr[0] != 0,
+ *   row_ptr[d_out] != nnz, decreasing row_ptr, a column outside [0, d_in)).
+ */
+whtq_status qwha_csr_transpose(const int32_t* row_ptr, const int32_t* col_idx, int64_t d_out, int64_t d_in,
+                               int64_t nnz, int32_t* t_row_ptr, int32_t* t_col_idx, int32_t* t_perm);
+
+/*
+ * qwha_permute_values -- out[j] = vals[perm[j]], j < nnz (device).  With the
+ * t_perm of qwha_csr_transpose it gives the values of F in the entry order of
+ * F^T.  vals / out: bf16 or f32 (val_dtype), out must not alias vals; perm
+ * entries must lie in [0, nnz) (not checked on the host).
+ */
+whtq_status qwha_permute_values(const void* vals, whtq_dtype val_dtype, const int32_t* perm, int64_t nnz,
+                                void* out, void* stream);
+
+/*
+ * qwha_adapter_backward_input -- dx = (dy F) Hn: dx[t][k] = (Hn u_t)[k] with
+ * u_t[j] = sum_{o in row j of F^T} F[o][j] dy[t][o].
+ *   dy [tokens][lddy] bf16 (d_out columns; 2-byte alignment suffices, 16-byte
+ *   aligned rows are read with 16-byte loads); dx [tokens][lddx] bf16 (d_in =
+ *   4096 columns, d_out in [1, 4096]).  F^T as CSR: t_row_ptr int32[d_in + 1],
+ *   t_col_idx int32[nnz] in [0, d_out), t_vals[nnz] (bf16 or f32), e.g. from
+ *   qwha_csr_transpose + qwha_permute_values; 16-byte aligned t_col_idx and
+ *   t_vals.  A malformed CSR gives undefined results (it is not read on the
+ *   host).
+ *   Arithmetic: dy is kept on chip in fp16 with a per-token power-of-two
+ *   scale (exact for bf16 inputs in range), fp32 accumulation of dy F, whose
+ *   rows are rounded once to bf16 on chip before the fp32 transform; each
+ *   output rounded once to bf16.
+ */
+whtq_status qwha_adapter_backward_input(const void* dy, whtq_dtype dy_dtype, int64_t tokens, int64_t d_out,
+                                        int64_t lddy, const int32_t* t_row_ptr, const int32_t* t_col_idx,
+                                        const void* t_vals, whtq_dtype val_dtype, int64_t d_in, int64_t nnz,
+                                        void* dx, whtq_dtype dx_dtype, int64_t lddx, void* stream);
+
+/*
+ * qwha_grad_values_workspace_bytes -- size in bytes of the workspace that
+ * qwha_adapter_grad_values needs for these sizes (a function of the sizes
+ * only); -1 for invalid sizes (d_in must be 4096), 0 when tokens or nnz is 0.
+ */
+int64_t qwha_grad_values_workspace_bytes(int64_t tokens, int64_t d_in, int64_t nnz);
+
+/*
+ * qwha_adapter_grad_values -- dc[e] = sum_t dy[t][o_e] * (Hn x_t)[col_idx[e]]
+ * for every entry e of F's CSR, o_e its row (the gradient of the values c).
+ *   x [tokens][ldx] bf16 (d_in = 4096); dy [tokens][lddy] bf16 (d_out in
+ *   [1, 4096], 2-byte alignment suffices); row_ptr int32[d_out + 1], col_idx int32[nnz] (the CSR of F;
+ *   not read on the host: malformed input gives undefined values, never an
+ *   access outside x, dy, dc or the workspace); dc float32[nnz] (written, in
+ *   CSR entry order).  tokens = 0 gives dc = 0.
+ *   workspace: device memory of at least
+ *   qwha_grad_values_workspace_bytes(tokens, d_in, nnz) bytes, 16-byte
+ *   aligned, overwritten (Hn x in fp32 and per-token-slab partial sums);
+ *   a smaller workspace_bytes returns WHTQ_EINVAL.
+ *   Arithmetic: Hn x in fp32; products and sums in fp32, over tokens in
+ *   order within fixed token slabs, then over slabs in order
+ *   (deterministic).
+ */
+whtq_status qwha_adapter_grad_values(const void* x, const void* dy, whtq_dtype dtype, int64_t tokens,
+                                     int64_t d_in, int64_t d_out, int64_t ldx, int64_t lddy,
+                                     const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz, float* dc,
+                                     void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * harp_rotate -- y = Stage_{m-1}( ... Stage_0( P x ) ), P = Hn S if

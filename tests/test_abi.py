@@ -26,20 +26,22 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"^\s*(?:whtq_status|const char\*|int)\s+(\w+)\s*\(", text, flags=re.M)
+    return re.findall(r"^\s*(?:whtq_status|const char\*|int|int64_t)\s+(\w+)\s*\(", text, flags=re.M)
 
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) >= {"wht_batched", "rht_quantize_rtn", "rht_dequantize_inverse",
                           "qwha_adapter_forward", "harp_rotate", "whtq_status_string",
-                          "whtq_last_hip_error", "whtq_abi_version"}
+                          "whtq_last_hip_error", "whtq_abi_version", "qwha_csr_transpose",
+                          "qwha_permute_values", "qwha_adapter_backward_input",
+                          "qwha_grad_values_workspace_bytes", "qwha_adapter_grad_values"}
     for nm in names:
         assert hasattr(lib, nm), nm
 
 
 def test_version_and_strings(lib):
-    assert lib.whtq_abi_version() == 1
+    assert lib.whtq_abi_version() == 2
     for s in range(5):
         assert lib.whtq_status_string(s)
     assert b"unknown" in lib.whtq_status_string(99)
@@ -141,3 +143,91 @@ def test_valid_call_without_device_is_ehip(lib):
     assert lib.whtq_last_hip_error() != 0
     assert q(lib) == EHIP and dq(lib) == EHIP
     assert qw(lib) == EHIP and hp(lib) == EHIP
+
+
+# ---- QWHA backward entry points
+
+def test_csr_transpose_matches_oracle():
+    """The host helper is integer work: bit-exact against the oracle's transpose
+    (empty rows and columns, a dense row, repeated columns across rows)."""
+    import numpy as np
+    from oracle import qwha
+    from wht_adapters_amd import whtq
+    rng = np.random.default_rng(5)
+    for d_out, d_in, per_row in ((7, 16, (0, 5)), (300, 4096, (0, 40)), (64, 64, (64, 65))):
+        lens = rng.integers(per_row[0], per_row[1], d_out)
+        lens[0] = 0
+        cols = np.concatenate([np.sort(rng.choice(d_in, int(l), replace=False)) for l in lens]).astype(np.int32)
+        rp = np.r_[0, np.cumsum(lens)].astype(np.int32)
+        t_rp, t_ci, t_pm = whtq.qwha_csr_transpose(rp, cols, d_in)
+        w_rp, w_ci, _, w_pm = qwha.csr_transpose(rp, cols, np.zeros(cols.size), d_in)
+        assert np.array_equal(t_rp, w_rp) and np.array_equal(t_ci, w_ci) and np.array_equal(t_pm, w_pm)
+
+
+def test_csr_transpose_rejects_malformed(lib):
+    import numpy as np
+    def run(rp, ci, d_out, d_in, nnz):
+        rp = np.asarray(rp, np.int32)
+        ci = np.asarray(ci, np.int32)
+        t_rp = np.empty(d_in + 1, np.int32)
+        t_ci = np.empty(max(nnz, 1), np.int32)
+        t_pm = np.empty(max(nnz, 1), np.int32)
+        vp = ctypes.c_void_p
+        return lib.qwha_csr_transpose(rp.ctypes.data_as(vp), ci.ctypes.data_as(vp), d_out, d_in, nnz,
+                                      t_rp.ctypes.data_as(vp), t_ci.ctypes.data_as(vp), t_pm.ctypes.data_as(vp))
+    assert run([0, 1, 2], [0, 3], 2, 4, 2) == OK
+    assert run([0, 1, 2], [0, 4], 2, 4, 2) == EINVAL     # column out of range
+    assert run([0, 2, 1], [0, 1], 2, 4, 2) == EINVAL     # decreasing row_ptr
+    assert run([1, 1, 2], [0, 1], 2, 4, 2) == EINVAL     # row_ptr[0] != 0
+    assert run([0, 1, 1], [0, 1], 2, 4, 2) == EINVAL     # row_ptr[d_out] != nnz
+    assert run([0, 0, 0], [0], 2, 4, 0) == OK            # empty F
+
+
+def bw(lib, dy=P, dyd=1, tokens=8, d_out=4096, lddy=4096, rp=P, ci=P, v=P, vd=1, d_in=4096, nnz=100,
+       dx=P, dxd=1, lddx=4096):
+    return lib.qwha_adapter_backward_input(dy, dyd, tokens, d_out, lddy, rp, ci, v, vd, d_in, nnz, dx, dxd,
+                                           lddx, NULL)
+
+
+def gv(lib, x=P, dy=P, dt=1, tokens=8, d_in=4096, d_out=4096, ldx=4096, lddy=4096, rp=P, ci=P, nnz=100,
+       dc=P, ws=P, wsb=1 << 40):
+    return lib.qwha_adapter_grad_values(x, dy, dt, tokens, d_in, d_out, ldx, lddy, rp, ci, nnz, dc, ws, wsb, NULL)
+
+
+def test_qwha_backward_validation(lib):
+    assert bw(lib, lddy=100) == EINVAL
+    assert bw(lib, lddx=100) == EINVAL
+    assert bw(lib, rp=NULL) == EINVAL
+    assert bw(lib, v=NULL) == EINVAL
+    assert bw(lib, d_in=2048, lddx=2048) == EUNSUP
+    assert bw(lib, d_out=5000, lddy=5000) == EUNSUP
+    assert bw(lib, dyd=0) == EUNSUP
+    assert bw(lib, vd=2) == EUNSUP
+    assert bw(lib, dx=P_MIS) == EALIGN
+    assert bw(lib, dy=ctypes.c_void_p(0x10001)) == EALIGN
+    assert bw(lib, ci=P_MIS) == EALIGN
+    assert bw(lib, tokens=0) == OK
+    assert gv(lib, ldx=100) == EINVAL
+    assert gv(lib, dc=NULL) == EINVAL
+    assert gv(lib, ws=NULL) == EINVAL
+    assert gv(lib, wsb=16) == EINVAL                        # workspace too small
+    assert gv(lib, d_in=2048, ldx=2048) == EUNSUP
+    assert gv(lib, dt=0) == EUNSUP
+    assert gv(lib, x=P_MIS) == EALIGN
+    assert gv(lib, ws=ctypes.c_void_p(0x10008)) == EALIGN
+    assert gv(lib, nnz=0, dc=NULL, ws=NULL, wsb=0) == OK     # empty support: nothing to do
+    assert lib.qwha_grad_values_workspace_bytes(8, 2048, 100) == -1
+    assert lib.qwha_grad_values_workspace_bytes(0, 4096, 100) == 0
+    # Hn x in fp32 (rounded up to 256 B) plus per-token-slab partial sums
+    need = lib.qwha_grad_values_workspace_bytes(2048, 4096, 262144)
+    assert need >= 2048 * 4096 * 4 and need % 4 == 0
+    vp = ctypes.c_void_p
+    assert lib.qwha_permute_values(P, 1, NULL, 10, P, NULL) == EINVAL
+    assert lib.qwha_permute_values(P, 1, P, 10, P, NULL) == EINVAL    # out aliases vals
+    assert lib.qwha_permute_values(P, 2, P, 10, vp(0x20000), NULL) == EUNSUP
+    assert lib.qwha_permute_values(P, 1, P, 0, vp(0x20000), NULL) == OK
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="needs a host without a GPU")
+def test_backward_valid_call_without_device_is_ehip(lib):
+    assert bw(lib) == EHIP and gv(lib) == EHIP

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <climits>
 #include <cmath>
 #include <mutex>
 
@@ -22,6 +23,16 @@ hipError_t launch_rht_dequant(int logn, int dout, int bits, int logg, const uint
 hipError_t launch_qwha(const void* x, int64_t tokens, int64_t ldx, const int32_t* row_ptr,
                        const int32_t* col_idx, const void* vals, int val_dt, int64_t d_out, int64_t nnz,
                        void* y, int64_t ldy, hipStream_t s);
+hipError_t launch_qwha_bwd_input(const void* dy, int64_t tokens, int64_t lddy, int64_t d_out,
+                                 const int32_t* t_row_ptr, const int32_t* t_col_idx, const void* t_vals,
+                                 int val_dt, int64_t nnz, void* dx, int64_t lddx, hipStream_t s);
+int64_t qwha_dc_workspace_bytes(int64_t tokens, int64_t nnz);
+hipError_t launch_qwha_dc(const void* x, int64_t ldx, const void* dy, int64_t lddy, int64_t tokens,
+                          int64_t d_out, const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
+                          float* dc, void* workspace, hipStream_t s);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+hipError_t launch_permute(const void* vals, int val_dt, const int32_t* perm, int64_t nnz, void* out,
+                          hipStream_t s);
 hipError_t launch_harp(const void* x, void* y, int dt, int64_t tokens, int64_t ldx, int64_t ldy,
                        const uint32_t* sbits, int precondition, const void* blocks, int bdt, hipStream_t s);
 
@@ -194,6 +205,106 @@ whtq_status qwha_adapter_forward(const void* x, whtq_dtype x_dtype, int64_t toke
   if (st != WHTQ_OK) return st;
   return hip_status(launch_qwha(x, tokens, ldx, row_ptr, col_idx, vals, val_dtype, d_out, nnz, y, ldy,
                                 (hipStream_t)stream));
+}
+
+whtq_status qwha_csr_transpose(const int32_t* row_ptr, const int32_t* col_idx, int64_t d_out, int64_t d_in,
+                               int64_t nnz, int32_t* t_row_ptr, int32_t* t_col_idx, int32_t* t_perm) {
+  if (d_out < 1 || d_in < 1 || nnz < 0 || d_out > INT32_MAX || d_in > INT32_MAX || nnz > INT32_MAX)
+    return WHTQ_EINVAL;
+  if (!row_ptr || !t_row_ptr || (nnz > 0 && (!col_idx || !t_col_idx || !t_perm))) return WHTQ_EINVAL;
+  // the CSR is read here, so it is checked in full first
+  if (row_ptr[0] != 0 || row_ptr[d_out] != nnz) return WHTQ_EINVAL;
+  for (int64_t o = 0; o < d_out; ++o)
+    if (row_ptr[o + 1] < row_ptr[o]) return WHTQ_EINVAL;
+  for (int64_t j = 0; j < nnz; ++j)
+    if (col_idx[j] < 0 || col_idx[j] >= d_in) return WHTQ_EINVAL;
+  // counting sort by column, stable in entry order (rows ascending within a
+  // column); t_row_ptr[k] serves as column k's cursor, then shifts back
+  for (int64_t k = 0; k <= d_in; ++k) t_row_ptr[k] = 0;
+  for (int64_t j = 0; j < nnz; ++j) ++t_row_ptr[col_idx[j] + 1];
+  for (int64_t k = 0; k < d_in; ++k) t_row_ptr[k + 1] += t_row_ptr[k];
+  for (int64_t o = 0; o < d_out; ++o)
+    for (int32_t j = row_ptr[o]; j < row_ptr[o + 1]; ++j) {
+      const int32_t pos = t_row_ptr[col_idx[j]]++;
+      t_col_idx[pos] = (int32_t)o;
+      t_perm[pos] = j;
+    }
+  for (int64_t k = d_in; k > 0; --k) t_row_ptr[k] = t_row_ptr[k - 1];
+  t_row_ptr[0] = 0;
+  return WHTQ_OK;
+}
+
+whtq_status qwha_permute_values(const void* vals, whtq_dtype val_dtype, const int32_t* perm, int64_t nnz,
+                                void* out, void* stream) {
+  if (!dt_valid(val_dtype) || nnz < 0) return WHTQ_EINVAL;
+  if (nnz > 0 && (!vals || !perm || !out)) return WHTQ_EINVAL;
+  if (nnz > 0 && vals == out) return WHTQ_EINVAL;
+  if (val_dtype == WHTQ_F16) return WHTQ_EUNSUPPORTED;
+  const uintptr_t esz = (uintptr_t)dt_bytes(val_dtype);
+  if ((reinterpret_cast<uintptr_t>(vals) % esz) || (reinterpret_cast<uintptr_t>(out) % esz) ||
+      (reinterpret_cast<uintptr_t>(perm) & 3u))
+    return WHTQ_EALIGN;
+  if (nnz == 0) return WHTQ_OK;
+  whtq_status st = need_device();
+  if (st != WHTQ_OK) return st;
+  return hip_status(launch_permute(vals, val_dtype, perm, nnz, out, (hipStream_t)stream));
+}
+
+whtq_status qwha_adapter_backward_input(const void* dy, whtq_dtype dy_dtype, int64_t tokens, int64_t d_out,
+                                        int64_t lddy, const int32_t* t_row_ptr, const int32_t* t_col_idx,
+                                        const void* t_vals, whtq_dtype val_dtype, int64_t d_in, int64_t nnz,
+                                        void* dx, whtq_dtype dx_dtype, int64_t lddx, void* stream) {
+  if (!dt_valid(dy_dtype) || !dt_valid(val_dtype) || !dt_valid(dx_dtype)) return WHTQ_EINVAL;
+  if (tokens < 0 || d_in < 1 || d_out < 1 || nnz < 0 || lddy < d_out || lddx < d_in) return WHTQ_EINVAL;
+  if (nnz > d_in * d_out) return WHTQ_EINVAL;
+  if (!t_row_ptr || (nnz > 0 && (!t_col_idx || !t_vals))) return WHTQ_EINVAL;
+  if (tokens > 0 && (!dy || !dx)) return WHTQ_EINVAL;
+  if (ilog2_pow2(d_in) < 0) return WHTQ_EUNSUPPORTED;
+  if (d_in != 4096 || d_out > 4096) return WHTQ_EUNSUPPORTED;
+  if (dy_dtype != WHTQ_BF16 || dx_dtype != WHTQ_BF16) return WHTQ_EUNSUPPORTED;
+  if (val_dtype != WHTQ_BF16 && val_dtype != WHTQ_F32) return WHTQ_EUNSUPPORTED;
+  // dy: element alignment suffices (16-byte loads are used where its rows allow them)
+  if ((reinterpret_cast<uintptr_t>(dy) & 1u) || !rows_aligned(dx, d_in, lddx, 2)) return WHTQ_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(t_row_ptr) & 3u) || !aligned16(t_col_idx) || !aligned16(t_vals))
+    return WHTQ_EALIGN;
+  if (tokens == 0) return WHTQ_OK;
+  whtq_status st = need_device();
+  if (st != WHTQ_OK) return st;
+  return hip_status(launch_qwha_bwd_input(dy, tokens, lddy, d_out, t_row_ptr, t_col_idx, t_vals, val_dtype, nnz,
+                                          dx, lddx, (hipStream_t)stream));
+}
+
+int64_t qwha_grad_values_workspace_bytes(int64_t tokens, int64_t d_in, int64_t nnz) {
+  if (tokens < 0 || nnz < 0 || d_in != 4096) return -1;
+  if (tokens == 0 || nnz == 0) return 0;
+  return qwha_dc_workspace_bytes(tokens, nnz);
+}
+
+whtq_status qwha_adapter_grad_values(const void* x, const void* dy, whtq_dtype dtype, int64_t tokens,
+                                     int64_t d_in, int64_t d_out, int64_t ldx, int64_t lddy,
+                                     const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz, float* dc,
+                                     void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!dt_valid(dtype)) return WHTQ_EINVAL;
+  if (tokens < 0 || d_in < 1 || d_out < 1 || nnz < 0 || ldx < d_in || lddy < d_out) return WHTQ_EINVAL;
+  if (nnz > d_in * d_out || nnz > INT32_MAX) return WHTQ_EINVAL;
+  if (!row_ptr || (nnz > 0 && (!col_idx || !dc))) return WHTQ_EINVAL;
+  if (tokens > 0 && nnz > 0 && (!x || !dy || !workspace)) return WHTQ_EINVAL;
+  if (ilog2_pow2(d_in) < 0) return WHTQ_EUNSUPPORTED;
+  if (d_in != 4096 || d_out > 4096) return WHTQ_EUNSUPPORTED;
+  if (dtype != WHTQ_BF16) return WHTQ_EUNSUPPORTED;
+  // dy is read with element loads: element alignment suffices
+  if (!rows_aligned(x, d_in, ldx, 2) || (reinterpret_cast<uintptr_t>(dy) & 1u)) return WHTQ_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(row_ptr) & 3u) || (reinterpret_cast<uintptr_t>(col_idx) & 3u) ||
+      (reinterpret_cast<uintptr_t>(dc) & 3u) || !aligned16(workspace))
+    return WHTQ_EALIGN;
+  if (tokens > 0 && nnz > 0 && workspace_bytes < qwha_dc_workspace_bytes(tokens, nnz)) return WHTQ_EINVAL;
+  if (nnz == 0) return WHTQ_OK;
+  whtq_status st = need_device();
+  if (st != WHTQ_OK) return st;
+  if (tokens == 0)  // an empty sum: dc = 0 (a fill kernel, not a memset node)
+    return hip_status(launch_fill_zero(dc, nnz, (hipStream_t)stream));
+  return hip_status(launch_qwha_dc(x, ldx, dy, lddy, tokens, d_out, row_ptr, col_idx, nnz, dc, workspace,
+                                   (hipStream_t)stream));
 }
 
 whtq_status harp_rotate(const void* x, void* y, whtq_dtype dtype, int64_t tokens, int64_t d, int64_t ldx,

@@ -21,6 +21,11 @@
 //      (v_fma_mix with the fp16 column), a quad DPP reduction per row; the
 //      results go to a token-major bf16 buffer in LDS;
 //   5. the chunk's outputs leave with 16-byte row-contiguous stores.
+//
+// The same kernel computes the adapter's gradient with respect to its input,
+// dx = dy Delta W = (dy F) Hn (Hn is symmetric): the tile is dy as it is (no
+// transform in step 1), the CSR is that of F^T, the gathered rows (dy F)
+// stay on chip in bf16 for all 4096 columns, and step 6 transforms them.
 #include "io.hpp"
 #include "launch.hpp"
 
@@ -38,23 +43,28 @@ constexpr int NBKT = 256;      // buckets: 16-entry steps per row, capped
 }  // namespace qw
 
 // LDS map (bytes):
-//   [0, 64K)      Z[k][tok] fp16, 16 B per column     (FWHT scratch before step 2)
-//   [64K, 128K)   staging Zt[tok][k] fp16 in steps 1-2; afterwards, per chunk,
+//   [0, 64K)      Z[k][tok] fp16, 16 B per column     (FWHT scratch before step 2,
+//                 and in the backward before step 6)
+//   [64K, ...)    staging Zt[tok][k] fp16 in steps 1-2; afterwards, per chunk,
 //                 the sorted row list (row u16, start i32, end i32) and the
-//                 output buffer O[tok][row] bf16
-//   [128K, +1K)   bucket counters (uint32)
-//   [+1K, +32)    per-token exponent
-constexpr int QW_LDS_Z = 0;
-constexpr int QW_LDS_ZT = 65536;
-constexpr int QW_LDS_RID = 65536;
-constexpr int QW_LDS_RBEG = QW_LDS_RID + 2 * qw::CHUNK;
-constexpr int QW_LDS_REND = QW_LDS_RBEG + 4 * qw::CHUNK;
-constexpr int QW_LDS_OUT = QW_LDS_REND + 4 * qw::CHUNK;
-constexpr int QW_LDS_BKT = 131072;
-constexpr int QW_LDS_EXP = QW_LDS_BKT + 4 * qw::NBKT;
-constexpr int QW_LDS_BYTES = QW_LDS_EXP + 4 * qw::TT;
-static_assert(QW_LDS_OUT % 16 == 0 && QW_LDS_OUT + 2 * qw::TT * qw::CHUNK <= QW_LDS_BKT,
-              "row list + output buffer fit the staging area");
+//                 output buffer O[tok][row] bf16 (the backward keeps all 4096
+//                 rows of it: [tok][4096])
+//   then          bucket counters (uint32), per-token exponent
+template <bool BWD>
+struct QwLds {
+  static constexpr int Z = 0;
+  static constexpr int ZT = 65536;
+  static constexpr int RID = 65536;
+  static constexpr int RBEG = RID + 2 * qw::CHUNK;
+  static constexpr int REND = RBEG + 4 * qw::CHUNK;
+  static constexpr int OUT = REND + 4 * qw::CHUNK;
+  static constexpr int OSTRIDE = BWD ? qw::N : qw::CHUNK;  // output buffer row stride (elements)
+  static constexpr int OUT_END = OUT + 2 * qw::TT * OSTRIDE;
+  static constexpr int BKT = OUT_END > 131072 ? OUT_END : 131072;
+  static constexpr int EXP = BKT + 4 * qw::NBKT;
+  static constexpr int BYTES = EXP + 4 * qw::TT;
+  static_assert(OUT % 16 == 0 && BYTES <= 160 * 1024, "LDS map");
+};
 
 // 16-entry steps of a row [beg, end) whose steps start at beg rounded down to a multiple of 4
 __device__ __forceinline__ int qw_steps(int beg, int end) { return end > beg ? (end - (beg & ~3) + 15) >> 4 : 0; }
@@ -79,25 +89,29 @@ template <> struct ValQuad<DT_F32> {  // 16 bytes
   static __device__ __forceinline__ float get(const raw& r, int q) { return r[q]; }
 };
 
-template <int VALDT>
+// Forward (BWD = false): x = activations, CSR of F (d_out rows), y = outputs.
+// Backward to the input (BWD = true): x = dy [tokens][in_cols], CSR of F^T
+// (d_in = 4096 rows, entries indexing columns of dy), y = dx [tokens][4096].
+template <int VALDT, bool BWD>
 __global__ __launch_bounds__(qw::THREADS) void k_qwha(const uint16_t* __restrict__ x, int64_t tokens,
-                                                      int64_t ldx, const int32_t* __restrict__ row_ptr,
+                                                      int64_t ldx, int in_cols, const int32_t* __restrict__ row_ptr,
                                                       const int32_t* __restrict__ col_idx,
                                                       const void* __restrict__ vals, int d_out, int nnz,
-                                                      uint16_t* __restrict__ y, int64_t ldy, int vec_out) {
+                                                      uint16_t* __restrict__ y, int64_t ldy, int vec) {
   using G = Geo<qw::LOGN>;
   using V = ValQuad<VALDT>;
+  using L = QwLds<BWD>;
   extern __shared__ __align__(16) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t tok0 = (int64_t)blockIdx.x * qw::TT;
   const int ntok = (int)min<int64_t>(qw::TT, tokens - tok0);
 
-  uint16_t* rid = reinterpret_cast<uint16_t*>(smem + QW_LDS_RID);
-  int* rbeg = reinterpret_cast<int*>(smem + QW_LDS_RBEG);
-  int* rend = reinterpret_cast<int*>(smem + QW_LDS_REND);
-  uint16_t* obuf = reinterpret_cast<uint16_t*>(smem + QW_LDS_OUT);
-  uint32_t* bkt = reinterpret_cast<uint32_t*>(smem + QW_LDS_BKT);
-  int* texp = reinterpret_cast<int*>(smem + QW_LDS_EXP);
+  uint16_t* rid = reinterpret_cast<uint16_t*>(smem + L::RID);
+  int* rbeg = reinterpret_cast<int*>(smem + L::RBEG);
+  int* rend = reinterpret_cast<int*>(smem + L::REND);
+  uint16_t* obuf = reinterpret_cast<uint16_t*>(smem + L::OUT);
+  uint32_t* bkt = reinterpret_cast<uint32_t*>(smem + L::BKT);
+  int* texp = reinterpret_cast<int*>(smem + L::EXP);
 
   auto histogram = [&](int base, int cn) {
     for (int r = tid; r < cn; r += qw::THREADS) {
@@ -111,12 +125,13 @@ __global__ __launch_bounds__(qw::THREADS) void k_qwha(const uint16_t* __restrict
   __syncthreads();
   histogram(0, min(qw::CHUNK, d_out));
 
-  // ---- 1. FWHT of the token rows, staged as fp16 token-major
+  // ---- 1. FWHT of the token rows (backward: the dy rows as they are),
+  // staged as fp16 token-major
   if (wave < qw::FWAVES) {
-    float* scratch = reinterpret_cast<float*>(smem + QW_LDS_Z) + wave * G::LDS_ROW;
-    uint16_t* zt = reinterpret_cast<uint16_t*>(smem + QW_LDS_ZT);
+    float* scratch = reinterpret_cast<float*>(smem + L::Z) + wave * G::LDS_ROW;
+    uint16_t* zt = reinterpret_cast<uint16_t*>(smem + L::ZT);
     const int t = lane;
-    const bool rho = rho_B<qw::LOGN>(t);
+    const bool rho = BWD ? false : rho_B<qw::LOGN>(t);
     int col[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) col[c] = G::idxA(t, c * 8);
@@ -125,15 +140,36 @@ __global__ __launch_bounds__(qw::THREADS) void k_qwha(const uint16_t* __restrict
       const int64_t tok = tok0 + min(k, ntok - 1);  // tail tokens recompute the last one
       const uint16_t* xr = x + tok * ldx;
       float v[64];
+      if constexpr (BWD) {
+        // lane t holds columns 64 t .. 64 t + 63 (layout B); columns past
+        // in_cols are zero (16-byte loads where a chunk lies inside and the
+        // rows are 16-byte aligned, `vec`; else element loads)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        Raw8 raw;
-        fetch8<DT_BF16>(xr, col[c], raw);
-        widen8<DT_BF16, false>(raw, v + 8 * c, nomask, 0u);
+        for (int q = 0; q < 8; ++q) {
+          const int c0 = 64 * t + 8 * q;
+          if (vec && c0 + 8 <= in_cols) {
+            const u32x4 w = ldg<u32x4>(xr + c0);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              v[8 * q + 2 * p] = bf16lo(w[p]);
+              v[8 * q + 2 * p + 1] = bf16hi(w[p]);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[8 * q + e] = c0 + e < in_cols ? as_f((uint32_t)xr[c0 + e] << 16) : 0.f;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          Raw8 raw;
+          fetch8<DT_BF16>(xr, col[c], raw);
+          widen8<DT_BF16, false>(raw, v + 8 * c, nomask, 0u);
+        }
+        stages_A<qw::LOGN, false>(v, t);
+        transpose_AB<qw::LOGN, 64>(scratch, v, t);
+        stages_B<qw::LOGN, 2>(v, t);
       }
-      stages_A<qw::LOGN, false>(v, t);
-      transpose_AB<qw::LOGN, 64>(scratch, v, t);
-      stages_B<qw::LOGN, 2>(v, t);
       // exact power-of-two scale putting max |z| in [2^13, 2^14)
       float a4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -159,8 +195,8 @@ __global__ __launch_bounds__(qw::THREADS) void k_qwha(const uint16_t* __restrict
 
   // ---- 2. Zt[tok][k] -> Z[k][tok]
   {
-    const uint16_t* zt = reinterpret_cast<const uint16_t*>(smem + QW_LDS_ZT);
-    u32x4* z = reinterpret_cast<u32x4*>(smem + QW_LDS_Z);
+    const uint16_t* zt = reinterpret_cast<const uint16_t*>(smem + L::ZT);
+    u32x4* z = reinterpret_cast<u32x4*>(smem + L::Z);
     for (int kk = tid; kk < qw::N; kk += qw::THREADS) {
       uint32_t h[qw::TT];
 #pragma unroll
@@ -213,7 +249,7 @@ __global__ __launch_bounds__(qw::THREADS) void k_qwha(const uint16_t* __restrict
     // loads run one step ahead, across group boundaries.
     const int ng = nnz > 0 ? (cn + 15) >> 4 : 0;
     if (nnz == 0)  // F = 0: every output is zero
-      for (int i = tid; i < qw::TT * cn; i += qw::THREADS) obuf[(i / cn) * qw::CHUNK + i % cn] = 0;
+      for (int i = tid; i < qw::TT * cn; i += qw::THREADS) obuf[(i / cn) * L::OSTRIDE + (BWD ? base : 0) + i % cn] = 0;
     struct Row {
       int r, beg, end, nst;
     };
@@ -265,7 +301,7 @@ __global__ __launch_bounds__(qw::THREADS) void k_qwha(const uint16_t* __restrict
       }
       u32x4 zv[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) zv[q] = *reinterpret_cast<const u32x4*>(smem + QW_LDS_Z + (cw[q] << 4));
+      for (int q = 0; q < 4; ++q) zv[q] = *reinterpret_cast<const u32x4*>(smem + L::Z + (cw[q] << 4));
       // (copied out as words: subscripting the loaded vectors with the
       // unrolled loop index was miscompiled into a single 4-byte read)
       uint32_t zc[4][4];
@@ -311,52 +347,104 @@ __global__ __launch_bounds__(qw::THREADS) void k_qwha(const uint16_t* __restrict
           b = slot == k ? acc[2 * k + 1] : b;
         }
         const uint32_t ab = pack_bf16(a * osc0, b * osc1);
-        obuf[(2 * slot) * qw::CHUNK + cur.r] = (uint16_t)(ab & 0xffffu);
-        obuf[(2 * slot + 1) * qw::CHUNK + cur.r] = (uint16_t)(ab >> 16);
+        const int oc = (BWD ? base : 0) + cur.r;
+        obuf[(2 * slot) * L::OSTRIDE + oc] = (uint16_t)(ab & 0xffffu);
+        obuf[(2 * slot + 1) * L::OSTRIDE + oc] = (uint16_t)(ab >> 16);
       }
       cur = nxt;
     }
     __syncthreads();
 
-    // ---- 5. the chunk's outputs, row-contiguous
-    const int cq = (cn + 7) >> 3;
-    for (int i = tid; i < ntok * cq; i += qw::THREADS) {
-      const int t = i / cq, q = i - t * cq;
-      const uint16_t* src = obuf + t * qw::CHUNK + 8 * q;
-      uint16_t* dst = y + (tok0 + t) * ldy + base + 8 * q;
-      if (vec_out && 8 * q + 8 <= cn) {
-        stg(dst, *reinterpret_cast<const u32x4*>(src));
-      } else {
-        for (int e = 0; e < 8 && 8 * q + e < cn; ++e) dst[e] = src[e];
+    // ---- 5. the chunk's outputs, row-contiguous (the backward keeps them on chip)
+    if constexpr (!BWD) {
+      const int cq = (cn + 7) >> 3;
+      for (int i = tid; i < ntok * cq; i += qw::THREADS) {
+        const int t = i / cq, q = i - t * cq;
+        const uint16_t* src = obuf + t * qw::CHUNK + 8 * q;
+        uint16_t* dst = y + (tok0 + t) * ldy + base + 8 * q;
+        if (vec && 8 * q + 8 <= cn) {
+          stg(dst, *reinterpret_cast<const u32x4*>(src));
+        } else {
+          for (int e = 0; e < 8 && 8 * q + e < cn; ++e) dst[e] = src[e];
+        }
       }
     }
     __syncthreads();  // the next chunk reuses the row list and the output buffer
   }
+
+  // ---- 6. backward only: dx_t = Hn (dy_t F).  The buffer holds (dy_t F) / 64
+  // in bf16, so the raw transform of each row finishes it; one wave per token
+  // row, its transpose scratch in the (now unused) Z tile and row lists.
+  if constexpr (BWD) {
+    static_assert(qw::TT * G::LDS_ROW * 4 <= L::OUT, "transpose scratch below the output buffer");
+    if (wave < qw::TT) {
+      const int k = wave, t = lane;
+      float* scratch = reinterpret_cast<float*>(smem) + wave * G::LDS_ROW;
+      const uint16_t* orow = obuf + k * qw::N;
+      const uint32_t nomask[4] = {0u, 0u, 0u, 0u};
+      float v[64];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        Raw8 raw;
+        raw.a = *reinterpret_cast<const u32x4*>(orow + G::idxA(t, c * 8));
+        widen8<DT_BF16, false>(raw, v + 8 * c, nomask, 0u);
+      }
+      stages_A<qw::LOGN, false>(v, t);
+      transpose_AB<qw::LOGN, 64>(scratch, v, t);
+      stages_B<qw::LOGN, 2>(v, t);
+      if (k < ntok) {
+        const float sg = rho_B<qw::LOGN>(t) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int e = 0; e < 64; ++e) v[e] *= sg;
+        uint16_t* dst = y + (tok0 + k) * ldy + 64 * t;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) store8<DT_BF16>(dst, 8 * q, v + 8 * q);
+      }
+    }
+  }
+}
+
+template <int VALDT, bool BWD>
+static void launch_one(const void* x, int64_t tokens, int64_t ldx, int in_cols, const int32_t* row_ptr,
+                       const int32_t* col_idx, const void* vals, int d_out, int nnz, void* y, int64_t ldy,
+                       int vec, hipStream_t s) {
+  static const bool attr = hipFuncSetAttribute((const void*)k_qwha<VALDT, BWD>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               QwLds<BWD>::BYTES) == hipSuccess;
+  (void)attr;
+  const unsigned grid = (unsigned)((tokens + qw::TT - 1) / qw::TT);
+  hipLaunchKernelGGL((k_qwha<VALDT, BWD>), dim3(grid), dim3(qw::THREADS), QwLds<BWD>::BYTES, s,
+                     (const uint16_t*)x, tokens, ldx, in_cols, row_ptr, col_idx, vals, d_out, nnz,
+                     (uint16_t*)y, ldy, vec);
 }
 
 hipError_t launch_qwha(const void* x, int64_t tokens, int64_t ldx, const int32_t* row_ptr,
                        const int32_t* col_idx, const void* vals, int val_dt, int64_t d_out, int64_t nnz,
                        void* y, int64_t ldy, hipStream_t s) {
-  const unsigned grid = (unsigned)((tokens + qw::TT - 1) / qw::TT);
   // 16-byte output stores need a 16-byte aligned base and row stride
   const int vec_out = ((reinterpret_cast<uintptr_t>(y) & 15u) == 0 && (ldy * 2) % 16 == 0) ? 1 : 0;
-  if (val_dt == DT_BF16) {
-    static const bool attr = hipFuncSetAttribute((const void*)k_qwha<DT_BF16>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 QW_LDS_BYTES) == hipSuccess;
-    (void)attr;
-    hipLaunchKernelGGL(k_qwha<DT_BF16>, dim3(grid), dim3(qw::THREADS), QW_LDS_BYTES, s,
-                       (const uint16_t*)x, tokens, ldx, row_ptr, col_idx, vals, (int)d_out, (int)nnz,
-                       (uint16_t*)y, ldy, vec_out);
-  } else {
-    static const bool attr = hipFuncSetAttribute((const void*)k_qwha<DT_F32>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 QW_LDS_BYTES) == hipSuccess;
-    (void)attr;
-    hipLaunchKernelGGL(k_qwha<DT_F32>, dim3(grid), dim3(qw::THREADS), QW_LDS_BYTES, s,
-                       (const uint16_t*)x, tokens, ldx, row_ptr, col_idx, vals, (int)d_out, (int)nnz,
-                       (uint16_t*)y, ldy, vec_out);
-  }
+  if (val_dt == DT_BF16)
+    launch_one<DT_BF16, false>(x, tokens, ldx, qw::N, row_ptr, col_idx, vals, (int)d_out, (int)nnz, y, ldy,
+                               vec_out, s);
+  else
+    launch_one<DT_F32, false>(x, tokens, ldx, qw::N, row_ptr, col_idx, vals, (int)d_out, (int)nnz, y, ldy,
+                              vec_out, s);
+  return hipGetLastError();
+}
+
+// dx = (dy F) Hn from the CSR of F^T (d_in = 4096 rows whose entries index
+// the d_out columns of dy).
+hipError_t launch_qwha_bwd_input(const void* dy, int64_t tokens, int64_t lddy, int64_t d_out,
+                                 const int32_t* t_row_ptr, const int32_t* t_col_idx, const void* t_vals,
+                                 int val_dt, int64_t nnz, void* dx, int64_t lddx, hipStream_t s) {
+  // 16-byte dy loads need a 16-byte aligned base and row stride
+  const int vec_in = ((reinterpret_cast<uintptr_t>(dy) & 15u) == 0 && (lddy * 2) % 16 == 0) ? 1 : 0;
+  if (val_dt == DT_BF16)
+    launch_one<DT_BF16, true>(dy, tokens, lddy, (int)d_out, t_row_ptr, t_col_idx, t_vals, qw::N, (int)nnz, dx,
+                              lddx, vec_in, s);
+  else
+    launch_one<DT_F32, true>(dy, tokens, lddy, (int)d_out, t_row_ptr, t_col_idx, t_vals, qw::N, (int)nnz, dx,
+                             lddx, vec_in, s);
   return hipGetLastError();
 }
 

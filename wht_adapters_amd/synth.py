@@ -144,6 +144,7 @@ WORKLOADS = {
     "fwht_f32_256x4096": "orthonormal FWHT only, fp32, 256 rows x 4096, N(0,1) from seed 0",
     "rht_int4_g128_4096x4096": "RHT + INT4 RTN g=128, bf16 4096 x 4096 Student-t weights",
     "qwha_2048x4096_nnz262144": "QWHA forward, 2048 tokens x 4096, F 4096 x 4096 with 262,144 nnz",
+    "qwha_bwd_2048x4096_nnz262144": "QWHA backward (dx and dc), same sizes, upstream dy ~ N(0,1)",
     "harp_8192x4096_r16x3": "HARP: RHT + three radix-16 stages, 8192 tokens x 4096",
     "rht_int2_g64_28672x8192": "RHT + INT2 RTN g=64, bf16 28672 x 8192 Student-t weights",
 }
@@ -176,6 +177,14 @@ def qwha(tokens=2048, d_in=4096, d_out=4096, nnz=262144):
     x = to_bf16(gaussian_rows(child_rng(3, 0), tokens, d_in))
     row_ptr, cols, vals = sparse_adapter(3, d_out, d_in, nnz)
     return {"x": x, "row_ptr": row_ptr, "col_idx": cols, "vals": vals, "d_out": d_out}
+
+
+def qwha_backward(tokens=2048, d_in=4096, d_out=4096, nnz=262144):
+    """The QWHA workload plus an upstream gradient dy [tokens, d_out] ~ N(0,1)
+    -> bf16 (child stream 4 of the same workload)."""
+    d = qwha(tokens, d_in, d_out, nnz)
+    d["dy"] = to_bf16(gaussian_rows(child_rng(3, 4), tokens, d_out))
+    return d
 
 
 def harp(tokens=8192, d=4096, radices=(16, 16, 16), outlier_frac=0.005, factor=30.0):

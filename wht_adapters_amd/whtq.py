@@ -27,11 +27,19 @@ _SIG = {
     "qwha_adapter_forward": [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _int, _i64, _i64, _vp, _int,
                              _i64, _vp],
     "harp_rotate": [_vp, _vp, _int, _i64, _i64, _i64, _i64, _vp, _int, _vp, _int, _vp, _int, _vp],
+    "qwha_csr_transpose": [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp],
+    "qwha_permute_values": [_vp, _int, _vp, _i64, _vp, _vp],
+    "qwha_adapter_backward_input": [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _int, _i64, _i64, _vp, _int,
+                                    _i64, _vp],
+    "qwha_adapter_grad_values": [_vp, _vp, _int, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64,
+                                 _vp],
 }
 for _name, _args in _SIG.items():
     _f = getattr(_lib, _name)
     _f.argtypes = _args
     _f.restype = _int
+_lib.qwha_grad_values_workspace_bytes.argtypes = [_i64, _i64, _i64]
+_lib.qwha_grad_values_workspace_bytes.restype = _i64
 _lib.whtq_status_string.argtypes = [_int]
 _lib.whtq_status_string.restype = ctypes.c_char_p
 _lib.whtq_last_hip_error.restype = _int
@@ -200,4 +208,104 @@ def harp_rotate(x, blocks, radices=(16, 16, 16), signs=None, precondition=True, 
         _check("harp_rotate", _lib.harp_rotate(
             _ptr(x), _ptr(out), _DT[x.dtype], tokens, d, ldx, ldy, _sign_ptr(signs, d, x.device),
             int(bool(precondition)), rad, len(radices), _ptr(blocks), _DT[blocks.dtype], _stream(x)))
+    return out
+
+
+def _csr_dev(**ts):
+    for nm, t in ts.items():
+        _need_cuda(nm, t)
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+
+
+def qwha_csr_transpose(row_ptr, col_idx, d_in):
+    """CSR of F^T from the CSR of F (host helper; numpy int32 arrays in and out).
+    Returns (t_row_ptr [d_in + 1], t_col_idx [nnz], t_perm [nnz])."""
+    import numpy as np
+    rp = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    ci = np.ascontiguousarray(col_idx, dtype=np.int32)
+    d_out, nnz = rp.size - 1, ci.size
+    t_rp = np.empty(d_in + 1, np.int32)
+    t_ci = np.empty(max(nnz, 1), np.int32)
+    t_pm = np.empty(max(nnz, 1), np.int32)
+    _check("qwha_csr_transpose", _lib.qwha_csr_transpose(
+        rp.ctypes.data_as(_vp), ci.ctypes.data_as(_vp), d_out, d_in, nnz, t_rp.ctypes.data_as(_vp),
+        t_ci.ctypes.data_as(_vp), t_pm.ctypes.data_as(_vp)))
+    return t_rp, t_ci[:nnz], t_pm[:nnz]
+
+
+def qwha_permute_values(vals, perm, out=None):
+    """out[j] = vals[perm[j]] on the device (F's values in F^T's entry order)."""
+    _csr_dev(vals=vals, perm=perm)
+    if perm.dtype != torch.int32:
+        raise ValueError("perm must be int32")
+    if out is None:
+        out = torch.empty(perm.numel(), dtype=vals.dtype, device=vals.device)
+    _csr_dev(out=out)
+    if out.numel() != perm.numel() or out.dtype != vals.dtype:
+        raise ValueError("out must match perm's length and vals' dtype")
+    with torch.cuda.device(vals.device):
+        _check("qwha_permute_values", _lib.qwha_permute_values(
+            _ptr(vals), _DT[vals.dtype], _ptr(perm), perm.numel(), _ptr(out), _stream(vals)))
+    return out
+
+
+def qwha_adapter_backward_input(dy, t_row_ptr, t_col_idx, t_vals, d_in=4096, out=None):
+    """dx = (dy F) Hn from the CSR of F^T (t_row_ptr [d_in + 1], t_col_idx, t_vals)."""
+    _need_cuda("dy", dy)
+    tokens, d_out, lddy = _rows_ld("dy", dy)
+    _csr_dev(t_row_ptr=t_row_ptr, t_col_idx=t_col_idx, t_vals=t_vals)
+    if t_row_ptr.dtype != torch.int32 or t_col_idx.dtype != torch.int32:
+        raise ValueError("t_row_ptr and t_col_idx must be int32")
+    if t_row_ptr.numel() != d_in + 1:
+        raise ValueError("t_row_ptr must have d_in + 1 entries")
+    nnz = t_col_idx.numel()
+    if t_vals.numel() != nnz:
+        raise ValueError("t_vals and t_col_idx must have the same length")
+    if out is None:
+        out = torch.empty((tokens, d_in), dtype=dy.dtype, device=dy.device)
+    r2, n2, lddx = _rows_ld("out", out)
+    if (r2, n2) != (tokens, d_in):
+        raise ValueError("out shape mismatch")
+    with torch.cuda.device(dy.device):
+        _check("qwha_adapter_backward_input", _lib.qwha_adapter_backward_input(
+            _ptr(dy), _DT[dy.dtype], tokens, d_out, lddy, _ptr(t_row_ptr), _ptr(t_col_idx), _ptr(t_vals),
+            _DT[t_vals.dtype], d_in, nnz, _ptr(out), _DT[out.dtype], lddx, _stream(dy)))
+    return out
+
+
+def qwha_grad_values_workspace_bytes(tokens, d_in, nnz):
+    return int(_lib.qwha_grad_values_workspace_bytes(tokens, d_in, nnz))
+
+
+def qwha_adapter_grad_values(x, dy, row_ptr, col_idx, out=None, workspace=None):
+    """dc[e] = sum_t dy[t, row(e)] (x Hn)[t, col_idx[e]] in float32, CSR entry order."""
+    _need_cuda("x", x)
+    _need_cuda("dy", dy)
+    tokens, d_in, ldx = _rows_ld("x", x)
+    t2, d_out, lddy = _rows_ld("dy", dy)
+    if t2 != tokens:
+        raise ValueError("x and dy must have the same number of tokens")
+    _csr_dev(row_ptr=row_ptr, col_idx=col_idx)
+    if row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+        raise ValueError("row_ptr and col_idx must be int32")
+    if row_ptr.numel() != d_out + 1:
+        raise ValueError("row_ptr must have d_out + 1 entries")
+    nnz = col_idx.numel()
+    if out is None:
+        out = torch.empty(nnz, dtype=torch.float32, device=x.device)
+    _csr_dev(out=out)
+    if out.dtype != torch.float32 or out.numel() != nnz:
+        raise ValueError("out must be float32 with nnz entries")
+    need = qwha_grad_values_workspace_bytes(tokens, d_in, nnz)
+    if need < 0:
+        raise WhtqError("qwha_grad_values_workspace_bytes", 2)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _csr_dev(workspace=workspace)
+    wbytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(x.device):
+        _check("qwha_adapter_grad_values", _lib.qwha_adapter_grad_values(
+            _ptr(x), _ptr(dy), _DT[x.dtype], tokens, d_in, d_out, ldx, lddy, _ptr(row_ptr), _ptr(col_idx),
+            nnz, _ptr(out), _ptr(workspace), wbytes, _stream(x)))
     return out
