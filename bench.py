@@ -5,8 +5,8 @@ Main workload (the one `value` is quoted on): RHT + INT4 round-to-nearest
 quantisation, bf16 weight matrix 4096 x 4096, group 128 along d_in, fp16
 scales, signed int4 codes -- one `rht_quantize_rtn` launch per step.  The
 other workloads (orthonormal FWHT 256 x 4096 fp32, the inverse of the INT4
-path, QWHA adapter forward, HARP rotation, 28672 x 8192 RHT + INT2) are
-timed the same way and reported under "workloads".
+path, QWHA adapter forward and backward, HARP rotation, 28672 x 8192 RHT +
+INT2) are timed the same way and reported under "workloads".
 
 Timing: each step processes a different copy of the input, rotating over
 copies totalling >= 1 GiB so that inputs come from HBM rather than the
@@ -39,6 +39,10 @@ ALGO_BYTES = {
     "rht_int4_g128_4096x4096_inverse": 4096 * 4096 * 2 + 512 + 4096 * 2048 + 4096 * 32 * 2,
     "qwha_2048x4096_nnz262144": 2 * 2048 * 4096 * 2 + 4097 * 4 + 262144 * 4 + 262144 * 2,
     "harp_8192x4096_r16x3": 2 * 8192 * 4096 * 2 + 3 * 256 * 16 * 16 * 2 + 512,  # fp16 blocks
+    # backward to the input: dy in, dx out, the CSR of F^T (row_ptr, col_idx, bf16 values)
+    "qwha_bwd_dx_2048x4096_nnz262144": 2 * 2048 * 4096 * 2 + 4097 * 4 + 262144 * 4 + 262144 * 2,
+    # gradient of the values: x and dy in, F's row_ptr and col_idx, fp32 dc out
+    "qwha_bwd_dc_2048x4096_nnz262144": 2 * 2048 * 4096 * 2 + 4097 * 4 + 262144 * 4 + 262144 * 4,
     "rht_int2_g64_28672x8192": 28672 * 8192 * 2 + 1024 + 28672 * 2048 + 28672 * 128 * 2,
     "rht_int2_g64_28672x8192_inverse": 28672 * 8192 * 2 + 1024 + 28672 * 2048 + 28672 * 128 * 2,
 }
@@ -46,6 +50,7 @@ ROWS = {
     "fwht_f32_256x4096": 256, "rht_int4_g128_4096x4096": 4096,
     "rht_int4_g128_4096x4096_inverse": 4096, "qwha_2048x4096_nnz262144": 2048,
     "harp_8192x4096_r16x3": 8192, "rht_int2_g64_28672x8192": 28672,
+    "qwha_bwd_dx_2048x4096_nnz262144": 2048, "qwha_bwd_dc_2048x4096_nnz262144": 2048,
     "rht_int2_g64_28672x8192_inverse": 28672,
 }
 MAIN = "rht_int4_g128_4096x4096"
@@ -176,7 +181,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workloads", default="all",
-                    help="all | main | comma list of fwht, qwha, harp, int2 (the main workload always runs)")
+                    help="all | main | comma list of fwht, qwha, qwha_bwd, harp, int2 "
+                         "(the main workload always runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (PMC calibration)")
@@ -206,7 +212,7 @@ def main():
         del a, b
         log("[bench] copy probe: 3 x 256 MiB device copy done")
 
-    sel = {"all": {"main", "fwht", "qwha", "harp", "int2"}, "main": {"main"}}.get(
+    sel = {"all": {"main", "fwht", "qwha", "qwha_bwd", "harp", "int2"}, "main": {"main"}}.get(
         args.workloads, set(args.workloads.split(",")))
     sel.add("main")  # `value` is always quoted on the main workload
     cfg_main = synth.rht_int4_g128()
@@ -223,6 +229,10 @@ def main():
     for fn, nm in (("qwha", "qwha_2048x4096_nnz262144"), ("harp", "harp_8192x4096_r16x3")):
         if fn in sel:
             res[nm] = bench_other(torch, W, mask_dev, synth, fn, nm, K, Wm)
+            log(f"[bench] {nm}: {res[nm]}")
+    if "qwha_bwd" in sel:
+        res.update(bench_qwha_bwd(torch, W, synth, K, Wm))
+        for nm in ("qwha_bwd_dx_2048x4096_nnz262144", "qwha_bwd_dc_2048x4096_nnz262144"):
             log(f"[bench] {nm}: {res[nm]}")
     if "int2" in sel:
         cfg5 = synth.rht_int2_g64()
@@ -258,6 +268,40 @@ def main():
         log("[bench] timing the CPU oracle on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline(cfg_main)
     print(json.dumps(line), flush=True)
+
+
+def bench_qwha_bwd(torch, W, synth, K, Wm):
+    """The adapter's backward at the QWHA workload: dx = (dy F) Hn (value
+    permutation into F^T's order + the transposed gather and transform) and
+    dc on F's support, timed separately."""
+    d = synth.qwha_backward()
+    rp = torch.from_numpy(d["row_ptr"]).to("cuda:0")
+    ci = torch.from_numpy(d["col_idx"]).to("cuda:0")
+    t_rp, t_ci, t_pm = W.qwha_csr_transpose(d["row_ptr"], d["col_idx"], 4096)
+    t_rp, t_ci, t_pm = (torch.from_numpy(a).to("cuda:0") for a in (t_rp, t_ci, t_pm))
+    v = d["vals"].to("cuda:0")
+    t_v = torch.empty_like(v)
+    dys = copies(torch, d["dy"].to("cuda:0"))
+    xs = copies(torch, d["x"].to("cuda:0"))
+    dxs = [torch.empty_like(x) for x in xs]
+    dcs = [torch.empty(ci.numel(), dtype=torch.float32, device="cuda:0") for _ in xs]
+    ws = torch.empty(W.qwha_grad_values_workspace_bytes(2048, 4096, ci.numel()), dtype=torch.uint8,
+                     device="cuda:0")
+
+    def dx_step(i):
+        W.qwha_permute_values(v, t_pm, out=t_v)
+        W.qwha_adapter_backward_input(dys[i % len(dys)], t_rp, t_ci, t_v, 4096, out=dxs[i % len(dxs)])
+
+    def dc_step(i):
+        W.qwha_adapter_grad_values(xs[i % len(xs)], dys[i % len(dys)], rp, ci, out=dcs[i % len(dcs)],
+                                   workspace=ws)
+
+    r = {}
+    for nm, fn in (("qwha_bwd_dx_2048x4096_nnz262144", dx_step), ("qwha_bwd_dc_2048x4096_nnz262144", dc_step)):
+        r[nm] = result(nm, Timed(torch, fn, K, Wm).run(), K)
+    del dys, xs, dxs, dcs, ws
+    torch.cuda.empty_cache()
+    return r
 
 
 def bench_other(torch, W, mask_dev, synth, fn, name, K, Wm):

@@ -7,15 +7,17 @@
 // a dense-dense product sampled on the support of F.
 //
 // Three launches on the caller's stream:
-//   1. Z = x Hn in fp32 (the FWHT engine, bf16 -> f32) into the workspace;
+//   1. k_qwha_z: Z = x Hn in fp32 (the FWHT engine) into the workspace,
+//      tile-interleaved (four tokens per 16-byte column);
 //   2. k_qwha_dc: the entries are cut into slabs of at most 16384 (16 per
-//      lane of a 1024-lane block) and the tokens into slabs of whole
-//      4-token tiles; block (entry slab, token slab) keeps its entries'
+//      lane of a 1024-lane block, placed so that LDS reads rarely collide,
+//      see the slot set-up) and the tokens into slabs of whole 4-token
+//      tiles; block (entry slab, token slab) keeps its entries'
 //      (column, row) pairs and fp32 sums in registers and, per tile, stages
 //      the tile's Z rows as Z[k][4 tokens] (one 16-byte column) and the dy
 //      values of the slab's rows as dy[o][4 tokens] in LDS, then adds four
-//      products per entry; the next tile's global loads are in flight while
-//      the current tile is summed.  Per-token-slab partial sums go to the
+//      products per entry; the global loads of the next two tiles are in
+//      flight while the current tile is summed.  Per-token-slab partial sums go to the
 //      workspace (or straight to dc when there is one token slab);
 //   3. k_qwha_dc_reduce: dc[e] = sum of the partials in slab order.
 // Every sum runs in a fixed order, so the result is deterministic.
@@ -28,9 +30,6 @@
 
 namespace whtq {
 
-hipError_t launch_wht(int logn, int din, int dout, const void* x, void* y, int64_t rows, int64_t ldx,
-                      int64_t ldy, const uint32_t* sbits, int sign_mode, float scale, hipStream_t s);
-
 namespace qg {
 constexpr int N = 4096;        // d_in
 constexpr int THREADS = 1024;
@@ -38,13 +37,73 @@ constexpr int EPL = 16;        // entries per lane
 constexpr int EPB = THREADS * EPL;
 constexpr int TQ = 4;          // tokens per tile (one 16-byte fp32 column)
 constexpr int XCDS = 8;
-constexpr int LDS_Z = 0;                    // Z[k][4] fp32, 64 KB
+constexpr int GROUPS = THREADS / 16;       // 16-lane groups, 16 * EPL entries each
+constexpr int GE = 16 * EPL;                // entries per group
+constexpr int NRES = 17;                    // column residues mod 16, plus "past the slab"
+constexpr int LDS_Z = 0;                    // Z[k][4] fp32, 64 KB; set-up counters before the tiles
 constexpr int LDS_D = N * 16;               // dy[o - o_lo][4] fp32, up to 64 KB; row_ptr at set-up
-constexpr int LDS_LIM = LDS_D + N * 16;     // first and last row of the slab
-constexpr int LDS_BYTES = LDS_LIM + 16;
+constexpr int LDS_T = LDS_D + N * 16;       // slot table: entry offsets within the slab (u16)
+constexpr int LDS_BYTES = LDS_T + EPB * 2;  // 160 KB
+// set-up only, in the Z region: residue counters and bases [GROUPS][NRES]
+// u32, the slab limits, each entry's column (u16); in the dy region after
+// the row_ptr copy: each entry's row (u16)
+constexpr int LDS_CNT = 0;
+constexpr int LDS_BASE = LDS_CNT + GROUPS * NRES * 4;
+constexpr int LDS_LIM = LDS_BASE + GROUPS * NRES * 4;
+constexpr int LDS_COL = 16384;
+constexpr int LDS_ROW = LDS_D + 16400;
+static_assert(LDS_LIM + 8 <= LDS_COL && LDS_COL + 2 * EPB <= LDS_D, "set-up tables in the Z region");
+static_assert(LDS_ROW + 2 * EPB <= LDS_T && LDS_D + 4 * (N + 1) <= LDS_ROW, "row table after row_ptr");
 constexpr int ZPT = N / THREADS;            // Z columns staged per thread (4)
-constexpr int DPT = N / THREADS;            // dy rows staged per thread, at most (4)
 }  // namespace qg
+
+// Z = x Hn in fp32, four tokens per block, written tile-interleaved:
+// zi[quad][k] = (Z[4 quad][k], .., Z[4 quad + 3][k]) as one 16-byte column,
+// zeros past the last token, so that a tile of k_qwha_dc is 64 KB of
+// contiguous columns that go to LDS as they are loaded.  Each wave
+// transforms one token row with the FWHT engine; the rows meet in LDS
+// (padded by 4 floats per 64: conflict-free both ways) and leave as columns.
+namespace qz {
+constexpr int ROW = 4096 + 256;  // padded row, floats
+constexpr int LDS_BYTES = 4 * ROW * 4;
+}  // namespace qz
+
+__global__ __launch_bounds__(256) void k_qwha_z(const uint16_t* __restrict__ x, int64_t tokens, int64_t ldx,
+                                                float* __restrict__ zi) {
+  using G = Geo<12>;
+  static_assert(4 * G::LDS_ROW <= 4 * qz::ROW, "transpose scratch fits in the row buffer");
+  extern __shared__ __align__(16) uint8_t smem[];
+  float* lds = reinterpret_cast<float*>(smem);
+  const int tid = threadIdx.x, w = tid >> 6, t = tid & 63;
+  const int64_t quad = blockIdx.x, tok = quad * 4 + w;
+  float v[64];
+  {
+    const uint32_t nomask[4] = {0u, 0u, 0u, 0u};
+    const uint16_t* xr = x + (tok < tokens ? tok : tokens - 1) * ldx;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      Raw8 raw;
+      fetch8<DT_BF16>(xr, G::idxA(t, c * 8), raw);
+      widen8<DT_BF16, false>(raw, v + 8 * c, nomask, 0u);
+    }
+    stages_A<12, false>(v, t);
+    transpose_AB<12, 64>(lds + w * G::LDS_ROW, v, t);
+    stages_B<12, 2>(v, t);
+  }
+  const float cs = tok < tokens ? (rho_B<12>(t) ? -1.0f / 64.0f : 1.0f / 64.0f) : 0.0f;
+  __syncthreads();  // every wave's transpose scratch is free
+  float* row = lds + w * qz::ROW + t * 68;
+#pragma unroll
+  for (int q = 0; q < 16; ++q)
+    *reinterpret_cast<f32x4*>(row + 4 * q) = f32x4{v[4 * q] * cs, v[4 * q + 1] * cs, v[4 * q + 2] * cs, v[4 * q + 3] * cs};
+  __syncthreads();
+  f32x4* dst = reinterpret_cast<f32x4*>(zi) + quad * 4096;
+#pragma unroll 4
+  for (int m = 0; m < 16; ++m) {
+    const int k = tid + 256 * m, ph = k + ((k >> 6) << 2);
+    dst[k] = f32x4{lds[ph], lds[qz::ROW + ph], lds[2 * qz::ROW + ph], lds[3 * qz::ROW + ph]};
+  }
+}
 
 struct DcGrid {
   int r_slabs, t_slabs, span, quads_per_slab;
@@ -62,6 +121,7 @@ static DcGrid dc_grid(int64_t tokens, int64_t nnz) {
   int64_t ts = std::max<int64_t>(1, (cus + g.r_slabs - 1) / g.r_slabs);
   ts = std::min<int64_t>(ts, quads);
   g.quads_per_slab = (int)((quads + ts - 1) / ts);
+  g.quads_per_slab += g.quads_per_slab & 1;  // the kernel runs tiles in pairs
   g.t_slabs = (int)((quads + g.quads_per_slab - 1) / g.quads_per_slab);
   return g;
 }
@@ -84,19 +144,25 @@ __global__ __launch_bounds__(qg::THREADS) void k_qwha_dc(
   f32x4* zq = reinterpret_cast<f32x4*>(smem + qg::LDS_Z);
   f32x4* dq = reinterpret_cast<f32x4*>(smem + qg::LDS_D);
   int* rp = reinterpret_cast<int*>(smem + qg::LDS_D);
+  uint16_t* slot = reinterpret_cast<uint16_t*>(smem + qg::LDS_T);
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(smem + qg::LDS_CNT);
+  uint32_t* bas = reinterpret_cast<uint32_t*>(smem + qg::LDS_BASE);
   int* lim = reinterpret_cast<int*>(smem + qg::LDS_LIM);
-  const int tid = threadIdx.x;
+  uint16_t* coltab = reinterpret_cast<uint16_t*>(smem + qg::LDS_COL);
+  uint16_t* rowtab = reinterpret_cast<uint16_t*>(smem + qg::LDS_ROW);
+  const int tid = threadIdx.x, grp = tid >> 4, gl = tid & 15;
   int r, p;
   dc_block(blockIdx.x, r_slabs, t_slabs, r, p);
   if (p >= t_slabs) return;  // grid rounded up to whole XCD rounds (uniform per block)
   const int e0 = r * span, e1 = min(nnz, e0 + span);
 
-  // ---- set-up: row_ptr in LDS, each entry's row by binary search
+  // ---- set-up: row_ptr in LDS; each entry's row and column; slot assignment
   for (int i = tid; i <= d_out; i += qg::THREADS) rp[i] = row_ptr[i];
+  for (int i = tid; i < qg::GROUPS * qg::NRES; i += qg::THREADS) cnt[i] = 0;
   __syncthreads();
-  // largest o in [0, d_out) with rp[o] <= e (the row holding entry e)
-  auto row_of = [&](int e) {
-    int pos = 0;
+  // largest o in [lo, d_out) with rp[o] <= e, for rp[lo] <= e (the row holding entry e)
+  auto row_from = [&](int lo, int e) {
+    int pos = lo;
     for (int step = 1 << 12; step > 0; step >>= 1) {
       const int c = pos + step;
       if (c < d_out && rp[c] <= e) pos = c;
@@ -104,105 +170,157 @@ __global__ __launch_bounds__(qg::THREADS) void k_qwha_dc(
     return pos;
   };
   if (tid == 0) {
-    lim[0] = row_of(e0);
-    lim[1] = row_of(e1 - 1);
+    lim[0] = row_from(0, e0);
+    lim[1] = row_from(0, e1 - 1);
+  }
+  // Slots.  16-lane group g owns the slab's entries [256 g, 256 g + 256); lane
+  // l sums, in its i-th slot, the entry at position 16 l + i of those entries
+  // ordered by column mod 16.  With about 16 entries per residue the 16 lanes
+  // of one slot then read Z columns in distinct 16-byte LDS bank slots
+  // (16-byte reads are served 16 lanes at a time over 64 banks), instead of
+  // colliding about 3x as random columns do; the entries of a slot stay
+  // within 256 consecutive entries, i.e. a few consecutive rows, so their dy
+  // reads are broadcasts or distinct banks too.  Which lane sums an entry
+  // does not change its value (the sum runs over tokens in order), so the
+  // ranks within a residue may come in any order.
+  //
+  // Lane l first takes the 16 consecutive entries 256 g + 16 l + j: one
+  // binary search finds the row of the first, the rest follow it forward (a
+  // new search only where an entry lies past the next row's start), and the
+  // rows and columns go to LDS tables indexed by the entry's offset.
+  {
+    uint32_t res[qg::EPL], rank[qg::EPL];
+    const int eb = e0 + qg::GE * grp + qg::EPL * gl;  // this lane's first entry
+    int o = row_from(0, min(eb, e1 - 1));
+#pragma unroll
+    for (int j = 0; j < qg::EPL; ++j) {
+      const int e = eb + j;
+      const bool ok = e < e1;
+      const int c = ok ? col_idx[e] & (qg::N - 1) : 0;
+      if (ok && o + 1 < d_out && rp[o + 1] <= e) o = row_from(o + 1, e);
+      res[j] = ok ? (uint32_t)c & 15u : 16u;
+      coltab[qg::GE * grp + qg::EPL * gl + j] = (uint16_t)c;
+      rowtab[qg::GE * grp + qg::EPL * gl + j] = (uint16_t)o;
+    }
+#pragma unroll
+    for (int j = 0; j < qg::EPL; ++j) rank[j] = atomicAdd(&cnt[grp * qg::NRES + res[j]], 1u);
+    __syncthreads();
+    if (gl == 0) {
+      uint32_t run = 0;
+      for (int b = 0; b < qg::NRES; ++b) {
+        bas[grp * qg::NRES + b] = run;
+        run += cnt[grp * qg::NRES + b];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < qg::EPL; ++j)
+      slot[qg::GE * grp + bas[grp * qg::NRES + res[j]] + rank[j]] = (uint16_t)(qg::GE * grp + qg::EPL * gl + j);
   }
   __syncthreads();
   const int o_lo = lim[0], nrows = lim[1] - lim[0] + 1;  // nrows <= d_out <= 4096
   uint32_t ent[qg::EPL];  // column | (row - o_lo) << 16
   float acc[qg::EPL];
-  {
-    int col[qg::EPL];
 #pragma unroll
-    for (int i = 0; i < qg::EPL; ++i) {
-      const int e = e0 + tid + qg::THREADS * i;
-      col[i] = e < e1 ? col_idx[e] & (qg::N - 1) : 0;
-    }
-    int pos[qg::EPL];
-#pragma unroll
-    for (int i = 0; i < qg::EPL; ++i) pos[i] = 0;
-    // the sixteen searches interleaved, one level at a time
-    for (int step = 1 << 12; step > 0; step >>= 1) {
-#pragma unroll
-      for (int i = 0; i < qg::EPL; ++i) {
-        const int e = min(e0 + tid + qg::THREADS * i, e1 - 1);
-        const int c = pos[i] + step;
-        if (c < d_out && rp[c] <= e) pos[i] = c;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < qg::EPL; ++i) {
-      const int o = min(max(pos[i] - o_lo, 0), nrows - 1);
-      ent[i] = (uint32_t)col[i] | ((uint32_t)o << 16);
-      acc[i] = 0.f;
-    }
+  for (int i = 0; i < qg::EPL; ++i) {
+    const int off = slot[qg::GE * grp + qg::EPL * gl + i];
+    const int o = min(max((int)rowtab[off] - o_lo, 0), nrows - 1);
+    ent[i] = (uint32_t)coltab[off] | ((uint32_t)o << 16);
+    acc[i] = 0.f;
   }
 
   // ---- tiles of 4 tokens
-  const int64_t quads = (tokens + qg::TQ - 1) / qg::TQ;
-  const int64_t q_beg = (int64_t)p * quads_per_slab;
-  const int64_t q_end = min<int64_t>(quads, q_beg + quads_per_slab);
-  // staged values of one tile: Z columns tid + 1024 m, dy rows o_lo + tid + 1024 m
-  float zr[qg::TQ][qg::ZPT];
-  u16x2 dr[qg::TQ / 2][qg::DPT];  // bf16 pairs of tokens (2 i, 2 i + 1)
-  auto fetch = [&](int64_t q) {
+  const int q_beg = p * quads_per_slab;  // quads_per_slab is even
+  const int q_end = q_beg + quads_per_slab;
+  const int last_tok = (int)tokens - 1;
+  // Staged values of a tile, fetched two tiles ahead into one of two register
+  // sets: Z columns tid + 1024 m and dy row o_lo + min(tid, nrows - 1), each
+  // kept as loaded (a 32-bit register per value, every load unconditional) so
+  // that nothing waits for them before they are staged.  Rows o_lo + tid +
+  // 1024 m, m >= 1 (only slabs of very short rows have them) are read when
+  // the tile is staged.
+  struct Pre {
+    f32x4 z[qg::ZPT];
+    uint32_t d[qg::TQ];
+  };
+  const int last_quad = (last_tok) / qg::TQ;
+  // (lane offsets are unsigned 32-bit and row bases block-uniform, so each
+  // load is an SGPR base plus one shared VGPR offset)
+  const uint32_t drow = (uint32_t)(o_lo + min(tid, nrows - 1));
+  auto fetch = [&](int q, Pre& b) {
+    // past the end: re-read the last tile (its dy is zeroed when staged)
+    const f32x4* zt = reinterpret_cast<const f32x4*>(z) + (int64_t)min(q, last_quad) * qg::N;
+#pragma unroll
+    for (int m = 0; m < qg::ZPT; ++m) b.z[m] = zt[(uint32_t)(tid + qg::THREADS * m)];
 #pragma unroll
     for (int j = 0; j < qg::TQ; ++j) {
-      const int64_t t = min<int64_t>(q * qg::TQ + j, tokens - 1);  // past the end: re-read the last token
-      const float* zrow = z + t * qg::N;
-      const uint16_t* drow = dy + t * lddy + o_lo;
-#pragma unroll
-      for (int m = 0; m < qg::ZPT; ++m) zr[j][m] = zrow[tid + qg::THREADS * m];
-#pragma unroll
-      for (int m = 0; m < qg::DPT; ++m) {
-        const int o = tid + qg::THREADS * m;
-        const uint16_t d = o < nrows ? drow[o] : (uint16_t)0;
-        if (j & 1) dr[j >> 1][m].y = d;
-        else dr[j >> 1][m].x = d;
-      }
+      const int t = min(q * qg::TQ + j, last_tok);
+      b.d[j] = dy[(int64_t)t * lddy + drow];
     }
   };
-  auto stage = [&](int64_t q) {
+  auto stage = [&](int q, const Pre& b) {
 #pragma unroll
-    for (int m = 0; m < qg::ZPT; ++m)
-      zq[tid + qg::THREADS * m] = f32x4{zr[0][m], zr[1][m], zr[2][m], zr[3][m]};
+    for (int m = 0; m < qg::ZPT; ++m) zq[tid + qg::THREADS * m] = b.z[m];
     // tokens past the end contribute nothing: their dy is zero
-    const int64_t t0 = q * qg::TQ;
+    const int t0 = q * qg::TQ;
+    if (tid < nrows) {
+      f32x4 d;
 #pragma unroll
-    for (int m = 0; m < qg::DPT; ++m) {
-      const int o = tid + qg::THREADS * m;
-      if (o < nrows) {
-        f32x4 d;
+      for (int j = 0; j < qg::TQ; ++j) d[j] = t0 + j <= last_tok ? as_f(b.d[j] << 16) : 0.f;
+      dq[tid] = d;
+    }
+    for (int o = tid + qg::THREADS; o < nrows; o += qg::THREADS) {
+      f32x4 d;
 #pragma unroll
-        for (int j = 0; j < qg::TQ; ++j)
-          d[j] = t0 + j < tokens ? as_f((uint32_t)((j & 1) ? dr[j >> 1][m].y : dr[j >> 1][m].x) << 16) : 0.f;
-        dq[o] = d;
+      for (int j = 0; j < qg::TQ; ++j)
+        d[j] = t0 + j <= last_tok ? as_f((uint32_t)dy[(int64_t)(t0 + j) * lddy + o_lo + o] << 16) : 0.f;
+      dq[o] = d;
+    }
+  };
+  // the sums, four entries (eight 16-byte LDS reads in flight) at a time
+  auto sum_tile = [&]() {
+#pragma unroll
+    for (int i0 = 0; i0 < qg::EPL; i0 += 4) {
+      f32x4 zc[4], dc[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        zc[u] = zq[ent[i0 + u] & 0xffffu];
+        dc[u] = dq[ent[i0 + u] >> 16];
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the 8 LDS reads first
+      __builtin_amdgcn_sched_group_barrier(0x002, 16, 0); // then the 16 FMAs
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float a = acc[i0 + u];
+        a = fmaf(dc[u][0], zc[u][0], a);
+        a = fmaf(dc[u][1], zc[u][1], a);
+        a = fmaf(dc[u][2], zc[u][2], a);
+        a = fmaf(dc[u][3], zc[u][3], a);
+        acc[i0 + u] = a;
       }
     }
   };
   __syncthreads();  // row_ptr copy no longer needed: its space becomes the dy tile
-  if (q_beg < q_end) fetch(q_beg);
-  for (int64_t q = q_beg; q < q_end; ++q) {
-    stage(q);
+  // Every block runs the same even number of tiles and every fetch is
+  // unconditional (tiles past the last token have zero dy and re-read valid
+  // rows), so the compiler's load counters stay exact: staging a tile waits
+  // only for its own loads, not for the set fetched after it.
+  Pre A;
+  fetch(q_beg, A);
+  for (int q = q_beg; q < q_end; ++q) {
+    stage(q, A);
     __syncthreads();
-    if (q + 1 < q_end) fetch(q + 1);  // in flight while this tile is summed
-#pragma unroll
-    for (int i = 0; i < qg::EPL; ++i) {
-      const f32x4 zc = zq[ent[i] & 0xffffu];
-      const f32x4 dc = dq[ent[i] >> 16];
-      float a = acc[i];
-      a = fmaf(dc[0], zc[0], a);
-      a = fmaf(dc[1], zc[1], a);
-      a = fmaf(dc[2], zc[2], a);
-      a = fmaf(dc[3], zc[3], a);
-      acc[i] = a;
-    }
+    fetch(q + 1, A);  // in flight while this tile is summed
+    // keep the loads ahead of the sums (the scheduler would otherwise sink
+    // them into the sum and wait for them before the next barrier)
+    __builtin_amdgcn_sched_barrier(0);
+    sum_tile();
     __syncthreads();
   }
   float* dst = out + (int64_t)p * nnz;
 #pragma unroll
   for (int i = 0; i < qg::EPL; ++i) {
-    const int e = e0 + tid + qg::THREADS * i;
+    const int e = e0 + slot[qg::GE * grp + qg::EPL * gl + i];
     if (e < e1) dst[e] = acc[i];
   }
 }
@@ -227,7 +345,7 @@ __global__ __launch_bounds__(256) void k_permute(const T* __restrict__ vals, con
 
 int64_t qwha_dc_workspace_bytes(int64_t tokens, int64_t nnz) {
   const DcGrid g = dc_grid(tokens, nnz);
-  const int64_t zb = tokens * qg::N * 4;
+  const int64_t zb = (tokens + 3) / 4 * qg::N * 16;  // tile-interleaved Z
   const int64_t pb = g.t_slabs > 1 ? (int64_t)g.t_slabs * nnz * 4 : 0;
   return ((zb + 255) & ~int64_t(255)) + pb;
 }
@@ -237,9 +355,14 @@ hipError_t launch_qwha_dc(const void* x, int64_t ldx, const void* dy, int64_t ld
                           float* dc, void* workspace, hipStream_t s) {
   const DcGrid g = dc_grid(tokens, nnz);
   float* z = reinterpret_cast<float*>(workspace);
-  const int64_t zb = ((tokens * qg::N * 4 + 255) & ~int64_t(255));
+  const int64_t zb = ((tokens + 3) / 4 * qg::N * 16 + 255) & ~int64_t(255);
   float* part = g.t_slabs > 1 ? reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) + zb) : dc;
-  hipError_t e = launch_wht(12, DT_BF16, DT_F32, x, z, tokens, ldx, qg::N, nullptr, 0, 1.0f / 64.0f, s);
+  static const bool zattr = hipFuncSetAttribute((const void*)k_qwha_z, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                qz::LDS_BYTES) == hipSuccess;
+  (void)zattr;
+  hipLaunchKernelGGL(k_qwha_z, dim3((unsigned)((tokens + 3) / 4)), dim3(256), qz::LDS_BYTES, s,
+                     (const uint16_t*)x, tokens, ldx, z);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   static const bool attr = hipFuncSetAttribute((const void*)k_qwha_dc, hipFuncAttributeMaxDynamicSharedMemorySize,
                                                qg::LDS_BYTES) == hipSuccess;
