@@ -15,8 +15,8 @@
 //      tiles; block (entry slab, token slab) keeps its entries'
 //      (column, row) pairs and fp32 sums in registers and, per tile, stages
 //      the tile's Z rows as Z[k][4 tokens] (one 16-byte column) and the dy
-//      values of the slab's rows as dy[o][4 tokens] in LDS, then adds four
-//      products per entry; the global loads of the next two tiles are in
+//      values of the slab's rows as dy[o][4 tokens] (bf16) in LDS, then adds
+//      four products per entry; the global loads of the next two tiles are in
 //      flight while the current tile is summed.  Per-token-slab partial sums go to the
 //      workspace (or straight to dc when there is one token slab);
 //   3. k_qwha_dc_reduce: dc[e] = sum of the partials in slab order.
@@ -41,7 +41,7 @@ constexpr int GROUPS = THREADS / 16;       // 16-lane groups, 16 * EPL entries e
 constexpr int GE = 16 * EPL;                // entries per group
 constexpr int NRES = 17;                    // column residues mod 16, plus "past the slab"
 constexpr int LDS_Z = 0;                    // Z[k][4] fp32, 64 KB; set-up counters before the tiles
-constexpr int LDS_D = N * 16;               // dy[o - o_lo][4] fp32, up to 64 KB; row_ptr at set-up
+constexpr int LDS_D = N * 16;               // dy[o - o_lo][4] bf16, up to 32 KB; set-up tables before
 constexpr int LDS_T = LDS_D + N * 16;       // slot table: entry offsets within the slab (u16)
 constexpr int LDS_BYTES = LDS_T + EPB * 2;  // 160 KB
 // set-up only, in the Z region: residue counters and bases [GROUPS][NRES]
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(qg::THREADS) void k_qwha_dc(
     int r_slabs, int t_slabs, int quads_per_slab, float* __restrict__ out) {
   extern __shared__ __align__(16) uint8_t smem[];
   f32x4* zq = reinterpret_cast<f32x4*>(smem + qg::LDS_Z);
-  f32x4* dq = reinterpret_cast<f32x4*>(smem + qg::LDS_D);
+  u32x2* dq = reinterpret_cast<u32x2*>(smem + qg::LDS_D);
   int* rp = reinterpret_cast<int*>(smem + qg::LDS_D);
   uint16_t* slot = reinterpret_cast<uint16_t*>(smem + qg::LDS_T);
   uint32_t* cnt = reinterpret_cast<uint32_t*>(smem + qg::LDS_CNT);
@@ -263,39 +263,42 @@ __global__ __launch_bounds__(qg::THREADS) void k_qwha_dc(
     for (int m = 0; m < qg::ZPT; ++m) zq[tid + qg::THREADS * m] = b.z[m];
     // tokens past the end contribute nothing: their dy is zero
     const int t0 = q * qg::TQ;
+    // dy stays bf16 in LDS (8 bytes per row and tile, widened at the sum):
+    // the sums are bound by LDS-to-register bytes, and this cuts them by a
+    // quarter
     if (tid < nrows) {
-      f32x4 d;
+      uint32_t h[qg::TQ];
 #pragma unroll
-      for (int j = 0; j < qg::TQ; ++j) d[j] = t0 + j <= last_tok ? as_f(b.d[j] << 16) : 0.f;
-      dq[tid] = d;
+      for (int j = 0; j < qg::TQ; ++j) h[j] = t0 + j <= last_tok ? b.d[j] : 0u;
+      dq[tid] = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
     }
     for (int o = tid + qg::THREADS; o < nrows; o += qg::THREADS) {
-      f32x4 d;
+      uint32_t h[qg::TQ];
 #pragma unroll
-      for (int j = 0; j < qg::TQ; ++j)
-        d[j] = t0 + j <= last_tok ? as_f((uint32_t)dy[(int64_t)(t0 + j) * lddy + o_lo + o] << 16) : 0.f;
-      dq[o] = d;
+      for (int j = 0; j < qg::TQ; ++j) h[j] = t0 + j <= last_tok ? (uint32_t)dy[(int64_t)(t0 + j) * lddy + o_lo + o] : 0u;
+      dq[o] = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
     }
   };
   // the sums, four entries (eight 16-byte LDS reads in flight) at a time
   auto sum_tile = [&]() {
 #pragma unroll
     for (int i0 = 0; i0 < qg::EPL; i0 += 4) {
-      f32x4 zc[4], dc[4];
+      f32x4 zc[4];
+      u32x2 dh[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         zc[u] = zq[ent[i0 + u] & 0xffffu];
-        dc[u] = dq[ent[i0 + u] >> 16];
+        dh[u] = dq[ent[i0 + u] >> 16];
       }
       __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the 8 LDS reads first
-      __builtin_amdgcn_sched_group_barrier(0x002, 16, 0); // then the 16 FMAs
+      __builtin_amdgcn_sched_group_barrier(0x002, 32, 0); // then widening and FMAs
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         float a = acc[i0 + u];
-        a = fmaf(dc[u][0], zc[u][0], a);
-        a = fmaf(dc[u][1], zc[u][1], a);
-        a = fmaf(dc[u][2], zc[u][2], a);
-        a = fmaf(dc[u][3], zc[u][3], a);
+        a = fmaf(bf16lo(dh[u].x), zc[u][0], a);
+        a = fmaf(bf16hi(dh[u].x), zc[u][1], a);
+        a = fmaf(bf16lo(dh[u].y), zc[u][2], a);
+        a = fmaf(bf16hi(dh[u].y), zc[u][3], a);
         acc[i0 + u] = a;
       }
     }
