@@ -123,8 +123,12 @@ def hp(lib, x=P, y=ctypes.c_void_p(0x20000), dt=1, tokens=8, d=4096, ldx=4096, l
 def test_harp_validation(lib):
     assert hp(lib, rad=(16, 16, 8)) == EINVAL              # product != d
     assert hp(lib, rad=(16, 16, 16, 1)) == EINVAL          # radix < 2
-    assert hp(lib, d=5120, ldx=5120, ldy=5120, rad=(8, 8, 8, 5, 2)) == EUNSUP  # valid schedule, no kernel
-    assert hp(lib, rad=(64, 64)) == EUNSUP
+    # the Sylvester preconditioning needs a power-of-two d
+    assert hp(lib, d=5120, ldx=5120, ldy=5120, rad=(8, 8, 8, 5, 2)) == EINVAL
+    assert hp(lib, rad=(64, 64)) == EUNSUP                 # radix above 16
+    assert hp(lib, d=17 * 4, ldx=72, ldy=72, rad=(17, 4), pre=0) == EUNSUP
+    assert hp(lib, d=16384, ldx=16384, ldy=16384, rad=(16, 16, 64)) == EUNSUP  # d above 8192
+    assert hp(lib, d=5120, ldx=5120, ldy=5120, rad=(8, 8, 8, 5, 2), pre=0, tokens=0) == OK
     assert hp(lib, y=P) == EINVAL                          # in place not allowed
     assert hp(lib, pre=3) == EINVAL
     assert hp(lib, blocks=NULL) == EINVAL

@@ -33,6 +33,9 @@ hipError_t launch_qwha_dc(const void* x, int64_t ldx, const void* dy, int64_t ld
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 hipError_t launch_permute(const void* vals, int val_dt, const int32_t* perm, int64_t nnz, void* out,
                           hipStream_t s);
+hipError_t launch_harp_gen(const void* x, void* y, int64_t tokens, int d, int64_t ldx, int64_t ldy,
+                           const uint32_t* sbits, int precondition, const int32_t* radices, int n_stages,
+                           const void* blocks, int bdt, hipStream_t s);
 hipError_t launch_harp(const void* x, void* y, int dt, int64_t tokens, int64_t ldx, int64_t ldy,
                        const uint32_t* sbits, int precondition, const void* blocks, int bdt, hipStream_t s);
 
@@ -323,8 +326,14 @@ whtq_status harp_rotate(const void* x, void* y, whtq_dtype dtype, int64_t tokens
   if (prod != d) return WHTQ_EINVAL;
   if (tokens > 0 && (!x || !y)) return WHTQ_EINVAL;
   if (tokens > 0 && x == y) return WHTQ_EINVAL;
-  if (d != 4096 || n_stages != 3 || radices[0] != 16 || radices[1] != 16 || radices[2] != 16)
-    return WHTQ_EUNSUPPORTED;
+  // the preconditioning is the Sylvester RHT, which exists for powers of two only
+  if (precondition && ilog2_pow2(d) < 0) return WHTQ_EINVAL;
+  const bool r16 = d == 4096 && n_stages == 3 && radices[0] == 16 && radices[1] == 16 && radices[2] == 16;
+  if (!r16) {
+    if (d > 8192 || n_stages > 16) return WHTQ_EUNSUPPORTED;
+    for (int t = 0; t < n_stages; ++t)
+      if (radices[t] > 16) return WHTQ_EUNSUPPORTED;
+  }
   if (dtype != WHTQ_BF16 || blocks_dtype == WHTQ_BF16) return WHTQ_EUNSUPPORTED;
   const int esz = dt_bytes(dtype);
   if (!rows_aligned(x, d, ldx, esz) || !rows_aligned(y, d, ldy, esz) || !aligned16(blocks)) return WHTQ_EALIGN;
@@ -332,8 +341,11 @@ whtq_status harp_rotate(const void* x, void* y, whtq_dtype dtype, int64_t tokens
   if (tokens == 0) return WHTQ_OK;
   whtq_status st = need_device();
   if (st != WHTQ_OK) return st;
-  return hip_status(launch_harp(x, y, dtype, tokens, ldx, ldy, sign_bits, precondition, blocks, blocks_dtype,
-                                (hipStream_t)stream));
+  if (r16)
+    return hip_status(launch_harp(x, y, dtype, tokens, ldx, ldy, sign_bits, precondition, blocks, blocks_dtype,
+                                  (hipStream_t)stream));
+  return hip_status(launch_harp_gen(x, y, tokens, (int)d, ldx, ldy, sign_bits, precondition, radices, n_stages,
+                                    blocks, blocks_dtype, (hipStream_t)stream));
 }
 
 }  // extern "C"
