@@ -5,8 +5,9 @@ Main workload (the one `value` is quoted on): RHT + INT4 round-to-nearest
 quantisation, bf16 weight matrix 4096 x 4096, group 128 along d_in, fp16
 scales, signed int4 codes -- one `rht_quantize_rtn` launch per step.  The
 other workloads (orthonormal FWHT 256 x 4096 fp32, the inverse of the INT4
-path, QWHA adapter forward and backward, HARP rotation, 28672 x 8192 RHT +
-INT2) are timed the same way and reported under "workloads".
+path, QWHA adapter forward and backward, HARP rotation with the radix-16
+schedule and with the mixed-radix 8*8*8*5*2 schedule at d = 5120, 28672 x
+8192 RHT + INT2) are timed the same way and reported under "workloads".
 
 Timing: each step processes a different copy of the input, rotating over
 copies totalling >= 1 GiB so that inputs come from HBM rather than the
@@ -43,6 +44,7 @@ ALGO_BYTES = {
     "qwha_bwd_dx_2048x4096_nnz262144": 2 * 2048 * 4096 * 2 + 4097 * 4 + 262144 * 4 + 262144 * 2,
     # gradient of the values: x and dy in, F's row_ptr and col_idx, fp32 dc out
     "qwha_bwd_dc_2048x4096_nnz262144": 2 * 2048 * 4096 * 2 + 4097 * 4 + 262144 * 4 + 262144 * 4,
+    "harp_8192x5120_r88852": 2 * 8192 * 5120 * 2 + 5120 * (8 + 8 + 8 + 5 + 2) * 2,  # fp16 blocks
     "rht_int2_g64_28672x8192": 28672 * 8192 * 2 + 1024 + 28672 * 2048 + 28672 * 128 * 2,
     "rht_int2_g64_28672x8192_inverse": 28672 * 8192 * 2 + 1024 + 28672 * 2048 + 28672 * 128 * 2,
 }
@@ -51,6 +53,7 @@ ROWS = {
     "rht_int4_g128_4096x4096_inverse": 4096, "qwha_2048x4096_nnz262144": 2048,
     "harp_8192x4096_r16x3": 8192, "rht_int2_g64_28672x8192": 28672,
     "qwha_bwd_dx_2048x4096_nnz262144": 2048, "qwha_bwd_dc_2048x4096_nnz262144": 2048,
+    "harp_8192x5120_r88852": 8192,
     "rht_int2_g64_28672x8192_inverse": 28672,
 }
 MAIN = "rht_int4_g128_4096x4096"
@@ -181,7 +184,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workloads", default="all",
-                    help="all | main | comma list of fwht, qwha, qwha_bwd, harp, int2 "
+                    help="all | main | comma list of fwht, qwha, qwha_bwd, harp, harp_gen, int2 "
                          "(the main workload always runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -212,7 +215,7 @@ def main():
         del a, b
         log("[bench] copy probe: 3 x 256 MiB device copy done")
 
-    sel = {"all": {"main", "fwht", "qwha", "qwha_bwd", "harp", "int2"}, "main": {"main"}}.get(
+    sel = {"all": {"main", "fwht", "qwha", "qwha_bwd", "harp", "harp_gen", "int2"}, "main": {"main"}}.get(
         args.workloads, set(args.workloads.split(",")))
     sel.add("main")  # `value` is always quoted on the main workload
     cfg_main = synth.rht_int4_g128()
@@ -226,7 +229,8 @@ def main():
         res["fwht_f32_256x4096"] = result("fwht_f32_256x4096", t.run(), K)
         log(f"[bench] fwht_f32_256x4096: {res['fwht_f32_256x4096']}")
         del xs, ys
-    for fn, nm in (("qwha", "qwha_2048x4096_nnz262144"), ("harp", "harp_8192x4096_r16x3")):
+    for fn, nm in (("qwha", "qwha_2048x4096_nnz262144"), ("harp", "harp_8192x4096_r16x3"),
+                   ("harp_gen", "harp_8192x5120_r88852")):
         if fn in sel:
             res[nm] = bench_other(torch, W, mask_dev, synth, fn, nm, K, Wm)
             log(f"[bench] {nm}: {res[nm]}")
@@ -315,6 +319,14 @@ def bench_other(torch, W, mask_dev, synth, fn, name, K, Wm):
         ys = [torch.empty((x0.shape[0], d["d_out"]), dtype=torch.bfloat16, device="cuda:0") for _ in xs]
         t = Timed(torch, lambda i: W.qwha_adapter_forward(xs[i % len(xs)], rp, ci, v, d["d_out"],
                                                           out=ys[i % len(xs)]), K, Wm)
+    elif fn == "harp_gen":
+        d = synth.harp_general()
+        x0 = d["x"].to("cuda:0")
+        blocks = torch.from_numpy(np.concatenate([b.reshape(-1) for b in d["blocks"]])).to("cuda:0").half()
+        xs = copies(torch, x0)
+        ys = [torch.empty_like(x0) for _ in xs]
+        t = Timed(torch, lambda i: W.harp_rotate(xs[i % len(xs)], blocks, d["radices"], None, False,
+                                                 out=ys[i % len(xs)]), K, Wm)
     else:
         d = synth.harp()
         x0 = d["x"].to("cuda:0")

@@ -28,7 +28,7 @@
 namespace whtq {
 
 namespace hg {
-constexpr int THREADS = 512;
+constexpr int THREADS = 1024;
 constexpr int MAXST = 20;          // stages, preconditioning factors included
 constexpr int MAXTT = 16;
 constexpr int LDS_FLOATS = 38912;  // 152 KB of tile
@@ -85,11 +85,18 @@ __device__ __forceinline__ void hg_stage(float* tile, int ldt, int nt, int d, in
     for (int r = 0; r < RPL; ++r)
 #pragma unroll
       for (int k = 0; k < B; ++k) co[r][k] = r0 + r < B ? blk_at<BDT>(blocks, bo + (r0 + r) * B + k) : 0.f;
+    // the item's LDS addresses, computed once for all its tokens (rows past
+    // the block's end, in the last lane of a split block, write nowhere)
+    int ia[B], oa[RPL];
+#pragma unroll
+    for (int k = 0; k < B; ++k) ia[k] = hg::pos(base + k * s);
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) oa[r] = r0 + r < B ? hg::pos(base + (r0 + r) * s) : -1;
     for (int j = j0; j < j1; ++j) {
       float* row = tile + j * ldt;
       float xv[B];
 #pragma unroll
-      for (int k = 0; k < B; ++k) xv[k] = row[hg::pos(base + k * s)];
+      for (int k = 0; k < B; ++k) xv[k] = row[ia[k]];
       float yv[RPL];
 #pragma unroll
       for (int r = 0; r < RPL; ++r) {
@@ -100,7 +107,7 @@ __device__ __forceinline__ void hg_stage(float* tile, int ldt, int nt, int d, in
       }
 #pragma unroll
       for (int r = 0; r < RPL; ++r)
-        if (r0 + r < B) row[hg::pos(base + (r0 + r) * s)] = yv[r];
+        if (RPL * LPB == B || oa[r] >= 0) row[oa[r]] = yv[r];
     }
   }
 }
@@ -114,12 +121,15 @@ __device__ __forceinline__ void hg_had(float* tile, int ldt, int nt, int d, int 
     const int j = f / groups, c = f - j * groups;
     const int base = (c % s) + (c / s) * s * B;
     float* row = tile + j * ldt;
+    int ia[B];
+#pragma unroll
+    for (int k = 0; k < B; ++k) ia[k] = hg::pos(base + k * s);
     float xv[B];
 #pragma unroll
-    for (int k = 0; k < B; ++k) xv[k] = row[hg::pos(base + k * s)];
+    for (int k = 0; k < B; ++k) xv[k] = row[ia[k]];
     had_regs<B>(xv);
 #pragma unroll
-    for (int k = 0; k < B; ++k) row[hg::pos(base + k * s)] = xv[k];
+    for (int k = 0; k < B; ++k) row[ia[k]] = xv[k];
   }
 }
 

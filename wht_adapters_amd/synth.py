@@ -146,6 +146,7 @@ WORKLOADS = {
     "qwha_2048x4096_nnz262144": "QWHA forward, 2048 tokens x 4096, F 4096 x 4096 with 262,144 nnz",
     "qwha_bwd_2048x4096_nnz262144": "QWHA backward (dx and dc), same sizes, upstream dy ~ N(0,1)",
     "harp_8192x4096_r16x3": "HARP: RHT + three radix-16 stages, 8192 tokens x 4096",
+    "harp_8192x5120_r88852": "HARP general schedule 8*8*8*5*2, 8192 tokens x 5120 (no preconditioning)",
     "rht_int2_g64_28672x8192": "RHT + INT2 RTN g=64, bf16 28672 x 8192 Student-t weights",
 }
 
@@ -185,6 +186,20 @@ def qwha_backward(tokens=2048, d_in=4096, d_out=4096, nnz=262144):
     d = qwha(tokens, d_in, d_out, nnz)
     d["dy"] = to_bf16(gaussian_rows(child_rng(3, 4), tokens, d_out))
     return d
+
+
+def harp_general(tokens=8192, radices=(8, 8, 8, 5, 2), outlier_frac=0.005, factor=30.0):
+    """The HARP recipe on the page's mixed-radix example d = 5120 = 8*8*8*5*2
+    (workload 6): N(0,1) activations with 0.5% channels x30 -> bf16, blocks =
+    QR of Gaussians per stage (no sign vector: 5120 is not a power of two,
+    so there is no Sylvester preconditioning)."""
+    d = int(np.prod(radices))
+    x = gaussian_rows(child_rng(6, 0), tokens, d)
+    ch = child_rng(6, 1).choice(d, int(round(outlier_frac * d)), replace=False)
+    x[:, ch] *= factor
+    rng_b = child_rng(6, 3)
+    blocks = [orthogonal_blocks(rng_b, d // b, b) for b in radices]
+    return {"x": to_bf16(x), "radices": list(radices), "blocks": blocks, "outlier_channels": ch}
 
 
 def harp(tokens=8192, d=4096, radices=(16, 16, 16), outlier_frac=0.005, factor=30.0):
