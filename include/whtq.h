@@ -221,19 +221,26 @@ whtq_status qwha_adapter_grad_values(const void* x, const void* dy, whtq_dtype d
  * precondition else I; stage t applies d / b_t independent b_t x b_t blocks
  * along digit t ([HARP] 2.1, 2.2).
  *   x, y [tokens][ld] in dtype (bf16 in this build); x == y not allowed.
- *   radices: HOST int32[n_stages], each >= 2, product == d.  This build runs
- *   d = 4096 with radices (16, 16, 16).
+ *   radices: HOST int32[n_stages], each >= 2, product == d ([HARP] 2.1:
+ *   e.g. 8, 8, 8, 5, 2 for d = 5120).  This build runs radices up to 16,
+ *   d <= 8192 and up to 16 stages (WHTQ_EUNSUPPORTED otherwise).
+ *   precondition: Hn is the Sylvester matrix, so it needs d a power of two
+ *   (WHTQ_EINVAL otherwise).
  *   blocks: device, stage-major, stage t as [d / b_t][b_t][b_t] row-major
- *   (B[k][j] at k * b_t + j), in blocks_dtype: WHTQ_F32, or WHTQ_F16 (half
- *   the bytes read per call; the kernel rounds fp32 blocks to fp16 itself,
- *   so both give the same result for the same fp16-representable values).
- *   Arithmetic: each token row is scaled by an exact power of two that puts
- *   its L2 norm in [2^13, 2^14) and kept on chip in fp16; the
- *   preconditioning Hn = (H16 / 4) (x) (H16 / 4) (x) (H16 / 4) and every
- *   block stage run as 16 x 16 x 16 MFMAs with fp16 operands and fp32
- *   accumulation, the result of each rounded to fp16; the output is
- *   unscaled and rounded once to bf16 (nearest even).
- *   sign_bits: uint32[d/32] or NULL (all +1); used when precondition != 0.
+ *   (B[k][j] at k * b_t + j), in blocks_dtype: WHTQ_F32 or WHTQ_F16 (half
+ *   the bytes read per call).
+ *   Arithmetic, d = 4096 with radices (16, 16, 16): each token row is scaled
+ *   by an exact power of two that puts its L2 norm in [2^13, 2^14) and kept
+ *   on chip in fp16; the preconditioning Hn = (H16 / 4) (x) (H16 / 4) (x)
+ *   (H16 / 4) and every block stage run as 16 x 16 x 16 MFMAs with fp16
+ *   operands and fp32 accumulation (fp32 blocks are rounded to fp16 in the
+ *   kernel, so both block dtypes give the same result for the same
+ *   fp16-representable values), the result of each rounded to fp16.  Every
+ *   other schedule: fp32 on chip and fp32 arithmetic (fp16 blocks widened
+ *   exactly), the preconditioning as in-register Hadamard butterflies.  The
+ *   output is rounded once to bf16 (nearest even).
+ *   sign_bits: uint32[ceil(d/32)] or NULL (all +1); used when
+ *   precondition != 0.
  */
 whtq_status harp_rotate(const void* x, void* y, whtq_dtype dtype, int64_t tokens, int64_t d,
                         int64_t ldx, int64_t ldy, const uint32_t* sign_bits, int precondition,
