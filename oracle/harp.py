@@ -78,3 +78,82 @@ def harp_rotate(x, radices, blocks, s=None, precondition=True):
     for t in range(len(radices)):
         z = z @ stage_matrix(blocks[t], t, radices).T
     return z
+
+
+# ---------------------------------------------------- block parametrisation
+#
+# [HARP] 2.2: each learned block is B_{t,c}(theta) = Q_{t,c}(theta) G_{b_t},
+# G a fixed base mixer (the normalised Sylvester Hadamard when b_t is a power
+# of two, otherwise a fixed orthogonal substitute such as the QR factor of a
+# Gaussian matrix), Q orthogonal: a Givens rotation when b_t = 2, a Cayley
+# map when b_t > 2; Theta = 0 gives Q = I, so B = G.  [HARP] 2.4: the
+# parameters may be stored as int8.
+#
+# Readings (the pages name the maps only):
+#   * Givens: Q = [[cos t, -sin t], [sin t, cos t]], one angle per block;
+#   * Cayley: Q = (I - A)(I + A)^-1 with A skew-symmetric, its b(b-1)/2
+#     parameters the strict upper triangle row by row (A[i][j] = p, i < j,
+#     A[j][i] = -p);
+#   * int8: theta = s_t * q with one fp32 scale s_t per stage;
+#   * layout: stage-major, stage t as [d / b_t][P_t] parameters.
+
+
+def params_per_block(b):
+    return 1 if b == 2 else b * (b - 1) // 2
+
+
+def skew_from_params(p, b):
+    a = np.zeros((b, b), dtype=np.float64)
+    iu = np.triu_indices(b, 1)
+    a[iu] = np.asarray(p, dtype=np.float64)
+    return a - a.T
+
+
+def cayley(a):
+    """Q = (I - A)(I + A)^-1 (orthogonal, det +1 for skew-symmetric A)."""
+    i = np.eye(a.shape[0])
+    return (i - a) @ np.linalg.inv(i + a)
+
+
+def givens(theta):
+    c, s = np.cos(theta), np.sin(theta)
+    return np.array([[c, -s], [s, c]], dtype=np.float64)
+
+
+def sylvester_mixer(b):
+    from .hadamard import sylvester
+    return sylvester(b).astype(np.float64) / np.sqrt(b)
+
+
+def build_blocks(params, radices, d, mixers=None):
+    """Blocks Q(theta) G per stage, fp64: a list of [d / b_t, b_t, b_t].
+
+    params: flat, stage-major ([d / b_t][P_t] per stage), already in radians /
+    Cayley units (see dequant_params for int8).  mixers: list of b_t x b_t
+    matrices, or None for the Sylvester mixer (every radix a power of two)."""
+    check_schedule(radices, d)
+    params = np.asarray(params, dtype=np.float64)
+    out, o = [], 0
+    for t, b in enumerate(radices):
+        g = sylvester_mixer(b) if mixers is None else np.asarray(mixers[t], dtype=np.float64)
+        p = params_per_block(b)
+        nb = d // b
+        blk = np.empty((nb, b, b), dtype=np.float64)
+        for c in range(nb):
+            th = params[o + c * p: o + (c + 1) * p]
+            q = givens(th[0]) if b == 2 else cayley(skew_from_params(th, b))
+            blk[c] = q @ g
+        out.append(blk)
+        o += nb * p
+    return out
+
+
+def dequant_params(q, scales, radices, d):
+    """theta = s_t * q for int8 codes q, one scale per stage."""
+    q = np.asarray(q, dtype=np.float64)
+    out, o = np.empty_like(q), 0
+    for t, b in enumerate(radices):
+        n = (d // b) * params_per_block(b)
+        out[o:o + n] = q[o:o + n] * float(scales[t])
+        o += n
+    return out

@@ -127,3 +127,37 @@ def test_mutant_qwha_grad_values_untransformed_x(monkeypatch):
         return np.einsum("te,te->e", np.asarray(dy)[:, rows], np.asarray(x)[:, col_idx])  # x, not x Hn
     monkeypatch.setattr(Q, "qwha_grad_values", gv)
     _fails(tq.test_qwha_grad_values_finite_differences)
+
+
+def test_mutant_cayley_inverse_order(monkeypatch):
+    """(I + A)(I - A)^-1 (the inverse rotation) fails the 2x2 closed form."""
+    from oracle import harp
+    monkeypatch.setattr(harp, "cayley", lambda a: (np.eye(a.shape[0]) + a) @ np.linalg.inv(np.eye(a.shape[0]) - a))
+    with pytest.raises(AssertionError):
+        import test_oracle_qwha_harp as T
+        T.test_cayley_2x2_closed_form()
+
+
+def test_mutant_mixer_on_the_left(monkeypatch):
+    """G Q instead of Q G fails the single-parameter placement pin."""
+    from oracle import harp
+    orig = harp.build_blocks
+
+    def mutant(params, radices, d, mixers=None):
+        blocks = orig(np.zeros_like(np.asarray(params, dtype=float)), radices, d, mixers)
+        out, o = [], 0
+        for t, b in enumerate(radices):
+            g = harp.sylvester_mixer(b) if mixers is None else np.asarray(mixers[t], dtype=float)
+            p = harp.params_per_block(b)
+            blk = blocks[t].copy()
+            for c in range(d // b):
+                th = np.asarray(params, dtype=float)[o + c * p: o + (c + 1) * p]
+                q = harp.givens(th[0]) if b == 2 else harp.cayley(harp.skew_from_params(th, b))
+                blk[c] = g @ q
+            out.append(blk)
+            o += (d // b) * p
+        return out
+    monkeypatch.setattr(harp, "build_blocks", mutant)
+    with pytest.raises(AssertionError):
+        import test_oracle_qwha_harp as T
+        T.test_build_blocks_single_parameter_placement()

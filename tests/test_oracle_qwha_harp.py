@@ -257,3 +257,82 @@ def test_harp_schedule_golden():
         else:
             with pytest.raises(ValueError):
                 harp.check_schedule(rad, d)
+
+
+# ------------------------------------------- HARP block parametrisation
+
+@pytest.mark.parametrize("b", [3, 4, 5, 8, 11, 16])
+def test_cayley_orthogonal_det_one_and_zero(b):
+    rng = np.random.default_rng(b)
+    a = harp.skew_from_params(0.3 * rng.standard_normal(b * (b - 1) // 2), b)
+    assert np.allclose(a, -a.T)
+    q = harp.cayley(a)
+    assert np.allclose(q.T @ q, np.eye(b), atol=1e-12)
+    assert np.isclose(np.linalg.det(q), 1.0)
+    assert np.array_equal(harp.cayley(np.zeros((b, b))), np.eye(b))
+    # the Cayley map is its own inverse on orthogonal matrices without -1 eigenvalues
+    back = (np.eye(b) - q) @ np.linalg.inv(np.eye(b) + q)
+    assert np.allclose(back, a, atol=1e-10)
+
+
+def test_cayley_2x2_closed_form():
+    """A = [[0, a], [-a, 0]]: (I - A)(I + A)^-1 = [[1 - a^2, -2a], [2a, 1 - a^2]] / (1 + a^2),
+    the rotation by 2 atan(a); a = 1 is the quarter turn [[0, -1], [1, 0]]."""
+    for a in (0.25, -0.7, 1.0, 3.0):
+        q = harp.cayley(harp.skew_from_params([a], 2))
+        want = np.array([[1 - a * a, -2 * a], [2 * a, 1 - a * a]]) / (1 + a * a)
+        assert np.allclose(q, want, atol=1e-14)
+        assert np.allclose(q, harp.givens(2 * np.arctan(a)), atol=1e-14)
+    assert np.allclose(harp.cayley(harp.skew_from_params([1.0], 2)), [[0, -1], [1, 0]], atol=1e-15)
+
+
+def test_skew_parameter_order():
+    """Parameters fill the strict upper triangle row by row."""
+    a = harp.skew_from_params([1, 2, 3, 4, 5, 6], 4)
+    assert a[0, 1] == 1 and a[0, 2] == 2 and a[0, 3] == 3 and a[1, 2] == 4 and a[1, 3] == 5 and a[2, 3] == 6
+    assert a[3, 2] == -6 and np.all(np.diag(a) == 0)
+
+
+def test_givens_closed_form():
+    assert np.allclose(harp.givens(np.pi / 2), [[0, -1], [1, 0]], atol=1e-15)
+    assert np.allclose(harp.givens(0.3) @ harp.givens(0.4), harp.givens(0.7), atol=1e-15)
+
+
+def test_build_blocks_theta_zero_is_the_mixer():
+    """Theta = 0 gives B = G: with Sylvester mixers the rotation is the WHT
+    ([HARP] 2.2: the fixed RHT is recovered at initialisation)."""
+    radices, d = [4, 2, 8], 64
+    n = sum((d // b) * harp.params_per_block(b) for b in radices)
+    blocks = harp.build_blocks(np.zeros(n), radices, d)
+    for b, blk in zip(radices, blocks):
+        assert np.array_equal(blk, np.broadcast_to(harp.sylvester_mixer(b), blk.shape))
+    x = np.random.default_rng(0).standard_normal((3, d))
+    assert np.allclose(harp.harp_rotate(x, radices, blocks, precondition=False), H.wht(x), atol=1e-12)
+
+
+def test_build_blocks_single_parameter_placement():
+    """One nonzero parameter touches one block of one stage."""
+    radices, d = [5, 2, 3], 30
+    mix = [np.linalg.qr(np.random.default_rng(b).standard_normal((b, b)))[0] for b in radices]
+    sizes = [(d // b) * harp.params_per_block(b) for b in radices]
+    p = np.zeros(sum(sizes))
+    t, c, k = 0, 4, 7          # stage 0 (b = 5, 10 params per block), block 4, parameter 7 = A[2][3]
+    p[c * 10 + k] = 0.5
+    blocks = harp.build_blocks(p, radices, d, mix)
+    for tt, (b, blk) in enumerate(zip(radices, blocks)):
+        for cc in range(d // b):
+            same = np.allclose(blk[cc], mix[tt])
+            assert same == (not (tt == t and cc == c))
+    a = np.zeros((5, 5)); a[2, 3], a[3, 2] = 0.5, -0.5
+    assert np.allclose(blocks[0][c], harp.cayley(a) @ mix[0])
+    # stage 1 (b = 2): a Givens angle
+    p = np.zeros(sum(sizes)); p[sizes[0] + 6] = 0.9
+    blocks = harp.build_blocks(p, radices, d, mix)
+    assert np.allclose(blocks[1][6], harp.givens(0.9) @ mix[1])
+
+
+def test_dequant_params():
+    radices, d = [2, 4], 8
+    q = np.arange(-4, 4 + 6 * 2 - 4, dtype=np.int8)[: 4 * 1 + 2 * 6]
+    th = harp.dequant_params(q, [0.5, 0.25], radices, d)
+    assert np.allclose(th[:4], 0.5 * q[:4]) and np.allclose(th[4:], 0.25 * q[4:])
