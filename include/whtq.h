@@ -70,7 +70,7 @@ typedef enum {
   WHTQ_EHIP = 4          /* HIP runtime / launch failure, including no device      */
 } whtq_status;
 
-typedef enum { WHTQ_F32 = 0, WHTQ_BF16 = 1, WHTQ_F16 = 2 } whtq_dtype;
+typedef enum { WHTQ_F32 = 0, WHTQ_BF16 = 1, WHTQ_F16 = 2, WHTQ_I8 = 3 } whtq_dtype;  /* I8: HARP parameters only */
 
 typedef enum {
   WHTQ_SIGN_NONE = 0,   /* y = Hn x        */
@@ -246,6 +246,31 @@ whtq_status harp_rotate(const void* x, void* y, whtq_dtype dtype, int64_t tokens
                         int64_t ldx, int64_t ldy, const uint32_t* sign_bits, int precondition,
                         const int32_t* radices, int n_stages, const void* blocks,
                         whtq_dtype blocks_dtype, void* stream);
+
+/*
+ * harp_build_blocks -- the blocks B_{t,c} = Q_{t,c}(theta) G_{b_t} that
+ * harp_rotate takes, from their parameters ([HARP] 2.2: Q a Givens rotation
+ * for b_t = 2, a Cayley map for b_t > 2, G a fixed base mixer; theta = 0
+ * gives B = G, the fixed Hadamard rotation; [HARP] 2.4: int8 storage).
+ *   Conventions: Givens Q = [[cos t, -sin t], [sin t, cos t]] (one angle per
+ *   block); Cayley Q = (I - A)(I + A)^-1 with A skew-symmetric, its
+ *   b(b-1)/2 parameters the strict upper triangle row by row (A[i][j] = p,
+ *   i < j, A[j][i] = -p).
+ *   params: device, stage-major, stage t as [d / b_t][P_t] with P_t = 1
+ *   (b_t = 2) or b_t (b_t - 1) / 2; WHTQ_F32 values, or WHTQ_I8 codes q with
+ *   theta = scales[t] * q (scales: device float32[n_stages], required then).
+ *   radices: HOST int32[n_stages], each in [2, 16] in this build, product d.
+ *   mixers: device float32, stage-major b_t x b_t matrices G_t (row-major),
+ *   or NULL for the normalised Sylvester Hadamard (every radix a power of
+ *   two, else WHTQ_EINVAL).
+ *   blocks: device, written in harp_rotate's layout ([d / b_t][b_t][b_t] per
+ *   stage, stage-major), WHTQ_F32 or WHTQ_F16 (rounded once).
+ *   Arithmetic: fp32; Q by Gauss-Jordan elimination of [I + A | I - A]
+ *   (I + A has the identity as symmetric part: no pivoting needed).
+ */
+whtq_status harp_build_blocks(const void* params, whtq_dtype params_dtype, const float* scales, int64_t d,
+                              const int32_t* radices, int n_stages, const float* mixers, void* blocks,
+                              whtq_dtype blocks_dtype, void* stream);
 
 const char* whtq_status_string(whtq_status s);
 int whtq_last_hip_error(void); /* hipError_t behind this thread's last WHTQ_EHIP */

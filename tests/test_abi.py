@@ -235,3 +235,25 @@ def test_qwha_backward_validation(lib):
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="needs a host without a GPU")
 def test_backward_valid_call_without_device_is_ehip(lib):
     assert bw(lib) == EHIP and gv(lib) == EHIP
+
+
+def hb(lib, p=P, pdt=0, sc=NULL, d=64, rad=(4, 16), mix=NULL, out=P, bdt=0):
+    arr = (ctypes.c_int32 * len(rad))(*rad)
+    return lib.harp_build_blocks(p, pdt, sc, d, arr, len(rad), mix, out, bdt, NULL)
+
+
+def test_harp_build_validation(lib):
+    assert hb(lib, rad=(4, 8)) == EINVAL                   # product != d
+    assert hb(lib, pdt=1) == EINVAL                        # bf16 parameters: not offered
+    assert hb(lib, pdt=3) == EINVAL                        # int8 needs scales
+    assert hb(lib, bdt=1) == EINVAL                        # bf16 blocks: not offered
+    assert hb(lib, d=60, rad=(4, 15)) == EINVAL            # no Sylvester mixer for 15
+    assert hb(lib, d=68, rad=(4, 17), mix=P) == EUNSUP     # radix above 16
+    assert hb(lib, p=NULL) == EINVAL
+    assert hb(lib, p=ctypes.c_void_p(0x10002)) == EALIGN   # fp32 parameters, 2-byte aligned
+    assert hb(lib, out=ctypes.c_void_p(0x10001), bdt=2) == EALIGN
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="needs a host without a GPU")
+def test_harp_build_valid_call_without_device_is_ehip(lib):
+    assert hb(lib) == EHIP

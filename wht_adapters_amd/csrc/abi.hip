@@ -36,6 +36,8 @@ hipError_t launch_permute(const void* vals, int val_dt, const int32_t* perm, int
 hipError_t launch_harp_gen(const void* x, void* y, int64_t tokens, int d, int64_t ldx, int64_t ldy,
                            const uint32_t* sbits, int precondition, const int32_t* radices, int n_stages,
                            const void* blocks, int bdt, hipStream_t s);
+hipError_t launch_harp_build(const void* params, int pdt, const float* scales, int64_t d, const int32_t* radices,
+                             int n_stages, const float* mixers, void* blocks, int bdt, hipStream_t s);
 hipError_t launch_harp(const void* x, void* y, int dt, int64_t tokens, int64_t ldx, int64_t ldy,
                        const uint32_t* sbits, int precondition, const void* blocks, int bdt, hipStream_t s);
 
@@ -346,6 +348,37 @@ whtq_status harp_rotate(const void* x, void* y, whtq_dtype dtype, int64_t tokens
                                   (hipStream_t)stream));
   return hip_status(launch_harp_gen(x, y, tokens, (int)d, ldx, ldy, sign_bits, precondition, radices, n_stages,
                                     blocks, blocks_dtype, (hipStream_t)stream));
+}
+
+whtq_status harp_build_blocks(const void* params, whtq_dtype params_dtype, const float* scales, int64_t d,
+                              const int32_t* radices, int n_stages, const float* mixers, void* blocks,
+                              whtq_dtype blocks_dtype, void* stream) {
+  if (params_dtype != WHTQ_F32 && params_dtype != WHTQ_I8) return WHTQ_EINVAL;
+  if (blocks_dtype != WHTQ_F32 && blocks_dtype != WHTQ_F16) return WHTQ_EINVAL;
+  if (!radices || n_stages < 1 || n_stages > 64 || d < 1 || !params || !blocks) return WHTQ_EINVAL;
+  if (params_dtype == WHTQ_I8 && !scales) return WHTQ_EINVAL;
+  int64_t prod = 1;
+  bool pow2 = true;
+  for (int t = 0; t < n_stages; ++t) {
+    if (radices[t] < 2) return WHTQ_EINVAL;
+    prod *= radices[t];
+    if (prod > d) return WHTQ_EINVAL;
+    pow2 = pow2 && (radices[t] & (radices[t] - 1)) == 0;
+  }
+  if (prod != d) return WHTQ_EINVAL;
+  // the Sylvester mixer exists for power-of-two radices only
+  if (!mixers && !pow2) return WHTQ_EINVAL;
+  if (n_stages > 16 || d > (int64_t(1) << 24)) return WHTQ_EUNSUPPORTED;
+  for (int t = 0; t < n_stages; ++t)
+    if (radices[t] > 16) return WHTQ_EUNSUPPORTED;
+  if ((params_dtype == WHTQ_F32 && (reinterpret_cast<uintptr_t>(params) & 3u)) ||
+      (reinterpret_cast<uintptr_t>(blocks) % (uintptr_t)dt_bytes(blocks_dtype)) ||
+      (reinterpret_cast<uintptr_t>(mixers) & 3u) || (reinterpret_cast<uintptr_t>(scales) & 3u))
+    return WHTQ_EALIGN;
+  whtq_status st = need_device();
+  if (st != WHTQ_OK) return st;
+  return hip_status(launch_harp_build(params, params_dtype, scales, d, radices, n_stages, mixers, blocks,
+                                      blocks_dtype, (hipStream_t)stream));
 }
 
 }  // extern "C"

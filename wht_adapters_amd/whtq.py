@@ -28,6 +28,7 @@ _SIG = {
                              _i64, _vp],
     "harp_rotate": [_vp, _vp, _int, _i64, _i64, _i64, _i64, _vp, _int, _vp, _int, _vp, _int, _vp],
     "qwha_csr_transpose": [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp],
+    "harp_build_blocks": [_vp, _int, _vp, _i64, _vp, _int, _vp, _vp, _int, _vp],
     "qwha_permute_values": [_vp, _int, _vp, _i64, _vp, _vp],
     "qwha_adapter_backward_input": [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _int, _i64, _i64, _vp, _int,
                                     _i64, _vp],
@@ -45,8 +46,8 @@ _lib.whtq_status_string.restype = ctypes.c_char_p
 _lib.whtq_last_hip_error.restype = _int
 _lib.whtq_abi_version.restype = _int
 
-F32, BF16, F16 = 0, 1, 2
-_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+F32, BF16, F16, I8 = 0, 1, 2, 3
+_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16, torch.int8: I8}
 SIGN_NONE, SIGN_BEFORE, SIGN_AFTER = 0, 1, 2
 _SIGN_MODES = {"none": SIGN_NONE, "before": SIGN_BEFORE, "after": SIGN_AFTER}
 
@@ -308,4 +309,31 @@ def qwha_adapter_grad_values(x, dy, row_ptr, col_idx, out=None, workspace=None):
         _check("qwha_adapter_grad_values", _lib.qwha_adapter_grad_values(
             _ptr(x), _ptr(dy), _DT[x.dtype], tokens, d_in, d_out, ldx, lddy, _ptr(row_ptr), _ptr(col_idx),
             nnz, _ptr(out), _ptr(workspace), wbytes, _stream(x)))
+    return out
+
+
+def harp_build_blocks(params, radices, d, scales=None, mixers=None, out=None, out_dtype=torch.float32):
+    """Blocks Q(theta) G for harp_rotate from float32 parameters, or int8 codes
+    with per-stage float32 scales; mixers float32 (stage-major) or None for Sylvester."""
+    _need_cuda("params", params)
+    if params.dtype not in (torch.float32, torch.int8) or not params.is_contiguous():
+        raise ValueError("params must be contiguous float32 or int8")
+    if params.dtype == torch.int8:
+        _need_cuda("scales", scales)
+        if scales.dtype != torch.float32 or scales.numel() != len(radices):
+            raise ValueError("int8 params need float32 scales, one per stage")
+    if mixers is not None:
+        _need_cuda("mixers", mixers)
+        if mixers.dtype != torch.float32 or not mixers.is_contiguous():
+            raise ValueError("mixers must be contiguous float32")
+    nblk = sum(d * int(b) for b in radices)
+    if out is None:
+        out = torch.empty(nblk, dtype=out_dtype, device=params.device)
+    if out.numel() != nblk or not out.is_contiguous():
+        raise ValueError("out must be contiguous with sum(d * b_t) elements")
+    rad = (ctypes.c_int32 * len(radices))(*[int(b) for b in radices])
+    with torch.cuda.device(params.device):
+        _check("harp_build_blocks", _lib.harp_build_blocks(
+            _ptr(params), _DT[params.dtype], _ptr(scales), d, rad, len(radices), _ptr(mixers), _ptr(out),
+            _DT[out.dtype], _stream(params)))
     return out
