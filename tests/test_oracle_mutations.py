@@ -161,3 +161,17 @@ def test_mutant_mixer_on_the_left(monkeypatch):
     with pytest.raises(AssertionError):
         import test_oracle_qwha_harp as T
         T.test_build_blocks_single_parameter_placement()
+
+
+def test_mutant_gemv_signs_on_the_code_side(monkeypatch):
+    """Applying S to the codes before the transform (Hn S (q s)) instead of after
+    it fails the brute-force layer."""
+    from oracle import gemv, rtn
+    import test_oracle_gemv as tg
+
+    def mutant(x, codes, s16, s, bits, group, n):
+        y_hat = rtn.dequantize(codes, s16, bits, group, n) * np.asarray(s)[None, :]
+        return np.asarray(x, dtype=float) @ H.wht(y_hat).T
+    monkeypatch.setattr(gemv, "rht_gemv", mutant)
+    with pytest.raises(AssertionError):
+        tg.test_gemv_bruteforce_tiny()
