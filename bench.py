@@ -47,6 +47,8 @@ ALGO_BYTES = {
     "harp_8192x5120_r88852": 2 * 8192 * 5120 * 2 + 5120 * (8 + 8 + 8 + 5 + 2) * 2,  # fp16 blocks
     "rht_int2_g64_28672x8192": 28672 * 8192 * 2 + 1024 + 28672 * 2048 + 28672 * 128 * 2,
     "rht_int2_g64_28672x8192_inverse": 28672 * 8192 * 2 + 1024 + 28672 * 2048 + 28672 * 128 * 2,
+    # decode through the INT2 layer: codes + fp16 scales + sign vector + one bf16 token in, bf16 y out
+    "gemv_int2_g64_28672x8192_t1": 28672 * 2048 + 28672 * 128 * 2 + 1024 + 8192 * 2 + 28672 * 2,
 }
 ROWS = {
     "fwht_f32_256x4096": 256, "rht_int4_g128_4096x4096": 4096,
@@ -55,6 +57,7 @@ ROWS = {
     "qwha_bwd_dx_2048x4096_nnz262144": 2048, "qwha_bwd_dc_2048x4096_nnz262144": 2048,
     "harp_8192x5120_r88852": 8192,
     "rht_int2_g64_28672x8192_inverse": 28672,
+    "gemv_int2_g64_28672x8192_t1": 28672,
 }
 MAIN = "rht_int4_g128_4096x4096"
 KERNEL_SOURCES = {  # sources a workload's kernel is built from (traffic counters go stale with them)
@@ -184,7 +187,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workloads", default="all",
-                    help="all | main | comma list of fwht, qwha, qwha_bwd, harp, harp_gen, int2 "
+                    help="all | main | comma list of fwht, qwha, qwha_bwd, harp, harp_gen, int2, gemv "
                          "(the main workload always runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -215,7 +218,8 @@ def main():
         del a, b
         log("[bench] copy probe: 3 x 256 MiB device copy done")
 
-    sel = {"all": {"main", "fwht", "qwha", "qwha_bwd", "harp", "harp_gen", "int2"}, "main": {"main"}}.get(
+    sel = {"all": {"main", "fwht", "qwha", "qwha_bwd", "harp", "harp_gen", "int2", "gemv"},
+           "main": {"main"}}.get(
         args.workloads, set(args.workloads.split(",")))
     sel.add("main")  # `value` is always quoted on the main workload
     cfg_main = synth.rht_int4_g128()
@@ -242,6 +246,10 @@ def main():
         cfg5 = synth.rht_int2_g64()
         res.update(bench_quant(torch, W, mask_dev, cfg5, "rht_int2_g64_28672x8192", 2, 64, K, Wm))
         log(f"[bench] rht_int2_g64_28672x8192: {res['rht_int2_g64_28672x8192']}")
+    if "gemv" in sel:
+        nm = "gemv_int2_g64_28672x8192_t1"
+        res[nm] = bench_gemv(torch, W, mask_dev, synth, nm, K, Wm)
+        log(f"[bench] {nm}: {res[nm]}")
 
     main_r = res[MAIN]
     per_launch = main_r["ms_per_launch"] / 1e3
@@ -304,6 +312,28 @@ def bench_qwha_bwd(torch, W, synth, K, Wm):
     for nm, fn in (("qwha_bwd_dx_2048x4096_nnz262144", dx_step), ("qwha_bwd_dc_2048x4096_nnz262144", dc_step)):
         r[nm] = result(nm, Timed(torch, fn, K, Wm).run(), K)
     del dys, xs, dxs, dcs, ws
+    torch.cuda.empty_cache()
+    return r
+
+
+def bench_gemv(torch, W, mask_dev, synth, name, K, Wm):
+    """One decode token through the 28672 x 8192 INT2 g=64 layer: the
+    online-RHT low-bit product, codes and scales rotating over >= 1 GiB of
+    copies so that each launch reads them from HBM."""
+    d = synth.gemv_int2_g64()
+    c0 = torch.from_numpy(d["codes"]).to("cuda:0")
+    s0 = torch.from_numpy(d["scales"]).to("cuda:0")
+    x = d["x"].to("cuda:0")
+    sg = mask_dev(d["signs"])
+    k = max(2, math.ceil(GIB / (c0.numel() + 2 * s0.numel())))
+    cs = [c0.clone() for _ in range(k)]
+    ss = [s0.clone() for _ in range(k)]
+    ys = [torch.empty((1, c0.shape[0]), dtype=torch.bfloat16, device="cuda:0") for _ in range(k)]
+    del c0, s0
+    t = Timed(torch, lambda i: W.rht_lowbit_gemv(x, cs[i % k], ss[i % k], sg, 2, 64, out=ys[i % k]), K, Wm)
+    r = result(name, t.run(), K)
+    r["tokens_per_s"] = 1e3 / r["ms_per_launch"]
+    del cs, ss, ys
     torch.cuda.empty_cache()
     return r
 

@@ -120,6 +120,29 @@ whtq_status rht_dequantize_inverse(const uint8_t* codes, const uint16_t* scales,
                                    void* out, whtq_dtype out_dtype, int64_t ldo, void* stream);
 
 /*
+ * rht_lowbit_gemv -- y[t][o] = sum_i x[t][i] W_hat[o][i], the product of
+ * activations with weights held as rht_quantize_rtn codes, W_hat[o] =
+ * S Hn (q[o] * s[o]) (the rows rht_dequantize_inverse would write).  The
+ * rotation is applied to the activations instead of the weights ([HARP] 1
+ * and 2.4: low-bit weights in the rotated basis, the RHT applied online in
+ * fused O(d log d) kernels): y[t][o] = sum_k q[o][k] s[o][k/g] (Hn S x_t)[k].
+ *   x [tokens][ldx] bf16; y [tokens][ldy] bf16 (column o of row t is the
+ *   output of weight row o; ldy >= rows).  codes / scales as written by
+ *   rht_quantize_rtn with the same n, bits, group and sign_bits.
+ *   n: 4096 or 8192.  bits: 2 or 4.  group: power of two in [32/bits, 256].
+ *   The rotated activations are rounded to fp16 after a per-token
+ *   power-of-two scale; accumulation is fp32.  Tokens are processed in
+ *   passes of up to 4 (n = 4096) or 2 (n = 8192), each reading the codes
+ *   once: a decode-size product, not a GEMM.
+ *   Errors: EINVAL for bad sizes or NULL pointers, EUNSUPPORTED for other
+ *   n, bits = 3 or smaller groups, EALIGN as in the common rules (y needs
+ *   2-byte alignment only).
+ */
+whtq_status rht_lowbit_gemv(const void* x, int64_t tokens, int64_t ldx, const uint8_t* codes,
+                            const uint16_t* scales, int64_t rows, int64_t n, const uint32_t* sign_bits,
+                            int bits, int group, void* y, int64_t ldy, void* stream);
+
+/*
  * qwha_adapter_forward -- y[t][o] = sum_{k in row o of F} F[o][k] * (Hn x_t)[k],
  * the QWHA adapter output x Delta W^T with Delta W = F Hn ([QWHA] 2.1).
  *   x [tokens][ldx] bf16; y [tokens][ldy] bf16; d_in = 4096 in this build.

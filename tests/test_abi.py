@@ -35,7 +35,8 @@ def test_exports_every_declared_symbol(lib):
                           "qwha_adapter_forward", "harp_rotate", "whtq_status_string",
                           "whtq_last_hip_error", "whtq_abi_version", "qwha_csr_transpose",
                           "qwha_permute_values", "qwha_adapter_backward_input",
-                          "qwha_grad_values_workspace_bytes", "qwha_adapter_grad_values"}
+                          "qwha_grad_values_workspace_bytes", "qwha_adapter_grad_values",
+                          "harp_build_blocks", "rht_lowbit_gemv"}
     for nm in names:
         assert hasattr(lib, nm), nm
 
@@ -95,6 +96,34 @@ def test_quant_validation(lib):
     assert q(lib, c=NULL) == EINVAL
     assert dq(lib, o=NULL) == EINVAL
     assert dq(lib, ldo=100) == EINVAL
+
+
+def lbg(lib, x=P, tokens=1, ldx=8192, c=P, s=P, rows=64, n=8192, sb=NULL, bits=2, g=64, y=P, ldy=64):
+    return lib.rht_lowbit_gemv(x, tokens, ldx, c, s, rows, n, sb, bits, g, y, ldy, NULL)
+
+
+def test_lowbit_gemv_validation(lib):
+    assert lbg(lib, bits=3) == EUNSUP                 # 3-bit codes are not offered
+    assert lbg(lib, bits=5) == EINVAL
+    assert lbg(lib, n=2048, ldx=2048) == EUNSUP       # n is 4096 or 8192
+    assert lbg(lib, n=6144, ldx=6144) == EUNSUP
+    assert lbg(lib, g=8) == EUNSUP                    # 2-bit codes need g >= 16
+    assert lbg(lib, g=48) == EINVAL
+    assert lbg(lib, g=512) == EUNSUP
+    assert lbg(lib, ldx=4096) == EINVAL               # ldx < n
+    assert lbg(lib, ldy=63) == EINVAL                 # ldy < rows
+    assert lbg(lib, tokens=-1) == EINVAL
+    assert lbg(lib, rows=-1) == EINVAL
+    for kw in ("x", "c", "s", "y"):
+        assert lbg(lib, **{kw: NULL}) == EINVAL
+    assert lbg(lib, x=P_MIS) == EALIGN
+    assert lbg(lib, ldx=8196) == EALIGN               # 8196 * 2 B rows are not 16-byte multiples
+    assert lbg(lib, c=P_MIS) == EALIGN
+    assert lbg(lib, s=P_MIS) == EALIGN
+    assert lbg(lib, y=ctypes.c_void_p(0x10001)) == EALIGN
+    assert lbg(lib, sb=ctypes.c_void_p(0x10002)) == EALIGN
+    assert lbg(lib, tokens=0) == OK                   # nothing to do
+    assert lbg(lib, rows=0, ldy=0) == OK
 
 
 def qw(lib, x=P, xd=1, tokens=8, d_in=4096, ldx=4096, rp=P, ci=P, v=P, vd=1, d_out=4096, nnz=100,

@@ -20,6 +20,9 @@ hipError_t launch_rht_quant(int logn, int din, int bits, int logg, const void* w
 hipError_t launch_rht_dequant(int logn, int dout, int bits, int logg, const uint8_t* codes,
                               const uint16_t* scales, int64_t rows, const uint32_t* sb, void* out,
                               int64_t ldo, hipStream_t s);
+hipError_t launch_rht_gemv(int logn, int bits, int logg, const void* x, int64_t tokens, int64_t ldx,
+                           const uint8_t* codes, const uint16_t* scales, int64_t rows, const uint32_t* sb,
+                           void* y, int64_t ldy, hipStream_t s);
 hipError_t launch_qwha(const void* x, int64_t tokens, int64_t ldx, const int32_t* row_ptr,
                        const int32_t* col_idx, const void* vals, int val_dt, int64_t d_out, int64_t nnz,
                        void* y, int64_t ldy, hipStream_t s);
@@ -188,6 +191,26 @@ whtq_status rht_dequantize_inverse(const uint8_t* codes, const uint16_t* scales,
   if (st != WHTQ_OK) return st;
   return hip_status(launch_rht_dequant(logn, out_dtype, bits, logg, codes, scales, rows, sign_bits, out, ldo,
                                        (hipStream_t)stream));
+}
+
+whtq_status rht_lowbit_gemv(const void* x, int64_t tokens, int64_t ldx, const uint8_t* codes,
+                            const uint16_t* scales, int64_t rows, int64_t n, const uint32_t* sign_bits,
+                            int bits, int group, void* y, int64_t ldy, void* stream) {
+  int logn = 0, logg = 0;
+  whtq_status st = check_quant_shape(rows, n, bits, group, &logn, &logg);
+  if (st != WHTQ_OK) return st;
+  if (tokens < 0 || ldx < n || ldy < rows) return WHTQ_EINVAL;
+  if (tokens > 0 && rows > 0 && (!x || !codes || !scales || !y)) return WHTQ_EINVAL;
+  if (bits == 3 || (logn != 12 && logn != 13) || (1 << logg) < 32 / bits) return WHTQ_EUNSUPPORTED;
+  if (!rows_aligned(x, n, ldx, 2) || !aligned16(codes) || !aligned16(scales) ||
+      (reinterpret_cast<uintptr_t>(y) & 1u))
+    return WHTQ_EALIGN;
+  if (sign_bits && (reinterpret_cast<uintptr_t>(sign_bits) & 3u)) return WHTQ_EALIGN;
+  if (tokens == 0 || rows == 0) return WHTQ_OK;
+  st = need_device();
+  if (st != WHTQ_OK) return st;
+  return hip_status(launch_rht_gemv(logn, bits, logg, x, tokens, ldx, codes, scales, rows, sign_bits, y, ldy,
+                                    (hipStream_t)stream));
 }
 
 whtq_status qwha_adapter_forward(const void* x, whtq_dtype x_dtype, int64_t tokens, int64_t d_in,

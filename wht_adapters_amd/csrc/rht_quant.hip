@@ -1,5 +1,6 @@
-// Dispatch of rht_quantize_rtn / rht_dequantize_inverse over the code width;
-// the kernels live in rht_quant.hpp, instantiated per width in rq_*_b*.hip.
+// Dispatch of rht_quantize_rtn / rht_dequantize_inverse / rht_lowbit_gemv over
+// the code width; the kernels live in rht_quant.hpp (instantiated per width in
+// rq_*_b*.hip) and rht_gemv.hpp (rg_b*.hip).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -19,6 +20,13 @@ extern template hipError_t launch_rht_dequant_bits<2>(int, int, int, const uint8
 extern template hipError_t launch_rht_dequant_bits<3>(int, int, int, const uint8_t*, const uint16_t*, int64_t, const uint32_t*, void*, int64_t, hipStream_t);
 extern template hipError_t launch_rht_dequant_bits<4>(int, int, int, const uint8_t*, const uint16_t*, int64_t, const uint32_t*, void*, int64_t, hipStream_t);
 
+template <int BITS>
+hipError_t launch_rht_gemv_bits(int logn, int logg, const void* x, int64_t tokens, int64_t ldx,
+                                const uint8_t* codes, const uint16_t* scales, int64_t rows, const uint32_t* sb,
+                                void* y, int64_t ldy, hipStream_t s);
+extern template hipError_t launch_rht_gemv_bits<2>(int, int, const void*, int64_t, int64_t, const uint8_t*, const uint16_t*, int64_t, const uint32_t*, void*, int64_t, hipStream_t);
+extern template hipError_t launch_rht_gemv_bits<4>(int, int, const void*, int64_t, int64_t, const uint8_t*, const uint16_t*, int64_t, const uint32_t*, void*, int64_t, hipStream_t);
+
 hipError_t launch_rht_quant(int logn, int din, int bits, int logg, const void* w, int64_t rows,
                             int64_t ldw, const uint32_t* sb, uint8_t* codes, uint16_t* scales,
                             hipStream_t s) {
@@ -37,6 +45,16 @@ hipError_t launch_rht_dequant(int logn, int dout, int bits, int logg, const uint
     case 2: return launch_rht_dequant_bits<2>(logn, dout, logg, codes, scales, rows, sb, out, ldo, s);
     case 3: return launch_rht_dequant_bits<3>(logn, dout, logg, codes, scales, rows, sb, out, ldo, s);
     case 4: return launch_rht_dequant_bits<4>(logn, dout, logg, codes, scales, rows, sb, out, ldo, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_rht_gemv(int logn, int bits, int logg, const void* x, int64_t tokens, int64_t ldx,
+                           const uint8_t* codes, const uint16_t* scales, int64_t rows, const uint32_t* sb,
+                           void* y, int64_t ldy, hipStream_t s) {
+  switch (bits) {
+    case 2: return launch_rht_gemv_bits<2>(logn, logg, x, tokens, ldx, codes, scales, rows, sb, y, ldy, s);
+    case 4: return launch_rht_gemv_bits<4>(logn, logg, x, tokens, ldx, codes, scales, rows, sb, y, ldy, s);
   }
   return hipErrorInvalidValue;
 }

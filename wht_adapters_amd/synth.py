@@ -148,6 +148,7 @@ WORKLOADS = {
     "harp_8192x4096_r16x3": "HARP: RHT + three radix-16 stages, 8192 tokens x 4096",
     "harp_8192x5120_r88852": "HARP general schedule 8*8*8*5*2, 8192 tokens x 5120 (no preconditioning)",
     "rht_int2_g64_28672x8192": "RHT + INT2 RTN g=64, bf16 28672 x 8192 Student-t weights",
+    "gemv_int2_g64_28672x8192_t1": "online-RHT INT2 g=64 product, 28672 x 8192 codes, one decode token",
 }
 
 
@@ -211,3 +212,27 @@ def harp(tokens=8192, d=4096, radices=(16, 16, 16), outlier_frac=0.005, factor=3
     blocks = [orthogonal_blocks(rng_b, d // b, b) for b in radices]
     return {"x": to_bf16(x), "signs": rademacher_mask(4, 2, d),
             "radices": list(radices), "blocks": blocks, "outlier_channels": ch}
+
+
+def lowbit_layer(cfg, rows, n, bits, group, tokens, scale_lo=0.002, scale_hi=0.05,
+                 outlier_frac=0.005, factor=30.0):
+    """A stored low-bit layer and decode activations for the online-RHT
+    product: codes are uniform random bytes (every b-bit field value occurs,
+    including the most negative one, which the quantiser never writes), fp16
+    scales log-uniform in [scale_lo, scale_hi], activations N(0,1) with a
+    fraction of channels x factor (the HARP activation recipe) -> bf16, and a
+    Rademacher sign vector.  Streams (cfg, 0..3)."""
+    codes = child_rng(cfg, 0).integers(0, 256, size=(rows, n * bits // 8), dtype=np.uint8)
+    lg = child_rng(cfg, 1).uniform(np.log(scale_lo), np.log(scale_hi), size=(rows, n // group))
+    scales = np.exp(lg).astype(np.float16)
+    x = gaussian_rows(child_rng(cfg, 2), tokens, n)
+    ch = child_rng(cfg, 3).choice(n, int(round(outlier_frac * n)), replace=False)
+    x[:, ch] *= factor
+    return {"x": to_bf16(x), "codes": codes, "scales": scales, "signs": rademacher_mask(cfg, 4, n),
+            "bits": bits, "group": group}
+
+
+def gemv_int2_g64(rows=28672, n=8192, tokens=1):
+    """Workload 7: decode through the 28672 x 8192 INT2 g=64 layer of workload 5."""
+    return lowbit_layer(7, rows, n, 2, 64, tokens)
+

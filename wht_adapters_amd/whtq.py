@@ -34,6 +34,7 @@ _SIG = {
                                     _i64, _vp],
     "qwha_adapter_grad_values": [_vp, _vp, _int, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64,
                                  _vp],
+    "rht_lowbit_gemv": [_vp, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _int, _int, _vp, _i64, _vp],
 }
 for _name, _args in _SIG.items():
     _f = getattr(_lib, _name)
@@ -160,6 +161,35 @@ def rht_dequantize_inverse(codes, scales, signs, bits, group, n, out=None, out_d
         _check("rht_dequantize_inverse", _lib.rht_dequantize_inverse(
             _ptr(codes), _ptr(scales), rows, n, _sign_ptr(signs, n, codes.device), bits, group,
             _ptr(out), _DT[out.dtype], ldo, _stream(codes)))
+    return out
+
+
+def rht_lowbit_gemv(x, codes, scales, signs, bits, group, out=None):
+    """y = x W_hat^T for W_hat the rows rht_dequantize_inverse would decode from
+    (codes, scales); x [tokens, n] bf16, y [tokens, rows] bf16."""
+    _need_cuda("x", x)
+    tokens, n, ldx = _rows_ld("x", x)
+    rows = codes.shape[0]
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bfloat16")
+    if codes.dtype != torch.uint8 or scales.dtype != torch.float16:
+        raise ValueError("codes must be uint8 and scales float16")
+    if codes.shape != (rows, n * bits // 8) or scales.shape != (rows, n // group):
+        raise ValueError("codes / scales shape mismatch")
+    if not (codes.is_contiguous() and scales.is_contiguous()):
+        raise ValueError("codes and scales must be contiguous")
+    if codes.device != x.device or scales.device != x.device:
+        raise ValueError("x, codes and scales must be on one device")
+    if out is None:
+        out = torch.empty((tokens, rows), dtype=torch.bfloat16, device=x.device)
+    _need_cuda("out", out)
+    t2, r2, ldy = _rows_ld("out", out)
+    if (t2, r2) != (tokens, rows) or out.dtype != torch.bfloat16:
+        raise ValueError("out must be bfloat16 [tokens, rows]")
+    with torch.cuda.device(x.device):
+        _check("rht_lowbit_gemv", _lib.rht_lowbit_gemv(
+            _ptr(x), tokens, ldx, _ptr(codes), _ptr(scales), rows, n, _sign_ptr(signs, n, x.device),
+            bits, group, _ptr(out), ldy, _stream(x)))
     return out
 
 
