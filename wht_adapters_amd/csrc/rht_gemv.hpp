@@ -8,17 +8,21 @@
 //     y[t][o] = sum_k q[o][k] s[o][k / g] xr_t[k],   xr_t = Hn (S x_t),
 // so the weights are read once, as codes, and never rotated back.
 //
-// One persistent block of eight waves per CU:
-//  1. every wave issues the loads of its first weight row;
-//  2. xr_t by a 256-thread FWHT per token (V = n / 256 values per lane:
-//     register and quad-DPP butterflies, one LDS transpose, another round of
-//     register and DPP butterflies); the DPP butterflies leave a sign on
-//     known index bits (RHO), folded in at step 3;
-//  3. a power-of-two sigma_t puts max |H S x_t| in [2^14, 2^15) (the 1/sqrt(n)
-//     of Hn is applied to the fp32 result); the values
-//     are rounded to fp16, each divided by 2^(bits pos) (step 4), and stored
-//     in LDS in the order the lanes consume them; every wave copies them into
-//     registers (n / 128 per token) and forms its per-group constants;
+// One persistent block per CU:
+//  1. the token rows are loaded first, then every wave puts its first PF
+//     weight rows in flight (loads complete in order, so the transform below
+//     does not wait for the weights);
+//  2. H S x_t by 4096-point jobs of 256 threads (16 values per lane:
+//     register and quad-DPP butterflies, one LDS transpose, another round);
+//     n = 8192 splits a token on its top index bit into the jobs lo + hi
+//     and lo - hi.  The DPP butterflies leave a sign on known index bits
+//     (RHO), folded in at step 3;
+//  3. a power-of-two sigma_t keeps max |H S x_t| below 2^15, from a bound
+//     known after the first round (the 1/sqrt(n) of Hn is applied to the
+//     fp32 result); the values are rounded
+//     to fp16, each divided by 2^(bits pos) (step 4), and stored in LDS in the
+//     order the lanes consume them; every wave copies them into registers
+//     (n / 128 per token) and forms its per-group constants;
 //  4. weight rows: lane l takes the 16-byte chunks l, l + 64, ... of a row.
 //     A code word with its sign bits flipped holds u = q + 2^(bits-1); one
 //     and-or onto 0x6400 (fp16 1024.0, ulp 1) turns two fields that sit at
@@ -36,29 +40,25 @@
 namespace whtq {
 
 namespace gv {
-constexpr int WAVES = 8;
-constexpr int THREADS = 64 * WAVES;
-constexpr int GT = 256;    // threads of one token's FWHT
-constexpr int NGRP = THREADS / GT;
+constexpr int GT = 256;  // threads of one 4096-point transform job
+constexpr int PF = 2;    // weight rows in flight per wave while one is consumed
+// LDS slot of transform index i: 4 floats per 32 keep the 16-byte round-1
+// writes conflict-free, 16 more per 1024 the round-2 reads
+__host__ __device__ constexpr int pos(int i) { return i + ((i >> 5) << 2) + ((i >> 10) << 4); }
 }  // namespace gv
 
-template <int LOGN>
-struct GvGeo {
-  static constexpr int N = 1 << LOGN;
-  static constexpr int LOGV = LOGN - 8;        // FWHT values per thread: 2^4 or 2^5
-  static constexpr int V = 1 << LOGV;
-  static constexpr int B1 = LOGV + 2;          // index bits of round 1 (registers + quad)
-  static constexpr int R2 = LOGN - B1 - LOGV;  // lane bits of round 2 (1 or 2)
+// A 4096-point transform job: 256 threads x 16 values.
+struct GvJob {
+  static constexpr int LOGN = 12, N = 4096;
+  static constexpr int LOGV = 4, V = 16;
+  static constexpr int B1 = 6;  // index bits of round 1 (4 registers + 2 quad)
+  static constexpr int R2 = 2;  // lane bits of round 2
   // index bits whose butterflies ran over DPP (upper lane negated)
-  static constexpr unsigned RHO = (3u << LOGV) | (((1u << R2) - 1u) << (B1 + LOGV));
-  // LDS slot of index i: 4 floats per 32 keep the 16-byte round-1 writes
-  // conflict-free, a shift of 64 / 2^R2 banks per round-2 lane block the
-  // round-2 reads
-  __host__ __device__ static constexpr int pos(int i) {
-    return i + ((i >> 5) << 2) + ((i >> (LOGN - R2)) << (6 - R2));
-  }
-  static constexpr int SCR = (pos(N - 1) + 4) & ~3;  // floats per token slot
-  static constexpr int NV = N / 128;                 // fp16-pair registers per token
+  static constexpr unsigned RHO = (3u << 4) | (3u << 10);
+  __host__ __device__ static constexpr int pos(int i) { return gv::pos(i); }
+  static constexpr int SCR = (gv::pos(N - 1) + 4) & ~3;
+  // round-2 index of (thread g, register r)
+  __device__ static int idx2(int g, int r) { return (g >> 2) | (r << 6) | ((g & 3) << 10); }
 };
 
 template <int BITS>
@@ -72,6 +72,24 @@ struct GvCode {
   static constexpr uint32_t FLIP = BITS == 2 ? 0xaaaaaaaau : 0x88888888u;
   static constexpr int OFF = 1 << (BITS - 1);
   __host__ __device__ static constexpr int pos_of(int p) { return p < POSMAX ? p : p - POSMAX; }
+  // fp16 bits of 1024 + OFF 2^(BITS pos), the weight of h in the constant part
+  __host__ __device__ static constexpr uint32_t kbits(int p) {
+    return 0x6400u + (uint32_t)(OFF << (BITS * pos_of(p)));
+  }
+};
+
+template <int LOGN, int BITS, int TT>
+struct GvShape {
+  static constexpr int N = 1 << LOGN;
+  static constexpr int NV = N / 128;            // fp16-pair registers per token
+  static constexpr int CPL = N * BITS / 8192;   // 16-byte code chunks per lane per row
+  static constexpr int HALVES = N / 4096;
+  static constexpr int JOBS = TT * HALVES;
+  // 16 waves (4 per SIMD, at most 128 VGPRs) for one token with at most two
+  // chunks per lane; more tokens or chunks take the registers of 8 waves
+  static constexpr int WAVES = TT == 1 && CPL <= 2 ? 16 : 8;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int NGRP = THREADS / gv::GT;  // jobs at a time
 };
 
 // Sum over the 64 lanes; the result is read from lane 63.
@@ -94,38 +112,91 @@ __device__ __forceinline__ float gv_wave_max(float v) {
 // x [tn][ldx] bf16 (tn <= TT tokens of this pass), codes [rows][n bits / 8],
 // scales [rows][n / g] fp16 bits, y [tn][ldy] bf16.
 template <int LOGN, int BITS, int GPC, int TT>
-__global__ __launch_bounds__(gv::THREADS) void k_rht_gemv(const uint16_t* __restrict__ x, int tn, int64_t ldx,
-                                                          const uint8_t* __restrict__ codes,
-                                                          const uint16_t* __restrict__ scales, int64_t rows,
-                                                          int logg, const uint32_t* __restrict__ sbits,
-                                                          uint16_t* __restrict__ y, int64_t ldy) {
-  using G = GvGeo<LOGN>;
+__global__ __launch_bounds__((GvShape<LOGN, BITS, TT>::THREADS)) void k_rht_gemv(
+    const uint16_t* __restrict__ x, int tn, int64_t ldx, const uint8_t* __restrict__ codes,
+    const uint16_t* __restrict__ scales, int64_t rows, int logg, const uint32_t* __restrict__ sbits,
+    uint16_t* __restrict__ y, int64_t ldy, int64_t lastq, int64_t lastr) {
+  using J = GvJob;
   using C = GvCode<BITS>;
-  constexpr int N = G::N, V = G::V, NV = G::NV;
-  constexpr int CPL = N * BITS / 8192;  // 16-byte chunks per lane per row
-  constexpr int RB = N * BITS / 8;      // bytes per code row
+  using S = GvShape<LOGN, BITS, TT>;
+  constexpr int N = S::N, NV = S::NV, V = J::V, WAVES = S::WAVES, NGRP = S::NGRP;
+  constexpr int PF = gv::PF;
+  constexpr int CPL = S::CPL;
+  constexpr int RB = N * BITS / 8;                 // bytes per code row
   constexpr float RSQRTN = LOGN == 12 ? 0.015625f : 0.011048543456039806f;  // 1 / sqrt(n)
   static_assert(CPL >= 1 && NV == CPL * 4 * C::HALF, "lane layout");
   static_assert(GPC == 1 || GPC == 2 || GPC == 4, "scale groups per chunk");
+  static_assert(NGRP % S::HALVES == 0, "a token's jobs run in one round");
 
-  __shared__ __align__(16) float scr[gv::NGRP][G::SCR];
+  __shared__ __align__(16) float scr[NGRP][J::SCR];
   __shared__ __align__(16) uint32_t hl[TT][NV / 4][64][4];
-  __shared__ float red[gv::NGRP][4];
+  __shared__ float red[NGRP][4];
   __shared__ float sig_inv[TT];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ng = (int)(N >> logg);  // scale groups per row
+  const int grp = wave / (gv::GT / 64), g = tid % gv::GT;
 
-  // ---- 1. first weight row in flight
+  // ---- 1. token rows, then the first weight rows
+  float v[V];
+  struct XRaw {
+    u32x4 a[V / 8], b[V / 8];
+    uint32_t sa, sb;
+  };
+  // loads of a job's inputs (issued ahead of the weight rows) ...
+  auto load_job = [&](int round, XRaw& xr) {
+    const int jb = round * NGRP + grp, ts = jb / S::HALVES;
+    if (jb >= S::JOBS || ts >= tn) return;
+    const uint16_t* xp = x + ts * ldx + g * V;
+#pragma unroll
+    for (int q = 0; q < V / 8; ++q) xr.a[q] = ldg<u32x4>(xp + 8 * q);
+    if constexpr (S::HALVES == 2) {
+#pragma unroll
+      for (int q = 0; q < V / 8; ++q) xr.b[q] = ldg<u32x4>(xp + 4096 + 8 * q);
+    }
+    // raw sign words, unconditional (kNoSigns stands in for no signs)
+    const uint32_t* sp = sbits ? sbits : kNoSigns;
+    xr.sa = sp[g >> 1];
+    if constexpr (S::HALVES == 2) xr.sb = sp[128 + (g >> 1)];
+  };
+  // ... and the job's first values: signs, then lo + hi or lo - hi
+  auto start_job = [&](int round, const XRaw& xr) {
+    const int jb = round * NGRP + grp, ts = jb / S::HALVES, half = jb % S::HALVES;
+    if (jb >= S::JOBS) return;
+    if (ts >= tn) {
+#pragma unroll
+      for (int r = 0; r < V; ++r) v[r] = 0.f;
+      return;
+    }
+    const uint32_t sa = xr.sa >> (16 * (g & 1));
+    const uint32_t sb = S::HALVES == 2 ? xr.sb >> (16 * (g & 1)) : 0u;
+#pragma unroll
+    for (int r = 0; r < V; ++r) {
+      const uint32_t wa = xr.a[r / 8][(r % 8) / 2];
+      const float xa = as_f(((r & 1) ? (wa & 0xffff0000u) : (wa << 16)) ^ (((sa >> r) & 1u) << 31));
+      if constexpr (S::HALVES == 2) {
+        const uint32_t wb = xr.b[r / 8][(r % 8) / 2];
+        const float xb = as_f(((r & 1) ? (wb & 0xffff0000u) : (wb << 16)) ^ (((sb >> r) & 1u) << 31));
+        v[r] = half ? xa - xb : xa + xb;
+      } else {
+        v[r] = xa;
+      }
+    }
+  };
+  XRaw xr0;
+  load_job(0, xr0);
+
   struct Row {
     u32x4 cw[CPL];
     uint32_t sc[CPL][GPC == 4 ? 2 : 1];
   };
+  const uint32_t loff = (uint32_t)lane * 16u;
   auto fetch = [&](Row& r, int64_t o) {
     const uint8_t* cr = codes + o * RB;
     const uint16_t* sr = scales + o * ng;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) r.cw[j] = ldg<u32x4>(cr + (j * 64 + lane) * 16);
+    for (int j = 0; j < CPL; ++j) r.cw[j] = ldg<u32x4>(cr + j * 1024 + loff);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const int first = ((j * 64 + lane) * C::CC) >> logg;
@@ -138,101 +209,94 @@ __global__ __launch_bounds__(gv::THREADS) void k_rht_gemv(const uint16_t* __rest
       }
     }
   };
-  const int64_t tw = (int64_t)gridDim.x * gv::WAVES;
-  int64_t o = (int64_t)blockIdx.x * gv::WAVES + wave;
-  Row cur;
-  fetch(cur, o < rows ? o : rows - 1);
+  const int64_t tw = (int64_t)gridDim.x * WAVES;
+  int64_t o = (int64_t)blockIdx.x * WAVES + wave;
+  constexpr int NS = PF + 1;  // ring slots: PF rows in flight while one is consumed
+  Row buf[NS];                // slot k % NS holds row o + k tw
+  // Look-ahead loads past the end re-read the wave's own last row (an L2
+  // hit, different for every wave): unconditional loads keep the in-order
+  // wait counts exact, and clamping to one shared row would make every wave
+  // hit the same addresses.
+  // last = the largest row below rows that is o mod tw (host: lastq = (rows - 1) / tw * tw,
+  // lastr = (rows - 1) % tw)
+  const int64_t last = o >= rows ? rows - 1 : o + (o <= lastr ? lastq : lastq - tw);
+#pragma unroll
+  for (int k = 0; k < PF; ++k) fetch(buf[k], o + k * tw < rows ? o + k * tw : last);
+  start_job(0, xr0);
 
-  // ---- 2./3. rotated activations
-  const int grp = tid / gv::GT, g = tid % gv::GT;
+  // ---- 2./3. rotated tokens
 #pragma unroll
-  for (int tb = 0; tb < TT; tb += gv::NGRP) {
-    const int ts = tb + grp;
-    const bool act = ts < TT;  // uniform per wave
-    float v[V];
+  for (int round = 0; round * NGRP < S::JOBS; ++round) {
+    const int jb = round * NGRP + grp, ts = jb / S::HALVES, half = jb % S::HALVES;
+    const bool act = jb < S::JOBS;  // uniform per wave
     float* sc = scr[grp];
+    if (round > 0) {
+      XRaw xr;
+      load_job(round, xr);
+      start_job(round, xr);
+    }
     if (act) {
-      if (ts < tn) {
-        const uint16_t* xr = x + ts * ldx + g * V;
-#pragma unroll
-        for (int q = 0; q < V / 8; ++q) {
-          const u32x4 w = ldg<u32x4>(xr + 8 * q);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[8 * q + 2 * e] = bf16lo(w[e]);
-            v[8 * q + 2 * e + 1] = bf16hi(w[e]);
-          }
-        }
-        if (sbits) {
-          const uint32_t sw = V == 32 ? sbits[g] : sbits[g >> 1] >> (16 * (g & 1));
-#pragma unroll
-          for (int r = 0; r < V; ++r) v[r] = as_f(as_u(v[r]) ^ (((sw >> r) & 1u) << 31));
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < V; ++r) v[r] = 0.f;
-      }
-      if constexpr (G::LOGV > 0) reg_stage<V, 0>(v);
-      if constexpr (G::LOGV > 1) reg_stage<V, 1>(v);
-      if constexpr (G::LOGV > 2) reg_stage<V, 2>(v);
-      if constexpr (G::LOGV > 3) reg_stage<V, 3>(v);
-      if constexpr (G::LOGV > 4) reg_stage<V, 4>(v);
+      reg_stage<V, 0>(v);
+      reg_stage<V, 1>(v);
+      reg_stage<V, 2>(v);
+      reg_stage<V, 3>(v);
       lane_stage<V, 0>(v, g);
       lane_stage<V, 1>(v, g);
+      float m = 0.f;
 #pragma unroll
       for (int r = 0; r < V; r += 4)
-        *reinterpret_cast<f32x4*>(sc + G::pos(g * V + r)) = f32x4{v[r], v[r + 1], v[r + 2], v[r + 3]};
-    }
-    __syncthreads();
-    auto idx2 = [&](int r) {
-      return (g >> G::R2) | (r << G::B1) | ((g & ((1 << G::R2) - 1)) << (G::B1 + G::LOGV));
-    };
-    if (act) {
-#pragma unroll
-      for (int r = 0; r < V; ++r) v[r] = sc[G::pos(idx2(r))];
-      if constexpr (G::LOGV > 0) reg_stage<V, 0>(v);
-      if constexpr (G::LOGV > 1) reg_stage<V, 1>(v);
-      if constexpr (G::LOGV > 2) reg_stage<V, 2>(v);
-      if constexpr (G::LOGV > 3) reg_stage<V, 3>(v);
-      if constexpr (G::LOGV > 4) reg_stage<V, 4>(v);
-      lane_stage<V, 0>(v, g);
-      if constexpr (G::R2 == 2) lane_stage<V, 1>(v, g);
-      float m = 0.f;
+        *reinterpret_cast<f32x4*>(sc + J::pos(g * V + r)) = f32x4{v[r], v[r + 1], v[r + 2], v[r + 3]};
 #pragma unroll
       for (int r = 0; r < V; ++r) m = fmaxf(m, fabsf(v[r]));
       m = gv_wave_max(m);
-      if (lane == 0) red[grp][(g >> 6)] = m;
+      if (lane == 0) red[grp][g >> 6] = m;
     }
     __syncthreads();
     if (act) {
-      const float mx = fmaxf(fmaxf(red[grp][0], red[grp][1]), fmaxf(red[grp][2], red[grp][3]));
-      // sigma = 2^(14 - e) with max = f 2^e, f in [1, 2); 1 for an all-zero
-      // or non-finite token
-      // (at most 2^126, so that 1 / sigma stays a normal fp32 number)
+#pragma unroll
+      for (int r = 0; r < V; ++r) v[r] = sc[J::pos(J::idx2(g, r))];
+      reg_stage<V, 0>(v);
+      reg_stage<V, 1>(v);
+      reg_stage<V, 2>(v);
+      reg_stage<V, 3>(v);
+      lane_stage<V, 0>(v, g);
+      lane_stage<V, 1>(v, g);
+      // The six butterfly levels of round 2 at most double a magnitude each,
+      // so max |H S x_t| <= 2^6 m1 with m1 the largest value after round 1.
+      // sigma = 2^(8 - e) with m1 = f 2^e, f in [1, 2), keeps every value
+      // below 2^15; fp16 keeps 11 bits of each value whatever the scale, so
+      // a loose bound only narrows the range of values that stay normal.
+      // At most 2^126, so that 1 / sigma is a normal fp32 number; 1 for an
+      // all-zero or non-finite token.
+      float mx = 0.f;
+      const int g0 = grp - half;  // the token's first job in this round
+#pragma unroll
+      for (int hh = 0; hh < S::HALVES; ++hh)
+        mx = fmaxf(mx, fmaxf(fmaxf(red[g0 + hh][0], red[g0 + hh][1]), fmaxf(red[g0 + hh][2], red[g0 + hh][3])));
       int e = 0;
       const bool fin = mx > 0.f && __builtin_isfinite(mx);
       if (fin) e = ((int)((as_u(mx) >> 23) & 0xffu)) - 127;
-      const int se = fin ? (14 - e < 126 ? 14 - e : 126) : 0;
+      const int se = fin ? (8 - e < 126 ? 8 - e : 126) : 0;
       uint16_t* hh = reinterpret_cast<uint16_t*>(&hl[ts][0][0][0]);
 #pragma unroll
       for (int r = 0; r < V; ++r) {
-        const int i = idx2(r);
-        const int c = i / C::CC, rem = i % C::CC;
+        const int i = J::idx2(g, r);
+        const int k = half * 4096 + i;  // code position
+        const int c = k / C::CC, rem = k % C::CC;
         const int l = c & 63, j = c >> 6;
         const int w = rem / C::CPW, f = rem % C::CPW;
-        const int half = f / C::HALF, p = f % C::HALF;
+        const int hs = f / C::HALF, p = f % C::HALF;
         const int vr = (j * 4 + w) * C::HALF + p;
-        const int pp = p < C::POSMAX ? p : p - C::POSMAX;
-        const float sgn = (__builtin_popcount((unsigned)i & G::RHO) & 1) ? -1.f : 1.f;
-        const float hv = ldexpf(v[r] * sgn, se - BITS * pp);
-        hh[(((vr >> 2) * 64 + l) * 4 + (vr & 3)) * 2 + half] = __builtin_bit_cast(uint16_t, (_Float16)hv);
+        const float sgn = (__builtin_popcount((unsigned)i & J::RHO) & 1) ? -1.f : 1.f;
+        const float hv = ldexpf(v[r] * sgn, se - BITS * C::pos_of(p));
+        hh[(((vr >> 2) * 64 + l) * 4 + (vr & 3)) * 2 + hs] = __builtin_bit_cast(uint16_t, (_Float16)hv);
       }
-      if (g == 0) sig_inv[ts] = ldexpf(1.f, -se);
+      if (g == 0 && half == 0) sig_inv[ts] = ldexpf(1.f, -se);
     }
     __syncthreads();
   }
 
-  // every wave's copy of the rotated activations, and its constants
+  // every wave's copy of the rotated tokens, and its constants
   uint32_t h[TT][NV];
   float corr[TT][CPL][GPC];
   float sinv[TT];
@@ -251,41 +315,38 @@ __global__ __launch_bounds__(gv::THREADS) void k_rht_gemv(const uint16_t* __rest
     for (int j = 0; j < CPL; ++j)
 #pragma unroll
       for (int gp = 0; gp < GPC; ++gp) {
-        float a = 0.f;
+        float a0 = 0.f, a1 = 0.f;
 #pragma unroll
         for (int w = gp * 4 / GPC; w < (gp + 1) * 4 / GPC; ++w)
 #pragma unroll
           for (int p = 0; p < C::HALF; ++p) {
+            const uint32_t kb = C::kbits(p) * 0x10001u;
             const f16x2_t hp = __builtin_bit_cast(f16x2_t, h[t][(j * 4 + w) * C::HALF + p]);
-            const float k = (float)(1024 + C::OFF * (1 << (BITS * C::pos_of(p))));
-            a = fmaf((float)hp[0], k, a);
-            a = fmaf((float)hp[1], k, a);
+            if (p & 1) a1 = __builtin_amdgcn_fdot2(hp, __builtin_bit_cast(f16x2_t, kb), a1, false);
+            else a0 = __builtin_amdgcn_fdot2(hp, __builtin_bit_cast(f16x2_t, kb), a0, false);
           }
-        corr[t][j][gp] = a;
+        corr[t][j][gp] = a0 + a1;
       }
   }
 
-  // ---- 4. weight rows
+  // ---- 4. weight rows, PF of each wave in flight
   uint32_t magic = 0x64006400u;
   asm volatile("" : "+v"(magic));
-  for (; o < rows; o += tw) {
-    Row nxt;
-    const int64_t on = o + tw;
-    fetch(nxt, on < rows ? on : rows - 1);
+  auto row_dot = [&](const Row& r, int64_t orow) {
     float ya[TT];
 #pragma unroll
     for (int t = 0; t < TT; ++t) ya[t] = 0.f;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-      float acc[TT][GPC];
+      float acc[TT][GPC][2];
 #pragma unroll
       for (int t = 0; t < TT; ++t)
 #pragma unroll
-        for (int gp = 0; gp < GPC; ++gp) acc[t][gp] = 0.f;
+        for (int gp = 0; gp < GPC; ++gp) acc[t][gp][0] = acc[t][gp][1] = 0.f;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const int gp = w * GPC / 4;
-        const uint32_t u = cur.cw[j][w] ^ C::FLIP;
+        const uint32_t u = r.cw[j][w] ^ C::FLIP;
         const uint32_t u2 = u >> C::SHIFT;
 #pragma unroll
         for (int p = 0; p < C::HALF; ++p) {
@@ -293,36 +354,47 @@ __global__ __launch_bounds__(gv::THREADS) void k_rht_gemv(const uint16_t* __rest
           const uint32_t b = ((p < C::POSMAX ? u : u2) & mask) | magic;
 #pragma unroll
           for (int t = 0; t < TT; ++t)
-            acc[t][gp] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, b),
-                                                __builtin_bit_cast(f16x2_t, h[t][(j * 4 + w) * C::HALF + p]),
-                                                acc[t][gp], false);
+            acc[t][gp][p & 1] = __builtin_amdgcn_fdot2(
+                __builtin_bit_cast(f16x2_t, b), __builtin_bit_cast(f16x2_t, h[t][(j * 4 + w) * C::HALF + p]),
+                acc[t][gp][p & 1], false);
         }
       }
 #pragma unroll
       for (int gp = 0; gp < GPC; ++gp) {
-        const uint32_t sw = GPC == 1 ? cur.sc[j][0] : cur.sc[j][gp >> 1] >> (16 * (gp & 1));
+        const uint32_t sw = GPC == 1 ? r.sc[j][0] : r.sc[j][gp >> 1] >> (16 * (gp & 1));
         const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(sw & 0xffffu));
 #pragma unroll
-        for (int t = 0; t < TT; ++t) ya[t] = fmaf(s, acc[t][gp] - corr[t][j][gp], ya[t]);
+        for (int t = 0; t < TT; ++t)
+          ya[t] = fmaf(s, (acc[t][gp][0] - corr[t][j][gp]) + acc[t][gp][1], ya[t]);
       }
     }
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
       const float tot = gv_wave_sum(ya[t]) * RSQRTN * sinv[t];
-      if (t < tn && lane == 0) y[t * ldy + o] = __builtin_bit_cast(uint16_t, (__bf16)tot);
+      if (t < tn && lane == 0) y[t * ldy + orow] = __builtin_bit_cast(uint16_t, (__bf16)tot);
     }
-    cur = nxt;
+  };
+  // the row PF tw further on goes out before each row is consumed
+  for (; o < rows; o += NS * tw) {
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const int64_t ok = o + k * tw, onext = ok + PF * tw;
+      fetch(buf[(k + PF) % NS], onext < rows ? onext : last);
+      if (ok < rows) row_dot(buf[k], ok);
+    }
   }
 }
 
 template <int LOGN, int BITS, int GPC, int TT>
 static hipError_t run_gemv(const void* x, int tn, int64_t ldx, const uint8_t* codes, const uint16_t* scales,
                            int64_t rows, int logg, const uint32_t* sb, void* y, int64_t ldy, hipStream_t s) {
+  using S = GvShape<LOGN, BITS, TT>;
   auto k = k_rht_gemv<LOGN, BITS, GPC, TT>;
-  // one block per CU: every block rotates the activations itself
-  const unsigned grid = persistent_grid((rows + gv::WAVES - 1) / gv::WAVES, 1);
-  hipLaunchKernelGGL(k, dim3(grid), dim3(gv::THREADS), 0, s, (const uint16_t*)x, tn, ldx, codes, scales, rows,
-                     logg, sb, (uint16_t*)y, ldy);
+  // one block per CU: every block rotates the tokens itself
+  const unsigned grid = persistent_grid((rows + S::WAVES - 1) / S::WAVES, 1);
+  const int64_t tw = (int64_t)grid * S::WAVES;
+  hipLaunchKernelGGL(k, dim3(grid), dim3(S::THREADS), 0, s, (const uint16_t*)x, tn, ldx, codes, scales, rows,
+                     logg, sb, (uint16_t*)y, ldy, (rows - 1) / tw * tw, (rows - 1) % tw);
   return hipGetLastError();
 }
 
@@ -340,8 +412,8 @@ static hipError_t gemv_gpc(const void* x, int tn, int64_t ldx, const uint8_t* co
 }
 
 // Tokens go in passes of up to 4 (n = 4096) or 2 (n = 8192): each pass holds
-// its rotated activations in registers (n / 128 per token) and reads the
-// weights once.
+// its rotated tokens in registers (n / 128 per token) and reads the weights
+// once.
 template <int BITS>
 hipError_t launch_rht_gemv_bits(int logn, int logg, const void* x, int64_t tokens, int64_t ldx,
                                 const uint8_t* codes, const uint16_t* scales, int64_t rows, const uint32_t* sb,
