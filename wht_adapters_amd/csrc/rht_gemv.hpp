@@ -9,29 +9,30 @@
 // so the weights are read once, as codes, and never rotated back.
 //
 // One persistent block per CU:
-//  1. the token rows are loaded first, then every wave puts its first PF
-//     weight rows in flight (loads complete in order, so the transform below
-//     does not wait for the weights);
+//  1. the token rows are requested first, then every wave puts its first
+//     weight row in flight (a CU returns vector loads in order, so the
+//     transform below does not wait for the weights);
 //  2. H S x_t by 4096-point jobs of 256 threads (16 values per lane:
 //     register and quad-DPP butterflies, one LDS transpose, another round);
 //     n = 8192 splits a token on its top index bit into the jobs lo + hi
 //     and lo - hi.  The DPP butterflies leave a sign on known index bits
-//     (RHO), folded in at step 3;
-//  3. a power-of-two sigma_t keeps max |H S x_t| below 2^15, from a bound
-//     known after the first round (the 1/sqrt(n) of Hn is applied to the
-//     fp32 result); the values are rounded
-//     to fp16, each divided by 2^(bits pos) (step 4), and stored in LDS in the
-//     order the lanes consume them; every wave copies them into registers
-//     (n / 128 per token) and forms its per-group constants;
+//     (RHO), folded in when the values go to LDS with the token's maximum;
+//  3. fixed point: a power-of-two sigma_t puts max |H S x_t| sigma_t in
+//     [2^13, 2^14) and X = rint(H S x_t sigma_t) is written as four signed
+//     base-16 digits, X = d0 + 16 d1 + 256 d2 + 4096 d3 (d in [-8, 7]:
+//     the nibbles of ((X + 0x8888) xor 0x8888)).  Digit p of eight codes'
+//     X makes one 32-bit "limb word"; the limb words go to LDS in the order
+//     the lanes consume them and every wave copies them into registers
+//     (n / 128 per token).  The 1/sqrt(n) of Hn and 1/sigma are applied to
+//     the fp32 result;
 //  4. weight rows: lane l takes the 16-byte chunks l, l + 64, ... of a row.
-//     A code word with its sign bits flipped holds u = q + 2^(bits-1); one
-//     and-or onto 0x6400 (fp16 1024.0, ulp 1) turns two fields that sit at
-//     mantissa bit bits * pos into the fp16 pair 1024 + u 2^(bits pos), and
-//     v_dot2_f32_f16 multiplies it by the stored pair xr 2^-(bits pos): two
-//     codes per dot2 and no conversion instruction per code.  The dot's
-//     constant part, sum_k h_k (1024 + 2^(bits-1) 2^(bits pos_k)), depends on
-//     the lane only and is subtracted once per scale group:
-//     y = sum_groups s (acc - corr), summed over the wave by DPP, / sigma.
+//     v_dot8_i32_i4 multiplies eight signed nibbles by eight signed nibbles:
+//     4-bit codes are such nibbles as stored; a word of sixteen 2-bit codes,
+//     its sign bits flipped to offset binary u = q + 2, splits into the even
+//     and odd codes' nibbles with two masks.  One dot8 per limb and eight
+//     codes, exact int32 sums per scale group, acc = sum_p 16^p acc_p minus
+//     2 sum X for the offset, then y += s (float) acc; summed over the wave
+//     by DPP and scaled by 1 / (sigma sqrt(n)).
 #pragma once
 
 #include "io.hpp"
@@ -41,7 +42,7 @@ namespace whtq {
 
 namespace gv {
 constexpr int GT = 256;  // threads of one 4096-point transform job
-constexpr int PF = 2;    // weight rows in flight per wave while one is consumed
+constexpr int PF = 1;    // weight rows in flight per wave while one is consumed
 // LDS slot of transform index i: 4 floats per 32 keep the 16-byte round-1
 // writes conflict-free, 16 more per 1024 the round-2 reads
 __host__ __device__ constexpr int pos(int i) { return i + ((i >> 5) << 2) + ((i >> 10) << 4); }
@@ -63,20 +64,16 @@ struct GvJob {
 
 template <int BITS>
 struct GvCode {
-  static constexpr int CPW = 32 / BITS;     // codes per 32-bit word
-  static constexpr int HALF = CPW / 2;      // pairs per word: fields (p, p + HALF)
-  static constexpr int CC = 4 * CPW;        // codes per 16-byte chunk
-  static constexpr int POSMAX = 10 / BITS;  // fields that fit the fp16 mantissa
-  static constexpr int SHIFT = POSMAX * BITS;
-  static constexpr uint32_t FIELD = (1u << BITS) - 1u;
-  static constexpr uint32_t FLIP = BITS == 2 ? 0xaaaaaaaau : 0x88888888u;
-  static constexpr int OFF = 1 << (BITS - 1);
-  __host__ __device__ static constexpr int pos_of(int p) { return p < POSMAX ? p : p - POSMAX; }
-  // fp16 bits of 1024 + OFF 2^(BITS pos), the weight of h in the constant part
-  __host__ __device__ static constexpr uint32_t kbits(int p) {
-    return 0x6400u + (uint32_t)(OFF << (BITS * pos_of(p)));
-  }
+  static constexpr int CPW = 32 / BITS;    // codes per 32-bit code word
+  static constexpr int CC = 4 * CPW;       // codes per 16-byte chunk
+  static constexpr int SETS = BITS == 2 ? 2 : 1;  // nibble words per code word (even / odd codes)
+  static constexpr int RPW = 4 * SETS;     // limb registers per code word
 };
+
+// LDS slot of code position k in the fixed-point staging rows: 4 floats per
+// 64 and 16 per 1024 keep both the transform's writes and the limb builder's
+// 16-byte reads free of bank conflicts
+__host__ __device__ constexpr int gv_xpos(int k) { return k + ((k >> 6) << 2) + ((k >> 10) << 4); }
 
 template <int LOGN, int BITS, int TT>
 struct GvShape {
@@ -103,6 +100,11 @@ __device__ __forceinline__ float gv_wave_sum(float v) {
   return as_f((uint32_t)__builtin_amdgcn_readlane((int)as_u(v), 63));
 }
 
+// Block barrier for LDS hand-offs only.  __syncthreads() also orders global
+// memory, which makes it wait for every load in flight, the rows streaming
+// into LDS among them; this one waits for the wave's LDS operations alone.
+__device__ __forceinline__ void gv_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ float gv_wave_max(float v) {
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
@@ -124,19 +126,26 @@ __global__ __launch_bounds__((GvShape<LOGN, BITS, TT>::THREADS)) void k_rht_gemv
   constexpr int CPL = S::CPL;
   constexpr int RB = N * BITS / 8;                 // bytes per code row
   constexpr float RSQRTN = LOGN == 12 ? 0.015625f : 0.011048543456039806f;  // 1 / sqrt(n)
-  static_assert(CPL >= 1 && NV == CPL * 4 * C::HALF, "lane layout");
+  static_assert(CPL >= 1 && NV == CPL * 4 * C::RPW, "lane layout");
   static_assert(GPC == 1 || GPC == 2 || GPC == 4, "scale groups per chunk");
   static_assert(NGRP % S::HALVES == 0, "a token's jobs run in one round");
+  constexpr int XT = (gv_xpos(N - 1) + 4) & ~3;  // floats per token staging row
+  constexpr int ITEMS = TT * (N / C::CPW);      // limb builder items: one code word of one token
 
-  __shared__ __align__(16) float scr[NGRP][J::SCR];
+  constexpr int SLOTS = NGRP < S::JOBS ? NGRP : S::JOBS;  // transform jobs per round
+  __shared__ __align__(16) float scr0[SLOTS * J::SCR];  // [SLOTS][SCR] transform scratch
+  __shared__ __align__(16) float xt[TT][XT];
   __shared__ __align__(16) uint32_t hl[TT][NV / 4][64][4];
-  __shared__ float red[NGRP][4];
-  __shared__ float sig_inv[TT];
+  __shared__ int corl[TT][CPL][GPC][64];  // sum of X over a lane's group part (2-bit codes)
+  __shared__ uint32_t tmax[TT];           // max |H S x_t| as float bits
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ng = (int)(N >> logg);  // scale groups per row
   const int grp = wave / (gv::GT / 64), g = tid % gv::GT;
+
+  for (int i = tid; i < TT * CPL * GPC * 64; i += S::THREADS) (&corl[0][0][0][0])[i] = 0;
+  if (tid < TT) tmax[tid] = 0u;
 
   // ---- 1. token rows, then the first weight rows
   float v[V];
@@ -192,22 +201,25 @@ __global__ __launch_bounds__((GvShape<LOGN, BITS, TT>::THREADS)) void k_rht_gemv
     uint32_t sc[CPL][GPC == 4 ? 2 : 1];
   };
   const uint32_t loff = (uint32_t)lane * 16u;
-  auto fetch = [&](Row& r, int64_t o) {
-    const uint8_t* cr = codes + o * RB;
+  auto fetch_sc = [&](uint32_t (&sc)[CPL][GPC == 4 ? 2 : 1], int64_t o) {
     const uint16_t* sr = scales + o * ng;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) r.cw[j] = ldg<u32x4>(cr + j * 1024 + loff);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const int first = ((j * 64 + lane) * C::CC) >> logg;
-      if constexpr (GPC == 1) r.sc[j][0] = sr[first];
-      else if constexpr (GPC == 2) r.sc[j][0] = ldg<uint32_t>(sr + first);
+      if constexpr (GPC == 1) sc[j][0] = sr[first];
+      else if constexpr (GPC == 2) sc[j][0] = ldg<uint32_t>(sr + first);
       else {
         const u32x2 w2 = ldg<u32x2>(sr + first);
-        r.sc[j][0] = w2[0];
-        r.sc[j][1] = w2[1];
+        sc[j][0] = w2[0];
+        sc[j][1] = w2[1];
       }
     }
+  };
+  auto fetch = [&](Row& r, int64_t o) {
+    const uint8_t* cr = codes + o * RB;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) r.cw[j] = ldg<u32x4>(cr + j * 1024 + loff);
+    fetch_sc(r.sc, o);
   };
   const int64_t tw = (int64_t)gridDim.x * WAVES;
   int64_t o = (int64_t)blockIdx.x * WAVES + wave;
@@ -224,12 +236,12 @@ __global__ __launch_bounds__((GvShape<LOGN, BITS, TT>::THREADS)) void k_rht_gemv
   for (int k = 0; k < PF; ++k) fetch(buf[k], o + k * tw < rows ? o + k * tw : last);
   start_job(0, xr0);
 
-  // ---- 2./3. rotated tokens
+  // ---- 2. rotated tokens into the staging rows, with each token's maximum
 #pragma unroll
   for (int round = 0; round * NGRP < S::JOBS; ++round) {
     const int jb = round * NGRP + grp, ts = jb / S::HALVES, half = jb % S::HALVES;
     const bool act = jb < S::JOBS;  // uniform per wave
-    float* sc = scr[grp];
+    float* sc = scr0 + (grp < SLOTS ? grp : 0) * J::SCR;
     if (round > 0) {
       XRaw xr;
       load_job(round, xr);
@@ -242,67 +254,94 @@ __global__ __launch_bounds__((GvShape<LOGN, BITS, TT>::THREADS)) void k_rht_gemv
       reg_stage<V, 3>(v);
       lane_stage<V, 0>(v, g);
       lane_stage<V, 1>(v, g);
-      float m = 0.f;
+      // the slots are affine in r: one base address, immediate offsets
+      float* w1 = sc + J::pos(g * V);  // pos(16 g + r) = pos(16 g) + r for r < 16
 #pragma unroll
       for (int r = 0; r < V; r += 4)
-        *reinterpret_cast<f32x4*>(sc + J::pos(g * V + r)) = f32x4{v[r], v[r + 1], v[r + 2], v[r + 3]};
-#pragma unroll
-      for (int r = 0; r < V; ++r) m = fmaxf(m, fabsf(v[r]));
-      m = gv_wave_max(m);
-      if (lane == 0) red[grp][g >> 6] = m;
+        *reinterpret_cast<f32x4*>(w1 + r) = f32x4{v[r], v[r + 1], v[r + 2], v[r + 3]};
     }
-    __syncthreads();
+    gv_barrier();
     if (act) {
+      const float* r2 = sc + J::pos(J::idx2(g, 0));  // + 72 r: r << 6 adds 64 r + 4 (2 r)
 #pragma unroll
-      for (int r = 0; r < V; ++r) v[r] = sc[J::pos(J::idx2(g, r))];
+      for (int r = 0; r < V; ++r) v[r] = r2[72 * r];
       reg_stage<V, 0>(v);
       reg_stage<V, 1>(v);
       reg_stage<V, 2>(v);
       reg_stage<V, 3>(v);
       lane_stage<V, 0>(v, g);
       lane_stage<V, 1>(v, g);
-      // The six butterfly levels of round 2 at most double a magnitude each,
-      // so max |H S x_t| <= 2^6 m1 with m1 the largest value after round 1.
-      // sigma = 2^(8 - e) with m1 = f 2^e, f in [1, 2), keeps every value
-      // below 2^15; fp16 keeps 11 bits of each value whatever the scale, so
-      // a loose bound only narrows the range of values that stay normal.
-      // At most 2^126, so that 1 / sigma is a normal fp32 number; 1 for an
-      // all-zero or non-finite token.
-      float mx = 0.f;
-      const int g0 = grp - half;  // the token's first job in this round
-#pragma unroll
-      for (int hh = 0; hh < S::HALVES; ++hh)
-        mx = fmaxf(mx, fmaxf(fmaxf(red[g0 + hh][0], red[g0 + hh][1]), fmaxf(red[g0 + hh][2], red[g0 + hh][3])));
-      int e = 0;
-      const bool fin = mx > 0.f && __builtin_isfinite(mx);
-      if (fin) e = ((int)((as_u(mx) >> 23) & 0xffu)) - 127;
-      const int se = fin ? (8 - e < 126 ? 8 - e : 126) : 0;
-      uint16_t* hh = reinterpret_cast<uint16_t*>(&hl[ts][0][0][0]);
+      // RHO's bits (4, 5, 10, 11) come from g alone, so the sign is the thread's;
+      // staging slots are xpos(k0) + 68 r (r << 6 adds 64 r + 4 r, never a 1024 carry)
+      const uint32_t sneg = (__builtin_popcount((unsigned)J::idx2(g, 0) & J::RHO) & 1) << 31;
+      float* w3 = &xt[ts][gv_xpos(half * 4096 + J::idx2(g, 0))];
+      float m = 0.f;
 #pragma unroll
       for (int r = 0; r < V; ++r) {
-        const int i = J::idx2(g, r);
-        const int k = half * 4096 + i;  // code position
-        const int c = k / C::CC, rem = k % C::CC;
-        const int l = c & 63, j = c >> 6;
-        const int w = rem / C::CPW, f = rem % C::CPW;
-        const int hs = f / C::HALF, p = f % C::HALF;
-        const int vr = (j * 4 + w) * C::HALF + p;
-        const float sgn = (__builtin_popcount((unsigned)i & J::RHO) & 1) ? -1.f : 1.f;
-        const float hv = ldexpf(v[r] * sgn, se - BITS * C::pos_of(p));
-        hh[(((vr >> 2) * 64 + l) * 4 + (vr & 3)) * 2 + hs] = __builtin_bit_cast(uint16_t, (_Float16)hv);
+        w3[68 * r] = as_f(as_u(v[r]) ^ sneg);
+        m = fmaxf(m, fabsf(v[r]));
       }
-      if (g == 0 && half == 0) sig_inv[ts] = ldexpf(1.f, -se);
+      m = gv_wave_max(m);
+      if (lane == 0) atomicMax(&tmax[ts], as_u(m));  // non-negative floats order as their bits
     }
-    __syncthreads();
+    gv_barrier();
   }
 
-  // every wave's copy of the rotated tokens, and its constants
+  // ---- 3. limb words: item = one code word (8 or 16 codes) of one token
+  for (int it = tid; it < ITEMS; it += S::THREADS) {
+    const int t = it / (N / C::CPW), k0 = (it % (N / C::CPW)) * C::CPW;
+    const int c = k0 / C::CC, l = c & 63, j = c >> 6, w = (k0 % C::CC) / C::CPW;
+    // sigma = 2^(13 - e) with max = f 2^e, f in [1, 2), at most 2^126 so
+    // that 1 / sigma stays a normal fp32 number; 1 for an all-zero or
+    // non-finite token
+    const float mx = as_f(tmax[t]);
+    int e = 0;
+    const bool fin = mx > 0.f && __builtin_isfinite(mx);
+    if (fin) e = ((int)((as_u(mx) >> 23) & 0xffu)) - 127;
+    const int se = fin ? (13 - e < 126 ? 13 - e : 126) : 0;
+    const float sig = ldexpf(1.f, se);
+    uint32_t z[C::CPW];
+    int xsum = 0;
+#pragma unroll
+    for (int q = 0; q < C::CPW / 4; ++q) {
+      const f32x4 f = *reinterpret_cast<const f32x4*>(&xt[t][gv_xpos(k0 + 4 * q)]);
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int X = (int)__builtin_rintf(f[e4] * sig);
+        xsum += X;
+        z[4 * q + e4] = (uint32_t)((X + 0x8888) ^ 0x8888);  // nibble p = digit p (two's complement)
+      }
+    }
+    uint32_t lw[C::SETS][4];
+#pragma unroll
+    for (int st = 0; st < C::SETS; ++st)
+#pragma unroll
+      for (int pl = 0; pl < 4; ++pl) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) acc |= ((z[C::SETS * m + st] >> (4 * pl)) & 15u) << (4 * m);
+        lw[st][pl] = acc;
+      }
+#pragma unroll
+    for (int st = 0; st < C::SETS; ++st)
+      *reinterpret_cast<u32x4*>(&hl[t][(j * 4 + w) * C::SETS + st][l][0]) =
+          u32x4{lw[st][0], lw[st][1], lw[st][2], lw[st][3]};
+    if constexpr (BITS == 2) atomicAdd(&corl[t][j][w * GPC / 4][l], xsum);
+  }
+  gv_barrier();
+
+  // every wave's copy of the limb words, and its constants
   uint32_t h[TT][NV];
-  float corr[TT][CPL][GPC];
+  int corr[TT][CPL][GPC];
   float sinv[TT];
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
-    sinv[t] = sig_inv[t];
+    const float mx = as_f(tmax[t]);
+    int e = 0;
+    const bool fin = mx > 0.f && __builtin_isfinite(mx);
+    if (fin) e = ((int)((as_u(mx) >> 23) & 0xffu)) - 127;
+    const int se = fin ? (13 - e < 126 ? 13 - e : 126) : 0;
+    sinv[t] = ldexpf(1.f, -se);
 #pragma unroll
     for (int q = 0; q < NV / 4; ++q) {
       const u32x4 w = *reinterpret_cast<const u32x4*>(&hl[t][q][lane][0]);
@@ -314,58 +353,53 @@ __global__ __launch_bounds__((GvShape<LOGN, BITS, TT>::THREADS)) void k_rht_gemv
 #pragma unroll
     for (int j = 0; j < CPL; ++j)
 #pragma unroll
-      for (int gp = 0; gp < GPC; ++gp) {
-        float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-        for (int w = gp * 4 / GPC; w < (gp + 1) * 4 / GPC; ++w)
-#pragma unroll
-          for (int p = 0; p < C::HALF; ++p) {
-            const uint32_t kb = C::kbits(p) * 0x10001u;
-            const f16x2_t hp = __builtin_bit_cast(f16x2_t, h[t][(j * 4 + w) * C::HALF + p]);
-            if (p & 1) a1 = __builtin_amdgcn_fdot2(hp, __builtin_bit_cast(f16x2_t, kb), a1, false);
-            else a0 = __builtin_amdgcn_fdot2(hp, __builtin_bit_cast(f16x2_t, kb), a0, false);
-          }
-        corr[t][j][gp] = a0 + a1;
-      }
+      for (int gp = 0; gp < GPC; ++gp) corr[t][j][gp] = BITS == 2 ? 2 * corl[t][j][gp][lane] : 0;
   }
 
   // ---- 4. weight rows, PF of each wave in flight
-  uint32_t magic = 0x64006400u;
-  asm volatile("" : "+v"(magic));
   auto row_dot = [&](const Row& r, int64_t orow) {
     float ya[TT];
 #pragma unroll
     for (int t = 0; t < TT; ++t) ya[t] = 0.f;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-      float acc[TT][GPC][2];
+      int acc[TT][GPC][4];
 #pragma unroll
       for (int t = 0; t < TT; ++t)
 #pragma unroll
-        for (int gp = 0; gp < GPC; ++gp) acc[t][gp][0] = acc[t][gp][1] = 0.f;
+        for (int gp = 0; gp < GPC; ++gp)
+#pragma unroll
+          for (int pl = 0; pl < 4; ++pl) acc[t][gp][pl] = 0;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const int gp = w * GPC / 4;
-        const uint32_t u = r.cw[j][w] ^ C::FLIP;
-        const uint32_t u2 = u >> C::SHIFT;
+        uint32_t nw[C::SETS];
+        if constexpr (BITS == 2) {
+          const uint32_t u = r.cw[j][w] ^ 0xaaaaaaaau;  // offset binary: u = q + 2
+          nw[0] = u & 0x33333333u;
+          nw[1] = (u >> 2) & 0x33333333u;
+        } else {
+          nw[0] = r.cw[j][w];
+        }
 #pragma unroll
-        for (int p = 0; p < C::HALF; ++p) {
-          const uint32_t mask = (C::FIELD << (BITS * C::pos_of(p))) * 0x10001u;
-          const uint32_t b = ((p < C::POSMAX ? u : u2) & mask) | magic;
+        for (int st = 0; st < C::SETS; ++st)
 #pragma unroll
           for (int t = 0; t < TT; ++t)
-            acc[t][gp][p & 1] = __builtin_amdgcn_fdot2(
-                __builtin_bit_cast(f16x2_t, b), __builtin_bit_cast(f16x2_t, h[t][(j * 4 + w) * C::HALF + p]),
-                acc[t][gp][p & 1], false);
-        }
+#pragma unroll
+            for (int pl = 0; pl < 4; ++pl)
+              acc[t][gp][pl] = __builtin_amdgcn_sdot8((int)nw[st], (int)h[t][((j * 4 + w) * C::SETS + st) * 4 + pl],
+                                                      acc[t][gp][pl], false);
       }
 #pragma unroll
       for (int gp = 0; gp < GPC; ++gp) {
         const uint32_t sw = GPC == 1 ? r.sc[j][0] : r.sc[j][gp >> 1] >> (16 * (gp & 1));
         const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(sw & 0xffffu));
 #pragma unroll
-        for (int t = 0; t < TT; ++t)
-          ya[t] = fmaf(s, (acc[t][gp][0] - corr[t][j][gp]) + acc[t][gp][1], ya[t]);
+        for (int t = 0; t < TT; ++t) {
+          const int a = acc[t][gp][0] + acc[t][gp][1] * 16 + acc[t][gp][2] * 256 + acc[t][gp][3] * 4096 -
+                        corr[t][j][gp];
+          ya[t] = fmaf(s, (float)a, ya[t]);
+        }
       }
     }
 #pragma unroll
