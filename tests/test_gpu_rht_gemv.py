@@ -154,3 +154,21 @@ def test_gemv_agrees_with_dequantised_product():
     ref = x.float() @ w_hat.t()
     torch.cuda.synchronize()
     check(host64(y), host64(ref))
+
+
+def test_gemv_spiky_rotated_token():
+    """A token whose rotation is one spike plus small noise (x = S H e_j / sqrt(n)
+    scaled, plus noise): the fixed-point rotated token keeps the spike at full
+    scale and rounds the rest; the product still matches the oracle."""
+    n, bits, group, rows = 8192, 2, 64, 600
+    d, x, c, s, m = layer(600, rows, n, bits, group, 1)
+    sv = H.signs_from_bits(d["signs"], n)
+    rng = np.random.default_rng(6)
+    e = np.zeros((1, n))
+    e[0, 1234] = 40.0
+    xs = H.irht(e, sv) + 1e-3 * rng.standard_normal((1, n))   # x = S Hn e + noise
+    xb = synth.to_bf16(xs)
+    y = W().rht_lowbit_gemv(dev(xb), c, s, m, bits, group)
+    torch.cuda.synchronize()
+    want = gemv.rht_gemv(synth.bf16_to_f64(xb), d["codes"], d["scales"], sv, bits, group, n)
+    check(host64(y), want)
