@@ -32,8 +32,10 @@ says so in the docstring ("reading: ...").  Modules:
   hadamard  Sylvester matrix, orthonormal WHT, sign diagonal, RHT / inverse
   rtn       per-group absmax RTN quantiser, bit packing, dequant + inverse
   qwha      dense QWHA adapter forward
-  harp      dense HARP stage matrices and rotation
+  harp      dense HARP stage matrices and rotation, block parametrisation
+  gemv      low-bit weight x activation product with the rotation online
+  qwha_init QWHA initialisation: error coefficients, AdaAlloc, refinement
   compare   parity rules used to compare a device result with the oracle
 """
 
-from . import hadamard, rtn, qwha, harp, compare  # noqa: F401
+from . import hadamard, rtn, qwha, harp, gemv, qwha_init, compare  # noqa: F401

@@ -175,3 +175,51 @@ def test_mutant_gemv_signs_on_the_code_side(monkeypatch):
     monkeypatch.setattr(gemv, "rht_gemv", mutant)
     with pytest.raises(AssertionError):
         tg.test_gemv_bruteforce_tiny()
+
+
+# ---- QWHA initialisation (AdaAlloc, refinement)
+import oracle.qwha_init as QI
+import test_oracle_qwha_init as ti
+
+
+def test_mutant_error_coeffs_without_transform(monkeypatch):
+    monkeypatch.setattr(QI, "error_coeffs", lambda w, c, s16, s, b, g: np.asarray(w, np.float64)
+                        - R.dequantize_inverse(c, s16, s, b, g, np.asarray(w).shape[1]))
+    _fails(ti.test_error_coeffs_bruteforce)
+
+
+def test_mutant_channel_errors_in_coefficient_basis(monkeypatch):
+    monkeypatch.setattr(QI, "channel_errors", lambda x, f: np.sqrt(((np.asarray(x) @ np.asarray(f).T) ** 2).sum(0)))
+    _fails(ti.test_channel_errors_bruteforce)
+
+
+def test_mutant_allocation_by_squared_error(monkeypatch):
+    orig = QI.allocate
+    monkeypatch.setattr(QI, "allocate", lambda e, p, fl, cap: orig(np.asarray(e, np.float64) ** 2, p, fl, cap))
+    _fails(ti.test_allocate_hand_worked)
+
+
+def test_mutant_selection_ties_to_higher_index(monkeypatch):
+    def sel(f, budgets):
+        f = np.abs(np.asarray(f, np.float64))
+        budgets = np.asarray(budgets)
+        row_ptr = np.concatenate([[0], np.cumsum(budgets)])
+        cols = np.concatenate([np.sort(np.lexsort((-np.arange(f.shape[1]), -f[o]))[:budgets[o]])
+                               for o in range(f.shape[0])])
+        return row_ptr, cols
+    monkeypatch.setattr(QI, "select", sel)
+    _fails(ti.test_select_bruteforce)
+
+
+def test_mutant_refine_without_transform(monkeypatch):
+    def ref(x, f, row_ptr, cols):
+        x = np.asarray(x, np.float64)
+        target = x @ H.wht(np.asarray(f, np.float64)).T
+        vals = np.empty(len(cols))
+        for o in range(len(row_ptr) - 1):
+            a, b = row_ptr[o], row_ptr[o + 1]
+            if a < b:
+                vals[a:b] = np.linalg.lstsq(x[:, cols[a:b]], target[:, o], rcond=None)[0]
+        return vals
+    monkeypatch.setattr(QI, "refine", ref)
+    _fails(ti.test_refine_normal_equations_and_gain)
