@@ -100,6 +100,15 @@ def select(f_dense, budgets):
     return row_ptr, cols
 
 
+def calibration_gram(x):
+    """G = (x Hn)^T (x Hn), fp64 [d_in, d_in]: the Gram matrix of the rotated
+    calibration tokens.  The refinement's least squares has the normal
+    equations G[E][E] c = (F_dense G)[o][E], and e_o^2 = F_dense[o] G F_dense[o]^T
+    (reading of [QWHA] 2.2: least squares on the selected transform columns)."""
+    z = wht(np.asarray(x, dtype=np.float64))
+    return z.T @ z
+
+
 def refine(x, f_dense, row_ptr, col_idx):
     """Least-squares values on the support: c_o = argmin ||x dW[o]^T - Z[:, E_o] c||
     with Z = x Hn and dW = F_dense Hn.  fp64, in CSR order."""

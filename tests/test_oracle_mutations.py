@@ -223,3 +223,10 @@ def test_mutant_refine_without_transform(monkeypatch):
         return vals
     monkeypatch.setattr(QI, "refine", ref)
     _fails(ti.test_refine_normal_equations_and_gain)
+
+
+def test_mutant_gram_without_transform(monkeypatch):
+    monkeypatch.setattr(QI, "calibration_gram", lambda x: np.asarray(x, np.float64).T @ np.asarray(x, np.float64))
+    _fails(ti.test_calibration_gram_bruteforce)
+    _fails(ti.test_calibration_gram_normal_equations)
+

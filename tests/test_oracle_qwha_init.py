@@ -144,3 +144,40 @@ def test_refine_closed_forms():
     vals = QI.refine(x, f, row_ptr, cols)
     assert np.allclose(vals, f.reshape(-1), atol=1e-10)
     assert QI.output_error(x, f, row_ptr, cols, vals) < 1e-18
+
+
+def test_calibration_gram_bruteforce():
+    """G[a][b] = sum_t (sum_i x[t][i] H[i][a]) (sum_j x[t][j] H[j][b]) / n, loops only."""
+    rng = np.random.default_rng(8)
+    n, t = 8, 5
+    x = rng.standard_normal((t, n))
+    g = QI.calibration_gram(x)
+    sgn = lambda i, k: -1.0 if bin(i & k).count("1") % 2 else 1.0
+    for a in range(n):
+        for b in range(n):
+            acc = 0.0
+            for r in range(t):
+                za = sum(x[r, i] * sgn(i, a) for i in range(n))
+                zb = sum(x[r, j] * sgn(j, b) for j in range(n))
+                acc += za * zb
+            assert abs(g[a, b] - acc / n) < 1e-12
+
+
+def test_calibration_gram_normal_equations():
+    """The quadratic form gives the channel errors; solving the normal
+    equations on a support gives the least-squares values refine returns."""
+    rng = np.random.default_rng(9)
+    n, d_out, t = 32, 6, 64
+    f = rng.standard_normal((d_out, n))
+    x = rng.standard_normal((t, n))
+    x[:, 5] *= 20.0                       # an outlier channel
+    g = QI.calibration_gram(x)
+    p = f @ g
+    assert np.allclose(np.sqrt(np.einsum("oi,oi->o", p, f)), QI.channel_errors(x, f), rtol=1e-12)
+    row_ptr, cols = QI.select(f, np.array([1, 4, 9, 16, 3, 32]))
+    vals = QI.refine(x, f, row_ptr, cols)
+    for o in range(d_out):
+        e = cols[row_ptr[o]:row_ptr[o + 1]]
+        c = np.linalg.solve(g[np.ix_(e, e)], p[o, e])
+        assert np.allclose(c, vals[row_ptr[o]:row_ptr[o + 1]], rtol=1e-9, atol=1e-11)
+
