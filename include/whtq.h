@@ -295,6 +295,88 @@ whtq_status harp_build_blocks(const void* params, whtq_dtype params_dtype, const
                               const int32_t* radices, int n_stages, const float* mixers, void* blocks,
                               whtq_dtype blocks_dtype, void* stream);
 
+/*
+ * QWHA adapter initialisation ([QWHA] 2.2: AdaAlloc spreads a parameter
+ * budget over the output channels in proportion to their activation error,
+ * with a per-channel minimum, and keeps each channel's largest-magnitude
+ * coefficients; refinement then sets the kept values by least squares on
+ * the layer output error).  With Delta W = F Hn ([QWHA] 2.1), Q the RHT +
+ * RTN quantiser above and x [T][n] calibration tokens:
+ *   F_dense = (W - Q(W)) Hn,   Z = x Hn,   G = Z^T Z,   P = F_dense G,
+ *   e_o = ||x (W - Q(W))[o]^T|| = sqrt(F_dense[o] G F_dense[o]^T),
+ *   c_o solves G[E_o][E_o] c = P[o][E_o]   (least squares on support E_o).
+ * A full initialisation is error_coeffs, gram (once per calibration batch,
+ * accumulate = 1 after the first), channel_errors, allocate (on the host),
+ * select, refine.  All arithmetic is fp32 (fp32 accumulation); the
+ * allocation is fp64 on the host.  n (d_in) is a power of two in
+ * [256, 8192] (WHTQ_EUNSUPPORTED otherwise; error_coeffs takes the
+ * quantiser's range); float matrices are 16-byte aligned with row strides a
+ * multiple of 4 elements.
+ *
+ * qwha_init_error_coeffs -- f[rows][ldf] (fp32, device) = (W - Q(W)) Hn for
+ *   stored codes/scales of W (as from rht_quantize_rtn with the same signs,
+ *   bits, group).  w must not alias f.
+ */
+#define WHTQ_QWHA_INIT_MAX_SUPPORT 128 /* largest per-channel budget refine takes */
+
+whtq_status qwha_init_error_coeffs(const void* w, whtq_dtype w_dtype, int64_t rows, int64_t n, int64_t ldw,
+                                   const uint8_t* codes, const uint16_t* scales, const uint32_t* sign_bits,
+                                   int bits, int group, float* f, int64_t ldf, void* stream);
+
+/*
+ * qwha_init_gram -- g (device fp32 [n][n], row stride n) = Z^T Z, or
+ *   g + Z^T Z with accumulate = 1, Z = x Hn for tokens rows of x (bf16, fp16
+ *   or fp32, row stride ldx).  z: device fp32 workspace [tokens][n] that
+ *   receives Z.  tokens = 0 with accumulate = 0 zeroes g.
+ */
+whtq_status qwha_init_gram(const void* x, whtq_dtype x_dtype, int64_t tokens, int64_t n, int64_t ldx, float* z,
+                           float* g, int accumulate, void* stream);
+
+/*
+ * qwha_init_channel_errors -- p (device fp32 [rows][n], row stride n) =
+ *   F_dense G and err[o] (device fp32[rows]) = sqrt(max(0, p[o] . f[o])),
+ *   the activation error of channel o.  g symmetric (from qwha_init_gram).
+ */
+whtq_status qwha_init_channel_errors(const float* f, int64_t rows, int64_t n, int64_t ldf, const float* g,
+                                     float* p, float* err, void* stream);
+
+/*
+ * qwha_init_allocate -- HOST call on host arrays: per-channel budgets
+ *   n_o in [floor, cap] with sum n_o = total, written as a CSR row pointer
+ *   row_ptr[rows + 1] (row_ptr[0] = 0).  Reading of [QWHA] 2.2: real budgets
+ *   clip(lam e_o, floor, cap) with lam found by bisection so that they sum
+ *   to total (the largest lam found whose sum does not exceed it), rounded
+ *   down, then one more to the channels of largest fractional part (ties to
+ *   the lower index; capped channels excluded); all-zero err gives total /
+ *   rows each.  WHTQ_EINVAL: total outside [floor rows, cap rows] or above
+ *   INT32_MAX, cap > n, negative or non-finite err, or a total that channels
+ *   with zero error (held at the floor) make unreachable;
+ *   WHTQ_EUNSUPPORTED: cap > WHTQ_QWHA_INIT_MAX_SUPPORT.
+ */
+whtq_status qwha_init_allocate(const float* err, int64_t rows, int64_t n, int64_t total, int floor, int cap,
+                               int32_t* row_ptr);
+
+/*
+ * qwha_init_select -- for each row the budget row_ptr[o+1] - row_ptr[o]
+ *   (device row_ptr, each budget in [0, n]) column indices of largest
+ *   |f[o][k]|, ties to the lower k, written ascending to device
+ *   col_idx[row_ptr[o] ..].  Rows whose budget is outside [0, n] are left
+ *   unwritten.
+ */
+whtq_status qwha_init_select(const float* f, int64_t rows, int64_t n, int64_t ldf, const int32_t* row_ptr,
+                             int32_t* col_idx, void* stream);
+
+/*
+ * qwha_init_refine -- vals[row_ptr[o] + a] (device fp32, CSR order) = c_a
+ *   with G[E][E] c = P[o][E], E = col_idx[row_ptr[o] .. row_ptr[o+1]) (from
+ *   qwha_init_select), p row stride n.  Cholesky factorisation in fp32; a row
+ *   whose G[E][E] is not positive definite (fewer calibration tokens than
+ *   its budget, a zero input) gives non-finite values; a row whose budget
+ *   exceeds WHTQ_QWHA_INIT_MAX_SUPPORT gives NaN.
+ */
+whtq_status qwha_init_refine(const float* g, int64_t n, const float* p, int64_t rows, const int32_t* row_ptr,
+                             const int32_t* col_idx, float* vals, void* stream);
+
 const char* whtq_status_string(whtq_status s);
 int whtq_last_hip_error(void); /* hipError_t behind this thread's last WHTQ_EHIP */
 int whtq_abi_version(void);

@@ -36,7 +36,9 @@ def test_exports_every_declared_symbol(lib):
                           "whtq_last_hip_error", "whtq_abi_version", "qwha_csr_transpose",
                           "qwha_permute_values", "qwha_adapter_backward_input",
                           "qwha_grad_values_workspace_bytes", "qwha_adapter_grad_values",
-                          "harp_build_blocks", "rht_lowbit_gemv"}
+                          "harp_build_blocks", "rht_lowbit_gemv", "qwha_init_error_coeffs",
+                          "qwha_init_gram", "qwha_init_channel_errors", "qwha_init_allocate",
+                          "qwha_init_select", "qwha_init_refine"}
     for nm in names:
         assert hasattr(lib, nm), nm
 
@@ -286,3 +288,85 @@ def test_harp_build_validation(lib):
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="needs a host without a GPU")
 def test_harp_build_valid_call_without_device_is_ehip(lib):
     assert hb(lib) == EHIP
+
+
+def qie(lib, w=P, wd=1, rows=8, n=4096, ldw=4096, c=P, s=P, sb=NULL, bits=4, g=128, f=P, ldf=4096):
+    return lib.qwha_init_error_coeffs(w, wd, rows, n, ldw, c, s, sb, bits, g, f, ldf, NULL)
+
+
+def test_qwha_init_error_coeffs_validation(lib):
+    assert qie(lib, bits=5) == EINVAL
+    assert qie(lib, g=96) == EINVAL
+    assert qie(lib, n=16384, ldw=16384, ldf=16384) == EUNSUP
+    assert qie(lib, wd=7) == EINVAL
+    assert qie(lib, ldw=4095) == EINVAL
+    assert qie(lib, ldf=100) == EINVAL
+    for kw in ("w", "c", "s", "f"):
+        assert qie(lib, **{kw: NULL}) == EINVAL
+    assert qie(lib, f=P, w=P) == EINVAL                  # w aliases f
+    assert qie(lib, w=ctypes.c_void_p(0x20001)) == EALIGN
+    assert qie(lib, w=ctypes.c_void_p(0x20000), f=P_MIS) == EALIGN
+    assert qie(lib, w=ctypes.c_void_p(0x20000), ldf=4097) == EALIGN
+    assert qie(lib, w=ctypes.c_void_p(0x20000), c=P_MIS) == EALIGN
+    assert qie(lib, w=ctypes.c_void_p(0x20000), sb=ctypes.c_void_p(0x10002)) == EALIGN
+    assert qie(lib, rows=0) == OK
+
+
+def qig(lib, x=P, xd=1, tokens=16, n=4096, ldx=4096, z=P, g=P, acc=0):
+    return lib.qwha_init_gram(x, xd, tokens, n, ldx, z, g, acc, NULL)
+
+
+def test_qwha_init_gram_validation(lib):
+    assert qig(lib, n=128, ldx=128) == EUNSUP            # n in [256, 8192]
+    assert qig(lib, n=16384, ldx=16384) == EUNSUP
+    assert qig(lib, n=3000, ldx=3000) == EINVAL
+    assert qig(lib, xd=9) == EINVAL
+    assert qig(lib, tokens=-1) == EINVAL
+    assert qig(lib, ldx=100) == EINVAL
+    assert qig(lib, acc=2) == EINVAL
+    for kw in ("x", "z", "g"):
+        assert qig(lib, **{kw: NULL}) == EINVAL
+    assert qig(lib, g=NULL, tokens=0) == EINVAL          # g is always written or read
+    assert qig(lib, x=P_MIS) == EALIGN
+    assert qig(lib, z=P_MIS) == EALIGN
+    assert qig(lib, g=P_MIS) == EALIGN
+    assert qig(lib, tokens=0, acc=1, x=NULL, z=NULL) == OK
+
+
+def qic(lib, f=P, rows=8, n=4096, ldf=4096, g=P, p=P, e=P):
+    return lib.qwha_init_channel_errors(f, rows, n, ldf, g, p, e, NULL)
+
+
+def qis(lib, f=P, rows=8, n=4096, ldf=4096, rp=P, ci=P):
+    return lib.qwha_init_select(f, rows, n, ldf, rp, ci, NULL)
+
+
+def qir(lib, g=P, n=4096, p=P, rows=8, rp=P, ci=P, v=P):
+    return lib.qwha_init_refine(g, n, p, rows, rp, ci, v, NULL)
+
+
+def test_qwha_init_device_calls_validation(lib):
+    assert qic(lib, n=64, ldf=64) == EUNSUP
+    assert qic(lib, ldf=100) == EINVAL
+    assert qic(lib, rows=-1) == EINVAL
+    for kw in ("f", "g", "p", "e"):
+        assert qic(lib, **{kw: NULL}) == EINVAL
+    assert qic(lib, f=P_MIS) == EALIGN
+    assert qic(lib, ldf=4098) == EALIGN
+    assert qic(lib, p=P_MIS) == EALIGN
+    assert qic(lib, e=ctypes.c_void_p(0x10002)) == EALIGN
+    assert qic(lib, rows=0) == OK
+    assert qis(lib, n=8192 * 2, ldf=8192 * 2) == EUNSUP
+    assert qis(lib, ldf=10) == EINVAL
+    for kw in ("f", "rp", "ci"):
+        assert qis(lib, **{kw: NULL}) == EINVAL
+    assert qis(lib, f=P_MIS) == EALIGN
+    assert qis(lib, ci=ctypes.c_void_p(0x10002)) == EALIGN
+    assert qis(lib, rows=0) == OK
+    assert qir(lib, n=100) == EINVAL
+    assert qir(lib, rows=-2) == EINVAL
+    for kw in ("g", "p", "rp", "ci", "v"):
+        assert qir(lib, **{kw: NULL}) == EINVAL
+    assert qir(lib, v=ctypes.c_void_p(0x10001)) == EALIGN
+    assert qir(lib, rows=0) == OK
+

@@ -4,9 +4,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <mutex>
+#include <vector>
 
 #include "../../include/whtq.h"
 
@@ -43,6 +45,17 @@ hipError_t launch_harp_build(const void* params, int pdt, const float* scales, i
                              int n_stages, const float* mixers, void* blocks, int bdt, hipStream_t s);
 hipError_t launch_harp(const void* x, void* y, int dt, int64_t tokens, int64_t ldx, int64_t ldy,
                        const uint32_t* sbits, int precondition, const void* blocks, int bdt, hipStream_t s);
+hipError_t launch_qi_sub(const void* w, int wdt, int64_t ldw, float* f, int64_t ldf, int64_t rows, int64_t n,
+                         hipStream_t s);
+hipError_t launch_qi_gram(const float* z, int64_t T, int64_t n, float* g, float beta, hipStream_t s);
+hipError_t launch_qi_fg(const float* f, int64_t ldf, int64_t rows, int64_t n, const float* g, float* p,
+                        hipStream_t s);
+hipError_t launch_qi_qform(const float* f, int64_t ldf, const float* p, int64_t rows, int64_t n, float* err,
+                           hipStream_t s);
+hipError_t launch_qi_select(const float* f, int64_t ldf, int64_t rows, int n, const int32_t* row_ptr,
+                            int32_t* col_idx, hipStream_t s);
+hipError_t launch_qi_refine(const float* g, int64_t n, const float* p, int64_t rows, const int32_t* row_ptr,
+                            const int32_t* col_idx, float* vals, hipStream_t s);
 
 static thread_local int g_last_hip = 0;
 
@@ -402,6 +415,167 @@ whtq_status harp_build_blocks(const void* params, whtq_dtype params_dtype, const
   if (st != WHTQ_OK) return st;
   return hip_status(launch_harp_build(params, params_dtype, scales, d, radices, n_stages, mixers, blocks,
                                       blocks_dtype, (hipStream_t)stream));
+}
+
+
+// ---------------------------------------------------------------- QWHA initialisation
+
+static bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// n of the initialisation calls after the error coefficients: a power of two in [256, 8192]
+static whtq_status qi_n(int64_t n) {
+  const int l = ilog2_pow2(n);
+  if (l < 0) return WHTQ_EINVAL;
+  if (l < 8 || l > 13) return WHTQ_EUNSUPPORTED;
+  return WHTQ_OK;
+}
+
+whtq_status qwha_init_error_coeffs(const void* w, whtq_dtype w_dtype, int64_t rows, int64_t n, int64_t ldw,
+                                   const uint8_t* codes, const uint16_t* scales, const uint32_t* sign_bits,
+                                   int bits, int group, float* f, int64_t ldf, void* stream) {
+  if (!dt_valid(w_dtype)) return WHTQ_EINVAL;
+  int logn = 0, logg = 0;
+  whtq_status st = check_quant_shape(rows, n, bits, group, &logn, &logg);
+  if (st != WHTQ_OK) return st;
+  if (ldw < n || ldf < n) return WHTQ_EINVAL;
+  if (rows > 0 && (!w || !codes || !scales || !f)) return WHTQ_EINVAL;
+  if (rows > 0 && static_cast<const void*>(f) == w) return WHTQ_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(w) % (uintptr_t)dt_bytes(w_dtype)) || !rows_aligned(f, n, ldf, 4) ||
+      !aligned16(codes) || !aligned16(scales))
+    return WHTQ_EALIGN;
+  if (sign_bits && !aligned4(sign_bits)) return WHTQ_EALIGN;
+  if (rows == 0) return WHTQ_OK;
+  st = need_device();
+  if (st != WHTQ_OK) return st;
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_rht_dequant(logn, WHTQ_F32, bits, logg, codes, scales, rows, sign_bits, f, ldf, s);
+  if (e == hipSuccess) e = launch_qi_sub(w, w_dtype, ldw, f, ldf, rows, n, s);
+  if (e == hipSuccess)
+    e = launch_wht(logn, WHTQ_F32, WHTQ_F32, f, f, rows, ldf, ldf, nullptr, WHTQ_SIGN_NONE,
+                   (float)(1.0 / std::sqrt((double)n)), s);
+  return hip_status(e);
+}
+
+whtq_status qwha_init_gram(const void* x, whtq_dtype x_dtype, int64_t tokens, int64_t n, int64_t ldx, float* z,
+                           float* g, int accumulate, void* stream) {
+  if (!dt_valid(x_dtype)) return WHTQ_EINVAL;
+  whtq_status st = qi_n(n);
+  if (st != WHTQ_OK) return st;
+  if (tokens < 0 || ldx < n || (accumulate != 0 && accumulate != 1)) return WHTQ_EINVAL;
+  if (!g || (tokens > 0 && (!x || !z))) return WHTQ_EINVAL;
+  if (!rows_aligned(x, n, ldx, dt_bytes(x_dtype)) || !aligned16(z) || !aligned16(g)) return WHTQ_EALIGN;
+  if (tokens == 0 && accumulate) return WHTQ_OK;
+  st = need_device();
+  if (st != WHTQ_OK) return st;
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (tokens > 0)
+    e = launch_wht(ilog2_pow2(n), x_dtype, WHTQ_F32, x, z, tokens, ldx, n, nullptr, WHTQ_SIGN_NONE,
+                   (float)(1.0 / std::sqrt((double)n)), s);
+  if (e == hipSuccess) e = launch_qi_gram(z, tokens, n, g, accumulate ? 1.f : 0.f, s);
+  return hip_status(e);
+}
+
+whtq_status qwha_init_channel_errors(const float* f, int64_t rows, int64_t n, int64_t ldf, const float* g,
+                                     float* p, float* err, void* stream) {
+  whtq_status st = qi_n(n);
+  if (st != WHTQ_OK) return st;
+  if (rows < 0 || ldf < n) return WHTQ_EINVAL;
+  if (rows > 0 && (!f || !g || !p || !err)) return WHTQ_EINVAL;
+  if (!rows_aligned(f, n, ldf, 4) || !aligned16(g) || !aligned16(p) || !aligned4(err)) return WHTQ_EALIGN;
+  if (rows == 0) return WHTQ_OK;
+  st = need_device();
+  if (st != WHTQ_OK) return st;
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_qi_fg(f, ldf, rows, n, g, p, s);
+  if (e == hipSuccess) e = launch_qi_qform(f, ldf, p, rows, n, err, s);
+  return hip_status(e);
+}
+
+whtq_status qwha_init_allocate(const float* err, int64_t rows, int64_t n, int64_t total, int floor, int cap,
+                               int32_t* row_ptr) {
+  if (rows < 1 || n < 1 || !err || !row_ptr) return WHTQ_EINVAL;
+  if (floor < 0 || cap < floor || cap > n) return WHTQ_EINVAL;
+  if (cap > WHTQ_QWHA_INIT_MAX_SUPPORT) return WHTQ_EUNSUPPORTED;
+  if (total < (int64_t)floor * rows || total > (int64_t)cap * rows || total > INT32_MAX) return WHTQ_EINVAL;
+  bool any = false;
+  for (int64_t o = 0; o < rows; ++o) {
+    if (!std::isfinite(err[o]) || err[o] < 0.f) return WHTQ_EINVAL;
+    any = any || err[o] > 0.f;
+  }
+  const double p = (double)total;
+  auto budget = [&](double lam) {
+    double sum = 0.0;
+    for (int64_t o = 0; o < rows; ++o) sum += std::min((double)cap, std::max((double)floor, lam * (double)err[o]));
+    return sum;
+  };
+  std::vector<double> real(rows);
+  if (!any) {
+    std::fill(real.begin(), real.end(), p / (double)rows);
+  } else {
+    // water level: the sum of clip(lam e, floor, cap) is continuous and
+    // non-decreasing in lam; the largest lam found with sum <= p leaves a
+    // non-negative remainder for the rounding below
+    double lo = 0.0, hi = 1.0;
+    int doublings = 0;
+    while (budget(hi) < p) {
+      hi *= 2.0;
+      if (++doublings > 2100) return WHTQ_EINVAL;  // channels without error sit at the floor
+    }
+    for (int it = 0; it < 200; ++it) {
+      const double mid = 0.5 * (lo + hi);
+      if (budget(mid) < p) lo = mid;
+      else hi = mid;
+    }
+    for (int64_t o = 0; o < rows; ++o)
+      real[o] = std::min((double)cap, std::max((double)floor, lo * (double)err[o]));
+  }
+  std::vector<int64_t> base(rows);
+  std::vector<int64_t> order;
+  int64_t sum = 0;
+  for (int64_t o = 0; o < rows; ++o) {
+    base[o] = (int64_t)std::floor(real[o]);
+    sum += base[o];
+    if (base[o] < cap) order.push_back(o);
+  }
+  const int64_t rem = total - sum;
+  if (rem < 0 || rem > (int64_t)order.size()) return WHTQ_EINVAL;
+  // largest fractional part first, ties to the lower channel index
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int64_t a, int64_t b) { return real[a] - (double)base[a] > real[b] - (double)base[b]; });
+  for (int64_t q = 0; q < rem; ++q) ++base[order[q]];
+  row_ptr[0] = 0;
+  for (int64_t o = 0; o < rows; ++o) row_ptr[o + 1] = row_ptr[o] + (int32_t)base[o];
+  return WHTQ_OK;
+}
+
+whtq_status qwha_init_select(const float* f, int64_t rows, int64_t n, int64_t ldf, const int32_t* row_ptr,
+                             int32_t* col_idx, void* stream) {
+  whtq_status st = qi_n(n);
+  if (st != WHTQ_OK) return st;
+  if (rows < 0 || ldf < n) return WHTQ_EINVAL;
+  if (rows > 0 && (!f || !row_ptr || !col_idx)) return WHTQ_EINVAL;
+  if (rows > INT32_MAX) return WHTQ_EUNSUPPORTED;
+  if (!rows_aligned(f, n, ldf, 4) || !aligned4(row_ptr) || !aligned4(col_idx)) return WHTQ_EALIGN;
+  if (rows == 0) return WHTQ_OK;
+  st = need_device();
+  if (st != WHTQ_OK) return st;
+  return hip_status(launch_qi_select(f, ldf, rows, (int)n, row_ptr, col_idx, (hipStream_t)stream));
+}
+
+whtq_status qwha_init_refine(const float* g, int64_t n, const float* p, int64_t rows, const int32_t* row_ptr,
+                             const int32_t* col_idx, float* vals, void* stream) {
+  whtq_status st = qi_n(n);
+  if (st != WHTQ_OK) return st;
+  if (rows < 0) return WHTQ_EINVAL;
+  if (rows > 0 && (!g || !p || !row_ptr || !col_idx || !vals)) return WHTQ_EINVAL;
+  if (rows > INT32_MAX) return WHTQ_EUNSUPPORTED;
+  if (!aligned4(g) || !aligned4(p) || !aligned4(row_ptr) || !aligned4(col_idx) || !aligned4(vals))
+    return WHTQ_EALIGN;
+  if (rows == 0) return WHTQ_OK;
+  st = need_device();
+  if (st != WHTQ_OK) return st;
+  return hip_status(launch_qi_refine(g, n, p, rows, row_ptr, col_idx, vals, (hipStream_t)stream));
 }
 
 }  // extern "C"

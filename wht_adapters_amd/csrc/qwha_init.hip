@@ -1,0 +1,455 @@
+// QWHA adapter initialisation on the device: error coefficients, the
+// calibration Gram matrix, activation errors, per-channel selection and
+// least-squares refinement.
+//
+// QWHA explainer, 2.2: AdaAlloc gives each output channel a share of the
+// parameter budget in proportion to its activation error (with a minimum),
+// keeps the channel's largest-magnitude coefficients, and refinement fits the
+// kept values by least squares to the layer output error.  With
+// Delta W = F Hn, F_dense = (W - Q(W)) Hn and calibration tokens as rows of x,
+// put Z = x Hn and G = Z^T Z (n x n, the rotated input Gram matrix).  Then
+//   e_o^2 = ||x Delta W[o]^T||^2 = F_dense[o] G F_dense[o]^T,
+// and the least-squares values on a support E solve the normal equations
+//   G[E][E] c = (F_dense G)[o][E].
+// Everything after G is independent of the number of calibration tokens, and
+// G accumulates over calibration batches.
+//
+// Kernels: W - Q(W) (the transforms and Q are the library's FWHT and
+// dequantise-inverse kernels), an fp32 GEMM on MFMA 16x16x4 f32 tiles for G
+// (symmetric: upper blocks only, mirrored) and for F_dense G, the per-row
+// quadratic form, a per-row radix top-k, and a per-row Cholesky solve with
+// the factor held in 4 x 4 register blocks.
+#include "io.hpp"
+#include "launch.hpp"
+
+namespace whtq {
+
+namespace qi {
+constexpr int KMAX = 128;     // largest support a row's refinement takes
+constexpr int BT = 128;       // GEMM block tile (M and N)
+constexpr int KS = 16;        // GEMM k-step staged in LDS
+constexpr int LDT = BT + 16;  // LDS row stride of a k-major tile (conflict-free MFMA operand reads)
+}  // namespace qi
+
+// f[r][i] = w[r][i] - f[r][i] (w bf16, f16 or f32; f fp32)
+template <int WDT>
+__global__ void k_qi_sub(const void* __restrict__ w, int64_t ldw, float* __restrict__ f, int64_t ldf, int64_t rows,
+                         int64_t n) {
+  const int64_t total = rows * n;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = e / n, i = e - r * n;
+    float wv;
+    if constexpr (WDT == DT_F32) {
+      wv = reinterpret_cast<const float*>(w)[r * ldw + i];
+    } else {
+      const uint16_t b = reinterpret_cast<const uint16_t*>(w)[r * ldw + i];
+      wv = WDT == DT_BF16 ? as_f((uint32_t)b << 16) : (float)__builtin_bit_cast(_Float16, b);
+    }
+    f[r * ldf + i] = wv - f[r * ldf + i];
+  }
+}
+
+hipError_t launch_qi_sub(const void* w, int wdt, int64_t ldw, float* f, int64_t ldf, int64_t rows, int64_t n,
+                         hipStream_t s) {
+  const unsigned grid = persistent_grid((rows * n + 255) / 256, 8);
+  if (wdt == DT_F32) hipLaunchKernelGGL(k_qi_sub<DT_F32>, dim3(grid), dim3(256), 0, s, w, ldw, f, ldf, rows, n);
+  else if (wdt == DT_F16) hipLaunchKernelGGL(k_qi_sub<DT_F16>, dim3(grid), dim3(256), 0, s, w, ldw, f, ldf, rows, n);
+  else hipLaunchKernelGGL(k_qi_sub<DT_BF16>, dim3(grid), dim3(256), 0, s, w, ldw, f, ldf, rows, n);
+  return hipGetLastError();
+}
+
+// C[m][c] = beta C[m][c] + sum_k A(m, k) B(k, c) in fp32.  B is k-major
+// (B[k * ldb + c]); A is m-major (A[m * lda + k]) when AM, else k-major
+// (A[k * lda + m]).  Requirements (checked by the callers): N % 128 == 0,
+// 16-byte aligned bases and strides; AM: K % 16 == 0 (rows past M read as
+// zero and are not stored); k-major A: M % 128 == 0 (k past K read as zero).
+// SYM (C = A^T A with A == B, M == N): only blocks bm <= bn are computed, and
+// each off-diagonal block also writes its mirror.
+//
+// 256 threads = 4 waves in 2 x 2, each wave a 64 x 64 quarter of the 128 x 128
+// block as 4 x 4 MFMA 16x16x4 tiles (operand lane l: row/col l % 16, k l / 16;
+// result register r of lane l: row 4 (l / 16) + r, col l % 16).  The next
+// k-step's global loads are in flight while the current one is multiplied.
+template <bool AM, bool SYM>
+__global__ __launch_bounds__(256) void k_qi_gemm(const float* __restrict__ A, int64_t lda,
+                                                const float* __restrict__ B, int64_t ldb, float* __restrict__ C,
+                                                int64_t ldc, int64_t M, int64_t K, float beta) {
+  using namespace qi;
+  __shared__ __align__(16) float As[KS][LDT];
+  __shared__ __align__(16) float Bs[KS][LDT];
+  const int bn = blockIdx.x, bm = blockIdx.y;
+  if (SYM && bm > bn) return;
+  const int64_t m0 = (int64_t)bm * BT, n0 = (int64_t)bn * BT;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+  const int li = lane & 15, lk = lane >> 4;
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 ga[2], gb[2];
+  auto load = [&](int64_t k0) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e = tid + 256 * h;
+      const int64_t kb = k0 + (e >> 5);
+      gb[h] = kb < K ? ldg<f32x4>(B + kb * ldb + n0 + (e & 31) * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (AM) {
+        const int64_t m = m0 + (e >> 2);
+        ga[h] = m < M ? ldg<f32x4>(A + m * lda + k0 + (e & 3) * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+      } else {
+        ga[h] = kb < K ? ldg<f32x4>(A + kb * lda + m0 + (e & 31) * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e = tid + 256 * h;
+      *reinterpret_cast<f32x4*>(&Bs[e >> 5][(e & 31) * 4]) = gb[h];
+      if constexpr (AM) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) As[(e & 3) * 4 + q][e >> 2] = ga[h][q];
+      } else {
+        *reinterpret_cast<f32x4*>(&As[e >> 5][(e & 31) * 4]) = ga[h];
+      }
+    }
+  };
+  load(0);
+  for (int64_t k0 = 0; k0 < K; k0 += KS) {
+    stage();
+    __syncthreads();
+    if (k0 + KS < K) load(k0 + KS);
+#pragma unroll
+    for (int kk = 0; kk < KS; kk += 4) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk + lk][wm + i * 16 + li];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk + lk][wn + j * 16 + li];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = m0 + wm + i * 16 + 4 * lk + r, c = n0 + wn + j * 16 + li;
+        if (AM && m >= M) continue;
+        float v = acc[i][j][r];
+        if (beta != 0.f) v = fmaf(beta, C[m * ldc + c], v);
+        C[m * ldc + c] = v;
+        if (SYM && bm != bn) {
+          float u = acc[i][j][r];
+          if (beta != 0.f) u = fmaf(beta, C[c * ldc + m], u);
+          C[c * ldc + m] = u;
+        }
+      }
+}
+
+// G = beta G + Z^T Z, Z [T][n] (row stride n), n % 128 == 0
+hipError_t launch_qi_gram(const float* z, int64_t T, int64_t n, float* g, float beta, hipStream_t s) {
+  const dim3 grid((unsigned)(n / qi::BT), (unsigned)(n / qi::BT));
+  hipLaunchKernelGGL((k_qi_gemm<false, true>), grid, dim3(256), 0, s, z, n, z, n, g, n, n, T, beta);
+  return hipGetLastError();
+}
+
+// P = F G, F [rows][n] (stride ldf), G [n][n] symmetric, P [rows][n] (stride n)
+hipError_t launch_qi_fg(const float* f, int64_t ldf, int64_t rows, int64_t n, const float* g, float* p,
+                        hipStream_t s) {
+  const dim3 grid((unsigned)(n / qi::BT), (unsigned)((rows + qi::BT - 1) / qi::BT));
+  hipLaunchKernelGGL((k_qi_gemm<true, false>), grid, dim3(256), 0, s, f, ldf, g, n, p, n, rows, n, 0.f);
+  return hipGetLastError();
+}
+
+// err[o] = sqrt(max(0, sum_i p[o][i] f[o][i])), one wave per row, n % 256 == 0
+__global__ __launch_bounds__(256) void k_qi_qform(const float* __restrict__ f, int64_t ldf,
+                                                 const float* __restrict__ p, int64_t rows, int64_t n,
+                                                 float* __restrict__ err) {
+  const int64_t o = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (o >= rows) return;
+  float a = 0.f;
+  for (int64_t i = lane * 4; i < n; i += 256) {
+    const f32x4 u = ldg<f32x4>(f + o * ldf + i), v = ldg<f32x4>(p + o * n + i);
+    a = fmaf(u[0], v[0], a);
+    a = fmaf(u[1], v[1], a);
+    a = fmaf(u[2], v[2], a);
+    a = fmaf(u[3], v[3], a);
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) a += __shfl_xor(a, m);
+  if (lane == 0) err[o] = __builtin_sqrtf(fmaxf(a, 0.f));
+}
+
+hipError_t launch_qi_qform(const float* f, int64_t ldf, const float* p, int64_t rows, int64_t n, float* err,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(k_qi_qform, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, f, ldf, p, rows, n, err);
+  return hipGetLastError();
+}
+
+// Per row: the k = row_ptr[r+1] - row_ptr[r] (<= n) indices of largest |f|,
+// ties to the lower index, ascending, into col_idx[row_ptr[r] ..).  Radix
+// select on the bit patterns of |f| (non-negative floats order as their
+// patterns): four 8-bit digit passes find the k-th largest key t; keys above
+// t are taken, and of the keys equal to t the lowest-index ones.  256
+// threads, thread tid holds the VPT = n / 256 contiguous values from tid VPT.
+template <int VPT>
+__global__ __launch_bounds__(256) void k_qi_select(const float* __restrict__ f, int64_t ldf, int n,
+                                                  const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t scan[256];
+  __shared__ uint32_t bc[2];
+  const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int base = row_ptr[r];
+  const int k = row_ptr[r + 1] - base;
+  if (k <= 0 || k > n) return;
+  uint32_t key[VPT];
+  const float* fr = f + r * ldf + tid * VPT;
+  if constexpr (VPT >= 4) {
+#pragma unroll
+    for (int q = 0; q < VPT; q += 4) {
+      const u32x4 v = ldg<u32x4>(fr + q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) key[q + e] = v[e] & 0x7fffffffu;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < VPT; ++q) key[q] = __builtin_bit_cast(uint32_t, fr[q]) & 0x7fffffffu;
+  }
+  const bool all = k == n;
+  uint32_t prefix = 0, want = (uint32_t)k;  // digits of t found so far; how many keys equal to them to take
+  if (!all) {
+    for (int pass = 3; pass >= 0; --pass) {
+      hist[tid] = 0;
+      __syncthreads();
+      const int sh = 8 * pass;
+#pragma unroll
+      for (int q = 0; q < VPT; ++q) {
+        const bool cand = pass == 3 || (key[q] >> (sh + 8)) == prefix;
+        if (cand) atomicAdd(&hist[(key[q] >> sh) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t cum = 0;
+        int d = 255;
+        for (; d > 0; --d) {
+          if (cum + hist[d] >= want) break;
+          cum += hist[d];
+        }
+        bc[0] = (prefix << 8) | (uint32_t)d;
+        bc[1] = want - cum;
+      }
+      __syncthreads();
+      prefix = bc[0];
+      want = bc[1];
+      __syncthreads();
+    }
+  }
+  const uint32_t t = prefix;
+  uint32_t nties = 0, nabove = 0;
+#pragma unroll
+  for (int q = 0; q < VPT; ++q) {
+    nabove += (all || key[q] > t) ? 1u : 0u;
+    nties += (!all && key[q] == t) ? 1u : 0u;
+  }
+  // exclusive prefix sums over threads (index order)
+  auto exscan = [&](uint32_t v) -> uint32_t {
+    scan[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const uint32_t add = tid >= off ? scan[tid - off] : 0u;
+      __syncthreads();
+      scan[tid] += add;
+      __syncthreads();
+    }
+    const uint32_t incl = scan[tid];
+    __syncthreads();
+    return incl - v;
+  };
+  const uint32_t tie0 = exscan(nties);
+  const uint32_t left = want > tie0 ? want - tie0 : 0u;
+  const uint32_t take = all ? 0u : (left < nties ? left : nties);  // this thread's ties that are taken
+  uint32_t pos = exscan(nabove + take), seen = 0;
+#pragma unroll
+  for (int q = 0; q < VPT; ++q) {
+    bool s = all || key[q] > t;
+    if (!s && key[q] == t) {
+      s = seen < take;
+      ++seen;
+    }
+    if (s) col_idx[base + pos++] = tid * VPT + q;
+  }
+}
+
+hipError_t launch_qi_select(const float* f, int64_t ldf, int64_t rows, int n, const int32_t* row_ptr,
+                            int32_t* col_idx, hipStream_t s) {
+  const dim3 g((unsigned)rows), b(256);
+  switch (n) {
+    case 256: hipLaunchKernelGGL(k_qi_select<1>, g, b, 0, s, f, ldf, n, row_ptr, col_idx); break;
+    case 512: hipLaunchKernelGGL(k_qi_select<2>, g, b, 0, s, f, ldf, n, row_ptr, col_idx); break;
+    case 1024: hipLaunchKernelGGL(k_qi_select<4>, g, b, 0, s, f, ldf, n, row_ptr, col_idx); break;
+    case 2048: hipLaunchKernelGGL(k_qi_select<8>, g, b, 0, s, f, ldf, n, row_ptr, col_idx); break;
+    case 4096: hipLaunchKernelGGL(k_qi_select<16>, g, b, 0, s, f, ldf, n, row_ptr, col_idx); break;
+    case 8192: hipLaunchKernelGGL(k_qi_select<32>, g, b, 0, s, f, ldf, n, row_ptr, col_idx); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+__device__ __forceinline__ float qi_pick(const float (&v)[4], int i) {
+  return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
+}
+
+// Per row r with support E (k = |E| <= KMAX): the normal equations
+// G[E][E] c = P[r][E] (P = F_dense G), solved by Cholesky G[E][E] = L L^T,
+// L y = b, L^T c = y; vals[row_ptr[r] + a] = c_a.  Rows with k > KMAX get NaN.
+// G[E][E] is padded to a multiple of 4 with identity rows.  Each thread holds
+// up to MAXP 4 x 4 blocks of the lower block triangle in registers; step j of
+// the right-looking factorisation publishes column j through LDS (double
+// buffered: one barrier per step), and every thread scales it and updates its
+// own trailing blocks.  L then goes to LDS and wave 0 does the two triangular
+// solves with b held two entries per lane.
+__global__ __launch_bounds__(256) void k_qi_refine(const float* __restrict__ g, int64_t n,
+                                                  const float* __restrict__ p, const int32_t* __restrict__ row_ptr,
+                                                  const int32_t* __restrict__ col_idx, float* __restrict__ vals) {
+  constexpr int KM = qi::KMAX, NBM = KM / 4, MAXP = (NBM * (NBM + 1) / 2 + 255) / 256;
+  __shared__ int sidx[KM];
+  __shared__ __align__(16) float colb[2][KM];
+  __shared__ float Ls[KM][KM + 1];
+  const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int base = row_ptr[r];
+  const int k = row_ptr[r + 1] - base;
+  if (k <= 0) return;
+  if (k > KM) {
+    for (int i = tid; i < k; i += 256) vals[base + i] = __builtin_nanf("");
+    return;
+  }
+  for (int i = tid; i < KM; i += 256) sidx[i] = i < k ? col_idx[base + i] : 0;
+  __syncthreads();
+  const int nb = (k + 3) >> 2, npair = nb * (nb + 1) / 2, kp = 4 * nb;
+  int pbi[MAXP], pbj[MAXP];
+  float acc[MAXP][4][4];
+#pragma unroll
+  for (int m = 0; m < MAXP; ++m) {
+    const int q = tid + 256 * m;
+    int bi = -1, bj = -1;
+    if (q < npair) {
+      bi = (int)((__builtin_sqrtf(8.f * (float)q + 1.f) - 1.f) * 0.5f);
+      while ((bi + 1) * (bi + 2) / 2 <= q) ++bi;
+      while (bi * (bi + 1) / 2 > q) --bi;
+      bj = q - bi * (bi + 1) / 2;
+    }
+    pbi[m] = bi;
+    pbj[m] = bj;
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        const int i = 4 * bi + x, l = 4 * bj + y;
+        float v = 0.f;
+        if (bi >= 0) {
+          if (i < k && l < k) v = g[(int64_t)sidx[i] * n + sidx[l]];
+          else if (i == l) v = 1.f;
+        }
+        acc[m][x][y] = v;
+      }
+  }
+  for (int j = 0; j < kp; ++j) {
+    float* cb = colb[j & 1];
+    const int jb = j >> 2, jy = j & 3;
+#pragma unroll
+    for (int m = 0; m < MAXP; ++m)
+      if (pbj[m] == jb) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) cb[4 * pbi[m] + x] = qi_pick(acc[m][x], jy);
+      }
+    __syncthreads();
+    const float d = __builtin_sqrtf(cb[j]);
+    const float rd = 1.f / d;
+#pragma unroll
+    for (int m = 0; m < MAXP; ++m) {
+      if (pbj[m] < jb) continue;  // also skips the empty slots (-1)
+      const int i0 = 4 * pbi[m], l0 = 4 * pbj[m];
+      const f32x4 ca = *reinterpret_cast<const f32x4*>(&cb[i0]);
+      const f32x4 cl = *reinterpret_cast<const f32x4*>(&cb[l0]);
+      float a[4], b[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) a[x] = i0 + x > j ? ca[x] * rd : 0.f;
+#pragma unroll
+      for (int y = 0; y < 4; ++y) b[y] = l0 + y > j ? cl[y] * rd : 0.f;
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[m][x][y] = fmaf(-a[x], b[y], acc[m][x][y]);
+      if (pbj[m] == jb) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int i = i0 + x;
+#pragma unroll
+          for (int y = 0; y < 4; ++y)
+            if (y == jy && i >= j) acc[m][x][y] = i == j ? d : a[x];
+        }
+      }
+    }
+  }
+  // L (lower triangle) to LDS
+#pragma unroll
+  for (int m = 0; m < MAXP; ++m) {
+    if (pbi[m] < 0) continue;
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        const int i = 4 * pbi[m] + x, l = 4 * pbj[m] + y;
+        if (l <= i) Ls[i][l] = acc[m][x][y];
+      }
+  }
+  __syncthreads();
+  if (tid >= 64) return;
+  const int lane = tid;
+  const float* pr = p + r * n;
+  float b0 = lane < k ? pr[sidx[lane]] : 0.f;
+  float b1 = lane + 64 < k ? pr[sidx[lane + 64]] : 0.f;
+  // L y = b
+  for (int j = 0; j < kp; ++j) {
+    const int src = __builtin_bit_cast(int, j < 64 ? b0 : b1);
+    const float yj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(src, j & 63)) / Ls[j][j];
+    if (lane > j) b0 = fmaf(-Ls[lane][j], yj, b0);
+    if (lane + 64 > j && lane + 64 < kp) b1 = fmaf(-Ls[lane + 64][j], yj, b1);
+    if (lane == (j & 63)) {
+      if (j < 64) b0 = yj;
+      else b1 = yj;
+    }
+  }
+  // L^T c = y
+  for (int j = kp - 1; j >= 0; --j) {
+    const int src = __builtin_bit_cast(int, j < 64 ? b0 : b1);
+    const float cj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(src, j & 63)) / Ls[j][j];
+    if (lane < j) b0 = fmaf(-Ls[j][lane], cj, b0);
+    if (lane + 64 < j) b1 = fmaf(-Ls[j][lane + 64], cj, b1);
+    if (lane == (j & 63)) {
+      if (j < 64) b0 = cj;
+      else b1 = cj;
+    }
+  }
+  if (lane < k) vals[base + lane] = b0;
+  if (lane + 64 < k) vals[base + lane + 64] = b1;
+}
+
+hipError_t launch_qi_refine(const float* g, int64_t n, const float* p, int64_t rows, const int32_t* row_ptr,
+                            const int32_t* col_idx, float* vals, hipStream_t s) {
+  hipLaunchKernelGGL(k_qi_refine, dim3((unsigned)rows), dim3(256), 0, s, g, n, p, row_ptr, col_idx, vals);
+  return hipGetLastError();
+}
+
+}  // namespace whtq

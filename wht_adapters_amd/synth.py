@@ -149,6 +149,8 @@ WORKLOADS = {
     "harp_8192x5120_r88852": "HARP general schedule 8*8*8*5*2, 8192 tokens x 5120 (no preconditioning)",
     "rht_int2_g64_28672x8192": "RHT + INT2 RTN g=64, bf16 28672 x 8192 Student-t weights",
     "gemv_int2_g64_28672x8192_t1": "online-RHT INT2 g=64 product, 28672 x 8192 codes, one decode token",
+    "qwha_init_4096x4096_int4_g128_t2048": "QWHA initialisation of a 4096 x 4096 INT4 g=128 layer from "
+                                           "2048 calibration tokens, budget 262,144, floor 16, cap 128",
 }
 
 
@@ -235,4 +237,24 @@ def lowbit_layer(cfg, rows, n, bits, group, tokens, scale_lo=0.002, scale_hi=0.0
 def gemv_int2_g64(rows=28672, n=8192, tokens=1):
     """Workload 7: decode through the 28672 x 8192 INT2 g=64 layer of workload 5."""
     return lowbit_layer(7, rows, n, 2, 64, tokens)
+
+
+def qinit_layer(cfg, d_out, n, tokens, bits, group, w_outlier_frac=0.001, x_outlier_frac=0.005, factor=30.0):
+    """A layer to initialise an adapter for: bf16 Student-t weights with
+    outlier columns (streams (cfg, 0..1)), calibration tokens N(0,1) with a
+    fraction of channels x factor -> bf16 (streams (cfg, 2..3)), and a
+    Rademacher sign vector (stream (cfg, 4))."""
+    w, _ = heavy_weights(cfg, d_out, n, max(1, int(round(w_outlier_frac * n))))
+    x = gaussian_rows(child_rng(cfg, 2), tokens, n)
+    ch = child_rng(cfg, 3).choice(n, max(1, int(round(x_outlier_frac * n))), replace=False)
+    x[:, ch] *= factor
+    return {"w": w, "x": to_bf16(x), "signs": rademacher_mask(cfg, 4, n), "bits": bits, "group": group}
+
+
+def qwha_init_int4_g128(d_out=4096, n=4096, tokens=2048):
+    """Workload 8: adapter initialisation of a 4096 x 4096 INT4 g=128 layer
+    (budget 64 per channel on average, the QWHA forward workload's 262,144)."""
+    d = qinit_layer(8, d_out, n, tokens, 4, 128)
+    d.update(total=64 * d_out, floor=16, cap=128)
+    return d
 

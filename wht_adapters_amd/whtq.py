@@ -35,6 +35,12 @@ _SIG = {
     "qwha_adapter_grad_values": [_vp, _vp, _int, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64,
                                  _vp],
     "rht_lowbit_gemv": [_vp, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _int, _int, _vp, _i64, _vp],
+    "qwha_init_error_coeffs": [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _int, _int, _vp, _i64, _vp],
+    "qwha_init_gram": [_vp, _int, _i64, _i64, _i64, _vp, _vp, _int, _vp],
+    "qwha_init_channel_errors": [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp],
+    "qwha_init_allocate": [_vp, _i64, _i64, _i64, _int, _int, _vp],
+    "qwha_init_select": [_vp, _i64, _i64, _i64, _vp, _vp, _vp],
+    "qwha_init_refine": [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp],
 }
 for _name, _args in _SIG.items():
     _f = getattr(_lib, _name)
@@ -367,3 +373,139 @@ def harp_build_blocks(params, radices, d, scales=None, mixers=None, out=None, ou
             _ptr(params), _DT[params.dtype], _ptr(scales), d, rad, len(radices), _ptr(mixers), _ptr(out),
             _DT[out.dtype], _stream(params)))
     return out
+
+
+# ------------------------------------------------------------ QWHA initialisation
+
+QWHA_INIT_MAX_SUPPORT = 128
+
+
+def _f32_rows(name, t):
+    _need_cuda(name, t)
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32")
+    return _rows_ld(name, t)
+
+
+def qwha_init_error_coeffs(w, codes, scales, signs, bits, group, out=None):
+    """F_dense = (W - Q(W)) Hn, float32 [rows, n], Q the RHT + RTN round trip of
+    the stored codes / scales."""
+    _need_cuda("w", w)
+    rows, n, ldw = _rows_ld("w", w)
+    if codes.shape != (rows, n * bits // 8) or scales.shape != (rows, n // group):
+        raise ValueError("codes / scales shape mismatch")
+    if not (codes.is_contiguous() and scales.is_contiguous()):
+        raise ValueError("codes and scales must be contiguous")
+    if out is None:
+        out = torch.empty((rows, n), dtype=torch.float32, device=w.device)
+    r2, n2, ldf = _f32_rows("out", out)
+    if (r2, n2) != (rows, n):
+        raise ValueError("out must be [rows, n]")
+    with torch.cuda.device(w.device):
+        _check("qwha_init_error_coeffs", _lib.qwha_init_error_coeffs(
+            _ptr(w), _DT[w.dtype], rows, n, ldw, _ptr(codes), _ptr(scales), _sign_ptr(signs, n, w.device),
+            bits, group, _ptr(out), ldf, _stream(w)))
+    return out
+
+
+def qwha_init_gram(x, g=None, accumulate=False, z=None):
+    """G (+)= (x Hn)^T (x Hn), float32 [n, n]; z is the [tokens, n] float32
+    workspace that receives x Hn.  Returns g."""
+    _need_cuda("x", x)
+    tokens, n, ldx = _rows_ld("x", x)
+    if g is None:
+        if accumulate:
+            raise ValueError("accumulate needs g")
+        g = torch.empty((n, n), dtype=torch.float32, device=x.device)
+    if g.shape != (n, n) or g.dtype != torch.float32 or not g.is_contiguous():
+        raise ValueError("g must be contiguous float32 [n, n]")
+    if z is None:
+        z = torch.empty((max(tokens, 1), n), dtype=torch.float32, device=x.device)
+    if z.dtype != torch.float32 or not z.is_contiguous() or z.numel() < tokens * n:
+        raise ValueError("z must be contiguous float32 with tokens * n elements")
+    with torch.cuda.device(x.device):
+        _check("qwha_init_gram", _lib.qwha_init_gram(
+            _ptr(x), _DT[x.dtype], tokens, n, ldx, _ptr(z), _ptr(g), int(bool(accumulate)), _stream(x)))
+    return g
+
+
+def qwha_init_channel_errors(f, g, p=None, err=None):
+    """(P = F G float32 [rows, n], err float32 [rows]) with err_o = sqrt(F[o] G F[o]^T)."""
+    rows, n, ldf = _f32_rows("f", f)
+    if g.shape != (n, n) or g.dtype != torch.float32 or not g.is_contiguous():
+        raise ValueError("g must be contiguous float32 [n, n]")
+    if p is None:
+        p = torch.empty((rows, n), dtype=torch.float32, device=f.device)
+    if err is None:
+        err = torch.empty(rows, dtype=torch.float32, device=f.device)
+    if p.shape != (rows, n) or p.dtype != torch.float32 or not p.is_contiguous():
+        raise ValueError("p must be contiguous float32 [rows, n]")
+    if err.shape != (rows,) or err.dtype != torch.float32:
+        raise ValueError("err must be float32 [rows]")
+    with torch.cuda.device(f.device):
+        _check("qwha_init_channel_errors", _lib.qwha_init_channel_errors(
+            _ptr(f), rows, n, ldf, _ptr(g), _ptr(p), _ptr(err), _stream(f)))
+    return p, err
+
+
+def qwha_init_allocate(err, n, total, floor, cap):
+    """Host call: int32 row_ptr [rows + 1] of the per-channel budgets."""
+    e = err.detach().to("cpu", torch.float32).contiguous()
+    rows = e.numel()
+    row_ptr = torch.empty(rows + 1, dtype=torch.int32)
+    _check("qwha_init_allocate", _lib.qwha_init_allocate(
+        _ptr(e), rows, n, int(total), int(floor), int(cap), _ptr(row_ptr)))
+    return row_ptr
+
+
+def qwha_init_select(f, row_ptr, col_idx=None):
+    """int32 col_idx: per row the budget's largest |F| columns (ties to the lower
+    column), ascending.  row_ptr: int32 device [rows + 1]."""
+    rows, n, ldf = _f32_rows("f", f)
+    _need_cuda("row_ptr", row_ptr)
+    if row_ptr.dtype != torch.int32 or row_ptr.shape != (rows + 1,) or not row_ptr.is_contiguous():
+        raise ValueError("row_ptr must be contiguous int32 [rows + 1]")
+    if col_idx is None:
+        col_idx = torch.empty(int(row_ptr[-1].item()), dtype=torch.int32, device=f.device)
+    if col_idx.dtype != torch.int32 or not col_idx.is_contiguous():
+        raise ValueError("col_idx must be contiguous int32")
+    with torch.cuda.device(f.device):
+        _check("qwha_init_select", _lib.qwha_init_select(
+            _ptr(f), rows, n, ldf, _ptr(row_ptr), _ptr(col_idx), _stream(f)))
+    return col_idx
+
+
+def qwha_init_refine(g, p, row_ptr, col_idx, vals=None):
+    """float32 vals (CSR order) solving G[E][E] c = P[o][E] per row."""
+    n = g.shape[0]
+    if g.shape != (n, n) or g.dtype != torch.float32 or not g.is_contiguous():
+        raise ValueError("g must be contiguous float32 [n, n]")
+    rows = p.shape[0]
+    if p.shape != (rows, n) or p.dtype != torch.float32 or not p.is_contiguous():
+        raise ValueError("p must be contiguous float32 [rows, n]")
+    for name, t in (("g", g), ("p", p), ("row_ptr", row_ptr), ("col_idx", col_idx)):
+        _need_cuda(name, t)
+    if row_ptr.dtype != torch.int32 or row_ptr.shape != (rows + 1,) or col_idx.dtype != torch.int32:
+        raise ValueError("row_ptr / col_idx must be int32, row_ptr [rows + 1]")
+    if vals is None:
+        vals = torch.empty(col_idx.numel(), dtype=torch.float32, device=g.device)
+    if vals.dtype != torch.float32 or vals.numel() != col_idx.numel():
+        raise ValueError("vals must be float32 with one entry per column index")
+    with torch.cuda.device(g.device):
+        _check("qwha_init_refine", _lib.qwha_init_refine(
+            _ptr(g), n, _ptr(p), rows, _ptr(row_ptr), _ptr(col_idx), _ptr(vals), _stream(g)))
+    return vals
+
+
+def qwha_initialize(w, codes, scales, signs, bits, group, x, total, floor, cap):
+    """The whole initialisation of one layer through the calls above:
+    returns (row_ptr int32, col_idx int32, vals float32) on w's device, plus
+    the channel errors.  The budget allocation waits for the errors on the
+    host (one device-to-host copy of rows floats)."""
+    f = qwha_init_error_coeffs(w, codes, scales, signs, bits, group)
+    g = qwha_init_gram(x)
+    p, err = qwha_init_channel_errors(f, g)
+    row_ptr = qwha_init_allocate(err, f.shape[1], total, floor, cap).to(w.device)
+    col_idx = qwha_init_select(f, row_ptr)
+    vals = qwha_init_refine(g, p, row_ptr, col_idx)
+    return row_ptr, col_idx, vals, err
