@@ -187,7 +187,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workloads", default="all",
-                    help="all | main | comma list of fwht, qwha, qwha_bwd, harp, harp_gen, int2, gemv "
+                    help="all | main | comma list of fwht, qwha, qwha_bwd, harp, harp_gen, int2, gemv, qinit "
                          "(the main workload always runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -218,7 +218,7 @@ def main():
         del a, b
         log("[bench] copy probe: 3 x 256 MiB device copy done")
 
-    sel = {"all": {"main", "fwht", "qwha", "qwha_bwd", "harp", "harp_gen", "int2", "gemv"},
+    sel = {"all": {"main", "fwht", "qwha", "qwha_bwd", "harp", "harp_gen", "int2", "gemv", "qinit"},
            "main": {"main"}}.get(
         args.workloads, set(args.workloads.split(",")))
     sel.add("main")  # `value` is always quoted on the main workload
@@ -250,6 +250,9 @@ def main():
         nm = "gemv_int2_g64_28672x8192_t1"
         res[nm] = bench_gemv(torch, W, mask_dev, synth, nm, K, Wm)
         log(f"[bench] {nm}: {res[nm]}")
+    if "qinit" in sel:
+        res[QINIT] = bench_qinit(torch, W, mask_dev, synth, K, Wm)
+        log(f"[bench] {QINIT}: {res[QINIT]}")
 
     main_r = res[MAIN]
     per_launch = main_r["ms_per_launch"] / 1e3
@@ -334,6 +337,63 @@ def bench_gemv(torch, W, mask_dev, synth, name, K, Wm):
     r = result(name, t.run(), K)
     r["tokens_per_s"] = 1e3 / r["ms_per_launch"]
     del cs, ss, ys
+    torch.cuda.empty_cache()
+    return r
+
+
+QINIT = "qwha_init_4096x4096_int4_g128_t2048"
+
+
+def bench_qinit(torch, W, mask_dev, synth, K, Wm):
+    """QWHA initialisation of the 4096 x 4096 INT4 g=128 layer from 2048
+    calibration tokens (budget 262,144, floor 16, cap 128): each device stage
+    timed alone (a HIP graph of K calls, same buffers), the host allocation on
+    the host clock, and the whole chain (device stages + the error copy to the
+    host, the allocation and the row pointer copy back) on the host clock."""
+    d = synth.qwha_init_int4_g128()
+    rows, n = d["w"].shape
+    T = d["x"].shape[0]
+    total, floor, cap = d["total"], d["floor"], d["cap"]
+    dv = "cuda:0"
+    w, x, sg = d["w"].to(dv), d["x"].to(dv), mask_dev(d["signs"])
+    codes, scales = W.rht_quantize_rtn(w, sg, 4, 128)
+    f = torch.empty((rows, n), dtype=torch.float32, device=dv)
+    z = torch.empty((T, n), dtype=torch.float32, device=dv)
+    g = torch.empty((n, n), dtype=torch.float32, device=dv)
+    p = torch.empty((rows, n), dtype=torch.float32, device=dv)
+    err = torch.empty(rows, dtype=torch.float32, device=dv)
+    col = torch.empty(total, dtype=torch.int32, device=dv)
+    vals = torch.empty(total, dtype=torch.float32, device=dv)
+    stage = {}
+    stage["error_coeffs"] = Timed(torch, lambda i: W.qwha_init_error_coeffs(w, codes, scales, sg, 4, 128, out=f),
+                                  K, Wm).run() / K
+    stage["gram"] = Timed(torch, lambda i: W.qwha_init_gram(x, g=g, z=z), K, Wm).run() / K
+    stage["channel_errors"] = Timed(torch, lambda i: W.qwha_init_channel_errors(f, g, p=p, err=err), K, Wm).run() / K
+    reps = max(3, K // 4)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        rp_host = W.qwha_init_allocate(err, n, total, floor, cap)
+    stage["allocate_host"] = (time.perf_counter() - t0) / reps
+    row_ptr = rp_host.to(dv)
+    stage["select"] = Timed(torch, lambda i: W.qwha_init_select(f, row_ptr, col_idx=col), K, Wm).run() / K
+    stage["refine"] = Timed(torch, lambda i: W.qwha_init_refine(g, p, row_ptr, col, vals=vals), K, Wm).run() / K
+    for _ in range(Wm):
+        W.qwha_initialize(w, codes, scales, sg, 4, 128, x, total, floor, cap)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        W.qwha_initialize(w, codes, scales, sg, 4, 128, x, total, floor, cap)
+    torch.cuda.synchronize()
+    step = (time.perf_counter() - t0) / K
+    gram_flop = n * (n + 1) * T        # unique entries of Z^T Z, 2 flops per product
+    fg_flop = 2 * rows * n * n
+    r = {"ms_per_step": step * 1e3, "layers_per_s": 1.0 / step,
+         "stage_ms": {k: v * 1e3 for k, v in stage.items()},
+         "gram_TFLOPs": gram_flop / stage["gram"] / 1e12,
+         "channel_errors_TFLOPs": fg_flop / stage["channel_errors"] / 1e12,
+         "frac_fp32_mfma_peak_channel_errors": fg_flop / stage["channel_errors"] / 157.3e12,
+         "select_GBps": rows * n * 4 / stage["select"] / 1e9}
+    del f, z, g, p, col, vals
     torch.cuda.empty_cache()
     return r
 

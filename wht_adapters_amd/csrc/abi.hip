@@ -504,10 +504,15 @@ whtq_status qwha_init_allocate(const float* err, int64_t rows, int64_t n, int64_
     any = any || err[o] > 0.f;
   }
   const double p = (double)total;
-  auto budget = [&](double lam) {
-    double sum = 0.0;
-    for (int64_t o = 0; o < rows; ++o) sum += std::min((double)cap, std::max((double)floor, lam * (double)err[o]));
-    return sum;
+  std::vector<double> e64(err, err + rows);
+  auto budget = [&](double lam) {  // four independent partial sums (vectorisable)
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    const double lo_v = (double)floor, hi_v = (double)cap;
+    int64_t o = 0;
+    for (; o + 4 <= rows; o += 4)
+      for (int q = 0; q < 4; ++q) acc[q] += std::min(hi_v, std::max(lo_v, lam * e64[o + q]));
+    for (; o < rows; ++o) acc[0] += std::min(hi_v, std::max(lo_v, lam * e64[o]));
+    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
   };
   std::vector<double> real(rows);
   if (!any) {
@@ -524,6 +529,7 @@ whtq_status qwha_init_allocate(const float* err, int64_t rows, int64_t n, int64_
     }
     for (int it = 0; it < 200; ++it) {
       const double mid = 0.5 * (lo + hi);
+      if (mid == lo || mid == hi) break;  // adjacent doubles: further steps change nothing
       if (budget(mid) < p) lo = mid;
       else hi = mid;
     }
@@ -540,9 +546,12 @@ whtq_status qwha_init_allocate(const float* err, int64_t rows, int64_t n, int64_
   }
   const int64_t rem = total - sum;
   if (rem < 0 || rem > (int64_t)order.size()) return WHTQ_EINVAL;
-  // largest fractional part first, ties to the lower channel index
-  std::stable_sort(order.begin(), order.end(),
-                   [&](int64_t a, int64_t b) { return real[a] - (double)base[a] > real[b] - (double)base[b]; });
+  // the rem channels of largest fractional part, ties to the lower channel index
+  if (rem > 0 && rem < (int64_t)order.size())
+    std::nth_element(order.begin(), order.begin() + rem, order.end(), [&](int64_t a, int64_t b) {
+      const double fa = real[a] - (double)base[a], fb = real[b] - (double)base[b];
+      return fa > fb || (fa == fb && a < b);
+    });
   for (int64_t q = 0; q < rem; ++q) ++base[order[q]];
   row_ptr[0] = 0;
   for (int64_t o = 0; o < rows; ++o) row_ptr[o + 1] = row_ptr[o] + (int32_t)base[o];

@@ -17,7 +17,7 @@
 // Kernels: W - Q(W) (the transforms and Q are the library's FWHT and
 // dequantise-inverse kernels), an fp32 GEMM on MFMA 16x16x4 f32 tiles for G
 // (symmetric: upper blocks only, mirrored) and for F_dense G, the per-row
-// quadratic form, a per-row radix top-k, and a per-row Cholesky solve with
+// quadratic form, a per-row bitwise top-k search, and a per-row Cholesky solve with
 // the factor held in 4 x 4 register blocks.
 #include "io.hpp"
 #include "launch.hpp"
@@ -195,20 +195,31 @@ hipError_t launch_qi_qform(const float* f, int64_t ldf, const float* p, int64_t 
   return hipGetLastError();
 }
 
+__device__ __forceinline__ uint32_t qi_wave_sum(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true);   // xor 1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true);   // xor 2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, true);  // half-row mirror
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, true);  // row mirror
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false); // row bcast 15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false); // row bcast 31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // Per row: the k = row_ptr[r+1] - row_ptr[r] (<= n) indices of largest |f|,
-// ties to the lower index, ascending, into col_idx[row_ptr[r] ..).  Radix
-// select on the bit patterns of |f| (non-negative floats order as their
-// patterns): four 8-bit digit passes find the k-th largest key t; keys above
-// t are taken, and of the keys equal to t the lowest-index ones.  256
-// threads, thread tid holds the VPT = n / 256 contiguous values from tid VPT.
+// ties to the lower index, ascending, into col_idx[row_ptr[r] ..).  The keys
+// are the bit patterns of |f| (non-negative floats order as their patterns).
+// The k-th largest key t is built bit by bit from the top: a bit is kept when
+// at least k keys are >= the candidate (31 block-wide counts, one barrier
+// each, no atomics).  Keys above t are taken, and of the keys equal to t the
+// lowest-index ones.  256 threads; thread tid holds the VPT = n / 256
+// contiguous values from tid VPT, so block-wide exclusive prefix sums in
+// thread order give each thread its output position.
 template <int VPT>
 __global__ __launch_bounds__(256) void k_qi_select(const float* __restrict__ f, int64_t ldf, int n,
                                                   const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t scan[256];
-  __shared__ uint32_t bc[2];
+  __shared__ uint32_t part[2][4];
   const int64_t r = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int base = row_ptr[r];
   const int k = row_ptr[r + 1] - base;
   if (k <= 0 || k > n) return;
@@ -225,60 +236,51 @@ __global__ __launch_bounds__(256) void k_qi_select(const float* __restrict__ f, 
 #pragma unroll
     for (int q = 0; q < VPT; ++q) key[q] = __builtin_bit_cast(uint32_t, fr[q]) & 0x7fffffffu;
   }
+  // block-wide sum; slots alternate so one barrier per call suffices
+  auto bsum = [&](uint32_t v, int slot) -> uint32_t {
+    v = qi_wave_sum(v);
+    if (lane == 0) part[slot][wv] = v;
+    __syncthreads();
+    return part[slot][0] + part[slot][1] + part[slot][2] + part[slot][3];
+  };
   const bool all = k == n;
-  uint32_t prefix = 0, want = (uint32_t)k;  // digits of t found so far; how many keys equal to them to take
+  uint32_t t = 0;
   if (!all) {
-    for (int pass = 3; pass >= 0; --pass) {
-      hist[tid] = 0;
-      __syncthreads();
-      const int sh = 8 * pass;
+    for (int b = 30; b >= 0; --b) {
+      const uint32_t cand = t | (1u << b);
+      uint32_t c = 0;
 #pragma unroll
-      for (int q = 0; q < VPT; ++q) {
-        const bool cand = pass == 3 || (key[q] >> (sh + 8)) == prefix;
-        if (cand) atomicAdd(&hist[(key[q] >> sh) & 255u], 1u);
-      }
-      __syncthreads();
-      if (tid == 0) {
-        uint32_t cum = 0;
-        int d = 255;
-        for (; d > 0; --d) {
-          if (cum + hist[d] >= want) break;
-          cum += hist[d];
-        }
-        bc[0] = (prefix << 8) | (uint32_t)d;
-        bc[1] = want - cum;
-      }
-      __syncthreads();
-      prefix = bc[0];
-      want = bc[1];
-      __syncthreads();
+      for (int q = 0; q < VPT; ++q) c += key[q] >= cand ? 1u : 0u;
+      if (bsum(c, b & 1) >= (uint32_t)k) t = cand;
     }
   }
-  const uint32_t t = prefix;
   uint32_t nties = 0, nabove = 0;
 #pragma unroll
   for (int q = 0; q < VPT; ++q) {
     nabove += (all || key[q] > t) ? 1u : 0u;
     nties += (!all && key[q] == t) ? 1u : 0u;
   }
-  // exclusive prefix sums over threads (index order)
-  auto exscan = [&](uint32_t v) -> uint32_t {
-    scan[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      const uint32_t add = tid >= off ? scan[tid - off] : 0u;
-      __syncthreads();
-      scan[tid] += add;
-      __syncthreads();
+  // exclusive prefix sums in thread order: wave scans, then the wave totals
+  __shared__ uint32_t wtot[2][4];
+  auto exscan = [&](uint32_t v, int slot) -> uint32_t {
+    uint32_t incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t u = (uint32_t)__shfl_up((int)incl, o);
+      if (lane >= o) incl += u;
     }
-    const uint32_t incl = scan[tid];
+    if (lane == 63) wtot[slot][wv] = incl;
     __syncthreads();
-    return incl - v;
+    uint32_t before = 0;
+    for (int w2 = 0; w2 < wv; ++w2) before += wtot[slot][w2];
+    return before + incl - v;
   };
-  const uint32_t tie0 = exscan(nties);
+  const uint32_t above_total = all ? (uint32_t)k : bsum(nabove, 1);  // slot 0 was the last search step's
+  const uint32_t want = (uint32_t)k - above_total;   // keys equal to t that are taken
+  const uint32_t tie0 = exscan(nties, 0);
   const uint32_t left = want > tie0 ? want - tie0 : 0u;
   const uint32_t take = all ? 0u : (left < nties ? left : nties);  // this thread's ties that are taken
-  uint32_t pos = exscan(nabove + take), seen = 0;
+  uint32_t pos = exscan(nabove + take, 1), seen = 0;
 #pragma unroll
   for (int q = 0; q < VPT; ++q) {
     bool s = all || key[q] > t;
@@ -315,16 +317,19 @@ __device__ __forceinline__ float qi_pick(const float (&v)[4], int i) {
 // G[E][E] is padded to a multiple of 4 with identity rows.  Each thread holds
 // up to MAXP 4 x 4 blocks of the lower block triangle in registers; step j of
 // the right-looking factorisation publishes column j through LDS (double
-// buffered: one barrier per step), and every thread scales it and updates its
-// own trailing blocks.  L then goes to LDS and wave 0 does the two triangular
-// solves with b held two entries per lane.
+// buffered: one barrier per step), and every thread scales it by the pivot's
+// reciprocal square root and updates its own trailing blocks.  L then goes to
+// LDS packed by rows (with the reciprocal diagonal alongside, so no division
+// sits on the solves' serial chain) and wave 0 does the two triangular solves
+// with b held two entries per lane.
 __global__ __launch_bounds__(256) void k_qi_refine(const float* __restrict__ g, int64_t n,
                                                   const float* __restrict__ p, const int32_t* __restrict__ row_ptr,
                                                   const int32_t* __restrict__ col_idx, float* __restrict__ vals) {
   constexpr int KM = qi::KMAX, NBM = KM / 4, MAXP = (NBM * (NBM + 1) / 2 + 255) / 256;
   __shared__ int sidx[KM];
   __shared__ __align__(16) float colb[2][KM];
-  __shared__ float Ls[KM][KM + 1];
+  __shared__ float Lp[KM * (KM + 1) / 2];  // L packed by rows: L[i][l] at i (i + 1) / 2 + l
+  __shared__ float invd[KM];
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x;
   const int base = row_ptr[r];
@@ -351,17 +356,27 @@ __global__ __launch_bounds__(256) void k_qi_refine(const float* __restrict__ g, 
     }
     pbi[m] = bi;
     pbj[m] = bj;
+    // every thread issues its 16 gathers unconditionally (indices clamped into
+    // the support) so that they are all in flight at once; padding and empty
+    // slots are patched afterwards
+    const int ib = bi < 0 ? 0 : bi, jb0 = bj < 0 ? 0 : bj;
+    int64_t rowoff[4];
+    int colv[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      rowoff[x] = (int64_t)sidx[min(4 * ib + x, k - 1)] * n;
+      colv[x] = sidx[min(4 * jb0 + x, k - 1)];
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) acc[m][x][y] = g[rowoff[x] + colv[y]];
 #pragma unroll
     for (int x = 0; x < 4; ++x)
 #pragma unroll
       for (int y = 0; y < 4; ++y) {
-        const int i = 4 * bi + x, l = 4 * bj + y;
-        float v = 0.f;
-        if (bi >= 0) {
-          if (i < k && l < k) v = g[(int64_t)sidx[i] * n + sidx[l]];
-          else if (i == l) v = 1.f;
-        }
-        acc[m][x][y] = v;
+        const int i = 4 * ib + x, l = 4 * jb0 + y;
+        if (bi < 0 || i >= k || l >= k) acc[m][x][y] = (bi >= 0 && i == l) ? 1.f : 0.f;
       }
   }
   for (int j = 0; j < kp; ++j) {
@@ -374,8 +389,9 @@ __global__ __launch_bounds__(256) void k_qi_refine(const float* __restrict__ g, 
         for (int x = 0; x < 4; ++x) cb[4 * pbi[m] + x] = qi_pick(acc[m][x], jy);
       }
     __syncthreads();
-    const float d = __builtin_sqrtf(cb[j]);
-    const float rd = 1.f / d;
+    const float rd = __builtin_amdgcn_rsqf(cb[j]);  // 1 / L[j][j]
+    const float d = cb[j] * rd;
+    if (tid == 0) invd[j] = rd;
 #pragma unroll
     for (int m = 0; m < MAXP; ++m) {
       if (pbj[m] < jb) continue;  // also skips the empty slots (-1)
@@ -411,21 +427,24 @@ __global__ __launch_bounds__(256) void k_qi_refine(const float* __restrict__ g, 
 #pragma unroll
       for (int y = 0; y < 4; ++y) {
         const int i = 4 * pbi[m] + x, l = 4 * pbj[m] + y;
-        if (l <= i) Ls[i][l] = acc[m][x][y];
+        if (l <= i) Lp[i * (i + 1) / 2 + l] = acc[m][x][y];
       }
   }
   __syncthreads();
   if (tid >= 64) return;
   const int lane = tid;
+  const int r0 = lane * (lane + 1) / 2, r1 = (lane + 64) * (lane + 65) / 2;
   const float* pr = p + r * n;
-  float b0 = lane < k ? pr[sidx[lane]] : 0.f;
-  float b1 = lane + 64 < k ? pr[sidx[lane + 64]] : 0.f;
+  float b0 = pr[sidx[min(lane, k - 1)]];
+  float b1 = pr[sidx[min(lane + 64, k - 1)]];
+  if (lane >= k) b0 = 0.f;
+  if (lane + 64 >= k) b1 = 0.f;
   // L y = b
   for (int j = 0; j < kp; ++j) {
     const int src = __builtin_bit_cast(int, j < 64 ? b0 : b1);
-    const float yj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(src, j & 63)) / Ls[j][j];
-    if (lane > j) b0 = fmaf(-Ls[lane][j], yj, b0);
-    if (lane + 64 > j && lane + 64 < kp) b1 = fmaf(-Ls[lane + 64][j], yj, b1);
+    const float yj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(src, j & 63)) * invd[j];
+    if (lane > j) b0 = fmaf(-Lp[r0 + j], yj, b0);
+    if (lane + 64 > j && lane + 64 < kp) b1 = fmaf(-Lp[r1 + j], yj, b1);
     if (lane == (j & 63)) {
       if (j < 64) b0 = yj;
       else b1 = yj;
@@ -434,9 +453,10 @@ __global__ __launch_bounds__(256) void k_qi_refine(const float* __restrict__ g, 
   // L^T c = y
   for (int j = kp - 1; j >= 0; --j) {
     const int src = __builtin_bit_cast(int, j < 64 ? b0 : b1);
-    const float cj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(src, j & 63)) / Ls[j][j];
-    if (lane < j) b0 = fmaf(-Ls[j][lane], cj, b0);
-    if (lane + 64 < j) b1 = fmaf(-Ls[j][lane + 64], cj, b1);
+    const float cj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(src, j & 63)) * invd[j];
+    const int rj = j * (j + 1) / 2;
+    if (lane < j) b0 = fmaf(-Lp[rj + lane], cj, b0);
+    if (lane + 64 < j) b1 = fmaf(-Lp[rj + lane + 64], cj, b1);
     if (lane == (j & 63)) {
       if (j < 64) b0 = cj;
       else b1 = cj;
