@@ -17,8 +17,8 @@
 // Kernels: W - Q(W) (the transforms and Q are the library's FWHT and
 // dequantise-inverse kernels), an fp32 GEMM on MFMA 16x16x4 f32 tiles for G
 // (symmetric: upper blocks only, mirrored) and for F_dense G, the per-row
-// quadratic form, a per-row bitwise top-k search, and a per-row Cholesky solve with
-// the factor held in 4 x 4 register blocks.
+// quadratic form, a per-row bitwise top-k search, and a per-row blocked
+// Cholesky solve with the factor held in 4 x 4 register blocks.
 #include "io.hpp"
 #include "launch.hpp"
 
@@ -63,56 +63,72 @@ hipError_t launch_qi_sub(const void* w, int wdt, int64_t ldw, float* f, int64_t 
 // (A[k * lda + m]).  Requirements (checked by the callers): N % 128 == 0,
 // 16-byte aligned bases and strides; AM: K % 16 == 0 (rows past M read as
 // zero and are not stored); k-major A: M % 128 == 0 (k past K read as zero).
-// SYM (C = A^T A with A == B, M == N): only blocks bm <= bn are computed, and
-// each off-diagonal block also writes its mirror.
+// SYM (C = A^T A with A == B, M == N): only the tiles that reach the upper
+// triangle are computed (those inside a 128 x 128 diagonal block in full),
+// and the others also write their mirror.
 //
-// 256 threads = 4 waves in 2 x 2, each wave a 64 x 64 quarter of the 128 x 128
-// block as 4 x 4 MFMA 16x16x4 tiles (operand lane l: row/col l % 16, k l / 16;
-// result register r of lane l: row 4 (l / 16) + r, col l % 16).  The next
-// k-step's global loads are in flight while the current one is multiplied.
-template <bool AM, bool SYM>
+// Block tile BM x 128 (BM 128 or 64), 256 threads = 4 waves in 2 x 2, each
+// wave a (BM / 2) x 64 part as (BM / 32) x 4 MFMA 16x16x4 tiles (operand lane
+// l: row/col l % 16, k l / 16; result register r of lane l: row 4 (l / 16) + r,
+// col l % 16).  The next k-step's global loads are in flight while the
+// current one is multiplied.
+template <bool AM, bool SYM, int BM>
 __global__ __launch_bounds__(256) void k_qi_gemm(const float* __restrict__ A, int64_t lda,
                                                 const float* __restrict__ B, int64_t ldb, float* __restrict__ C,
                                                 int64_t ldc, int64_t M, int64_t K, float beta) {
   using namespace qi;
-  __shared__ __align__(16) float As[KS][LDT];
+  constexpr int MT = BM / 32;          // MFMA row tiles per wave
+  constexpr int AL = BM * KS / 4 / 256;  // float4 loads of A per thread and k-step
+  constexpr int BL = BT * KS / 4 / 256;  // and of B
+  static_assert(KS == 16, "the scheduling groups below count a 16-deep k-step");
+  __shared__ __align__(16) float As[KS][BM + 16];
   __shared__ __align__(16) float Bs[KS][LDT];
   const int bn = blockIdx.x, bm = blockIdx.y;
-  if (SYM && bm > bn) return;
-  const int64_t m0 = (int64_t)bm * BT, n0 = (int64_t)bn * BT;
+  if (SYM && bm * BM >= (bn + 1) * BT) return;
+  const bool mirror = SYM && (bm * BM) / BT != bn;
+  const int64_t m0 = (int64_t)bm * BM, n0 = (int64_t)bn * BT;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+  const int wm = (w >> 1) * (BM / 2), wn = (w & 1) * 64;
   const int li = lane & 15, lk = lane >> 4;
-  f32x4 acc[4][4];
+  f32x4 acc[MT][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 ga[2], gb[2];
+  f32x4 ga[AL], gb[BL];
   auto load = [&](int64_t k0) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < BL; ++h) {
       const int e = tid + 256 * h;
       const int64_t kb = k0 + (e >> 5);
       gb[h] = kb < K ? ldg<f32x4>(B + kb * ldb + n0 + (e & 31) * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int h = 0; h < AL; ++h) {
+      const int e = tid + 256 * h;
       if constexpr (AM) {
-        const int64_t m = m0 + (e >> 2);
-        ga[h] = m < M ? ldg<f32x4>(A + m * lda + k0 + (e & 3) * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        const int64_t m = m0 + e / (KS / 4);
+        ga[h] = m < M ? ldg<f32x4>(A + m * lda + k0 + (e % (KS / 4)) * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
       } else {
-        ga[h] = kb < K ? ldg<f32x4>(A + kb * lda + m0 + (e & 31) * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        const int64_t kb = k0 + e / (BM / 4);
+        ga[h] = kb < K ? ldg<f32x4>(A + kb * lda + m0 + (e % (BM / 4)) * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
   };
   auto stage = [&]() {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < BL; ++h) {
       const int e = tid + 256 * h;
       *reinterpret_cast<f32x4*>(&Bs[e >> 5][(e & 31) * 4]) = gb[h];
+    }
+#pragma unroll
+    for (int h = 0; h < AL; ++h) {
+      const int e = tid + 256 * h;
       if constexpr (AM) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) As[(e & 3) * 4 + q][e >> 2] = ga[h][q];
+        for (int q = 0; q < 4; ++q) As[(e % (KS / 4)) * 4 + q][e / (KS / 4)] = ga[h][q];
       } else {
-        *reinterpret_cast<f32x4*>(&As[e >> 5][(e & 31) * 4]) = ga[h];
+        *reinterpret_cast<f32x4*>(&As[e / (BM / 4)][(e % (BM / 4)) * 4]) = ga[h];
       }
     }
   };
@@ -121,24 +137,32 @@ __global__ __launch_bounds__(256) void k_qi_gemm(const float* __restrict__ A, in
     stage();
     __syncthreads();
     if (k0 + KS < K) load(k0 + KS);
+    // all of the k-step's operands first (one LDS wait), then the MFMAs back to back
+    float a[KS / 4][MT], b[KS / 4][4];
 #pragma unroll
-    for (int kk = 0; kk < KS; kk += 4) {
-      float a[4], b[4];
+    for (int kk = 0; kk < KS / 4; ++kk) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = As[kk + lk][wm + i * 16 + li];
+      for (int i = 0; i < MT; ++i) a[kk][i] = As[4 * kk + lk][wm + i * 16 + li];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = Bs[kk + lk][wn + j * 16 + li];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 4; ++j) b[kk][j] = Bs[4 * kk + lk][wn + j * 16 + li];
     }
+#pragma unroll
+    for (int kk = 0; kk < KS / 4; ++kk)
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk][i], b[kk][j], acc[i][j], 0, 0, 0);
+    // keep that order: the next k-step's global loads, every LDS read, then the MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x020, AL + BL, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * (MT + 4), 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * MT * 4, 0);
     __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t m = m0 + wm + i * 16 + 4 * lk + r, c = n0 + wn + j * 16 + li;
@@ -146,18 +170,27 @@ __global__ __launch_bounds__(256) void k_qi_gemm(const float* __restrict__ A, in
         float v = acc[i][j][r];
         if (beta != 0.f) v = fmaf(beta, C[m * ldc + c], v);
         C[m * ldc + c] = v;
-        if (SYM && bm != bn) {
-          float u = acc[i][j][r];
-          if (beta != 0.f) u = fmaf(beta, C[c * ldc + m], u);
-          C[c * ldc + m] = u;
-        }
       }
+      if (mirror) {
+        // the mirror C[c][m .. m + 3]: a lane's four registers are consecutive m
+        const int64_t m = m0 + wm + i * 16 + 4 * lk, c = n0 + wn + j * 16 + li;
+        f32x4 u = acc[i][j];
+        if (beta != 0.f) {
+          const f32x4 o = ldg<f32x4>(C + c * ldc + m);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) u[e] = fmaf(beta, o[e], u[e]);
+        }
+        stg<f32x4>(C + c * ldc + m, u);
+      }
+    }
 }
 
-// G = beta G + Z^T Z, Z [T][n] (row stride n), n % 128 == 0
+// G = beta G + Z^T Z, Z [T][n] (row stride n), n % 128 == 0.  64-row tiles:
+// about twice as many upper-triangle tiles as CUs' worth of 128 x 128 ones,
+// which evens out the work per CU.
 hipError_t launch_qi_gram(const float* z, int64_t T, int64_t n, float* g, float beta, hipStream_t s) {
-  const dim3 grid((unsigned)(n / qi::BT), (unsigned)(n / qi::BT));
-  hipLaunchKernelGGL((k_qi_gemm<false, true>), grid, dim3(256), 0, s, z, n, z, n, g, n, n, T, beta);
+  const dim3 grid((unsigned)(n / qi::BT), (unsigned)(n / 64));
+  hipLaunchKernelGGL((k_qi_gemm<false, true, 64>), grid, dim3(256), 0, s, z, n, z, n, g, n, n, T, beta);
   return hipGetLastError();
 }
 
@@ -165,7 +198,7 @@ hipError_t launch_qi_gram(const float* z, int64_t T, int64_t n, float* g, float 
 hipError_t launch_qi_fg(const float* f, int64_t ldf, int64_t rows, int64_t n, const float* g, float* p,
                         hipStream_t s) {
   const dim3 grid((unsigned)(n / qi::BT), (unsigned)((rows + qi::BT - 1) / qi::BT));
-  hipLaunchKernelGGL((k_qi_gemm<true, false>), grid, dim3(256), 0, s, f, ldf, g, n, p, n, rows, n, 0.f);
+  hipLaunchKernelGGL((k_qi_gemm<true, false, 128>), grid, dim3(256), 0, s, f, ldf, g, n, p, n, rows, n, 0.f);
   return hipGetLastError();
 }
 
@@ -307,29 +340,31 @@ hipError_t launch_qi_select(const float* f, int64_t ldf, int64_t rows, int n, co
   return hipGetLastError();
 }
 
-__device__ __forceinline__ float qi_pick(const float (&v)[4], int i) {
-  return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
-}
-
 // Per row r with support E (k = |E| <= KMAX): the normal equations
 // G[E][E] c = P[r][E] (P = F_dense G), solved by Cholesky G[E][E] = L L^T,
 // L y = b, L^T c = y; vals[row_ptr[r] + a] = c_a.  Rows with k > KMAX get NaN.
-// G[E][E] is padded to a multiple of 4 with identity rows.  Each thread holds
-// up to MAXP 4 x 4 blocks of the lower block triangle in registers; step j of
-// the right-looking factorisation publishes column j through LDS (double
-// buffered: one barrier per step), and every thread scales it by the pivot's
-// reciprocal square root and updates its own trailing blocks.  L then goes to
-// LDS packed by rows (with the reciprocal diagonal alongside, so no division
-// sits on the solves' serial chain) and wave 0 does the two triangular solves
-// with b held two entries per lane.
+//
+// Blocked by 4: G[E][E] is padded to kp = 4 ceil(k / 4) with identity rows and
+// cut into 4 x 4 blocks; each thread owns up to MAXP blocks of the lower block
+// triangle in registers, and the right-hand side rides along as one more
+// block row R (its row 0 holds b), so that the factorisation turns it into y
+// (forward substitution for free).  Block step J: the owner of (J, J)
+// factorises it in registers and publishes L_JJ and its reciprocal diagonal;
+// the owners of (I, J), I > J (R included), form L_IJ = A_IJ L_JJ^-T and
+// publish it; every owner of (I, K), K > J, subtracts L_IJ L_KJ^T.  Two
+// barriers per block step.  Back substitution then walks J downwards: the
+// owner of (J, J) solves L_JJ^T c_J = y_J, and the owners of (J, K), K < J,
+// subtract L_JK^T c_J from y_K (one writer per K and step).  L never leaves
+// the registers; pivots use the reciprocal square root.
 __global__ __launch_bounds__(256) void k_qi_refine(const float* __restrict__ g, int64_t n,
                                                   const float* __restrict__ p, const int32_t* __restrict__ row_ptr,
                                                   const int32_t* __restrict__ col_idx, float* __restrict__ vals) {
-  constexpr int KM = qi::KMAX, NBM = KM / 4, MAXP = (NBM * (NBM + 1) / 2 + 255) / 256;
+  constexpr int KM = qi::KMAX, NBM = KM / 4, MAXP = (NBM * (NBM + 1) / 2 + NBM + 255) / 256;
   __shared__ int sidx[KM];
-  __shared__ __align__(16) float colb[2][KM];
-  __shared__ float Lp[KM * (KM + 1) / 2];  // L packed by rows: L[i][l] at i (i + 1) / 2 + l
-  __shared__ float invd[KM];
+  __shared__ __align__(16) float panel[KM + 4][4];  // L_IJ rows of the current block column; row KM: R
+  __shared__ __align__(16) float ljj[16];           // L_JJ row-major
+  __shared__ float invd[KM];                         // 1 / L[i][i]
+  __shared__ float yv[KM];                           // y, then c
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x;
   const int base = row_ptr[r];
@@ -341,9 +376,11 @@ __global__ __launch_bounds__(256) void k_qi_refine(const float* __restrict__ g, 
   }
   for (int i = tid; i < KM; i += 256) sidx[i] = i < k ? col_idx[base + i] : 0;
   __syncthreads();
-  const int nb = (k + 3) >> 2, npair = nb * (nb + 1) / 2, kp = 4 * nb;
+  const int nb = (k + 3) >> 2, npair = nb * (nb + 1) / 2;
+  // slot m: a lower block (bi >= bj), an R block (bi == nb), or empty (-1)
   int pbi[MAXP], pbj[MAXP];
   float acc[MAXP][4][4];
+  const float* pr = p + r * n;
 #pragma unroll
   for (int m = 0; m < MAXP; ++m) {
     const int q = tid + 256 * m;
@@ -353,13 +390,14 @@ __global__ __launch_bounds__(256) void k_qi_refine(const float* __restrict__ g, 
       while ((bi + 1) * (bi + 2) / 2 <= q) ++bi;
       while (bi * (bi + 1) / 2 > q) --bi;
       bj = q - bi * (bi + 1) / 2;
+    } else if (q < npair + nb) {
+      bi = nb;
+      bj = q - npair;
     }
     pbi[m] = bi;
     pbj[m] = bj;
-    // every thread issues its 16 gathers unconditionally (indices clamped into
-    // the support) so that they are all in flight at once; padding and empty
-    // slots are patched afterwards
-    const int ib = bi < 0 ? 0 : bi, jb0 = bj < 0 ? 0 : bj;
+    // gathers issued unconditionally (indices clamped into the support), patched below
+    const int ib = (bi < 0 || bi == nb) ? 0 : bi, jb0 = bj < 0 ? 0 : bj;
     int64_t rowoff[4];
     int colv[4];
 #pragma unroll
@@ -367,103 +405,152 @@ __global__ __launch_bounds__(256) void k_qi_refine(const float* __restrict__ g, 
       rowoff[x] = (int64_t)sidx[min(4 * ib + x, k - 1)] * n;
       colv[x] = sidx[min(4 * jb0 + x, k - 1)];
     }
+    if (bi == nb) {
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+      for (int y = 0; y < 4; ++y) acc[m][0][y] = 4 * jb0 + y < k ? pr[colv[y]] : 0.f;
 #pragma unroll
-      for (int y = 0; y < 4; ++y) acc[m][x][y] = g[rowoff[x] + colv[y]];
+      for (int x = 1; x < 4; ++x)
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        const int i = 4 * ib + x, l = 4 * jb0 + y;
-        if (bi < 0 || i >= k || l >= k) acc[m][x][y] = (bi >= 0 && i == l) ? 1.f : 0.f;
-      }
-  }
-  for (int j = 0; j < kp; ++j) {
-    float* cb = colb[j & 1];
-    const int jb = j >> 2, jy = j & 3;
-#pragma unroll
-    for (int m = 0; m < MAXP; ++m)
-      if (pbj[m] == jb) {
-#pragma unroll
-        for (int x = 0; x < 4; ++x) cb[4 * pbi[m] + x] = qi_pick(acc[m][x], jy);
-      }
-    __syncthreads();
-    const float rd = __builtin_amdgcn_rsqf(cb[j]);  // 1 / L[j][j]
-    const float d = cb[j] * rd;
-    if (tid == 0) invd[j] = rd;
-#pragma unroll
-    for (int m = 0; m < MAXP; ++m) {
-      if (pbj[m] < jb) continue;  // also skips the empty slots (-1)
-      const int i0 = 4 * pbi[m], l0 = 4 * pbj[m];
-      const f32x4 ca = *reinterpret_cast<const f32x4*>(&cb[i0]);
-      const f32x4 cl = *reinterpret_cast<const f32x4*>(&cb[l0]);
-      float a[4], b[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) a[x] = i0 + x > j ? ca[x] * rd : 0.f;
-#pragma unroll
-      for (int y = 0; y < 4; ++y) b[y] = l0 + y > j ? cl[y] * rd : 0.f;
+        for (int y = 0; y < 4; ++y) acc[m][x][y] = 0.f;
+    } else {
 #pragma unroll
       for (int x = 0; x < 4; ++x)
 #pragma unroll
-        for (int y = 0; y < 4; ++y) acc[m][x][y] = fmaf(-a[x], b[y], acc[m][x][y]);
-      if (pbj[m] == jb) {
+        for (int y = 0; y < 4; ++y) acc[m][x][y] = g[rowoff[x] + colv[y]];
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+          const int i = 4 * ib + x, l = 4 * jb0 + y;
+          if (bi < 0 || i >= k || l >= k) acc[m][x][y] = (bi >= 0 && i == l) ? 1.f : 0.f;
+        }
+    }
+  }
+  for (int J = 0; J < nb; ++J) {
+    // (1) the diagonal block
+#pragma unroll
+    for (int m = 0; m < MAXP; ++m) {
+      if (pbi[m] != J || pbj[m] != J) continue;
+      float(&a)[4][4] = acc[m];
+      const float i0 = __builtin_amdgcn_rsqf(a[0][0]);
+      a[0][0] *= i0;
+      a[1][0] *= i0;
+      a[2][0] *= i0;
+      a[3][0] *= i0;
+      a[1][1] = fmaf(-a[1][0], a[1][0], a[1][1]);
+      const float i1 = __builtin_amdgcn_rsqf(a[1][1]);
+      a[1][1] *= i1;
+      a[2][1] = fmaf(-a[2][0], a[1][0], a[2][1]) * i1;
+      a[3][1] = fmaf(-a[3][0], a[1][0], a[3][1]) * i1;
+      a[2][2] = fmaf(-a[2][1], a[2][1], fmaf(-a[2][0], a[2][0], a[2][2]));
+      const float i2 = __builtin_amdgcn_rsqf(a[2][2]);
+      a[2][2] *= i2;
+      a[3][2] = fmaf(-a[3][1], a[2][1], fmaf(-a[3][0], a[2][0], a[3][2])) * i2;
+      a[3][3] = fmaf(-a[3][2], a[3][2], fmaf(-a[3][1], a[3][1], fmaf(-a[3][0], a[3][0], a[3][3])));
+      const float i3 = __builtin_amdgcn_rsqf(a[3][3]);
+      a[3][3] *= i3;
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) ljj[4 * x + y] = y <= x ? a[x][y] : 0.f;
+      invd[4 * J + 0] = i0;
+      invd[4 * J + 1] = i1;
+      invd[4 * J + 2] = i2;
+      invd[4 * J + 3] = i3;
+    }
+    __syncthreads();
+    // (2) the panel below it: L_IJ = A_IJ L_JJ^-T, row by row
+    {
+      float L[4][4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&ljj[4 * x]);
+        L[x][0] = v[0];
+        L[x][1] = v[1];
+        L[x][2] = v[2];
+        L[x][3] = v[3];
+      }
+      const float d0 = invd[4 * J], d1 = invd[4 * J + 1], d2 = invd[4 * J + 2], d3 = invd[4 * J + 3];
+#pragma unroll
+      for (int m = 0; m < MAXP; ++m) {
+        if (pbj[m] != J || pbi[m] <= J) continue;
+        float(&a)[4][4] = acc[m];
+        const int prow = pbi[m] == nb ? KM : 4 * pbi[m];
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-          const int i = i0 + x;
-#pragma unroll
-          for (int y = 0; y < 4; ++y)
-            if (y == jy && i >= j) acc[m][x][y] = i == j ? d : a[x];
+          const float l0 = a[x][0] * d0;
+          const float l1 = fmaf(-l0, L[1][0], a[x][1]) * d1;
+          const float l2 = fmaf(-l1, L[2][1], fmaf(-l0, L[2][0], a[x][2])) * d2;
+          const float l3 = fmaf(-l2, L[3][2], fmaf(-l1, L[3][1], fmaf(-l0, L[3][0], a[x][3]))) * d3;
+          a[x][0] = l0;
+          a[x][1] = l1;
+          a[x][2] = l2;
+          a[x][3] = l3;
+          *reinterpret_cast<f32x4*>(&panel[prow + x][0]) = f32x4{l0, l1, l2, l3};
         }
       }
     }
-  }
-  // L (lower triangle) to LDS
+    __syncthreads();
+    // (3) trailing update A_IK -= L_IJ L_KJ^T for the blocks right of column J
 #pragma unroll
-  for (int m = 0; m < MAXP; ++m) {
-    if (pbi[m] < 0) continue;
+    for (int m = 0; m < MAXP; ++m) {
+      if (pbj[m] <= J) continue;  // also skips empty slots (-1)
+      const int prow = pbi[m] == nb ? KM : 4 * pbi[m], krow = 4 * pbj[m];
+      f32x4 li[4], lk[4];
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        const int i = 4 * pbi[m] + x, l = 4 * pbj[m] + y;
-        if (l <= i) Lp[i * (i + 1) / 2 + l] = acc[m][x][y];
+      for (int x = 0; x < 4; ++x) {
+        li[x] = *reinterpret_cast<const f32x4*>(&panel[prow + x][0]);
+        lk[x] = *reinterpret_cast<const f32x4*>(&panel[krow + x][0]);
       }
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+          float v = acc[m][x][y];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) v = fmaf(-li[x][c], lk[y][c], v);
+          acc[m][x][y] = v;
+        }
+    }
   }
+  // y (row 0 of the R blocks) to LDS
+#pragma unroll
+  for (int m = 0; m < MAXP; ++m)
+    if (pbi[m] == nb) {
+#pragma unroll
+      for (int y = 0; y < 4; ++y) yv[4 * pbj[m] + y] = acc[m][0][y];
+    }
   __syncthreads();
-  if (tid >= 64) return;
-  const int lane = tid;
-  const int r0 = lane * (lane + 1) / 2, r1 = (lane + 64) * (lane + 65) / 2;
-  const float* pr = p + r * n;
-  float b0 = pr[sidx[min(lane, k - 1)]];
-  float b1 = pr[sidx[min(lane + 64, k - 1)]];
-  if (lane >= k) b0 = 0.f;
-  if (lane + 64 >= k) b1 = 0.f;
-  // L y = b
-  for (int j = 0; j < kp; ++j) {
-    const int src = __builtin_bit_cast(int, j < 64 ? b0 : b1);
-    const float yj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(src, j & 63)) * invd[j];
-    if (lane > j) b0 = fmaf(-Lp[r0 + j], yj, b0);
-    if (lane + 64 > j && lane + 64 < kp) b1 = fmaf(-Lp[r1 + j], yj, b1);
-    if (lane == (j & 63)) {
-      if (j < 64) b0 = yj;
-      else b1 = yj;
+  for (int J = nb - 1; J >= 0; --J) {
+    // L_JJ^T c_J = y_J
+#pragma unroll
+    for (int m = 0; m < MAXP; ++m) {
+      if (pbi[m] != J || pbj[m] != J) continue;
+      const float(&a)[4][4] = acc[m];
+      const float c3 = yv[4 * J + 3] * invd[4 * J + 3];
+      const float c2 = fmaf(-a[3][2], c3, yv[4 * J + 2]) * invd[4 * J + 2];
+      const float c1 = fmaf(-a[3][1], c3, fmaf(-a[2][1], c2, yv[4 * J + 1])) * invd[4 * J + 1];
+      const float c0 = fmaf(-a[3][0], c3, fmaf(-a[2][0], c2, fmaf(-a[1][0], c1, yv[4 * J]))) * invd[4 * J];
+      yv[4 * J] = c0;
+      yv[4 * J + 1] = c1;
+      yv[4 * J + 2] = c2;
+      yv[4 * J + 3] = c3;
     }
-  }
-  // L^T c = y
-  for (int j = kp - 1; j >= 0; --j) {
-    const int src = __builtin_bit_cast(int, j < 64 ? b0 : b1);
-    const float cj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(src, j & 63)) * invd[j];
-    const int rj = j * (j + 1) / 2;
-    if (lane < j) b0 = fmaf(-Lp[rj + lane], cj, b0);
-    if (lane + 64 < j) b1 = fmaf(-Lp[rj + lane + 64], cj, b1);
-    if (lane == (j & 63)) {
-      if (j < 64) b0 = cj;
-      else b1 = cj;
+    __syncthreads();
+    // y_K -= L_JK^T c_J for K < J
+#pragma unroll
+    for (int m = 0; m < MAXP; ++m) {
+      if (pbi[m] != J || pbj[m] >= J || pbj[m] < 0) continue;
+      const float(&a)[4][4] = acc[m];
+      const int K = pbj[m];
+      const float c0 = yv[4 * J], c1 = yv[4 * J + 1], c2 = yv[4 * J + 2], c3 = yv[4 * J + 3];
+#pragma unroll
+      for (int y = 0; y < 4; ++y)
+        yv[4 * K + y] = fmaf(-a[3][y], c3, fmaf(-a[2][y], c2, fmaf(-a[1][y], c1, fmaf(-a[0][y], c0, yv[4 * K + y]))));
     }
+    __syncthreads();
   }
-  if (lane < k) vals[base + lane] = b0;
-  if (lane + 64 < k) vals[base + lane + 64] = b1;
+  for (int i = tid; i < k; i += 256) vals[base + i] = yv[i];
 }
 
 hipError_t launch_qi_refine(const float* g, int64_t n, const float* p, int64_t rows, const int32_t* row_ptr,
