@@ -371,8 +371,9 @@ whtq_status qwha_init_select(const float* f, int64_t rows, int64_t n, int64_t ld
  *   with G[E][E] c = P[o][E], E = col_idx[row_ptr[o] .. row_ptr[o+1]) (from
  *   qwha_init_select), p row stride n.  Cholesky factorisation in fp32; a row
  *   whose G[E][E] is not positive definite (fewer calibration tokens than
- *   its budget, a zero input) gives non-finite values; a row whose budget
- *   exceeds WHTQ_QWHA_INIT_MAX_SUPPORT gives NaN.
+ *   its budget) gives values without meaning, NaN where a pivot is zero or
+ *   negative (a zero G gives NaN throughout); a row whose budget exceeds
+ *   WHTQ_QWHA_INIT_MAX_SUPPORT gives NaN.
  */
 whtq_status qwha_init_refine(const float* g, int64_t n, const float* p, int64_t rows, const int32_t* row_ptr,
                              const int32_t* col_idx, float* vals, void* stream);

@@ -261,3 +261,33 @@ def test_initialize_full_size_sampled():
     rng = np.random.default_rng(11)
     sample = np.unique(np.concatenate([rng.choice(4096, 40, replace=False), [0, 4095]]))
     end_to_end(d, d["total"], d["floor"], d["cap"], sample=sample)
+
+
+def test_refine_zero_gram_is_nan():
+    """A zero Gram matrix (no calibration signal) has zero pivots: every
+    value comes out NaN, and rows without a budget are left alone."""
+    n = 256
+    g = torch.zeros((n, n), dtype=torch.float32, device="cuda:0")
+    p = torch.zeros((3, n), dtype=torch.float32, device="cuda:0")
+    row_ptr = i32([0, 8, 8, 20])
+    cols = i32(list(range(8)) + list(range(100, 112)))
+    vals = torch.full((20,), 7.0, dtype=torch.float32, device="cuda:0")
+    W().qwha_init_refine(g, p, row_ptr, cols, vals=vals)
+    assert torch.isnan(vals).all()
+
+
+def test_initialize_on_a_side_stream():
+    """The chain runs on the caller's current stream; results match the
+    default-stream run bit for bit."""
+    d = synth.qinit_layer(380, 96, 512, 200, 2, 32)
+    w64, s, codes, s16 = quantized(d)
+    args = (dev(d["w"]), dev(codes), scales_dev(s16), mask_dev(d["signs"]), 2, 32, dev(d["x"]), 96 * 20, 4, 64)
+    ref = W().qwha_initialize(*args)
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        got = W().qwha_initialize(*args)
+    st.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a.cpu(), b.cpu())
+
