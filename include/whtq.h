@@ -327,7 +327,8 @@ whtq_status qwha_init_error_coeffs(const void* w, whtq_dtype w_dtype, int64_t ro
  * qwha_init_gram -- g (device fp32 [n][n], row stride n) = Z^T Z, or
  *   g + Z^T Z with accumulate = 1, Z = x Hn for tokens rows of x (bf16, fp16
  *   or fp32, row stride ldx).  z: device fp32 workspace [tokens][n] that
- *   receives Z.  tokens = 0 with accumulate = 0 zeroes g.
+ *   receives Z (z == g is WHTQ_EINVAL).  tokens = 0 with accumulate = 0
+ *   zeroes g.
  */
 whtq_status qwha_init_gram(const void* x, whtq_dtype x_dtype, int64_t tokens, int64_t n, int64_t ldx, float* z,
                            float* g, int accumulate, void* stream);
@@ -336,6 +337,7 @@ whtq_status qwha_init_gram(const void* x, whtq_dtype x_dtype, int64_t tokens, in
  * qwha_init_channel_errors -- p (device fp32 [rows][n], row stride n) =
  *   F_dense G and err[o] (device fp32[rows]) = sqrt(max(0, p[o] . f[o])),
  *   the activation error of channel o.  g symmetric (from qwha_init_gram).
+ *   p or err equal to f, g or each other is WHTQ_EINVAL.
  */
 whtq_status qwha_init_channel_errors(const float* f, int64_t rows, int64_t n, int64_t ldf, const float* g,
                                      float* p, float* err, void* stream);

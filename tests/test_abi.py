@@ -312,7 +312,8 @@ def test_qwha_init_error_coeffs_validation(lib):
     assert qie(lib, rows=0) == OK
 
 
-def qig(lib, x=P, xd=1, tokens=16, n=4096, ldx=4096, z=P, g=P, acc=0):
+def qig(lib, x=P, xd=1, tokens=16, n=4096, ldx=4096, z=ctypes.c_void_p(0x20000), g=ctypes.c_void_p(0x30000),
+        acc=0):
     return lib.qwha_init_gram(x, xd, tokens, n, ldx, z, g, acc, NULL)
 
 
@@ -331,9 +332,11 @@ def test_qwha_init_gram_validation(lib):
     assert qig(lib, z=P_MIS) == EALIGN
     assert qig(lib, g=P_MIS) == EALIGN
     assert qig(lib, tokens=0, acc=1, x=NULL, z=NULL) == OK
+    assert qig(lib, z=P, g=P) == EINVAL                  # z overlays g
 
 
-def qic(lib, f=P, rows=8, n=4096, ldf=4096, g=P, p=P, e=P):
+def qic(lib, f=P, rows=8, n=4096, ldf=4096, g=ctypes.c_void_p(0x20000), p=ctypes.c_void_p(0x30000),
+        e=ctypes.c_void_p(0x40000)):
     return lib.qwha_init_channel_errors(f, rows, n, ldf, g, p, e, NULL)
 
 
@@ -356,6 +359,10 @@ def test_qwha_init_device_calls_validation(lib):
     assert qic(lib, p=P_MIS) == EALIGN
     assert qic(lib, e=ctypes.c_void_p(0x10002)) == EALIGN
     assert qic(lib, rows=0) == OK
+    Q = ctypes.c_void_p(0x30000)
+    assert qic(lib, f=P, g=Q, p=P) == EINVAL             # p overlays f
+    assert qic(lib, f=Q, g=P, p=P) == EINVAL             # p overlays g
+    assert qic(lib, f=Q, g=ctypes.c_void_p(0x40000), p=P, e=P) == EINVAL   # err overlays p
     assert qis(lib, n=8192 * 2, ldf=8192 * 2) == EUNSUP
     assert qis(lib, ldf=10) == EINVAL
     for kw in ("f", "rp", "ci"):

@@ -463,6 +463,7 @@ whtq_status qwha_init_gram(const void* x, whtq_dtype x_dtype, int64_t tokens, in
   if (st != WHTQ_OK) return st;
   if (tokens < 0 || ldx < n || (accumulate != 0 && accumulate != 1)) return WHTQ_EINVAL;
   if (!g || (tokens > 0 && (!x || !z))) return WHTQ_EINVAL;
+  if (tokens > 0 && z == g) return WHTQ_EINVAL;  // Z is read while G is written
   if (!rows_aligned(x, n, ldx, dt_bytes(x_dtype)) || !aligned16(z) || !aligned16(g)) return WHTQ_EALIGN;
   if (tokens == 0 && accumulate) return WHTQ_OK;
   st = need_device();
@@ -482,6 +483,9 @@ whtq_status qwha_init_channel_errors(const float* f, int64_t rows, int64_t n, in
   if (st != WHTQ_OK) return st;
   if (rows < 0 || ldf < n) return WHTQ_EINVAL;
   if (rows > 0 && (!f || !g || !p || !err)) return WHTQ_EINVAL;
+  if (rows > 0 && (p == f || p == g || static_cast<const void*>(err) == static_cast<const void*>(f) ||
+                   static_cast<const void*>(err) == static_cast<const void*>(g) || err == p))
+    return WHTQ_EINVAL;  // outputs must not overlay the inputs
   if (!rows_aligned(f, n, ldf, 4) || !aligned16(g) || !aligned16(p) || !aligned4(err)) return WHTQ_EALIGN;
   if (rows == 0) return WHTQ_OK;
   st = need_device();
