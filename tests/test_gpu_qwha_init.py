@@ -253,6 +253,13 @@ def test_initialize_end_to_end():
     end_to_end(d, total=40 * 384, floor=8, cap=128)
 
 
+def test_initialize_end_to_end_widest():
+    """n = 8192: every kernel at its largest width (Gram and F G tiles, 32
+    values per selection thread, G indices past 2^26)."""
+    d = synth.qinit_layer(390, 160, 8192, 400, 2, 64)
+    end_to_end(d, total=48 * 160, floor=8, cap=128)
+
+
 def test_initialize_full_size_sampled():
     """The 4096 x 4096 INT4 g=128 layer with 2048 calibration tokens, budget
     262,144 (floor 16, cap 128): every error magnitude and budget, sampled
