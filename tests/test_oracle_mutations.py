@@ -230,3 +230,57 @@ def test_mutant_gram_without_transform(monkeypatch):
     _fails(ti.test_calibration_gram_bruteforce)
     _fails(ti.test_calibration_gram_normal_equations)
 
+
+
+# ---- parity rules (oracle/compare.py): each mutant is the module's own
+# function with one plausible slip written into its source
+import inspect
+import oracle.compare as C
+import test_oracle_compare as tc
+
+
+def _mutant_of(fn, old, new):
+    src = inspect.getsource(fn)
+    assert old in src, old
+    ns = dict(vars(C))
+    exec(src.replace(old, new), ns)
+    return ns[fn.__name__]
+
+
+def test_mutant_boundary_at_integers(monkeypatch):
+    monkeypatch.setattr(C, "near_boundary", _mutant_of(C.near_boundary, "np.floor(v) + 0.5", "np.rint(v)"))
+    _fails(tc.test_near_boundary_hand_worked)
+
+
+def test_mutant_absolute_window(monkeypatch):
+    monkeypatch.setattr(C, "near_boundary", _mutant_of(C.near_boundary, "window * np.abs(b)", "window"))
+    _fails(tc.test_near_boundary_hand_worked)
+
+
+def test_mutant_midpoint_without_adjacency(monkeypatch):
+    monkeypatch.setattr(C, "_fp16_midpoint_exempt",
+                        _mutant_of(C._fp16_midpoint_exempt, "return adjacent & (", "return ("))
+    _fails(tc.test_fp16_midpoint_adjacency)
+
+
+def test_mutant_rederive_with_oracle_scale(monkeypatch):
+    monkeypatch.setattr(C, "compare_quant",
+                        _mutant_of(C.compare_quant, "sd = float(s_dev[r, c])", "sd = float(s_or[r, c])"))
+    _fails(tc.test_compare_quant_scale_exempt_rederives_with_device_scale)
+
+
+def test_mutant_no_exempt_budget(monkeypatch):
+    monkeypatch.setattr(C, "compare_quant",
+                        _mutant_of(C.compare_quant, "and rep[\"exempt_frac\"] < EXEMPT_BUDGET", ""))
+    _fails(tc.test_compare_quant_code_window_and_budget)
+
+
+def test_mutant_rms_over_the_matrix(monkeypatch):
+    monkeypatch.setattr(C, "float_err",
+                        _mutant_of(C.float_err, "np.mean(o * o, axis=1, keepdims=True)", "np.mean(o * o, keepdims=True)"))
+    _fails(tc.test_float_err_row_rms_floor)
+
+
+def test_mutant_no_rms_floor(monkeypatch):
+    monkeypatch.setattr(C, "float_err", _mutant_of(C.float_err, "np.maximum(np.abs(o), rms)", "np.abs(o)"))
+    _fails(tc.test_float_err_row_rms_floor)
