@@ -5,7 +5,7 @@ import torch
 
 from oracle import hadamard as H, harp, compare
 from wht_adapters_amd import synth
-from gpu_util import dev, mask_dev, host64
+from gpu_util import write_report, dev, mask_dev, host64
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -104,13 +104,13 @@ def test_fp16_blocks_match_fp32_blocks():
 
 
 @pytest.mark.parametrize("bdt", [torch.float16, torch.float32])
-def test_full_config_8192x4096_sampled(bdt):
-    """At the full size, with fp16 blocks as bench.py times them and fp32 blocks."""
+def test_full_config_8192x4096(bdt):
+    """At the full size, with fp16 blocks as bench.py times them and fp32
+    blocks: every one of the 8192 tokens against the oracle."""
     d = synth.harp()
-    y = W().harp_rotate(dev(d["x"]), dev(flat(d["blocks"], bdt)), d["radices"], mask_dev(d["signs"]), True)
-    sel = np.r_[0:40, 4090:4110, 8150:8192]
-    want = harp.harp_rotate(synth.bf16_to_f64(d["x"][sel]), RAD, d["blocks"],
-                            s=H.signs_from_bits(d["signs"], 4096))
-    err, roww = compare.float_err(host64(y[sel]), want)
-    print(f"full config, sampled rows: max scaled error {err:.3e}, max row relative error {roww:.3e}")
+    y = host64(W().harp_rotate(dev(d["x"]), dev(flat(d["blocks"], bdt)), d["radices"], mask_dev(d["signs"]), True))
+    want = harp.harp_rotate(synth.bf16_to_f64(d["x"]), RAD, d["blocks"], s=H.signs_from_bits(d["signs"], 4096))
+    err, roww = compare.float_err(y, want)
+    write_report("parity_harp_8192x4096_" + str(bdt).split(".")[-1] + "_blocks",
+                 {"tokens": 8192, "max_scaled_err": err, "max_row_rel_err": roww, "tol": TOL})
     assert err <= TOL

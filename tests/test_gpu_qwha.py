@@ -5,7 +5,7 @@ import torch
 
 from oracle import hadamard as H, qwha, compare
 from wht_adapters_amd import synth
-from gpu_util import dev, host64
+from gpu_util import write_report, dev, host64
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -112,5 +112,6 @@ def test_full_config_2048x4096_nnz262144():
     want = qwha.qwha_forward(synth.bf16_to_f64(d["x"]), d["row_ptr"], d["col_idx"],
                              synth.bf16_to_f64(d["vals"]), d["d_out"])
     err, roww = compare.float_err(host64(y), want)
-    print(f"qwha 2048x4096 nnz 262144: max scaled error {err:.3e}, max row relative error {roww:.3e}")
+    write_report("parity_qwha_forward_2048x4096_nnz262144",
+                 {"tokens": 2048, "max_scaled_err": err, "max_row_rel_err": roww, "tol": TOL})
     assert err <= TOL
