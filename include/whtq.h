@@ -380,6 +380,17 @@ whtq_status qwha_init_select(const float* f, int64_t rows, int64_t n, int64_t ld
 whtq_status qwha_init_refine(const float* g, int64_t n, const float* p, int64_t rows, const int32_t* row_ptr,
                              const int32_t* col_idx, float* vals, void* stream);
 
+/*
+ * whtq_stream_probe -- measurement helper, not part of the transform path:
+ *   reads in_bytes of src and writes out_bytes of dst (an index pattern) with
+ *   coalesced 16-byte accesses, blocks split between the two streams in
+ *   proportion to their bytes.  It is the plain-copy reference against which
+ *   a kernel moving the same bytes reports its "% achievable" bandwidth.
+ *   Sizes must be non-negative multiples of 16 (EINVAL), pointers 16-byte
+ *   aligned (EALIGN); src is only read, dst's contents are overwritten.
+ */
+whtq_status whtq_stream_probe(const void* src, int64_t in_bytes, void* dst, int64_t out_bytes, void* stream);
+
 const char* whtq_status_string(whtq_status s);
 int whtq_last_hip_error(void); /* hipError_t behind this thread's last WHTQ_EHIP */
 int whtq_abi_version(void);

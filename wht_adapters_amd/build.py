@@ -26,9 +26,15 @@ FLAGS = [
 ]
 
 
+# per-source extra flags: the matrix-core quantiser keeps its MFMA
+# accumulators in ordinary VGPRs (the VALU stages read them directly, and the
+# AGPR form would add a copy per value and cost occupancy)
+EXTRA = {f"rq_fwd_b{b}.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"] for b in (2, 3, 4)}
+
+
 def _compile(src):
     obj = os.path.join(OUT_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     t0 = time.time()
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:

@@ -14,6 +14,7 @@
 
 namespace whtq {
 
+hipError_t launch_stream_probe(const void* src, int64_t in_bytes, void* dst, int64_t out_bytes, hipStream_t s);
 hipError_t launch_wht(int logn, int din, int dout, const void* x, void* y, int64_t rows, int64_t ldx,
                       int64_t ldy, const uint32_t* sbits, int sign_mode, float scale, hipStream_t s);
 hipError_t launch_rht_quant(int logn, int din, int bits, int logg, const void* w, int64_t rows,
@@ -118,6 +119,16 @@ extern "C" {
 int whtq_abi_version(void) { return WHTQ_ABI_VERSION; }
 
 int whtq_last_hip_error(void) { return g_last_hip; }
+
+whtq_status whtq_stream_probe(const void* src, int64_t in_bytes, void* dst, int64_t out_bytes, void* stream) {
+  if (in_bytes < 0 || out_bytes < 0 || (in_bytes & 15) || (out_bytes & 15)) return WHTQ_EINVAL;
+  if ((in_bytes > 0 && !src) || (out_bytes > 0 && !dst)) return WHTQ_EINVAL;
+  if ((src && !aligned16(src)) || (dst && !aligned16(dst))) return WHTQ_EALIGN;
+  if (in_bytes == 0 && out_bytes == 0) return WHTQ_OK;
+  whtq_status st = need_device();
+  if (st != WHTQ_OK) return st;
+  return hip_status(whtq::launch_stream_probe(src, in_bytes, dst, out_bytes, (hipStream_t)stream));
+}
 
 const char* whtq_status_string(whtq_status s) {
   switch (s) {

@@ -398,9 +398,16 @@ __global__ __launch_bounds__(Geo<LOGN>::THREADS) void k_rht_dequant(
 
 // ------------------------------------------------------------------ dispatch
 
+// 16-bit rows of n = 4096 or 8192 take the matrix-core kernel (rht_quant_mx.hpp).
+template <int LOGN, int DIN, int BITS, int LOGG>
+static hipError_t run_q_mx(const void* w, int64_t rows, int64_t ldw, const uint32_t* sb, uint8_t* codes,
+                           uint16_t* scales, hipStream_t s);
+
 template <int LOGN, int DIN, int BITS, int LOGG>
 static hipError_t run_q(const void* w, int64_t rows, int64_t ldw, const uint32_t* sb, uint8_t* codes,
                         uint16_t* scales, hipStream_t s) {
+  if constexpr ((LOGN == 12 || LOGN == 13) && DIN != DT_F32)
+    return run_q_mx<LOGN, DIN, BITS, LOGG>(w, rows, ldw, sb, codes, scales, s);
   using G = Geo<LOGN>;
   auto k = k_rht_quant<LOGN, DIN, BITS, LOGG>;
   static const int nb = blocks_per_cu(k, G::THREADS, 0);

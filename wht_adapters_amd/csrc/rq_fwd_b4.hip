@@ -1,5 +1,5 @@
 // Instances of the RHT + RTN quantiser for 4-bit codes.
-#include "rht_quant.hpp"
+#include "rht_quant_mx.hpp"
 
 namespace whtq {
 template hipError_t launch_rht_quant_bits<4>(int, int, int, const void*, int64_t, int64_t, const uint32_t*,

@@ -41,6 +41,7 @@ _SIG = {
     "qwha_init_allocate": [_vp, _i64, _i64, _i64, _int, _int, _vp],
     "qwha_init_select": [_vp, _i64, _i64, _i64, _vp, _vp, _vp],
     "qwha_init_refine": [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp],
+    "whtq_stream_probe": [_vp, _i64, _vp, _i64, _vp],
 }
 for _name, _args in _SIG.items():
     _f = getattr(_lib, _name)
@@ -509,3 +510,16 @@ def qwha_initialize(w, codes, scales, signs, bits, group, x, total, floor, cap):
     col_idx = qwha_init_select(f, row_ptr)
     vals = qwha_init_refine(g, p, row_ptr, col_idx)
     return row_ptr, col_idx, vals, err
+
+
+def stream_probe(src, dst):
+    """Measurement helper: read all bytes of `src` and write all bytes of `dst`
+    with a plain 16-byte streaming kernel (the "% achievable" reference)."""
+    _need_cuda("src", src)
+    _need_cuda("dst", dst)
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("src and dst must be contiguous")
+    ib, ob = src.numel() * src.element_size(), dst.numel() * dst.element_size()
+    with torch.cuda.device(src.device):
+        _check("whtq_stream_probe", _lib.whtq_stream_probe(_ptr(src), ib, _ptr(dst), ob, _stream(src)))
+    return dst
