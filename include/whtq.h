@@ -60,14 +60,15 @@
 extern "C" {
 #endif
 
-#define WHTQ_ABI_VERSION 2
+#define WHTQ_ABI_VERSION 3
 
 typedef enum {
   WHTQ_OK = 0,
   WHTQ_EINVAL = 1,       /* bad size, null pointer, bits/group/schedule out of rule */
   WHTQ_EUNSUPPORTED = 2, /* valid request this build has no kernel for            */
   WHTQ_EALIGN = 3,       /* pointer or row stride not 16-byte aligned              */
-  WHTQ_EHIP = 4          /* HIP runtime / launch failure, including no device      */
+  WHTQ_EHIP = 4,         /* HIP runtime / launch failure, including no device      */
+  WHTQ_ESCRATCH = 5      /* sizes need more than the library's fixed scratch array */
 } whtq_status;
 
 typedef enum { WHTQ_F32 = 0, WHTQ_BF16 = 1, WHTQ_F16 = 2, WHTQ_I8 = 3 } whtq_dtype;  /* I8: HARP parameters only */
@@ -238,6 +239,30 @@ whtq_status qwha_adapter_grad_values(const void* x, const void* dy, whtq_dtype d
                                      int64_t d_in, int64_t d_out, int64_t ldx, int64_t lddy,
                                      const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz, float* dc,
                                      void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * qwha_adapter_grad_values_noalloc -- qwha_adapter_grad_values without a
+ * workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments (minus workspace / workspace_bytes), kernels,
+ * arithmetic and results; the scratch space lives in a file-scope device
+ * array of WHTQ_QWHA_DC_SCRATCH_BYTES bytes that each GPU the library runs
+ * on holds until the process ends.  The call allocates nothing.
+ *   Sizes whose qwha_grad_values_workspace_bytes exceeds
+ *   WHTQ_QWHA_DC_SCRATCH_BYTES return WHTQ_ESCRATCH before any HIP call
+ *   (64 MiB covers 2048 tokens x 262,144 entries; roughly tokens * 16 KiB +
+ *   token slabs * nnz * 4 bytes).
+ *   Every call on one GPU shares that GPU's array: calls that overlap in time
+ *   on one GPU (different streams, or different host threads) race and give
+ *   undefined results.  Calls ordered on one stream are safe; nothing carries
+ *   over from one call to the next (every scratch byte a call reads, the
+ *   same call has written).
+ */
+#define WHTQ_QWHA_DC_SCRATCH_BYTES (64ll << 20)
+whtq_status qwha_adapter_grad_values_noalloc(const void* x, const void* dy, whtq_dtype dtype, int64_t tokens,
+                                             int64_t d_in, int64_t d_out, int64_t ldx, int64_t lddy,
+                                             const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
+                                             float* dc, void* stream);
 
 /*
  * harp_rotate -- y = Stage_{m-1}( ... Stage_0( P x ) ), P = Hn S if

@@ -38,14 +38,15 @@ def test_exports_every_declared_symbol(lib):
                           "qwha_grad_values_workspace_bytes", "qwha_adapter_grad_values",
                           "harp_build_blocks", "rht_lowbit_gemv", "qwha_init_error_coeffs",
                           "qwha_init_gram", "qwha_init_channel_errors", "qwha_init_allocate",
-                          "qwha_init_select", "qwha_init_refine"}
+                          "qwha_init_select", "qwha_init_refine", "qwha_adapter_grad_values_noalloc",
+                          "whtq_stream_probe"}
     for nm in names:
         assert hasattr(lib, nm), nm
 
 
 def test_version_and_strings(lib):
-    assert lib.whtq_abi_version() == 2
-    for s in range(5):
+    assert lib.whtq_abi_version() == 3
+    for s in range(6):
         assert lib.whtq_status_string(s)
     assert b"unknown" in lib.whtq_status_string(99)
 
@@ -229,6 +230,11 @@ def gv(lib, x=P, dy=P, dt=1, tokens=8, d_in=4096, d_out=4096, ldx=4096, lddy=409
     return lib.qwha_adapter_grad_values(x, dy, dt, tokens, d_in, d_out, ldx, lddy, rp, ci, nnz, dc, ws, wsb, NULL)
 
 
+def _gv_args(x=P, dy=P, dt=1, tokens=8, d_in=4096, d_out=4096, ldx=4096, lddy=4096, rp=P, ci=P, nnz=100,
+             dc=P):
+    return (x, dy, dt, tokens, d_in, d_out, ldx, lddy, rp, ci, nnz, dc, NULL)
+
+
 def test_qwha_backward_validation(lib):
     assert bw(lib, lddy=100) == EINVAL
     assert bw(lib, lddx=100) == EINVAL
@@ -251,6 +257,15 @@ def test_qwha_backward_validation(lib):
     assert gv(lib, x=P_MIS) == EALIGN
     assert gv(lib, ws=ctypes.c_void_p(0x10008)) == EALIGN
     assert gv(lib, nnz=0, dc=NULL, ws=NULL, wsb=0) == OK     # empty support: nothing to do
+    # the allocation-free variant: the same checks, then its fixed capacity
+    na = lambda **kw: lib.qwha_adapter_grad_values_noalloc(*_gv_args(**kw))
+    assert na(ldx=100) == EINVAL
+    assert na(dc=NULL) == EINVAL
+    assert na(d_in=2048, ldx=2048) == EUNSUP
+    assert na(x=P_MIS) == EALIGN
+    assert na(nnz=0, dc=NULL) == OK
+    assert na(tokens=5000) == 5                              # 5000 x 16 KiB of Hn x > 64 MiB
+    assert lib.qwha_grad_values_workspace_bytes(2048, 4096, 262144) <= 64 << 20
     assert lib.qwha_grad_values_workspace_bytes(8, 2048, 100) == -1
     assert lib.qwha_grad_values_workspace_bytes(0, 4096, 100) == 0
     # Hn x in fp32 (rounded up to 256 B) plus per-token-slab partial sums

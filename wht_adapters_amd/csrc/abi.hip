@@ -137,6 +137,7 @@ const char* whtq_status_string(whtq_status s) {
     case WHTQ_EUNSUPPORTED: return "unsupported configuration";
     case WHTQ_EALIGN: return "misaligned pointer or row stride";
     case WHTQ_EHIP: return "HIP runtime error";
+    case WHTQ_ESCRATCH: return "sizes exceed the fixed scratch capacity";
   }
   return "unknown status";
 }
@@ -356,6 +357,63 @@ whtq_status qwha_adapter_grad_values(const void* x, const void* dy, whtq_dtype d
   if (tokens == 0)  // an empty sum: dc = 0 (a fill kernel, not a memset node)
     return hip_status(launch_fill_zero(dc, nnz, (hipStream_t)stream));
   return hip_status(launch_qwha_dc(x, ldx, dy, lddy, tokens, d_out, row_ptr, col_idx, nnz, dc, workspace,
+                                   (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+// Scratch of the allocation-free value gradient: one array per GPU, resolved
+// to a device address once per device with that device current (the array's
+// name in host code is only a host-side handle, never a device address).
+static __device__ __align__(256) uint8_t scratch[WHTQ_QWHA_DC_SCRATCH_BYTES];
+static void* g_scratch_ptr[kMaxDevices];
+static hipError_t g_scratch_err[kMaxDevices];
+static std::once_flag g_scratch_once[kMaxDevices];
+
+static whtq_status scratch_of_current_device(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return WHTQ_EUNSUPPORTED;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return hip_status(g_scratch_err[dev]);
+  *ptr = g_scratch_ptr[dev];
+  return WHTQ_OK;
+}
+
+extern "C" {
+
+whtq_status qwha_adapter_grad_values_noalloc(const void* x, const void* dy, whtq_dtype dtype, int64_t tokens,
+                                             int64_t d_in, int64_t d_out, int64_t ldx, int64_t lddy,
+                                             const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
+                                             float* dc, void* stream) {
+  // the same checks as qwha_adapter_grad_values, then the capacity
+  if (!dt_valid(dtype)) return WHTQ_EINVAL;
+  if (tokens < 0 || d_in < 1 || d_out < 1 || nnz < 0 || ldx < d_in || lddy < d_out) return WHTQ_EINVAL;
+  if (nnz > d_in * d_out || nnz > INT32_MAX) return WHTQ_EINVAL;
+  if (!row_ptr || (nnz > 0 && (!col_idx || !dc))) return WHTQ_EINVAL;
+  if (tokens > 0 && nnz > 0 && (!x || !dy)) return WHTQ_EINVAL;
+  if (ilog2_pow2(d_in) < 0) return WHTQ_EUNSUPPORTED;
+  if (d_in != 4096 || d_out > 4096) return WHTQ_EUNSUPPORTED;
+  if (dtype != WHTQ_BF16) return WHTQ_EUNSUPPORTED;
+  if (!rows_aligned(x, d_in, ldx, 2) || (reinterpret_cast<uintptr_t>(dy) & 1u)) return WHTQ_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(row_ptr) & 3u) || (reinterpret_cast<uintptr_t>(col_idx) & 3u) ||
+      (reinterpret_cast<uintptr_t>(dc) & 3u))
+    return WHTQ_EALIGN;
+  if (tokens > 0 && nnz > 0 && qwha_dc_workspace_bytes(tokens, nnz) > WHTQ_QWHA_DC_SCRATCH_BYTES)
+    return WHTQ_ESCRATCH;
+  if (nnz == 0) return WHTQ_OK;
+  whtq_status st = need_device();
+  if (st != WHTQ_OK) return st;
+  if (tokens == 0) return hip_status(launch_fill_zero(dc, nnz, (hipStream_t)stream));
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != WHTQ_OK) return st;
+  return hip_status(launch_qwha_dc(x, ldx, dy, lddy, tokens, d_out, row_ptr, col_idx, nnz, dc, ws,
                                    (hipStream_t)stream));
 }
 

@@ -42,6 +42,8 @@ _SIG = {
     "qwha_init_select": [_vp, _i64, _i64, _i64, _vp, _vp, _vp],
     "qwha_init_refine": [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp],
     "whtq_stream_probe": [_vp, _i64, _vp, _i64, _vp],
+    "qwha_adapter_grad_values_noalloc": [_vp, _vp, _int, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp,
+                                         _vp],
 }
 for _name, _args in _SIG.items():
     _f = getattr(_lib, _name)
@@ -346,6 +348,34 @@ def qwha_adapter_grad_values(x, dy, row_ptr, col_idx, out=None, workspace=None):
         _check("qwha_adapter_grad_values", _lib.qwha_adapter_grad_values(
             _ptr(x), _ptr(dy), _DT[x.dtype], tokens, d_in, d_out, ldx, lddy, _ptr(row_ptr), _ptr(col_idx),
             nnz, _ptr(out), _ptr(workspace), wbytes, _stream(x)))
+    return out
+
+
+def qwha_adapter_grad_values_noalloc(x, dy, row_ptr, col_idx, out=None):
+    """qwha_adapter_grad_values with the library's fixed per-GPU scratch array
+    instead of a workspace (the library call allocates nothing; `out` is the
+    caller's).  Calls that overlap on one GPU race."""
+    _need_cuda("x", x)
+    _need_cuda("dy", dy)
+    tokens, d_in, ldx = _rows_ld("x", x)
+    t2, d_out, lddy = _rows_ld("dy", dy)
+    if t2 != tokens:
+        raise ValueError("x and dy must have the same number of tokens")
+    _csr_dev(row_ptr=row_ptr, col_idx=col_idx)
+    if row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+        raise ValueError("row_ptr and col_idx must be int32")
+    if row_ptr.numel() != d_out + 1:
+        raise ValueError("row_ptr must have d_out + 1 entries")
+    nnz = col_idx.numel()
+    if out is None:
+        out = torch.empty(nnz, dtype=torch.float32, device=x.device)
+    _csr_dev(out=out)
+    if out.dtype != torch.float32 or out.numel() != nnz:
+        raise ValueError("out must be float32 with nnz entries")
+    with torch.cuda.device(x.device):
+        _check("qwha_adapter_grad_values_noalloc", _lib.qwha_adapter_grad_values_noalloc(
+            _ptr(x), _ptr(dy), _DT[x.dtype], tokens, d_in, d_out, ldx, lddy, _ptr(row_ptr), _ptr(col_idx),
+            nnz, _ptr(out), _stream(x)))
     return out
 
 
