@@ -273,14 +273,25 @@ __device__ __forceinline__ void dequant_lane_h64(const uint32_t* cw, float s, fl
 }
 
 // The 64 codes (8*BITS bytes) of one lane.
+// The inverse streams codes in and rows out once each: non-temporal accesses
+// (11.4 vs 14.3 us at 4096 x 4096 INT4 on MI355X).
+template <typename V>
+__device__ __forceinline__ V ldg_dq(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+}
+template <typename V>
+__device__ __forceinline__ void stg_dq(void* p, V v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
+}
+
 template <int BITS>
 __device__ __forceinline__ void fetch_codes(const uint8_t* cr, uint32_t* cw) {
   if constexpr (BITS == 4) {
-    u32x4 a = ldg<u32x4>(cr), b = ldg<u32x4>(cr + 16);
+    u32x4 a = ldg_dq<u32x4>(cr), b = ldg_dq<u32x4>(cr + 16);
     cw[0] = a[0]; cw[1] = a[1]; cw[2] = a[2]; cw[3] = a[3];
     cw[4] = b[0]; cw[5] = b[1]; cw[6] = b[2]; cw[7] = b[3];
   } else if constexpr (BITS == 2) {
-    u32x4 a = ldg<u32x4>(cr);
+    u32x4 a = ldg_dq<u32x4>(cr);
     cw[0] = a[0]; cw[1] = a[1]; cw[2] = a[2]; cw[3] = a[3];
   } else {
 #pragma unroll
@@ -385,7 +396,7 @@ __global__ __launch_bounds__(Geo<LOGN>::THREADS) void k_rht_dequant(
                                              : pack_f16(v[c * 8 + 2 * q], v[c * 8 + 2 * q + 1]);
           wv[q] = p ^ m[c][q];
         }
-        stg<u32x4>(reinterpret_cast<uint16_t*>(orow) + i, wv);
+        stg_dq<u32x4>(reinterpret_cast<uint16_t*>(orow) + i, wv);
       }
     }
   };
