@@ -4,20 +4,30 @@
 Main workload (the one `value` is quoted on): RHT + INT4 round-to-nearest
 quantisation, bf16 weight matrix 4096 x 4096, group 128 along d_in, fp16
 scales, signed int4 codes -- one `rht_quantize_rtn` launch per step.  The
-other workloads (orthonormal FWHT 256 x 4096 fp32, the inverse of the INT4
-path, QWHA adapter forward and backward, HARP rotation with the radix-16
-schedule and with the mixed-radix 8*8*8*5*2 schedule at d = 5120, 28672 x
-8192 RHT + INT2) are timed the same way and reported under "workloads".
+other workloads (orthonormal FWHT 256 x 4096 fp32 and its row sweep, the
+inverse of the INT4 path, QWHA adapter forward and backward, HARP rotation
+with the radix-16 schedule and with the mixed-radix 8*8*8*5*2 schedule at
+d = 5120, 28672 x 8192 RHT + INT2 and its inverse, the online-RHT INT2
+product, the QWHA initialisation) are timed the same way and reported under
+"workloads".
 
-Timing: each step processes a different copy of the input, rotating over
-copies totalling >= 1 GiB so that inputs come from HBM rather than the
-256 MB last-level cache; the K launches are captured once in a HIP graph
-(no host launch overhead) and replayed inside a HIP-event pair on the
-launch stream.  Data are synthetic (seeded generators in
-wht_adapters_amd.synth, whose docstrings give each recipe) with the shapes
-and value structure of the workloads.
+Timing: every launch processes a different copy of the input, rotating over
+copies totalling >= 1 GiB, and at least one launch per copy is timed, so the
+inputs come from HBM rather than the 256 MB last-level cache.  The launches
+are captured once in a HIP graph and replayed between two HIP events on the
+launch stream, REPS times; each replay gives one per-launch time, and the
+line reports their median, p10, p90 and min (`value` uses the median).  For
+the bandwidth-bound workloads a plain 16-byte streaming kernel moving the
+same bytes (whtq_stream_probe) is timed the same way: "% achievable".
+
+Data are synthetic (seeded generators in wht_adapters_amd.synth, whose
+docstrings give each recipe) with the shapes and value structure of the
+workloads.  `python bench.py --summarize-pmc DIR...` turns rocprofv3 counter
+CSVs into profiles/counters.json (read back here, per kernel source hash).
 """
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import math
@@ -31,7 +41,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PEAK_F16_MFMA_TFLOPS = 2500.0     # dense fp16/bf16 matrix peak
+VALU_LANE_OPS = 256 * 64 * 2.4e9  # non-packed fp32 lane-ops/s: 256 CUs x 4 SIMD16 x 2.4 GHz
 GIB = 1 << 30
+REPS = 9
 
 # algorithmic HBM bytes per launch: inputs read once + outputs written once
 ALGO_BYTES = {
@@ -59,10 +72,28 @@ ROWS = {
     "rht_int2_g64_28672x8192_inverse": 28672,
     "gemv_int2_g64_28672x8192_t1": 28672,
 }
+# k_harp: per 16-token tile, six radix-16 passes of 256 16x16x16 products plus
+# the chained learned stage along digit 0 (256 more): 7 x 256 MFMAs of 8192 flop
+HARP_MFMA_FLOP = 8192 // 16 * 7 * 256 * 2 * 16 * 16 * 16
 MAIN = "rht_int4_g128_4096x4096"
-KERNEL_SOURCES = {  # sources a workload's kernel is built from (traffic counters go stale with them)
-    MAIN: ["rht_quant.hpp", "rq_fwd_b4.hip", "engine.hpp", "io.hpp", "common.hpp", "launch.hpp"],
+KERNELS = {  # kernel (as rocprofv3 names it) and the sources it is built from, per workload
+    MAIN: ("k_rht_quant_mx<12, 1, 4, 7>",
+           ["rht_quant_mx.hpp", "rht_quant.hpp", "rq_fwd_b4.hip", "engine.hpp", "io.hpp", "common.hpp",
+            "launch.hpp"]),
+    "rht_int2_g64_28672x8192": ("k_rht_quant_mx<13, 1, 2, 6>",
+                                ["rht_quant_mx.hpp", "rht_quant.hpp", "rq_fwd_b2.hip", "engine.hpp", "io.hpp",
+                                 "common.hpp", "launch.hpp"]),
+    "rht_int4_g128_4096x4096_inverse": ("k_rht_dequant<12, 4, 7, 1>",
+                                        ["rht_quant.hpp", "rq_inv_b4.hip", "engine.hpp", "io.hpp", "common.hpp",
+                                         "launch.hpp"]),
+    "rht_int2_g64_28672x8192_inverse": ("k_rht_dequant<13, 2, 6, 1>",
+                                        ["rht_quant.hpp", "rq_inv_b2.hip", "engine.hpp", "io.hpp", "common.hpp",
+                                         "launch.hpp"]),
+    "harp_8192x4096_r16x3": ("k_harp<true>", ["harp.hip", "common.hpp", "launch.hpp"]),
+    "qwha_2048x4096_nnz262144": ("k_qwha<1, false>", ["qwha.hip", "engine.hpp", "io.hpp", "common.hpp",
+                                                      "launch.hpp"]),
 }
+COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
 
 def log(*a):
@@ -77,24 +108,23 @@ def src_hash(files):
     return h.hexdigest()[:16]
 
 
-def traffic_for(name, launches_bytes):
-    """HBM bytes per launch from committed rocprofv3 PMC counters, if they
-    were taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if name not in KERNEL_SOURCES or not os.path.exists(path):
+def counters_for(name):
+    """Per-launch rocprofv3 counters committed under profiles/counters.json,
+    if they were taken on the current kernel sources; else None."""
+    if name not in KERNELS or not os.path.exists(COUNTERS):
         return None
-    with open(path) as fh:
-        tr = json.load(fh).get(name)
-    if not tr or tr.get("src_sha") != src_hash(KERNEL_SOURCES[name]):
+    with open(COUNTERS) as fh:
+        c = json.load(fh).get(name)
+    if not c or c.get("src_sha") != src_hash(KERNELS[name][1]):
         return None
-    return tr["bytes_per_launch"]
+    return c
 
 
 class Timed:
-    """K launches of `launch(i)` captured in one HIP graph, replayed between
+    """n launches of `launch(i)` captured in one HIP graph, replayed between
     two HIP events on the capture stream."""
 
-    def __init__(self, torch, launch, steps, warmup):
+    def __init__(self, torch, launch, n, warmup):
         self.torch = torch
         for i in range(warmup):
             launch(i)
@@ -105,42 +135,79 @@ class Timed:
             launch(0)                      # first call on this stream outside the capture
         torch.cuda.synchronize()
         with torch.cuda.graph(self.graph, stream=self.stream):
-            for i in range(steps):
+            for i in range(n):
                 launch(i)
         torch.cuda.synchronize()
-        self.steps = steps
+        self.n = n
 
-    def run(self):
+    def run(self, reps=REPS):
+        """Per-launch seconds, one value per replay."""
         torch = self.torch
         with torch.cuda.stream(self.stream):
             self.graph.replay()            # untimed replay: pages in the graph
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(self.stream):
-            # a ~2 ms device-side spin ahead of the start event: the host has queued
-            # the whole graph before the GPU reaches e0, so submission latency stays
-            # outside the timed region and the per-launch average is kernel time
-            torch.cuda._sleep(5_000_000)
-            e0.record(self.stream)
-            self.graph.replay()
-            e1.record(self.stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / 1e3   # seconds for self.steps launches
+        out = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(self.stream):
+                # a ~2 ms device-side spin ahead of the start event: the host has queued
+                # the whole graph before the GPU reaches e0, so submission latency stays
+                # outside the timed region and the per-launch average is kernel time
+                torch.cuda._sleep(5_000_000)
+                e0.record(self.stream)
+                self.graph.replay()
+                e1.record(self.stream)
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) / 1e3 / self.n)
+        return out
 
 
-def copies(torch, t, total_bytes=GIB, cap=64):
+def n_launch(K, ncopies):
+    """Launches per graph: K, and at least one per copy of the input."""
+    return max(K, ncopies)
+
+
+def copies(torch, t, total_bytes=GIB, cap=256):
     k = max(2, min(cap, math.ceil(total_bytes / max(1, t.numel() * t.element_size()))))
     return [t.clone() for _ in range(k)]
 
 
-def result(name, secs, steps):
-    per = secs / steps
-    gbs = ALGO_BYTES[name] / per / 1e9
-    return {"ms_per_launch": per * 1e3, "rows_per_s": ROWS[name] / per, "GBps": gbs,
-            "frac_hbm_peak": gbs / PEAK_HBM_GBS, "algo_bytes": ALGO_BYTES[name]}
+def stats(per):
+    a = np.sort(np.asarray(per, dtype=np.float64))
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "min": float(a[0]), "reps": int(a.size)}
 
 
-def bench_quant(torch, W, mask_dev, cfg, name, bits, g, steps, warmup):
+def result(name, per, rows=None, algo=None):
+    st = stats(per)
+    med = st["median"]
+    algo = ALGO_BYTES[name] if algo is None else algo
+    rows = ROWS[name] if rows is None else rows
+    gbs = algo / med / 1e9
+    return {"ms_per_launch": med * 1e3, "us_p10": st["p10"] * 1e6, "us_p90": st["p90"] * 1e6,
+            "us_min": st["min"] * 1e6, "reps": st["reps"], "rows_per_s": rows / med, "GBps": gbs,
+            "frac_hbm_peak": gbs / PEAK_HBM_GBS, "algo_bytes": algo}
+
+
+def achievable(torch, W, r, in_bytes, out_bytes, K, Wm):
+    """Time whtq_stream_probe moving the same bytes (rotated the same way) and
+    add it to the result r as the achievable reference."""
+    ib, ob = in_bytes // 16 * 16, out_bytes // 16 * 16
+    k = max(2, math.ceil(GIB / max(1, ib)))
+    srcs = [torch.empty(ib, dtype=torch.uint8, device="cuda:0") for _ in range(k)]
+    dsts = [torch.empty(max(ob, 16), dtype=torch.uint8, device="cuda:0")[:ob] for _ in range(k)]
+    for s in srcs:
+        s.fill_(1)
+    t = Timed(torch, lambda i: W.stream_probe(srcs[i % k], dsts[i % k]), n_launch(K, k), Wm)
+    med = stats(t.run())["median"]
+    r["stream_probe_us"] = med * 1e6
+    r["stream_probe_frac_hbm_peak"] = (ib + ob) / med / 1e9 / PEAK_HBM_GBS
+    r["frac_achievable"] = med / (r["ms_per_launch"] / 1e3)
+    del srcs, dsts
+    torch.cuda.empty_cache()
+
+
+def bench_quant(torch, W, mask_dev, cfg, name, bits, g, K, Wm):
     w0 = cfg["w"].to("cuda:0")
     rows, n = w0.shape
     ws = copies(torch, w0)
@@ -148,37 +215,104 @@ def bench_quant(torch, W, mask_dev, cfg, name, bits, g, steps, warmup):
     cs = [torch.empty((rows, n * bits // 8), dtype=torch.uint8, device="cuda:0") for _ in ws]
     ss = [torch.empty((rows, n // g), dtype=torch.float16, device="cuda:0") for _ in ws]
     del w0
+    nl = n_launch(K, len(ws))
     fwd = Timed(torch, lambda i: W.rht_quantize_rtn(ws[i % len(ws)], sg, bits, g, cs[i % len(ws)],
-                                                    ss[i % len(ws)]), steps, warmup)
+                                                    ss[i % len(ws)]), nl, Wm)
     outs = [torch.empty((rows, n), dtype=torch.bfloat16, device="cuda:0") for _ in ws]
     inv = Timed(torch, lambda i: W.rht_dequantize_inverse(cs[i % len(ws)], ss[i % len(ws)], sg, bits, g, n,
-                                                          out=outs[i % len(ws)]), steps, warmup)
-    r = {name: result(name, fwd.run(), steps)}
-    r[name + "_inverse"] = result(name + "_inverse", inv.run(), steps)
+                                                          out=outs[i % len(ws)]), nl, Wm)
+    r = {name: result(name, fwd.run())}
+    r[name + "_inverse"] = result(name + "_inverse", inv.run())
+    W.rht_quantize_rtn(ws[0], sg, bits, g, cs[0], ss[0])
+    torch.cuda.synchronize()
+    first = (cs[0].cpu().numpy(), ss[0].cpu().numpy())   # kept for the parity report
     del ws, cs, ss, outs
     torch.cuda.empty_cache()
+    code_b = rows * n * bits // 8 + rows * (n // g) * 2
+    achievable(torch, W, r[name], rows * n * 2, code_b, K, Wm)
+    achievable(torch, W, r[name + "_inverse"], code_b, rows * n * 2, K, Wm)
+    return r, first
+
+
+def bench_fwht(torch, W, synth, K, Wm):
+    """The 256 x 4096 fp32 FWHT, then a labelled row sweep (256 .. 65,536 rows)
+    that shows where the launch stops being latency-bound."""
+    nm = "fwht_f32_256x4096"
+    x = torch.from_numpy(synth.fwht_f32()["x"]).to("cuda:0")
+    xs = copies(torch, x)
+    ys = [torch.empty_like(x) for _ in xs]
+    t = Timed(torch, lambda i: W.wht_batched(xs[i % len(xs)], out=ys[i % len(xs)]), n_launch(K, len(xs)), Wm)
+    r = {nm: result(nm, t.run())}
+    del xs, ys
+    achievable(torch, W, r[nm], 256 * 4096 * 4, 256 * 4096 * 4, K, Wm)
+    sweep = {}
+    for rows in (256, 1024, 4096, 16384, 65536):
+        x = torch.randn((rows, 4096), device="cuda:0")
+        xs = copies(torch, x)
+        ys = [torch.empty_like(x) for _ in xs]
+        t = Timed(torch, lambda i: W.wht_batched(xs[i % len(xs)], out=ys[i % len(xs)]), n_launch(K, len(xs)), Wm)
+        s = result(nm, t.run(), rows=rows, algo=2 * rows * 4096 * 4)
+        sweep[str(rows)] = {k: s[k] for k in ("ms_per_launch", "us_p10", "us_p90", "rows_per_s", "GBps",
+                                              "frac_hbm_peak")}
+        del x, xs, ys
+        torch.cuda.empty_cache()
+    r["fwht_f32_rows_x4096_sweep"] = sweep
     return r
 
 
-def cpu_baseline(cfg, budget_s=12.0):
-    """The oracle as it stands, timed on this host on a bounded row sample of
-    the main workload."""
-    import numpy as np
+def cpu_baselines(first_main, budget_s=4.0):
+    """The oracle as it stands, timed on this host: all 4096 rows of the main
+    workload (also compared with the GPU's codes for the parity report), and
+    bounded samples of the other workloads."""
     from threadpoolctl import threadpool_info
-    from oracle import hadamard as H, rtn
+    from oracle import compare, hadamard as H, harp, qwha, rtn
     from wht_adapters_amd import synth
-    w = synth.bf16_to_f64(cfg["w"])
-    s = H.signs_from_bits(cfg["signs"], w.shape[1])
-    rows_done, t0 = 0, time.perf_counter()
-    chunk = 256
-    while rows_done < w.shape[0] and time.perf_counter() - t0 < budget_s:
-        rtn.rht_quantize(w[rows_done:rows_done + chunk], s, 4, 128)
-        rows_done += chunk
-    secs = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    return {"value": rows_done / secs, "unit": "rows/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{rows_done} of 4096 rows of the 4096x4096 INT4 g128 workload "
-                      f"(dense fp64 Sylvester product + naive RTN), {secs:.1f} s"}
+    host = len(os.sched_getaffinity(0))
+    out = {}
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        res = fn()
+        return res, time.perf_counter() - t0
+
+    # main workload, whole matrix
+    cfg = synth.rht_int4_g128()
+    w = synth.bf16_to_f64(cfg["w"])
+    s = H.signs_from_bits(cfg["signs"], 4096)
+    (codes, s16, q, v, s_pre, y), secs = timed(lambda: rtn.rht_quantize(w, s, 4, 128))
+    main = {"value": 4096 / secs, "unit": "rows/s", "cores": int(threads), "host_cores": host,
+            "kind": "oracle",
+            "sample": f"all 4096 rows of the 4096x4096 INT4 g128 workload (dense fp64 Sylvester product + "
+                      f"naive RTN), {secs:.2f} s"}
+    q_dev = rtn.unpack_codes(first_main[0], 4, 4096)
+    rep = compare.compare_quant(q_dev, first_main[1].astype(np.float16), y, s16, q, v, s_pre, 4, 128)
+    parity = dict(rep, config=MAIN, rows=4096)
+    del w, y, v, q
+
+    def sample(name, unit, rows_total, fn, rows_done, what):
+        _, secs = timed(fn)
+        out[name] = {"value": rows_done / secs, "unit": unit, "cores": int(threads), "host_cores": host,
+                     "kind": "oracle", "sample": f"{rows_done} of {rows_total} {what}, {secs:.2f} s"}
+
+    x1 = synth.fwht_f32()["x"].astype(np.float64)
+    sample("fwht_f32_256x4096", "rows/s", 256, lambda: H.wht(x1), 256, "rows (dense Sylvester product)")
+    c5 = synth.rht_int2_g64(rows=512)
+    w5 = synth.bf16_to_f64(c5["w"])
+    sample("rht_int2_g64_28672x8192", "rows/s", 28672,
+           lambda: rtn.rht_quantize(w5, H.signs_from_bits(c5["signs"], 8192), 2, 64), 512,
+           "rows (512 rows drawn by the same recipe; dense fp64 Sylvester product + naive RTN)")
+    d3 = synth.qwha(tokens=256)
+    sample("qwha_2048x4096_nnz262144", "tokens/s", 2048,
+           lambda: qwha.qwha_forward(synth.bf16_to_f64(d3["x"]), d3["row_ptr"], d3["col_idx"],
+                                     synth.bf16_to_f64(d3["vals"]), d3["d_out"]), 256,
+           "tokens (dense F, dense Sylvester product)")
+    d4 = synth.harp(tokens=128)
+    sample("harp_8192x4096_r16x3", "tokens/s", 8192,
+           lambda: harp.harp_rotate(synth.bf16_to_f64(d4["x"]), d4["radices"], d4["blocks"],
+                                    s=H.signs_from_bits(d4["signs"], 4096)), 128,
+           "tokens (dense stage matrices built and applied)")
+    return main, out, parity
 
 
 def main():
@@ -192,7 +326,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (PMC calibration)")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
+                    help="write profiles/counters.json from rocprofv3 counter CSVs under DIRs and exit")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards rows "
               f"with no communication, so N GPUs would each run this same kernel on rows/N.",
@@ -207,7 +346,7 @@ def main():
 
     torch.cuda.init()
     K, Wm = args.steps, args.warmup
-    log(f"[bench] device {torch.cuda.get_device_name(0)}, steps {K}, warmup {Wm}")
+    log(f"[bench] device {torch.cuda.get_device_name(0)}, steps {K}, warmup {Wm}, reps {REPS}")
 
     if args.copy_probe:
         a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda:0")
@@ -223,16 +362,11 @@ def main():
         args.workloads, set(args.workloads.split(",")))
     sel.add("main")  # `value` is always quoted on the main workload
     cfg_main = synth.rht_int4_g128()
-    res = bench_quant(torch, W, mask_dev, cfg_main, MAIN, 4, 128, K, Wm)
+    res, first_main = bench_quant(torch, W, mask_dev, cfg_main, MAIN, 4, 128, K, Wm)
     log(f"[bench] {MAIN}: {res[MAIN]}")
     if "fwht" in sel:
-        x = torch.from_numpy(synth.fwht_f32()["x"]).to("cuda:0")
-        xs = copies(torch, x, cap=256)
-        ys = [torch.empty_like(x) for _ in xs]
-        t = Timed(torch, lambda i: W.wht_batched(xs[i % len(xs)], out=ys[i % len(xs)]), K, Wm)
-        res["fwht_f32_256x4096"] = result("fwht_f32_256x4096", t.run(), K)
+        res.update(bench_fwht(torch, W, synth, K, Wm))
         log(f"[bench] fwht_f32_256x4096: {res['fwht_f32_256x4096']}")
-        del xs, ys
     for fn, nm in (("qwha", "qwha_2048x4096_nnz262144"), ("harp", "harp_8192x4096_r16x3"),
                    ("harp_gen", "harp_8192x5120_r88852")):
         if fn in sel:
@@ -244,7 +378,9 @@ def main():
             log(f"[bench] {nm}: {res[nm]}")
     if "int2" in sel:
         cfg5 = synth.rht_int2_g64()
-        res.update(bench_quant(torch, W, mask_dev, cfg5, "rht_int2_g64_28672x8192", 2, 64, K, Wm))
+        r5, _ = bench_quant(torch, W, mask_dev, cfg5, "rht_int2_g64_28672x8192", 2, 64, K, Wm)
+        res.update(r5)
+        del cfg5
         log(f"[bench] rht_int2_g64_28672x8192: {res['rht_int2_g64_28672x8192']}")
     if "gemv" in sel:
         nm = "gemv_int2_g64_28672x8192_t1"
@@ -254,9 +390,25 @@ def main():
         res[QINIT] = bench_qinit(torch, W, mask_dev, synth, K, Wm)
         log(f"[bench] {QINIT}: {res[QINIT]}")
 
+    # what the committed rocprofv3 counters say about each kernel (per launch)
+    for nm in KERNELS:
+        c = counters_for(nm)
+        if nm in res and c:
+            res[nm]["counters"] = {k: c[k] for k in ("hbm_bytes", "traffic_ratio", "valu_insts", "valu_busy_pct",
+                                                     "mfma_busy_pct", "from") if k in c}
+    if "harp_8192x4096_r16x3" in res:
+        hr = res["harp_8192x4096_r16x3"]
+        hr["mfma_TFLOPs"] = HARP_MFMA_FLOP / (hr["ms_per_launch"] / 1e3) / 1e12
+        hr["frac_f16_mfma_peak"] = hr["mfma_TFLOPs"] / PEAK_F16_MFMA_TFLOPS
+
     main_r = res[MAIN]
     per_launch = main_r["ms_per_launch"] / 1e3
-    traffic = traffic_for(MAIN, ALGO_BYTES[MAIN])
+    cm = counters_for(MAIN)
+    valu = None
+    if cm and "valu_insts" in cm:
+        valu = {"valu_insts_per_launch": cm["valu_insts"],
+                "valu_floor_us": cm["valu_insts"] * 64 / VALU_LANE_OPS * 1e6,
+                "frac_of_valu_floor": cm["valu_insts"] * 64 / VALU_LANE_OPS / per_launch}
     line = {
         "metric": "rows/s and HBM GB/s (% of peak) for RHT+quant at d=4096/8192",
         "value": main_r["rows_per_s"],
@@ -274,14 +426,20 @@ def main():
                    "group": 128, "input": "bf16 Student-t(3)*0.02, 0.1% outlier columns x20",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": main_r["GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": main_r["GBps"] / PEAK_HBM_GBS, "traffic": traffic,
-                     "kernel": "k_rht_quant<12,bf16,4,7>", "algo_bytes_per_launch": ALGO_BYTES[MAIN],
-                     "avg_launch_us": per_launch * 1e6},
+                     "frac": main_r["GBps"] / PEAK_HBM_GBS,
+                     "traffic": cm["hbm_bytes"] if cm and "hbm_bytes" in cm else None,
+                     "kernel": KERNELS[MAIN][0], "algo_bytes_per_launch": ALGO_BYTES[MAIN],
+                     "avg_launch_us": per_launch * 1e6,
+                     "achievable_us": main_r["stream_probe_us"], "frac_achievable": main_r["frac_achievable"],
+                     "valu": valu},
+        "timing": {"launches_per_replay": n_launch(K, 32), "replays": REPS,
+                   "statistic": "median over replays of the per-launch time (p10/p90/min beside it)",
+                   "inputs": "rotate over copies totalling >= 1 GiB, each copy at least once per replay"},
         "workloads": res,
     }
     if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a bounded sample ...")
-        line["cpu_baseline"] = cpu_baseline(cfg_main)
+        log("[bench] timing the CPU oracle ...")
+        line["cpu_baseline"], line["cpu_baseline_other"], line["parity"] = cpu_baselines(first_main)
     print(json.dumps(line), flush=True)
 
 
@@ -313,7 +471,7 @@ def bench_qwha_bwd(torch, W, synth, K, Wm):
 
     r = {}
     for nm, fn in (("qwha_bwd_dx_2048x4096_nnz262144", dx_step), ("qwha_bwd_dc_2048x4096_nnz262144", dc_step)):
-        r[nm] = result(nm, Timed(torch, fn, K, Wm).run(), K)
+        r[nm] = result(nm, Timed(torch, fn, n_launch(K, len(xs)), Wm).run())
     del dys, xs, dxs, dcs, ws
     torch.cuda.empty_cache()
     return r
@@ -333,11 +491,13 @@ def bench_gemv(torch, W, mask_dev, synth, name, K, Wm):
     ss = [s0.clone() for _ in range(k)]
     ys = [torch.empty((1, c0.shape[0]), dtype=torch.bfloat16, device="cuda:0") for _ in range(k)]
     del c0, s0
-    t = Timed(torch, lambda i: W.rht_lowbit_gemv(x, cs[i % k], ss[i % k], sg, 2, 64, out=ys[i % k]), K, Wm)
-    r = result(name, t.run(), K)
+    t = Timed(torch, lambda i: W.rht_lowbit_gemv(x, cs[i % k], ss[i % k], sg, 2, 64, out=ys[i % k]),
+              n_launch(K, k), Wm)
+    r = result(name, t.run())
     r["tokens_per_s"] = 1e3 / r["ms_per_launch"]
     del cs, ss, ys
     torch.cuda.empty_cache()
+    achievable(torch, W, r, ALGO_BYTES[name] - 28672 * 2, 28672 * 2, K, Wm)
     return r
 
 
@@ -365,18 +525,19 @@ def bench_qinit(torch, W, mask_dev, synth, K, Wm):
     col = torch.empty(total, dtype=torch.int32, device=dv)
     vals = torch.empty(total, dtype=torch.float32, device=dv)
     stage = {}
-    stage["error_coeffs"] = Timed(torch, lambda i: W.qwha_init_error_coeffs(w, codes, scales, sg, 4, 128, out=f),
-                                  K, Wm).run() / K
-    stage["gram"] = Timed(torch, lambda i: W.qwha_init_gram(x, g=g, z=z), K, Wm).run() / K
-    stage["channel_errors"] = Timed(torch, lambda i: W.qwha_init_channel_errors(f, g, p=p, err=err), K, Wm).run() / K
+    med = lambda t: stats(t.run(3))["median"]
+    stage["error_coeffs"] = med(Timed(torch, lambda i: W.qwha_init_error_coeffs(w, codes, scales, sg, 4, 128, out=f),
+                                      K, Wm))
+    stage["gram"] = med(Timed(torch, lambda i: W.qwha_init_gram(x, g=g, z=z), K, Wm))
+    stage["channel_errors"] = med(Timed(torch, lambda i: W.qwha_init_channel_errors(f, g, p=p, err=err), K, Wm))
     reps = max(3, K // 4)
     t0 = time.perf_counter()
     for _ in range(reps):
         rp_host = W.qwha_init_allocate(err, n, total, floor, cap)
     stage["allocate_host"] = (time.perf_counter() - t0) / reps
     row_ptr = rp_host.to(dv)
-    stage["select"] = Timed(torch, lambda i: W.qwha_init_select(f, row_ptr, col_idx=col), K, Wm).run() / K
-    stage["refine"] = Timed(torch, lambda i: W.qwha_init_refine(g, p, row_ptr, col, vals=vals), K, Wm).run() / K
+    stage["select"] = med(Timed(torch, lambda i: W.qwha_init_select(f, row_ptr, col_idx=col), K, Wm))
+    stage["refine"] = med(Timed(torch, lambda i: W.qwha_init_refine(g, p, row_ptr, col, vals=vals), K, Wm))
     for _ in range(Wm):
         W.qwha_initialize(w, codes, scales, sg, 4, 128, x, total, floor, cap)
     torch.cuda.synchronize()
@@ -408,7 +569,7 @@ def bench_other(torch, W, mask_dev, synth, fn, name, K, Wm):
         xs = copies(torch, x0)
         ys = [torch.empty((x0.shape[0], d["d_out"]), dtype=torch.bfloat16, device="cuda:0") for _ in xs]
         t = Timed(torch, lambda i: W.qwha_adapter_forward(xs[i % len(xs)], rp, ci, v, d["d_out"],
-                                                          out=ys[i % len(xs)]), K, Wm)
+                                                          out=ys[i % len(xs)]), n_launch(K, len(xs)), Wm)
     elif fn == "harp_gen":
         d = synth.harp_general()
         x0 = d["x"].to("cuda:0")
@@ -416,7 +577,7 @@ def bench_other(torch, W, mask_dev, synth, fn, name, K, Wm):
         xs = copies(torch, x0)
         ys = [torch.empty_like(x0) for _ in xs]
         t = Timed(torch, lambda i: W.harp_rotate(xs[i % len(xs)], blocks, d["radices"], None, False,
-                                                 out=ys[i % len(xs)]), K, Wm)
+                                                 out=ys[i % len(xs)]), n_launch(K, len(xs)), Wm)
     else:
         d = synth.harp()
         x0 = d["x"].to("cuda:0")
@@ -426,10 +587,56 @@ def bench_other(torch, W, mask_dev, synth, fn, name, K, Wm):
         xs = copies(torch, x0)
         ys = [torch.empty_like(x0) for _ in xs]
         t = Timed(torch, lambda i: W.harp_rotate(xs[i % len(xs)], blocks, d["radices"], sg, True,
-                                                 out=ys[i % len(xs)]), K, Wm)
-    r = result(name, t.run(), K)
+                                                 out=ys[i % len(xs)]), n_launch(K, len(xs)), Wm)
+    r = result(name, t.run())
+    nb = x0.numel() * x0.element_size()
+    del xs, ys
     torch.cuda.empty_cache()
+    if fn != "qwha":
+        achievable(torch, W, r, nb, nb, K, Wm)
     return r
+
+
+# ---------------------------------------------------------------- counters
+
+def summarize_pmc(dirs):
+    """profiles/counters.json from rocprofv3 --pmc CSVs (one counter set per
+    run) of the bench command: per kernel of KERNELS, the per-dispatch average
+    of each counter.  HBM bytes = 2 x FETCH_SIZE + WRITE_SIZE (KiB), the
+    factors a plain 256 MiB device copy gives these counters on MI355X
+    (FETCH_SIZE reads 131,087 KiB for 262,144 KiB moved, WRITE_SIZE
+    262,144 KiB)."""
+    per = {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    per.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], {}).setdefault(
+                        r["Dispatch_Id"], 0.0)
+                    per[r["Kernel_Name"]][r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    out = json.load(open(COUNTERS)) if os.path.exists(COUNTERS) else {}
+    for nm, (kern, srcs) in KERNELS.items():
+        hits = [k for k in per if kern in k]
+        if not hits:
+            continue
+        c = per[hits[0]]
+        avg = {cn: sum(v.values()) / len(v) for cn, v in c.items()}
+        e = {"src_sha": src_hash(srcs), "kernel": kern, "from": "profiles/ (rocprofv3 --pmc, bench.py command)"}
+        if "FETCH_SIZE" in avg and "WRITE_SIZE" in avg:
+            e["hbm_bytes"] = int((2.0 * avg["FETCH_SIZE"] + avg["WRITE_SIZE"]) * 1024)
+            e["traffic_ratio"] = e["hbm_bytes"] / ALGO_BYTES[nm]
+        if "SQ_INSTS_VALU" in avg:
+            e["valu_insts"] = avg["SQ_INSTS_VALU"]
+        if "VALUBusy" in avg:
+            e["valu_busy_pct"] = avg["VALUBusy"]
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and "GRBM_GUI_ACTIVE" in avg:
+            # MFMA busy cycles summed over the 1024 SIMDs; GRBM_GUI_ACTIVE summed over the 8 XCDs
+            e["mfma_busy_pct"] = 100.0 * avg["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024 / (avg["GRBM_GUI_ACTIVE"] / 8)
+        e["counters"] = avg
+        out[nm] = e
+    with open(COUNTERS, "w") as fh:
+        json.dump(out, fh, indent=1, sort_keys=True)
+    print(f"wrote {COUNTERS}: {sorted(out)}")
 
 
 if __name__ == "__main__":
