@@ -131,8 +131,11 @@ whtq_status rht_dequantize_inverse(const uint8_t* codes, const uint16_t* scales,
  *   output of weight row o; ldy >= rows).  codes / scales as written by
  *   rht_quantize_rtn with the same n, bits, group and sign_bits.
  *   n: 4096 or 8192.  bits: 2 or 4.  group: power of two in [32/bits, 256].
- *   The rotated activations are rounded to fp16 after a per-token
- *   power-of-two scale; accumulation is fp32.  Tokens are processed in
+ *   Arithmetic: (Hn S x_t) in fp32, multiplied by a per-token power of two
+ *   sigma that puts its largest magnitude in [2^13, 2^14) and rounded to
+ *   16-bit integers X (fixed point); the code x X products of one scale
+ *   group are summed exactly in int32 (4-bit integer dot products), then
+ *   y += s * acc in fp32, y * 1/(sigma sqrt(n)) rounded once to bf16.  Tokens are processed in
  *   passes of up to 4 (n = 4096) or 2 (n = 8192), each reading the codes
  *   once: a decode-size product, not a GEMM.
  *   Errors: EINVAL for bad sizes or NULL pointers, EUNSUPPORTED for other
@@ -388,7 +391,9 @@ whtq_status qwha_init_allocate(const float* err, int64_t rows, int64_t n, int64_
  *   (device row_ptr, each budget in [0, n]) column indices of largest
  *   |f[o][k]|, ties to the lower k, written ascending to device
  *   col_idx[row_ptr[o] ..].  Rows whose budget is outside [0, n] are left
- *   unwritten.
+ *   unwritten.  row_ptr must start at 0 and be non-decreasing, and col_idx
+ *   must hold at least row_ptr[rows] entries: neither is read on the host,
+ *   and a row_ptr that points past col_idx writes out of bounds.
  */
 whtq_status qwha_init_select(const float* f, int64_t rows, int64_t n, int64_t ldf, const int32_t* row_ptr,
                              int32_t* col_idx, void* stream);
@@ -400,7 +405,10 @@ whtq_status qwha_init_select(const float* f, int64_t rows, int64_t n, int64_t ld
  *   whose G[E][E] is not positive definite (fewer calibration tokens than
  *   its budget) gives values without meaning, NaN where a pivot is zero or
  *   negative (a zero G gives NaN throughout); a row whose budget exceeds
- *   WHTQ_QWHA_INIT_MAX_SUPPORT gives NaN.
+ *   WHTQ_QWHA_INIT_MAX_SUPPORT gives NaN.  row_ptr must start at 0 and be
+ *   non-decreasing, col_idx and vals must hold at least row_ptr[rows]
+ *   entries, and every col_idx entry must lie in [0, n): they are not read
+ *   on the host, and values outside these rules read or write out of bounds.
  */
 whtq_status qwha_init_refine(const float* g, int64_t n, const float* p, int64_t rows, const int32_t* row_ptr,
                              const int32_t* col_idx, float* vals, void* stream);

@@ -496,10 +496,14 @@ def qwha_init_select(f, row_ptr, col_idx=None):
     _need_cuda("row_ptr", row_ptr)
     if row_ptr.dtype != torch.int32 or row_ptr.shape != (rows + 1,) or not row_ptr.is_contiguous():
         raise ValueError("row_ptr must be contiguous int32 [rows + 1]")
+    total = int(row_ptr[-1].item())
     if col_idx is None:
-        col_idx = torch.empty(int(row_ptr[-1].item()), dtype=torch.int32, device=f.device)
+        col_idx = torch.empty(total, dtype=torch.int32, device=f.device)
+    _need_cuda("col_idx", col_idx)
     if col_idx.dtype != torch.int32 or not col_idx.is_contiguous():
         raise ValueError("col_idx must be contiguous int32")
+    if col_idx.numel() < total:
+        raise ValueError("col_idx must hold row_ptr[-1] entries")
     with torch.cuda.device(f.device):
         _check("qwha_init_select", _lib.qwha_init_select(
             _ptr(f), rows, n, ldf, _ptr(row_ptr), _ptr(col_idx), _stream(f)))
@@ -518,10 +522,15 @@ def qwha_init_refine(g, p, row_ptr, col_idx, vals=None):
         _need_cuda(name, t)
     if row_ptr.dtype != torch.int32 or row_ptr.shape != (rows + 1,) or col_idx.dtype != torch.int32:
         raise ValueError("row_ptr / col_idx must be int32, row_ptr [rows + 1]")
+    if not (row_ptr.is_contiguous() and col_idx.is_contiguous()):
+        raise ValueError("row_ptr and col_idx must be contiguous")
     if vals is None:
         vals = torch.empty(col_idx.numel(), dtype=torch.float32, device=g.device)
-    if vals.dtype != torch.float32 or vals.numel() != col_idx.numel():
-        raise ValueError("vals must be float32 with one entry per column index")
+    _need_cuda("vals", vals)
+    if vals.dtype != torch.float32 or vals.numel() != col_idx.numel() or not vals.is_contiguous():
+        raise ValueError("vals must be contiguous float32 with one entry per column index")
+    if col_idx.numel() < int(row_ptr[-1].item()):
+        raise ValueError("col_idx and vals must hold row_ptr[-1] entries")
     with torch.cuda.device(g.device):
         _check("qwha_init_refine", _lib.qwha_init_refine(
             _ptr(g), n, _ptr(p), rows, _ptr(row_ptr), _ptr(col_idx), _ptr(vals), _stream(g)))
