@@ -271,7 +271,8 @@ whtq_status qwha_adapter_grad_values_noalloc(const void* x, const void* dy, whtq
  * harp_rotate -- y = Stage_{m-1}( ... Stage_0( P x ) ), P = Hn S if
  * precondition else I; stage t applies d / b_t independent b_t x b_t blocks
  * along digit t ([HARP] 2.1, 2.2).
- *   x, y [tokens][ld] in dtype (bf16 in this build); x == y not allowed.
+ *   x, y [tokens][ld] in dtype, WHTQ_BF16 or WHTQ_F32 (both the same
+ *   dtype; WHTQ_F16 rows are WHTQ_EUNSUPPORTED); x == y not allowed.
  *   radices: HOST int32[n_stages], each >= 2, product == d ([HARP] 2.1:
  *   e.g. 8, 8, 8, 5, 2 for d = 5120).  This build runs radices up to 16,
  *   d <= 8192 and up to 16 stages (WHTQ_EUNSUPPORTED otherwise).
@@ -280,16 +281,17 @@ whtq_status qwha_adapter_grad_values_noalloc(const void* x, const void* dy, whtq
  *   blocks: device, stage-major, stage t as [d / b_t][b_t][b_t] row-major
  *   (B[k][j] at k * b_t + j), in blocks_dtype: WHTQ_F32 or WHTQ_F16 (half
  *   the bytes read per call).
- *   Arithmetic, d = 4096 with radices (16, 16, 16): each token row is scaled
+ *   Arithmetic, bf16 rows with d = 4096 and radices (16, 16, 16): each token row is scaled
  *   by an exact power of two that puts its L2 norm in [2^13, 2^14) and kept
  *   on chip in fp16; the preconditioning Hn = (H16 / 4) (x) (H16 / 4) (x)
  *   (H16 / 4) and every block stage run as 16 x 16 x 16 MFMAs with fp16
  *   operands and fp32 accumulation (fp32 blocks are rounded to fp16 in the
  *   kernel, so both block dtypes give the same result for the same
  *   fp16-representable values), the result of each rounded to fp16.  Every
- *   other schedule: fp32 on chip and fp32 arithmetic (fp16 blocks widened
- *   exactly), the preconditioning as in-register Hadamard butterflies.  The
- *   output is rounded once to bf16 (nearest even).
+ *   other schedule, and fp32 rows with any schedule: fp32 on chip and fp32
+ *   arithmetic (fp16 blocks widened exactly), the preconditioning as
+ *   in-register Hadamard butterflies.  bf16 output is rounded once (nearest
+ *   even); fp32 output is the fp32 result.
  *   sign_bits: uint32[ceil(d/32)] or NULL (all +1); used when
  *   precondition != 0.
  */

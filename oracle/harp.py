@@ -157,3 +157,30 @@ def dequant_params(q, scales, radices, d):
         out[o:o + n] = q[o:o + n] * float(scales[t])
         o += n
     return out
+
+
+# ------------------------------------------------------ two-sided application
+#
+# [HARP] technical summary, proposal paragraph: HARP is a learnable two-sided
+# orthogonal processor replacing the fixed RHT of incoherence processing.
+# Reading: for a weight matrix W [d_out x d_in] of a layer y = W x, the input
+# side rotates every row of W (the d_in coordinates) with R_in and the output
+# side every column (the d_out coordinates) with R_out, so the processed
+# weight is W~ = R_out W R_in^T (and the layer's output is R_out y when its
+# input is R_in x).  Each side is one harp_rotate with its own schedule,
+# blocks, signs and preconditioning.
+
+
+def rotation_matrix(d, radices, blocks, s=None, precondition=True):
+    """The d x d matrix R with harp_rotate(x) = x R^T for row vectors x."""
+    return harp_rotate(np.eye(d), radices, blocks, s=s, precondition=precondition).T
+
+
+def harp_two_sided(w, out_side, in_side):
+    """W~ = R_out W R_in^T, fp64.  out_side / in_side: dicts of
+    (radices, blocks, s, precondition) for harp_rotate on the d_out and d_in
+    coordinates."""
+    w = np.asarray(w, dtype=np.float64)
+    r_out = rotation_matrix(w.shape[0], **out_side)
+    r_in = rotation_matrix(w.shape[1], **in_side)
+    return r_out @ w @ r_in.T

@@ -164,8 +164,9 @@ def test_harp_validation(lib):
     assert hp(lib, y=P) == EINVAL                          # in place not allowed
     assert hp(lib, pre=3) == EINVAL
     assert hp(lib, blocks=NULL) == EINVAL
-    assert hp(lib, dt=2) == EUNSUP
-    assert hp(lib, dt=0) == EUNSUP
+    assert hp(lib, dt=2) == EUNSUP                         # fp16 rows
+    assert hp(lib, dt=0, tokens=0) == OK                   # fp32 rows accepted (any schedule)
+    assert hp(lib, dt=0, x=ctypes.c_void_p(0x10008)) == EALIGN
     assert hp(lib, bd=7) == EINVAL                         # not a dtype
     assert hp(lib, bd=1) == EUNSUP                         # bf16 blocks: no kernel
     assert hp(lib, bd=2, tokens=0) == OK                   # fp16 blocks accepted

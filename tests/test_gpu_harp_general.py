@@ -148,3 +148,77 @@ def test_orthogonal_inverse_roundtrip():
         m = harp.stage_matrix(blocks[t], t, list(radices)) @ m
     back = host64(y) @ m   # y = x M^T  ->  x = y M
     assert compare.float_err(back, synth.bf16_to_f64(x))[0] <= 2e-2
+
+
+TOL_F32 = 1e-5   # fp32 output
+
+
+def padded_rows_f32(x):
+    t, d = x.shape
+    ld = d if d * 4 < 16 else -(-d // 4) * 4
+    buf = torch.zeros((t, ld), dtype=torch.float32, device="cuda")
+    buf[:, :d] = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to("cuda")
+    return buf[:, :d]
+
+
+@pytest.mark.parametrize("radices,tokens,pre", [((16, 16, 16), 37, True), ((8, 8, 8, 5, 2), 11, False),
+                                                ((5, 3, 2), 40, False), ((3, 7, 5), 9, False),
+                                                ((2,) * 13, 5, True), ((16, 16, 16, 2), 3, True)])
+def test_f32_rows(radices, tokens, pre):
+    """fp32 rows (every schedule, the radix-16 one included, on the fp32 tile):
+    the fp32 rule against the oracle."""
+    rng = np.random.default_rng(sum(radices) + tokens)
+    d = int(np.prod(radices))
+    x = rng.standard_normal((tokens, d)).astype(np.float32)
+    blocks = rand_blocks(rng, radices)
+    mask = synth.sign_bits_to_mask(rng.integers(0, 2, d)) if pre else None
+    out = padded_rows_f32(np.zeros_like(x))
+    y = W().harp_rotate(padded_rows_f32(x), dev(flat(blocks)), tuple(radices),
+                        mask_dev(mask) if mask is not None else None, pre, out=out)
+    want = harp.harp_rotate(x.astype(np.float64), list(radices), blocks,
+                            s=H.signs_from_bits(mask, d) if pre else None, precondition=pre)
+    assert compare.float_err(host64(y), want)[0] <= TOL_F32
+
+
+def _two_sided_gpu(w_dev, out_side, in_side):
+    """W~ = R_out W R_in^T as two harp_rotate calls: the rows of W (input
+    side), then the rows of the transpose (output side)."""
+    def rot(x, sd):
+        mask = sd["mask"]
+        return W().harp_rotate(x, dev(flat(sd["blocks"])), tuple(sd["radices"]),
+                               mask_dev(mask) if mask is not None else None, sd["precondition"])
+    t = rot(w_dev, in_side)
+    return rot(t.t().contiguous(), out_side).t()
+
+
+def _side(rng, radices, pre):
+    d = int(np.prod(radices))
+    mask = synth.sign_bits_to_mask(rng.integers(0, 2, d)) if pre else None
+    return {"radices": list(radices), "blocks": rand_blocks(rng, radices), "mask": mask, "precondition": pre}
+
+
+def _oracle_side(sd):
+    d = int(np.prod(sd["radices"]))
+    return {"radices": sd["radices"], "blocks": sd["blocks"],
+            "s": H.signs_from_bits(sd["mask"], d) if sd["mask"] is not None else None,
+            "precondition": sd["precondition"]}
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_two_sided(dt):
+    """A 320 x 4096 weight: the input side the radix-16 schedule with the
+    RHT preconditioning, the output side 8 * 8 * 5; and a 4096 x 5120 bf16
+    weight with the page's 8 * 8 * 8 * 5 * 2 schedule on the input side."""
+    rng = np.random.default_rng(7 if dt == torch.float32 else 8)
+    cases = [((8, 8, 5), False, (16, 16, 16), True)]
+    if dt == torch.bfloat16:
+        cases.append(((16, 16, 16), True, (8, 8, 8, 5, 2), False))
+    for rout, pout, rin, pin in cases:
+        so, si = _side(rng, rout, pout), _side(rng, rin, pin)
+        d_out, d_in = int(np.prod(rout)), int(np.prod(rin))
+        w = (0.02 * rng.standard_t(3, size=(d_out, d_in))).astype(np.float32)
+        w_dev = torch.from_numpy(w).to("cuda").to(dt)
+        got = host64(_two_sided_gpu(w_dev, so, si))
+        want = harp.harp_two_sided(host64(w_dev), _oracle_side(so), _oracle_side(si))
+        err = compare.float_err(got, want)[0]
+        assert err <= (TOL_F32 if dt == torch.float32 else TOL), (rout, rin, err)

@@ -284,3 +284,15 @@ def test_mutant_rms_over_the_matrix(monkeypatch):
 def test_mutant_no_rms_floor(monkeypatch):
     monkeypatch.setattr(C, "float_err", _mutant_of(C.float_err, "np.maximum(np.abs(o), rms)", "np.abs(o)"))
     _fails(tc.test_float_err_row_rms_floor)
+
+
+def test_mutant_two_sided_untransposed_input_rotation(monkeypatch):
+    """R_out W R_in (R_in not transposed) fails the brute-force loops."""
+    from oracle import harp
+    import test_oracle_harp_two_sided as t2
+
+    def mutant(w, out_side, in_side):
+        w = np.asarray(w, dtype=np.float64)
+        return harp.rotation_matrix(w.shape[0], **out_side) @ w @ harp.rotation_matrix(w.shape[1], **in_side)
+    monkeypatch.setattr(harp, "harp_two_sided", mutant)
+    _fails(t2.test_two_sided_bruteforce, (3, 2), (2, 4))

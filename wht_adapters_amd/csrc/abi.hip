@@ -39,7 +39,7 @@ hipError_t launch_qwha_dc(const void* x, int64_t ldx, const void* dy, int64_t ld
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 hipError_t launch_permute(const void* vals, int val_dt, const int32_t* perm, int64_t nnz, void* out,
                           hipStream_t s);
-hipError_t launch_harp_gen(const void* x, void* y, int64_t tokens, int d, int64_t ldx, int64_t ldy,
+hipError_t launch_harp_gen(const void* x, void* y, int xdt, int64_t tokens, int d, int64_t ldx, int64_t ldy,
                            const uint32_t* sbits, int precondition, const int32_t* radices, int n_stages,
                            const void* blocks, int bdt, hipStream_t s);
 hipError_t launch_harp_build(const void* params, int pdt, const float* scales, int64_t d, const int32_t* radices,
@@ -435,13 +435,16 @@ whtq_status harp_rotate(const void* x, void* y, whtq_dtype dtype, int64_t tokens
   if (tokens > 0 && x == y) return WHTQ_EINVAL;
   // the preconditioning is the Sylvester RHT, which exists for powers of two only
   if (precondition && ilog2_pow2(d) < 0) return WHTQ_EINVAL;
-  const bool r16 = d == 4096 && n_stages == 3 && radices[0] == 16 && radices[1] == 16 && radices[2] == 16;
+  // fp32 rows take the fp32-tile kernel for every schedule (the radix-16 one
+  // multiplies in fp16)
+  const bool r16 = dtype == WHTQ_BF16 && d == 4096 && n_stages == 3 && radices[0] == 16 && radices[1] == 16 &&
+                   radices[2] == 16;
   if (!r16) {
     if (d > 8192 || n_stages > 16) return WHTQ_EUNSUPPORTED;
     for (int t = 0; t < n_stages; ++t)
       if (radices[t] > 16) return WHTQ_EUNSUPPORTED;
   }
-  if (dtype != WHTQ_BF16 || blocks_dtype == WHTQ_BF16) return WHTQ_EUNSUPPORTED;
+  if ((dtype != WHTQ_BF16 && dtype != WHTQ_F32) || blocks_dtype == WHTQ_BF16) return WHTQ_EUNSUPPORTED;
   const int esz = dt_bytes(dtype);
   if (!rows_aligned(x, d, ldx, esz) || !rows_aligned(y, d, ldy, esz) || !aligned16(blocks)) return WHTQ_EALIGN;
   if (sign_bits && (reinterpret_cast<uintptr_t>(sign_bits) & 3u)) return WHTQ_EALIGN;
@@ -451,7 +454,7 @@ whtq_status harp_rotate(const void* x, void* y, whtq_dtype dtype, int64_t tokens
   if (r16)
     return hip_status(launch_harp(x, y, dtype, tokens, ldx, ldy, sign_bits, precondition, blocks, blocks_dtype,
                                   (hipStream_t)stream));
-  return hip_status(launch_harp_gen(x, y, tokens, (int)d, ldx, ldy, sign_bits, precondition, radices, n_stages,
+  return hip_status(launch_harp_gen(x, y, dtype, tokens, (int)d, ldx, ldy, sign_bits, precondition, radices, n_stages,
                                     blocks, blocks_dtype, (hipStream_t)stream));
 }
 

@@ -133,8 +133,8 @@ __device__ __forceinline__ void hg_had(float* tile, int ldt, int nt, int d, int 
   }
 }
 
-template <int BDT>
-__global__ __launch_bounds__(hg::THREADS) void k_harp_gen(const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
+template <int BDT, int XDT>
+__global__ __launch_bounds__(hg::THREADS) void k_harp_gen(const void* __restrict__ xv_, void* __restrict__ yv_,
                                                          int64_t tokens, int64_t ldx, int64_t ldy, int d, int ldt,
                                                          int tt, const uint32_t* __restrict__ sbits,
                                                          const void* __restrict__ blocks, HgSched sc, int vec) {
@@ -143,22 +143,38 @@ __global__ __launch_bounds__(hg::THREADS) void k_harp_gen(const uint16_t* __rest
   const int nt = (int)min<int64_t>(tt, tokens - tok0);
   const int nch = (d + 7) >> 3;  // 8-value chunks per row
 
-  // ---- load (signs flipped on the way when preconditioning)
+  // ---- load (signs flipped on the way when preconditioning); rows are bf16
+  // or fp32 (XDT), the tile fp32 either way
   for (int f = threadIdx.x; f < nt * nch; f += hg::THREADS) {
     const int j = f / nch, i0 = 8 * (f - j * nch);
-    const uint16_t* xr = x + (tok0 + j) * ldx;
     uint32_t sb = sbits ? (sbits[i0 >> 5] >> (i0 & 31)) & 0xffu : 0u;
     float v[8];
-    if (vec && i0 + 8 <= d) {
-      const u32x4 w = ldg<u32x4>(xr + i0);
+    if constexpr (XDT == DT_F32) {
+      const float* xr = reinterpret_cast<const float*>(xv_) + (tok0 + j) * ldx;
+      if (vec && i0 + 8 <= d) {
+        const f32x4 a = ldg<f32x4>(xr + i0), b = ldg<f32x4>(xr + i0 + 4);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v[2 * q] = bf16lo(w[q]);
-        v[2 * q + 1] = bf16hi(w[q]);
+        for (int q = 0; q < 4; ++q) {
+          v[q] = a[q];
+          v[4 + q] = b[q];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = i0 + e < d ? xr[i0 + e] : 0.f;
       }
     } else {
+      const uint16_t* xr = reinterpret_cast<const uint16_t*>(xv_) + (tok0 + j) * ldx;
+      if (vec && i0 + 8 <= d) {
+        const u32x4 w = ldg<u32x4>(xr + i0);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = i0 + e < d ? as_f((uint32_t)xr[i0 + e] << 16) : 0.f;
+        for (int q = 0; q < 4; ++q) {
+          v[2 * q] = bf16lo(w[q]);
+          v[2 * q + 1] = bf16hi(w[q]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = i0 + e < d ? as_f((uint32_t)xr[i0 + e] << 16) : 0.f;
+      }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e)
@@ -190,25 +206,49 @@ __global__ __launch_bounds__(hg::THREADS) void k_harp_gen(const uint16_t* __rest
     __syncthreads();
   }
 
-  // ---- store, rounded once to bf16
+  // ---- store: fp32 as is, or rounded once to bf16
   for (int f = threadIdx.x; f < nt * nch; f += hg::THREADS) {
     const int j = f / nch, i0 = 8 * (f - j * nch);
-    uint16_t* yr = y + (tok0 + j) * ldy;
     const float* row = tile + j * ldt;
-    if (vec && i0 + 8 <= d) {
-      u32x4 w;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) w[q] = pack_bf16(row[hg::pos(i0 + 2 * q)], row[hg::pos(i0 + 2 * q + 1)]);
-      stg(yr + i0, w);
+    if constexpr (XDT == DT_F32) {
+      float* yr = reinterpret_cast<float*>(yv_) + (tok0 + j) * ldy;
+      if (vec && i0 + 8 <= d) {
+        stg(yr + i0, f32x4{row[hg::pos(i0)], row[hg::pos(i0 + 1)], row[hg::pos(i0 + 2)], row[hg::pos(i0 + 3)]});
+        stg(yr + i0 + 4,
+            f32x4{row[hg::pos(i0 + 4)], row[hg::pos(i0 + 5)], row[hg::pos(i0 + 6)], row[hg::pos(i0 + 7)]});
+      } else {
+        for (int e = 0; e < 8 && i0 + e < d; ++e) yr[i0 + e] = row[hg::pos(i0 + e)];
+      }
     } else {
-      for (int e = 0; e < 8 && i0 + e < d; ++e) yr[i0 + e] = (uint16_t)(pack_bf16(row[hg::pos(i0 + e)], 0.f) & 0xffffu);
+      uint16_t* yr = reinterpret_cast<uint16_t*>(yv_) + (tok0 + j) * ldy;
+      if (vec && i0 + 8 <= d) {
+        u32x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = pack_bf16(row[hg::pos(i0 + 2 * q)], row[hg::pos(i0 + 2 * q + 1)]);
+        stg(yr + i0, w);
+      } else {
+        for (int e = 0; e < 8 && i0 + e < d; ++e)
+          yr[i0 + e] = (uint16_t)(pack_bf16(row[hg::pos(i0 + e)], 0.f) & 0xffffu);
+      }
     }
   }
 }
 
 // Entry from the C ABI (arguments validated there): radices each in [2, 16],
 // product d <= 8192, precondition only for d a power of two.
-hipError_t launch_harp_gen(const void* x, void* y, int64_t tokens, int d, int64_t ldx, int64_t ldy,
+template <int BDT, int XDT>
+static void launch_hg(const void* x, void* y, int64_t tokens, int64_t ldx, int64_t ldy, int d, int ldt, int tt,
+                      const uint32_t* sbits, const void* blocks, const HgSched& sc, int vec, unsigned grid,
+                      size_t lds, hipStream_t s) {
+  static const bool a = hipFuncSetAttribute((const void*)k_harp_gen<BDT, XDT>,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, hg::LDS_FLOATS * 4) ==
+                        hipSuccess;
+  (void)a;
+  hipLaunchKernelGGL((k_harp_gen<BDT, XDT>), dim3(grid), dim3(hg::THREADS), lds, s, x, y, tokens, ldx, ldy, d, ldt,
+                     tt, sbits, blocks, sc, vec);
+}
+
+hipError_t launch_harp_gen(const void* x, void* y, int xdt, int64_t tokens, int d, int64_t ldx, int64_t ldy,
                            const uint32_t* sbits, int precondition, const int32_t* radices, int n_stages,
                            const void* blocks, int bdt, hipStream_t s) {
   HgSched sc{};
@@ -244,23 +284,16 @@ hipError_t launch_harp_gen(const void* x, void* y, int64_t tokens, int d, int64_
   const int tt = std::max(1, std::min(hg::MAXTT, hg::LDS_FLOATS / ldt));
   const size_t lds = (size_t)tt * ldt * sizeof(float);
   // 16-byte row accesses need a 16-byte aligned base and row stride on both sides
+  const int esz = xdt == DT_F32 ? 4 : 2;
   const int vec = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15u) == 0 &&
-                          (ldx * 2) % 16 == 0 && (ldy * 2) % 16 == 0
+                          (ldx * esz) % 16 == 0 && (ldy * esz) % 16 == 0
                       ? 1 : 0;
   const unsigned grid = (unsigned)((tokens + tt - 1) / tt);
-  if (bdt == DT_F16) {
-    static const bool a = hipFuncSetAttribute((const void*)k_harp_gen<DT_F16>,
-                                              hipFuncAttributeMaxDynamicSharedMemorySize, hg::LDS_FLOATS * 4) == hipSuccess;
-    (void)a;
-    hipLaunchKernelGGL(k_harp_gen<DT_F16>, dim3(grid), dim3(hg::THREADS), lds, s, (const uint16_t*)x, (uint16_t*)y,
-                       tokens, ldx, ldy, d, ldt, tt, precondition ? sbits : nullptr, blocks, sc, vec);
-  } else {
-    static const bool a = hipFuncSetAttribute((const void*)k_harp_gen<DT_F32>,
-                                              hipFuncAttributeMaxDynamicSharedMemorySize, hg::LDS_FLOATS * 4) == hipSuccess;
-    (void)a;
-    hipLaunchKernelGGL(k_harp_gen<DT_F32>, dim3(grid), dim3(hg::THREADS), lds, s, (const uint16_t*)x, (uint16_t*)y,
-                       tokens, ldx, ldy, d, ldt, tt, precondition ? sbits : nullptr, blocks, sc, vec);
-  }
+  const uint32_t* sb = precondition ? sbits : nullptr;
+  if (bdt == DT_F16 && xdt == DT_F32) launch_hg<DT_F16, DT_F32>(x, y, tokens, ldx, ldy, d, ldt, tt, sb, blocks, sc, vec, grid, lds, s);
+  else if (bdt == DT_F16) launch_hg<DT_F16, DT_BF16>(x, y, tokens, ldx, ldy, d, ldt, tt, sb, blocks, sc, vec, grid, lds, s);
+  else if (xdt == DT_F32) launch_hg<DT_F32, DT_F32>(x, y, tokens, ldx, ldy, d, ldt, tt, sb, blocks, sc, vec, grid, lds, s);
+  else launch_hg<DT_F32, DT_BF16>(x, y, tokens, ldx, ldy, d, ldt, tt, sb, blocks, sc, vec, grid, lds, s);
   return hipGetLastError();
 }
 

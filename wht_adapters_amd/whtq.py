@@ -242,8 +242,8 @@ def harp_rotate(x, blocks, radices=(16, 16, 16), signs=None, precondition=True, 
     if out is None:
         out = torch.empty_like(x)
     r2, d2, ldy = _rows_ld("out", out)
-    if (r2, d2) != (tokens, d):
-        raise ValueError("out shape mismatch")
+    if (r2, d2) != (tokens, d) or out.dtype != x.dtype:
+        raise ValueError("out shape or dtype mismatch")
     with torch.cuda.device(x.device):
         _check("harp_rotate", _lib.harp_rotate(
             _ptr(x), _ptr(out), _DT[x.dtype], tokens, d, ldx, ldy, _sign_ptr(signs, d, x.device),
