@@ -149,7 +149,8 @@ whtq_status rht_lowbit_gemv(const void* x, int64_t tokens, int64_t ldx, const ui
 /*
  * qwha_adapter_forward -- y[t][o] = sum_{k in row o of F} F[o][k] * (Hn x_t)[k],
  * the QWHA adapter output x Delta W^T with Delta W = F Hn ([QWHA] 2.1).
- *   x [tokens][ldx] bf16; y [tokens][ldy] bf16; d_in = 4096 in this build.
+ *   x [tokens][ldx] bf16; y [tokens][ldy] bf16; d_in a power of two in
+ *   [64, 8192] (others: WHTQ_EUNSUPPORTED).
  *   F: CSR [d_out x d_in]: row_ptr int32[d_out + 1] (row_ptr[0] = 0,
  *   row_ptr[d_out] = nnz, non-decreasing), col_idx int32[nnz] in [0, d_in),
  *   vals[nnz] in val_dtype (bf16 or f32).  The library does not read the CSR
@@ -157,6 +158,12 @@ whtq_status rht_lowbit_gemv(const void* x, int64_t tokens, int64_t ldx, const ui
  *   d_out in [1, 4096] (any value); col_idx and vals 16-byte aligned (the
  *   common rule).  Accumulation in fp32; Hn x is kept on chip in fp16 with a
  *   per-token power-of-two scale; each output is rounded once to bf16.
+ *   Widths other than 4096 use two exact identities of the Sylvester matrix:
+ *   for d_in < 4096, (Hn x)[k] is the k-th entry of the 4096-point transform
+ *   of x zero-extended, times 64 / sqrt(d_in); for d_in = 8192, the half h of
+ *   H_8192 x is H_4096 (x_lo + x_hi) or H_4096 (x_lo - x_hi) over 1/sqrt(2),
+ *   and each token's fp16 scale then comes from the bound 64 ||x||_2 rather
+ *   than from max |(Hn x)_k| (fewer bits for small entries of that token).
  */
 whtq_status qwha_adapter_forward(const void* x, whtq_dtype x_dtype, int64_t tokens, int64_t d_in,
                                  int64_t ldx, const int32_t* row_ptr, const int32_t* col_idx,
@@ -199,8 +206,8 @@ whtq_status qwha_permute_values(const void* vals, whtq_dtype val_dtype, const in
  * qwha_adapter_backward_input -- dx = (dy F) Hn: dx[t][k] = (Hn u_t)[k] with
  * u_t[j] = sum_{o in row j of F^T} F[o][j] dy[t][o].
  *   dy [tokens][lddy] bf16 (d_out columns; 2-byte alignment suffices, 16-byte
- *   aligned rows are read with 16-byte loads); dx [tokens][lddx] bf16 (d_in =
- *   4096 columns, d_out in [1, 4096]).  F^T as CSR: t_row_ptr int32[d_in + 1],
+ *   aligned rows are read with 16-byte loads); dx [tokens][lddx] bf16 (d_in
+ *   columns, a power of two in [64, 8192]; d_out in [1, 4096]).  F^T as CSR: t_row_ptr int32[d_in + 1],
  *   t_col_idx int32[nnz] in [0, d_out), t_vals[nnz] (bf16 or f32), e.g. from
  *   qwha_csr_transpose + qwha_permute_values; 16-byte aligned t_col_idx and
  *   t_vals.  A malformed CSR gives undefined results (it is not read on the
@@ -208,7 +215,9 @@ whtq_status qwha_permute_values(const void* vals, whtq_dtype val_dtype, const in
  *   Arithmetic: dy is kept on chip in fp16 with a per-token power-of-two
  *   scale (exact for bf16 inputs in range), fp32 accumulation of dy F, whose
  *   rows are rounded once to bf16 on chip before the fp32 transform; each
- *   output rounded once to bf16.
+ *   output rounded once to bf16.  d_in other than 4096: the identities of
+ *   qwha_adapter_forward (zero extension below 4096, the top-bit split at
+ *   8192).
  */
 whtq_status qwha_adapter_backward_input(const void* dy, whtq_dtype dy_dtype, int64_t tokens, int64_t d_out,
                                         int64_t lddy, const int32_t* t_row_ptr, const int32_t* t_col_idx,
@@ -218,14 +227,16 @@ whtq_status qwha_adapter_backward_input(const void* dy, whtq_dtype dy_dtype, int
 /*
  * qwha_grad_values_workspace_bytes -- size in bytes of the workspace that
  * qwha_adapter_grad_values needs for these sizes (a function of the sizes
- * only); -1 for invalid sizes (d_in must be 4096), 0 when tokens or nnz is 0.
+ * only); -1 for invalid sizes (d_in must be a power of two in [64, 8192]), 0
+ * when tokens or nnz is 0.
  */
 int64_t qwha_grad_values_workspace_bytes(int64_t tokens, int64_t d_in, int64_t nnz);
 
 /*
  * qwha_adapter_grad_values -- dc[e] = sum_t dy[t][o_e] * (Hn x_t)[col_idx[e]]
  * for every entry e of F's CSR, o_e its row (the gradient of the values c).
- *   x [tokens][ldx] bf16 (d_in = 4096); dy [tokens][lddy] bf16 (d_out in
+ *   x [tokens][ldx] bf16 (d_in a power of two in [64, 8192]); dy
+ *   [tokens][lddy] bf16 (d_out in
  *   [1, 4096], 2-byte alignment suffices); row_ptr int32[d_out + 1], col_idx int32[nnz] (the CSR of F;
  *   not read on the host: malformed input gives undefined values, never an
  *   access outside x, dy, dc or the workspace); dc float32[nnz] (written, in
@@ -234,9 +245,10 @@ int64_t qwha_grad_values_workspace_bytes(int64_t tokens, int64_t d_in, int64_t n
  *   qwha_grad_values_workspace_bytes(tokens, d_in, nnz) bytes, 16-byte
  *   aligned, overwritten (Hn x in fp32 and per-token-slab partial sums);
  *   a smaller workspace_bytes returns WHTQ_EINVAL.
- *   Arithmetic: Hn x in fp32; products and sums in fp32, over tokens in
- *   order within fixed token slabs, then over slabs in order
- *   (deterministic).
+ *   Arithmetic: Hn x in fp32 (d_in < 4096: the 4096-point transform of x
+ *   zero-extended, scaled; d_in = 8192: the two 4096-point halves of the
+ *   top-bit split); products and sums in fp32, over tokens in order within
+ *   fixed token slabs, then over slabs in order (deterministic).
  */
 whtq_status qwha_adapter_grad_values(const void* x, const void* dy, whtq_dtype dtype, int64_t tokens,
                                      int64_t d_in, int64_t d_out, int64_t ldx, int64_t lddy,
@@ -253,8 +265,8 @@ whtq_status qwha_adapter_grad_values(const void* x, const void* dy, whtq_dtype d
  * on holds until the process ends.  The call allocates nothing.
  *   Sizes whose qwha_grad_values_workspace_bytes exceeds
  *   WHTQ_QWHA_DC_SCRATCH_BYTES return WHTQ_ESCRATCH before any HIP call
- *   (64 MiB covers 2048 tokens x 262,144 entries; roughly tokens * 16 KiB +
- *   token slabs * nnz * 4 bytes).
+ *   (64 MiB covers 2048 tokens x 262,144 entries at d_in <= 4096; roughly
+ *   tokens * 16 KiB (32 KiB at d_in = 8192) + token slabs * nnz * 4 bytes).
  *   Every call on one GPU shares that GPU's array: calls that overlap in time
  *   on one GPU (different streams, or different host threads) race and give
  *   undefined results.  Calls ordered on one stream are safe; nothing carries

@@ -139,7 +139,11 @@ def test_qwha_validation(lib):
     assert qw(lib, rp=NULL) == EINVAL
     assert qw(lib, nnz=4096 * 4096 + 1) == EINVAL
     assert qw(lib, d_in=3000, ldx=3000) == EUNSUP
-    assert qw(lib, d_in=2048, ldx=2048) == EUNSUP
+    assert qw(lib, d_in=32, ldx=32) == EUNSUP          # d_in a power of two in [64, 8192]
+    assert qw(lib, d_in=16384, ldx=16384) == EUNSUP
+    assert qw(lib, d_in=8192, ldx=4096) == EINVAL       # ldx < d_in
+    assert qw(lib, d_in=2048, ldx=2048, tokens=0) == OK
+    assert qw(lib, d_in=8192, ldx=8192, tokens=0) == OK
     assert qw(lib, xd=0) == EUNSUP
     assert qw(lib, vd=2) == EUNSUP
     assert qw(lib, x=P_MIS) == EALIGN
@@ -241,7 +245,10 @@ def test_qwha_backward_validation(lib):
     assert bw(lib, lddx=100) == EINVAL
     assert bw(lib, rp=NULL) == EINVAL
     assert bw(lib, v=NULL) == EINVAL
-    assert bw(lib, d_in=2048, lddx=2048) == EUNSUP
+    assert bw(lib, d_in=32, lddx=32) == EUNSUP
+    assert bw(lib, d_in=16384, lddx=16384) == EUNSUP
+    assert bw(lib, d_in=8192, lddx=4096) == EINVAL
+    assert bw(lib, d_in=64, lddx=64, tokens=0) == OK
     assert bw(lib, d_out=5000, lddy=5000) == EUNSUP
     assert bw(lib, dyd=0) == EUNSUP
     assert bw(lib, vd=2) == EUNSUP
@@ -253,7 +260,9 @@ def test_qwha_backward_validation(lib):
     assert gv(lib, dc=NULL) == EINVAL
     assert gv(lib, ws=NULL) == EINVAL
     assert gv(lib, wsb=16) == EINVAL                        # workspace too small
-    assert gv(lib, d_in=2048, ldx=2048) == EUNSUP
+    assert gv(lib, d_in=32, ldx=32) == EUNSUP
+    assert gv(lib, d_in=3000, ldx=3000) == EUNSUP
+    assert gv(lib, d_in=8192, ldx=4096) == EINVAL
     assert gv(lib, dt=0) == EUNSUP
     assert gv(lib, x=P_MIS) == EALIGN
     assert gv(lib, ws=ctypes.c_void_p(0x10008)) == EALIGN
@@ -262,12 +271,18 @@ def test_qwha_backward_validation(lib):
     na = lambda **kw: lib.qwha_adapter_grad_values_noalloc(*_gv_args(**kw))
     assert na(ldx=100) == EINVAL
     assert na(dc=NULL) == EINVAL
-    assert na(d_in=2048, ldx=2048) == EUNSUP
+    assert na(d_in=16384, ldx=16384) == EUNSUP
     assert na(x=P_MIS) == EALIGN
     assert na(nnz=0, dc=NULL) == OK
     assert na(tokens=5000) == 5                              # 5000 x 16 KiB of Hn x > 64 MiB
     assert lib.qwha_grad_values_workspace_bytes(2048, 4096, 262144) <= 64 << 20
-    assert lib.qwha_grad_values_workspace_bytes(8, 2048, 100) == -1
+    assert lib.qwha_grad_values_workspace_bytes(8, 32, 100) == -1
+    assert lib.qwha_grad_values_workspace_bytes(8, 3000, 100) == -1
+    assert lib.qwha_grad_values_workspace_bytes(8, 16384, 100) == -1
+    # d_in below 4096 keeps the 4096-column Z layout; 8192 doubles it
+    assert lib.qwha_grad_values_workspace_bytes(64, 2048, 1000) == lib.qwha_grad_values_workspace_bytes(64, 4096, 1000)
+    assert lib.qwha_grad_values_workspace_bytes(64, 8192, 1000) >= 64 * 8192 * 4
+    assert na(d_in=8192, ldx=8192, tokens=2500) == 5          # 2500 x 32 KiB of Hn x > 64 MiB
     assert lib.qwha_grad_values_workspace_bytes(0, 4096, 100) == 0
     # Hn x in fp32 (rounded up to 256 B) plus per-token-slab partial sums
     need = lib.qwha_grad_values_workspace_bytes(2048, 4096, 262144)

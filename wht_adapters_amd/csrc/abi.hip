@@ -26,14 +26,14 @@ hipError_t launch_rht_dequant(int logn, int dout, int bits, int logg, const uint
 hipError_t launch_rht_gemv(int logn, int bits, int logg, const void* x, int64_t tokens, int64_t ldx,
                            const uint8_t* codes, const uint16_t* scales, int64_t rows, const uint32_t* sb,
                            void* y, int64_t ldy, hipStream_t s);
-hipError_t launch_qwha(const void* x, int64_t tokens, int64_t ldx, const int32_t* row_ptr,
+hipError_t launch_qwha(const void* x, int64_t tokens, int64_t d_in, int64_t ldx, const int32_t* row_ptr,
                        const int32_t* col_idx, const void* vals, int val_dt, int64_t d_out, int64_t nnz,
                        void* y, int64_t ldy, hipStream_t s);
 hipError_t launch_qwha_bwd_input(const void* dy, int64_t tokens, int64_t lddy, int64_t d_out,
                                  const int32_t* t_row_ptr, const int32_t* t_col_idx, const void* t_vals,
-                                 int val_dt, int64_t nnz, void* dx, int64_t lddx, hipStream_t s);
-int64_t qwha_dc_workspace_bytes(int64_t tokens, int64_t nnz);
-hipError_t launch_qwha_dc(const void* x, int64_t ldx, const void* dy, int64_t lddy, int64_t tokens,
+                                 int val_dt, int64_t d_in, int64_t nnz, void* dx, int64_t lddx, hipStream_t s);
+int64_t qwha_dc_workspace_bytes(int64_t tokens, int64_t d_in, int64_t nnz);
+hipError_t launch_qwha_dc(const void* x, int64_t ldx, const void* dy, int64_t lddy, int64_t tokens, int64_t d_in,
                           int64_t d_out, const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
                           float* dc, void* workspace, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
@@ -247,8 +247,7 @@ whtq_status qwha_adapter_forward(const void* x, whtq_dtype x_dtype, int64_t toke
   if (nnz > d_in * d_out) return WHTQ_EINVAL;
   if (!row_ptr || (nnz > 0 && (!col_idx || !vals))) return WHTQ_EINVAL;
   if (tokens > 0 && (!x || !y)) return WHTQ_EINVAL;
-  if (ilog2_pow2(d_in) < 0) return WHTQ_EUNSUPPORTED;
-  if (d_in != 4096 || d_out > 4096) return WHTQ_EUNSUPPORTED;
+  if (ilog2_pow2(d_in) < 6 || ilog2_pow2(d_in) > 13 || d_out > 4096) return WHTQ_EUNSUPPORTED;
   if (x_dtype != WHTQ_BF16 || y_dtype != WHTQ_BF16) return WHTQ_EUNSUPPORTED;
   if (val_dtype != WHTQ_BF16 && val_dtype != WHTQ_F32) return WHTQ_EUNSUPPORTED;
   if (!rows_aligned(x, d_in, ldx, 2) || !rows_aligned(y, d_out, ldy, 2)) return WHTQ_EALIGN;
@@ -256,7 +255,7 @@ whtq_status qwha_adapter_forward(const void* x, whtq_dtype x_dtype, int64_t toke
   if (tokens == 0) return WHTQ_OK;
   whtq_status st = need_device();
   if (st != WHTQ_OK) return st;
-  return hip_status(launch_qwha(x, tokens, ldx, row_ptr, col_idx, vals, val_dtype, d_out, nnz, y, ldy,
+  return hip_status(launch_qwha(x, tokens, d_in, ldx, row_ptr, col_idx, vals, val_dtype, d_out, nnz, y, ldy,
                                 (hipStream_t)stream));
 }
 
@@ -312,8 +311,7 @@ whtq_status qwha_adapter_backward_input(const void* dy, whtq_dtype dy_dtype, int
   if (nnz > d_in * d_out) return WHTQ_EINVAL;
   if (!t_row_ptr || (nnz > 0 && (!t_col_idx || !t_vals))) return WHTQ_EINVAL;
   if (tokens > 0 && (!dy || !dx)) return WHTQ_EINVAL;
-  if (ilog2_pow2(d_in) < 0) return WHTQ_EUNSUPPORTED;
-  if (d_in != 4096 || d_out > 4096) return WHTQ_EUNSUPPORTED;
+  if (ilog2_pow2(d_in) < 6 || ilog2_pow2(d_in) > 13 || d_out > 4096) return WHTQ_EUNSUPPORTED;
   if (dy_dtype != WHTQ_BF16 || dx_dtype != WHTQ_BF16) return WHTQ_EUNSUPPORTED;
   if (val_dtype != WHTQ_BF16 && val_dtype != WHTQ_F32) return WHTQ_EUNSUPPORTED;
   // dy: element alignment suffices (16-byte loads are used where its rows allow them)
@@ -323,14 +321,14 @@ whtq_status qwha_adapter_backward_input(const void* dy, whtq_dtype dy_dtype, int
   if (tokens == 0) return WHTQ_OK;
   whtq_status st = need_device();
   if (st != WHTQ_OK) return st;
-  return hip_status(launch_qwha_bwd_input(dy, tokens, lddy, d_out, t_row_ptr, t_col_idx, t_vals, val_dtype, nnz,
-                                          dx, lddx, (hipStream_t)stream));
+  return hip_status(launch_qwha_bwd_input(dy, tokens, lddy, d_out, t_row_ptr, t_col_idx, t_vals, val_dtype, d_in,
+                                          nnz, dx, lddx, (hipStream_t)stream));
 }
 
 int64_t qwha_grad_values_workspace_bytes(int64_t tokens, int64_t d_in, int64_t nnz) {
-  if (tokens < 0 || nnz < 0 || d_in != 4096) return -1;
+  if (tokens < 0 || nnz < 0 || ilog2_pow2(d_in) < 6 || ilog2_pow2(d_in) > 13) return -1;
   if (tokens == 0 || nnz == 0) return 0;
-  return qwha_dc_workspace_bytes(tokens, nnz);
+  return qwha_dc_workspace_bytes(tokens, d_in, nnz);
 }
 
 whtq_status qwha_adapter_grad_values(const void* x, const void* dy, whtq_dtype dtype, int64_t tokens,
@@ -342,21 +340,20 @@ whtq_status qwha_adapter_grad_values(const void* x, const void* dy, whtq_dtype d
   if (nnz > d_in * d_out || nnz > INT32_MAX) return WHTQ_EINVAL;
   if (!row_ptr || (nnz > 0 && (!col_idx || !dc))) return WHTQ_EINVAL;
   if (tokens > 0 && nnz > 0 && (!x || !dy || !workspace)) return WHTQ_EINVAL;
-  if (ilog2_pow2(d_in) < 0) return WHTQ_EUNSUPPORTED;
-  if (d_in != 4096 || d_out > 4096) return WHTQ_EUNSUPPORTED;
+  if (ilog2_pow2(d_in) < 6 || ilog2_pow2(d_in) > 13 || d_out > 4096) return WHTQ_EUNSUPPORTED;
   if (dtype != WHTQ_BF16) return WHTQ_EUNSUPPORTED;
   // dy is read with element loads: element alignment suffices
   if (!rows_aligned(x, d_in, ldx, 2) || (reinterpret_cast<uintptr_t>(dy) & 1u)) return WHTQ_EALIGN;
   if ((reinterpret_cast<uintptr_t>(row_ptr) & 3u) || (reinterpret_cast<uintptr_t>(col_idx) & 3u) ||
       (reinterpret_cast<uintptr_t>(dc) & 3u) || !aligned16(workspace))
     return WHTQ_EALIGN;
-  if (tokens > 0 && nnz > 0 && workspace_bytes < qwha_dc_workspace_bytes(tokens, nnz)) return WHTQ_EINVAL;
+  if (tokens > 0 && nnz > 0 && workspace_bytes < qwha_dc_workspace_bytes(tokens, d_in, nnz)) return WHTQ_EINVAL;
   if (nnz == 0) return WHTQ_OK;
   whtq_status st = need_device();
   if (st != WHTQ_OK) return st;
   if (tokens == 0)  // an empty sum: dc = 0 (a fill kernel, not a memset node)
     return hip_status(launch_fill_zero(dc, nnz, (hipStream_t)stream));
-  return hip_status(launch_qwha_dc(x, ldx, dy, lddy, tokens, d_out, row_ptr, col_idx, nnz, dc, workspace,
+  return hip_status(launch_qwha_dc(x, ldx, dy, lddy, tokens, d_in, d_out, row_ptr, col_idx, nnz, dc, workspace,
                                    (hipStream_t)stream));
 }
 
@@ -397,14 +394,13 @@ whtq_status qwha_adapter_grad_values_noalloc(const void* x, const void* dy, whtq
   if (nnz > d_in * d_out || nnz > INT32_MAX) return WHTQ_EINVAL;
   if (!row_ptr || (nnz > 0 && (!col_idx || !dc))) return WHTQ_EINVAL;
   if (tokens > 0 && nnz > 0 && (!x || !dy)) return WHTQ_EINVAL;
-  if (ilog2_pow2(d_in) < 0) return WHTQ_EUNSUPPORTED;
-  if (d_in != 4096 || d_out > 4096) return WHTQ_EUNSUPPORTED;
+  if (ilog2_pow2(d_in) < 6 || ilog2_pow2(d_in) > 13 || d_out > 4096) return WHTQ_EUNSUPPORTED;
   if (dtype != WHTQ_BF16) return WHTQ_EUNSUPPORTED;
   if (!rows_aligned(x, d_in, ldx, 2) || (reinterpret_cast<uintptr_t>(dy) & 1u)) return WHTQ_EALIGN;
   if ((reinterpret_cast<uintptr_t>(row_ptr) & 3u) || (reinterpret_cast<uintptr_t>(col_idx) & 3u) ||
       (reinterpret_cast<uintptr_t>(dc) & 3u))
     return WHTQ_EALIGN;
-  if (tokens > 0 && nnz > 0 && qwha_dc_workspace_bytes(tokens, nnz) > WHTQ_QWHA_DC_SCRATCH_BYTES)
+  if (tokens > 0 && nnz > 0 && qwha_dc_workspace_bytes(tokens, d_in, nnz) > WHTQ_QWHA_DC_SCRATCH_BYTES)
     return WHTQ_ESCRATCH;
   if (nnz == 0) return WHTQ_OK;
   whtq_status st = need_device();
@@ -413,7 +409,7 @@ whtq_status qwha_adapter_grad_values_noalloc(const void* x, const void* dy, whtq
   void* ws = nullptr;
   st = scratch_of_current_device(&ws);
   if (st != WHTQ_OK) return st;
-  return hip_status(launch_qwha_dc(x, ldx, dy, lddy, tokens, d_out, row_ptr, col_idx, nnz, dc, ws,
+  return hip_status(launch_qwha_dc(x, ldx, dy, lddy, tokens, d_in, d_out, row_ptr, col_idx, nnz, dc, ws,
                                    (hipStream_t)stream));
 }
 

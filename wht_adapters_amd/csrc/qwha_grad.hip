@@ -8,7 +8,8 @@
 //
 // Three launches on the caller's stream:
 //   1. k_qwha_z: Z = x Hn in fp32 (the FWHT engine) into the workspace,
-//      tile-interleaved (four tokens per 16-byte column);
+//      tile-interleaved (four tokens per 16-byte column); d_in < 4096 is
+//      zero-extended, d_in = 8192 transformed as two halves;
 //   2. k_qwha_dc: the entries are cut into slabs of at most 16384 (16 per
 //      lane of a 1024-lane block, placed so that LDS reads rarely collide,
 //      see the slot set-up) and the tokens into slabs of whole 4-token
@@ -25,6 +26,8 @@
 // Blocks that share a token slab read the same Z rows; they are placed on
 // the same XCD (the hardware deals consecutive blocks out to the 8 XCDs in
 // turn), so those rows are fetched once into that XCD's L2.
+#include <cmath>
+
 #include "io.hpp"
 #include "launch.hpp"
 
@@ -68,40 +71,61 @@ constexpr int ROW = 4096 + 256;  // padded row, floats
 constexpr int LDS_BYTES = 4 * ROW * 4;
 }  // namespace qz
 
+// d_in < 4096 is zero-extended (the first d_in outputs of H_4096 [x; 0] are
+// H_d x, scale 1 / sqrt(d_in)); d_in = 8192 (WIDE) writes the two halves
+// H_4096 (x_lo + x_hi) and H_4096 (x_lo - x_hi) of H_8192 x in turn, the
+// quad's columns [h 4096, h 4096 + 4096).
+template <bool WIDE>
 __global__ __launch_bounds__(256) void k_qwha_z(const uint16_t* __restrict__ x, int64_t tokens, int64_t ldx,
-                                                float* __restrict__ zi) {
+                                                int in_cols, float scale, float* __restrict__ zi) {
   using G = Geo<12>;
   static_assert(4 * G::LDS_ROW <= 4 * qz::ROW, "transpose scratch fits in the row buffer");
+  constexpr int ZS = WIDE ? 8192 : 4096;  // columns per quad
   extern __shared__ __align__(16) uint8_t smem[];
   float* lds = reinterpret_cast<float*>(smem);
   const int tid = threadIdx.x, w = tid >> 6, t = tid & 63;
   const int64_t quad = blockIdx.x, tok = quad * 4 + w;
-  float v[64];
-  {
-    const uint32_t nomask[4] = {0u, 0u, 0u, 0u};
-    const uint16_t* xr = x + (tok < tokens ? tok : tokens - 1) * ldx;
+  const uint32_t nomask[4] = {0u, 0u, 0u, 0u};
+  const uint16_t* xr = x + (tok < tokens ? tok : tokens - 1) * ldx;
+#pragma unroll 1
+  for (int h = 0; h < (WIDE ? 2 : 1); ++h) {
+    float v[64];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      Raw8 raw;
-      fetch8<DT_BF16>(xr, G::idxA(t, c * 8), raw);
-      widen8<DT_BF16, false>(raw, v + 8 * c, nomask, 0u);
+      const int col = G::idxA(t, c * 8);
+      if constexpr (WIDE) {
+        Raw8 rl, rh;
+        fetch8<DT_BF16>(xr, col, rl);
+        fetch8<DT_BF16>(xr, col + 4096, rh);
+        float vh[8];
+        widen8<DT_BF16, false>(rl, v + 8 * c, nomask, 0u);
+        widen8<DT_BF16, false>(rh, vh, nomask, 0u);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[8 * c + e] = h ? v[8 * c + e] - vh[e] : v[8 * c + e] + vh[e];
+      } else {
+        Raw8 raw{};
+        if (col < in_cols) fetch8<DT_BF16>(xr, col, raw);
+        widen8<DT_BF16, false>(raw, v + 8 * c, nomask, 0u);
+      }
     }
+    if (h) __syncthreads();  // the previous half's columns have left the row buffer
     stages_A<12, false>(v, t);
     transpose_AB<12, 64>(lds + w * G::LDS_ROW, v, t);
     stages_B<12, 2>(v, t);
-  }
-  const float cs = tok < tokens ? (rho_B<12>(t) ? -1.0f / 64.0f : 1.0f / 64.0f) : 0.0f;
-  __syncthreads();  // every wave's transpose scratch is free
-  float* row = lds + w * qz::ROW + t * 68;
+    const float cs = tok < tokens ? (rho_B<12>(t) ? -scale : scale) : 0.0f;
+    __syncthreads();  // every wave's transpose scratch is free
+    float* row = lds + w * qz::ROW + t * 68;
 #pragma unroll
-  for (int q = 0; q < 16; ++q)
-    *reinterpret_cast<f32x4*>(row + 4 * q) = f32x4{v[4 * q] * cs, v[4 * q + 1] * cs, v[4 * q + 2] * cs, v[4 * q + 3] * cs};
-  __syncthreads();
-  f32x4* dst = reinterpret_cast<f32x4*>(zi) + quad * 4096;
+    for (int q = 0; q < 16; ++q)
+      *reinterpret_cast<f32x4*>(row + 4 * q) =
+          f32x4{v[4 * q] * cs, v[4 * q + 1] * cs, v[4 * q + 2] * cs, v[4 * q + 3] * cs};
+    __syncthreads();
+    f32x4* dst = reinterpret_cast<f32x4*>(zi) + quad * ZS + h * 4096;
 #pragma unroll 4
-  for (int m = 0; m < 16; ++m) {
-    const int k = tid + 256 * m, ph = k + ((k >> 6) << 2);
-    dst[k] = f32x4{lds[ph], lds[qz::ROW + ph], lds[2 * qz::ROW + ph], lds[3 * qz::ROW + ph]};
+    for (int m = 0; m < 16; ++m) {
+      const int k = tid + 256 * m, ph = k + ((k >> 6) << 2);
+      dst[k] = f32x4{lds[ph], lds[qz::ROW + ph], lds[2 * qz::ROW + ph], lds[3 * qz::ROW + ph]};
+    }
   }
 }
 
@@ -139,7 +163,7 @@ __device__ __forceinline__ void dc_block(int b, int r_slabs, int t_slabs, int& r
 __global__ __launch_bounds__(qg::THREADS) void k_qwha_dc(
     const float* __restrict__ z, int64_t tokens, const uint16_t* __restrict__ dy, int64_t lddy,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int d_out, int nnz, int span,
-    int r_slabs, int t_slabs, int quads_per_slab, float* __restrict__ out) {
+    int r_slabs, int t_slabs, int quads_per_slab, int zstride, int kbase, float* __restrict__ out) {
   extern __shared__ __align__(16) uint8_t smem[];
   f32x4* zq = reinterpret_cast<f32x4*>(smem + qg::LDS_Z);
   u32x2* dq = reinterpret_cast<u32x2*>(smem + qg::LDS_D);
@@ -196,10 +220,15 @@ __global__ __launch_bounds__(qg::THREADS) void k_qwha_dc(
     for (int j = 0; j < qg::EPL; ++j) {
       const int e = eb + j;
       const bool ok = e < e1;
-      const int c = ok ? col_idx[e] & (qg::N - 1) : 0;
+      const int cf = ok ? col_idx[e] : 0;
+      const int c = cf & (qg::N - 1);
+      // this launch covers the columns [kbase, kbase + 4096) of Z; an entry
+      // outside them is summed against the window's column c (harmless) and
+      // not written (the other window's launch writes it)
+      const bool out_win = ok && (cf & ~(qg::N - 1)) != kbase;
       if (ok && o + 1 < d_out && rp[o + 1] <= e) o = row_from(o + 1, e);
       res[j] = ok ? (uint32_t)c & 15u : 16u;
-      coltab[qg::GE * grp + qg::EPL * gl + j] = (uint16_t)c;
+      coltab[qg::GE * grp + qg::EPL * gl + j] = (uint16_t)(c | (out_win ? 0x8000 : 0));
       rowtab[qg::GE * grp + qg::EPL * gl + j] = (uint16_t)o;
     }
 #pragma unroll
@@ -220,12 +249,14 @@ __global__ __launch_bounds__(qg::THREADS) void k_qwha_dc(
   __syncthreads();
   const int o_lo = lim[0], nrows = lim[1] - lim[0] + 1;  // nrows <= d_out <= 4096
   uint32_t ent[qg::EPL];  // column | (row - o_lo) << 16
+  uint32_t skip = 0u;     // bit i: entry i lies outside this launch's column window
   float acc[qg::EPL];
 #pragma unroll
   for (int i = 0; i < qg::EPL; ++i) {
     const int off = slot[qg::GE * grp + qg::EPL * gl + i];
     const int o = min(max((int)rowtab[off] - o_lo, 0), nrows - 1);
-    ent[i] = (uint32_t)coltab[off] | ((uint32_t)o << 16);
+    ent[i] = ((uint32_t)coltab[off] & (qg::N - 1)) | ((uint32_t)o << 16);
+    skip |= (uint32_t)(coltab[off] >> 15) << i;
     acc[i] = 0.f;
   }
 
@@ -249,7 +280,7 @@ __global__ __launch_bounds__(qg::THREADS) void k_qwha_dc(
   const uint32_t drow = (uint32_t)(o_lo + min(tid, nrows - 1));
   auto fetch = [&](int q, Pre& b) {
     // past the end: re-read the last tile (its dy is zeroed when staged)
-    const f32x4* zt = reinterpret_cast<const f32x4*>(z) + (int64_t)min(q, last_quad) * qg::N;
+    const f32x4* zt = reinterpret_cast<const f32x4*>(z) + (int64_t)min(q, last_quad) * zstride + kbase;
 #pragma unroll
     for (int m = 0; m < qg::ZPT; ++m) b.z[m] = zt[(uint32_t)(tid + qg::THREADS * m)];
 #pragma unroll
@@ -324,7 +355,7 @@ __global__ __launch_bounds__(qg::THREADS) void k_qwha_dc(
 #pragma unroll
   for (int i = 0; i < qg::EPL; ++i) {
     const int e = e0 + slot[qg::GE * grp + qg::EPL * gl + i];
-    if (e < e1) dst[e] = acc[i];
+    if (e < e1 && !((skip >> i) & 1u)) dst[e] = acc[i];
   }
 }
 
@@ -346,25 +377,37 @@ __global__ __launch_bounds__(256) void k_permute(const T* __restrict__ vals, con
   if (j < nnz) out[j] = vals[perm[j]];
 }
 
-int64_t qwha_dc_workspace_bytes(int64_t tokens, int64_t nnz) {
+// Z columns per 4-token quad in the workspace: d_in = 8192 keeps both halves
+static int64_t dc_zstride(int64_t d_in) { return d_in == 8192 ? 8192 : qg::N; }
+
+int64_t qwha_dc_workspace_bytes(int64_t tokens, int64_t d_in, int64_t nnz) {
   const DcGrid g = dc_grid(tokens, nnz);
-  const int64_t zb = (tokens + 3) / 4 * qg::N * 16;  // tile-interleaved Z
+  const int64_t zb = (tokens + 3) / 4 * dc_zstride(d_in) * 16;  // tile-interleaved Z
   const int64_t pb = g.t_slabs > 1 ? (int64_t)g.t_slabs * nnz * 4 : 0;
   return ((zb + 255) & ~int64_t(255)) + pb;
 }
 
-hipError_t launch_qwha_dc(const void* x, int64_t ldx, const void* dy, int64_t lddy, int64_t tokens,
+template <bool WIDE>
+static void launch_z(const void* x, int64_t tokens, int64_t ldx, int in_cols, float scale, float* z, hipStream_t s) {
+  static const bool zattr = hipFuncSetAttribute((const void*)k_qwha_z<WIDE>,
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, qz::LDS_BYTES) == hipSuccess;
+  (void)zattr;
+  hipLaunchKernelGGL(k_qwha_z<WIDE>, dim3((unsigned)((tokens + 3) / 4)), dim3(256), qz::LDS_BYTES, s,
+                     (const uint16_t*)x, tokens, ldx, in_cols, scale, z);
+}
+
+hipError_t launch_qwha_dc(const void* x, int64_t ldx, const void* dy, int64_t lddy, int64_t tokens, int64_t d_in,
                           int64_t d_out, const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
                           float* dc, void* workspace, hipStream_t s) {
   const DcGrid g = dc_grid(tokens, nnz);
+  const bool wide = d_in == 8192;
+  const int64_t zs = dc_zstride(d_in);
   float* z = reinterpret_cast<float*>(workspace);
-  const int64_t zb = ((tokens + 3) / 4 * qg::N * 16 + 255) & ~int64_t(255);
+  const int64_t zb = ((tokens + 3) / 4 * zs * 16 + 255) & ~int64_t(255);
   float* part = g.t_slabs > 1 ? reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) + zb) : dc;
-  static const bool zattr = hipFuncSetAttribute((const void*)k_qwha_z, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                qz::LDS_BYTES) == hipSuccess;
-  (void)zattr;
-  hipLaunchKernelGGL(k_qwha_z, dim3((unsigned)((tokens + 3) / 4)), dim3(256), qz::LDS_BYTES, s,
-                     (const uint16_t*)x, tokens, ldx, z);
+  const float scale = (float)(1.0 / std::sqrt((double)d_in));
+  if (wide) launch_z<true>(x, tokens, ldx, (int)d_in, scale, z, s);
+  else launch_z<false>(x, tokens, ldx, (int)d_in, scale, z, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   static const bool attr = hipFuncSetAttribute((const void*)k_qwha_dc, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -373,10 +416,14 @@ hipError_t launch_qwha_dc(const void* x, int64_t ldx, const void* dy, int64_t ld
   // whole rounds of 8 token slabs per XCD lane: blocks with p >= t_slabs exit at once
   const int64_t p_rounds = (g.t_slabs + qg::XCDS - 1) / qg::XCDS;
   const unsigned grid = (unsigned)(p_rounds * qg::XCDS * g.r_slabs);
-  hipLaunchKernelGGL(k_qwha_dc, dim3(grid), dim3(qg::THREADS), qg::LDS_BYTES, s, z, tokens,
-                     (const uint16_t*)dy, lddy, row_ptr, col_idx, (int)d_out, (int)nnz, g.span, g.r_slabs,
-                     g.t_slabs, g.quads_per_slab, part);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // one launch per 4096-column window of Z (two at d_in = 8192); each entry
+  // is written by the launch whose window holds its column
+  for (int kb = 0; kb < (wide ? 8192 : qg::N); kb += qg::N) {
+    hipLaunchKernelGGL(k_qwha_dc, dim3(grid), dim3(qg::THREADS), qg::LDS_BYTES, s, z, tokens,
+                       (const uint16_t*)dy, lddy, row_ptr, col_idx, (int)d_out, (int)nnz, g.span, g.r_slabs,
+                       g.t_slabs, g.quads_per_slab, (int)zs, kb, part);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (g.t_slabs > 1) {
     hipLaunchKernelGGL(k_qwha_dc_reduce, dim3((unsigned)((nnz + 255) / 256)), dim3(256), 0, s, part, g.t_slabs,
                        (int)nnz, dc);
