@@ -115,3 +115,39 @@ def test_full_config_2048x4096_nnz262144():
     write_report("parity_qwha_forward_2048x4096_nnz262144",
                  {"tokens": 2048, "max_scaled_err": err, "max_row_rel_err": roww, "tol": TOL})
     assert err <= TOL
+
+
+@pytest.mark.parametrize("tokens", [37, 300])
+def test_long_rows_split_into_segments(tokens):
+    """Rows of 1..4096 entries next to short and empty ones: long rows are cut
+    into 128-entry segments whose partial sums fill the per-chunk slots, so
+    the rows are spread over several chunks; lengths at the segment edges
+    (127..129, 255..257) and unaligned row starts included."""
+    rng = np.random.default_rng(tokens)
+    d_out = 700
+    lens = rng.integers(0, 40, d_out)
+    lens[::7] = rng.integers(1000, 4097, lens[::7].size)
+    lens[3:12] = [127, 128, 129, 255, 256, 257, 4096, 1, 0]
+    cols = np.concatenate([np.sort(rng.choice(4096, int(l), replace=False)) for l in lens]).astype(np.int32)
+    rp = np.r_[0, np.cumsum(lens)].astype(np.int32)
+    x = synth.to_bf16(rng.standard_normal((tokens, 4096)))
+    v = synth.to_bf16(0.05 * rng.standard_normal(cols.size))
+    y = run(x, rp, cols, v, d_out)
+    want = qwha.qwha_forward(synth.bf16_to_f64(x), rp, cols, synth.bf16_to_f64(v), d_out)
+    err, _ = compare.float_err(host64(y), want)
+    assert err <= TOL, err
+    assert torch.equal(y, run(x, rp, cols, v, d_out))  # deterministic
+
+
+def test_row_of_repeated_columns():
+    """A row of 20,000 entries with repeated columns (longer than any row of
+    distinct columns): kept whole; the oracle sums the repeats."""
+    rng = np.random.default_rng(20000)
+    lens = np.array([3, 20000, 0, 50, 7])
+    cols = np.concatenate([rng.integers(0, 4096, int(l)) for l in lens]).astype(np.int32)
+    rp = np.r_[0, np.cumsum(lens)].astype(np.int32)
+    x = synth.to_bf16(rng.standard_normal((20, 4096)))
+    v = synth.to_bf16(0.01 * rng.standard_normal(cols.size))
+    y = run(x, rp, cols, v, 5)
+    want = qwha.qwha_forward(synth.bf16_to_f64(x), rp, cols, synth.bf16_to_f64(v), 5)
+    assert compare.float_err(host64(y), want)[0] <= TOL

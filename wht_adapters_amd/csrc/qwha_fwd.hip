@@ -1,0 +1,619 @@
+// qwha_adapter_forward for d_in <= 4096: y = (x Hn) F^T with F sparse (CSR).
+//
+// QWHA explainer, 2.1: the adapter is Delta W = F H^-1, one Walsh-Hadamard
+// transform on the input side and a sparse coefficient matrix F; with the
+// orthonormal Hn this is y = x Delta W^T = (x Hn) F^T.
+//
+// One block of 16 waves per (tile of 16 tokens, range of F's rows).  A token
+// tile is shared by S blocks, each taking a range of rows with about nnz / S
+// entries, so that tokens / 16 * S blocks cover the chip.
+//   1. Each wave transforms one token on the matrix cores.  With i = 64a + b
+//      the Sylvester matrix factors as H_4096[i][i'] = H_64[a][a'] H_64[b][b']
+//      (popcount(i & i') adds over the two 6-bit fields), so for the token
+//      viewed as M[a][b] = x[64a + b] the raw transform is H_64 M H_64: pass 1
+//      T = M H_64 (bf16 MFMA straight from the token's 16-byte loads, which
+//      are already in the A-operand layout), T rescaled by an exact power of
+//      two and rounded to fp16, pass 2 Y = H_64 T (fp16 MFMA; the D layout of
+//      pass 1 is used as the B operand by pairing each contraction slot with
+//      the row of T the lane already holds).  The power-of-two scale comes
+//      from the bound |(H_4096 x)_k| <= 64 ||x||_2 (one per token), so every
+//      staged value is below 2^13.  d_in < 4096 is zero-extended: the first
+//      d_in entries of the 4096-point transform of [x; 0] are H_d x (the
+//      factor 64 / sqrt(d_in) is applied to the outputs).
+//   2. Y goes to Z in LDS as two planes of 16-byte columns (tokens 0-7 and
+//      8-15): one column read gives a row entry's value for 8 tokens.
+//   3. The block's rows are taken in chunks of 512 and bucketed by the
+//      number of 16-entry steps they need (longest first), so the 16 rows a
+//      wave runs together finish at about the same time.
+//   4. CSR gather: a quad of lanes per row, each lane taking 4 consecutive
+//      entries per step with 16-byte index loads, two column reads per entry
+//      and 16 fp32 accumulators per lane (v_fma_mix with the fp16 column),
+//      a quad DPP reduction per row, results to a token-major bf16 buffer.
+//   5. The chunk's outputs leave with 16-byte row-contiguous stores.
+#include <climits>
+#include <cmath>
+
+#include "io.hpp"
+
+namespace whtq {
+
+namespace qf {
+constexpr int THREADS = 1024;  // 16 waves, one per token of the tile
+constexpr int NW = THREADS / 64;
+constexpr int TT = 16;         // tokens per tile
+constexpr int CHUNK = 512;     // at most this many rows per output chunk
+constexpr int SEG = 8;         // 16-entry steps per segment: longer rows are split
+constexpr int PSLOTS = 112;    // fp32 partial-sum slots per chunk (segments of split rows)
+constexpr int SEGCAP = CHUNK + PSLOTS;
+constexpr int NBKT = SEG + 2;  // segment buckets: longer than SEG steps (a row kept whole), SEG, ..., 0
+constexpr int RW = CHUNK / 64; // waves that take the chunk's rows (one row per lane)
+
+constexpr int NZ = 4096;       // transform width (zero-extended below)
+// LDS map (bytes)
+constexpr int ZP = NZ * 16;                     // plane p: tokens 8p..8p+7, column k at 16 k
+constexpr int OUT = 2 * ZP;                     // bf16 [TT][CHUNK]
+constexpr int PART = OUT + TT * CHUNK * 2;      // fp32 [PSLOTS][TT]
+constexpr int SBEG = PART + PSLOTS * TT * 4;    // int [SEGCAP]: segment's first entry
+constexpr int SEND = SBEG + SEGCAP * 4;         // int [SEGCAP]: segment's end entry
+constexpr int SRID = SEND + SEGCAP * 4;         // uint16 [SEGCAP]: row within the chunk
+constexpr int SPS = SRID + SEGCAP * 2;          // int8 [SEGCAP]: partial slot, -1 for a whole row
+constexpr int ROWPS = SPS + SEGCAP;             // uint16 [CHUNK]: first partial slot of a split row
+constexpr int RNSEG = ROWPS + CHUNK * 2;        // uint8 [CHUNK]: segments of the row
+constexpr int CNT = RNSEG + CHUNK;              // uint32 [NBKT][RW]: segment counts, then starts
+constexpr int WT = CNT + NBKT * RW * 4;         // int [RW]: per-wave partial-slot totals
+constexpr int SPLIT = WT + RW * 4;              // uint16 [PSLOTS / 2]: the chunk's split rows
+constexpr int EXP = SPLIT + PSLOTS;             // int [TT]: per-token exponents
+constexpr int MISC = EXP + TT * 4;              // int [8]: row range, chunk size, segments, split rows
+constexpr int BYTES = MISC + 32;
+static_assert(BYTES <= 160 * 1024, "LDS map");
+static_assert(NZ / (16 * SEG) + 1 <= PSLOTS && PSLOTS < 128, "a row of NZ entries fits the partial slots");
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mma_bf16(const u32x4& a, const u32x4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_f16(const u32x4& a, const u32x4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                0, 0, 0);
+}
+
+// Inclusive prefix sum over the 64 lanes: row_shr 1, 2, 4, 8 within rows of
+// 16 lanes, then row_bcast 15 / 31 carry the row totals upwards.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);
+  return x;
+}
+
+__device__ __forceinline__ float wave_incl_scan_f(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x112, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x114, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x118, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142, 0xa, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x143, 0xc, 0xf, false));
+  return x;
+}
+
+// 16-entry steps of a row [beg, end) whose steps start at beg rounded down to a multiple of 4
+__device__ __forceinline__ int steps_of(int beg, int end) { return end > beg ? (end - (beg & ~3) + 15) >> 4 : 0; }
+}  // namespace qf
+
+// four consecutive values of F, from an index that is a multiple of 4
+template <int VALDT> struct FVal;
+template <> struct FVal<DT_BF16> {
+  typedef u32x2 raw;
+  static __device__ __forceinline__ raw load(const void* v, int j) {
+    return ldg<u32x2>(reinterpret_cast<const uint8_t*>(v) + 2u * (uint32_t)j);
+  }
+  static __device__ __forceinline__ float get(const raw& r, int q) {
+    const uint32_t w = q < 2 ? r.x : r.y;
+    return (q & 1) ? bf16hi(w) : bf16lo(w);
+  }
+};
+template <> struct FVal<DT_F32> {
+  typedef f32x4 raw;
+  static __device__ __forceinline__ raw load(const void* v, int j) {
+    return ldg<f32x4>(reinterpret_cast<const uint8_t*>(v) + 4u * (uint32_t)j);
+  }
+  static __device__ __forceinline__ float get(const raw& r, int q) { return r[q]; }
+};
+
+template <int VALDT>
+__global__ __launch_bounds__(qf::THREADS) void k_qwha_fwd(const uint16_t* __restrict__ x, int64_t tokens, int64_t ldx,
+                                                          int in_cols, const int32_t* __restrict__ row_ptr,
+                                                          const int32_t* __restrict__ col_idx,
+                                                          const void* __restrict__ vals, int d_out, int nnz,
+                                                          uint16_t* __restrict__ y, int64_t ldy, int vec,
+                                                          float wscale, int tiles, int splits) {
+  using V = FVal<VALDT>;
+  constexpr int TT = qf::TT;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // split-major block order: the blocks of one token tile are `tiles` apart,
+  // on one XCD when tiles is a multiple of 8 (x is then read once per XCD)
+  const int tile = (int)(blockIdx.x % (unsigned)tiles), split = (int)(blockIdx.x / (unsigned)tiles);
+  const int64_t tok0 = (int64_t)tile * TT;
+  const int ntok = (int)min<int64_t>(TT, tokens - tok0);
+
+  uint16_t* obuf = reinterpret_cast<uint16_t*>(smem + qf::OUT);
+  float* part = reinterpret_cast<float*>(smem + qf::PART);
+  int* s_beg = reinterpret_cast<int*>(smem + qf::SBEG);
+  uint16_t* s_rid = reinterpret_cast<uint16_t*>(smem + qf::SRID);
+  int* s_end = reinterpret_cast<int*>(smem + qf::SEND);
+  int8_t* s_ps = reinterpret_cast<int8_t*>(smem + qf::SPS);
+  uint16_t* rowps = reinterpret_cast<uint16_t*>(smem + qf::ROWPS);
+  uint8_t* rnseg = reinterpret_cast<uint8_t*>(smem + qf::RNSEG);
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(smem + qf::CNT);
+  int* wt = reinterpret_cast<int*>(smem + qf::WT);
+  uint16_t* splitrows = reinterpret_cast<uint16_t*>(smem + qf::SPLIT);
+  int* texp = reinterpret_cast<int*>(smem + qf::EXP);
+  int* misc = reinterpret_cast<int*>(smem + qf::MISC);
+
+  // ---- the token rows' loads go out first (one wave per token; each 16-byte
+  // load is the A operand of pass 1: lane (q, r) holds M[16 ab + r][32 kb + 8 q + 0..7])
+  const int r16 = lane & 15, q4 = lane >> 4;
+  u32x4 xa[4][2];
+  {
+    const int64_t tok = tok0 + wave;
+    const uint16_t* xr = x + (tok < tokens ? tok : 0) * ldx;
+#pragma unroll
+    for (int ab = 0; ab < 4; ++ab)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int c = 64 * (16 * ab + r16) + 32 * kb + 8 * q4;
+        xa[ab][kb] = (tok < tokens && c < in_cols) ? ldg<u32x4>(xr + c) : u32x4{0u, 0u, 0u, 0u};
+      }
+  }
+
+  // ---- the block's rows: [lower_bound(row_ptr, nnz s / S)] rounded down to
+  // a multiple of 8 (aligned output stores), for s = split and split + 1
+  if (tid < 2) misc[tid] = (split + tid >= splits) ? d_out : d_out + 1;
+  __syncthreads();
+  if (splits > 1) {
+    // every thread's row_ptr entries are requested at once (d_out <= 4096:
+    // at most five per thread), then compared
+    constexpr int PER = (4096 + qf::THREADS) / qf::THREADS;
+    int cur[PER], prv[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int o = tid + i * qf::THREADS;
+      cur[i] = o <= d_out ? row_ptr[o] : INT_MAX;
+      prv[i] = (o >= 1 && o <= d_out) ? row_ptr[o - 1] : INT_MIN;
+    }
+#pragma unroll
+    for (int side = 0; side < 2; ++side) {
+      if (split + side == 0 || split + side >= splits) continue;
+      const int64_t target = (int64_t)nnz * (split + side) / splits;
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (cur[i] != INT_MAX && cur[i] >= target && prv[i] < target)
+          atomicMin(&misc[side], (tid + i * qf::THREADS) & ~7);
+    }
+  }
+  __syncthreads();
+  const int r_lo = split == 0 ? 0 : min(misc[0], d_out);
+  const int r_hi = max(r_lo, min(misc[1], d_out));
+  // the first chunk's slice of row_ptr (the partial slots are free until the
+  // gather); its loads complete behind the transform
+  int* rps = reinterpret_cast<int*>(smem + qf::PART);
+  static_assert((qf::CHUNK + 1) * 4 <= qf::PSLOTS * qf::TT * 4, "row_ptr slice in the partial slots");
+  for (int i = tid; i <= min(qf::CHUNK, r_hi - r_lo) && r_lo < r_hi; i += qf::THREADS) rps[i] = row_ptr[r_lo + i];
+
+  // ---- 1-2. the token's transform on the matrix cores, into the Z planes
+  {
+    // ||x||^2: bf16 pairs squared and summed in fp32, the wave total
+    // broadcast from one lane (the same value in every lane)
+    float nrm = 0.f;
+#pragma unroll
+    for (int ab = 0; ab < 4; ++ab)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          nrm = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xa[ab][kb][p]),
+                                                __builtin_bit_cast(bf16x2_t, xa[ab][kb][p]), nrm, false);
+    nrm = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, qf::wave_incl_scan_f(nrm)), 63));
+    int en = 0;
+    const float nx = __builtin_sqrtf(nrm);
+    if (nx > 0.f) (void)frexpf(nx, &en);  // ||x|| < 2^en
+    // |T| <= 8 ||x|| < 2^(en+3): pass 1 multiplies by 2^s1, s1 = 9 - en, so
+    // T 2^s1 < 2^12 in fp16; pass 2's +-1/4 leaves |Z| = |H_4096 x| 2^(s1-2) < 2^13.
+    // 2^s1 must be a normal bf16: s1 <= 127 (only for ||x|| < 2^-118 does the
+    // cap bind; the staged values are then smaller, the bookkeeping exact)
+    const int s1 = min(9 - en, 127);
+    if (lane == 0) texp[wave] = -4 - s1;  // (Hn x)_k = Z_k 2^(2-s1) / 64
+    // Sylvester signs over the operand layouts.  Pass 1, B[8q + j][r] =
+    // H_64[32 kb + 8q + j][16 nb + r]: popcount((32 kb + 8q + j) & (16 nb + r))
+    // = popcount(j & r & 7) + q0 r3 + q1 nb0 + kb nb1.  Pass 2, A[r][8q + j] =
+    // H_64[16 ab2 + r][32 kb2 + 16 [j >= 4] + 4q + (j & 3)]: popcount = popcount(r & j & 3)
+    // + popcount((r >> 2) & q) + ab2_0 [j >= 4] + ab2_1 kb2.
+    constexpr uint32_t FLIP = 0x80008000u;
+    const uint32_t e1 = (uint32_t)(s1 + 127) << 7;  // bf16 exponent field of 2^s1
+    u32x4 pb, pa;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t w1 = e1 | (e1 << 16), w2 = 0x3400u | (0x3400u << 16);  // 2^s1 (bf16), 1/4 (fp16)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int j = 2 * p + e;
+        w1 |= (uint32_t)((__builtin_popcount(j & r16 & 7) + ((q4 & 1) & (r16 >> 3))) & 1) << (15 + 16 * e);
+        w2 |= (uint32_t)((__builtin_popcount(r16 & j & 3) + __builtin_popcount((r16 >> 2) & q4)) & 1) << (15 + 16 * e);
+      }
+      pb[p] = w1;
+      pa[p] = w2;
+    }
+    const uint32_t fq1 = (q4 >> 1) ? FLIP : 0u;
+    uint16_t* zcol = reinterpret_cast<uint16_t*>(smem + (wave >> 3) * qf::ZP) + (wave & 7);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      f32x4 t[4];
+#pragma unroll
+      for (int ab = 0; ab < 4; ++ab) {
+        t[ab] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const uint32_t f = ((nb & 1) ? fq1 : 0u) ^ ((kb & (nb >> 1)) ? FLIP : 0u);
+          const u32x4 hb = u32x4{pb[0] ^ f, pb[1] ^ f, pb[2] ^ f, pb[3] ^ f};
+          t[ab] = qf::mma_bf16(xa[ab][kb], hb, t[ab]);
+        }
+      }
+      // pass-2 B operand, contraction slot 8q + j <-> row a' of T: the rows
+      // 32 kb2 + 4q + j (j < 4) and 32 kb2 + 16 + 4q + (j - 4) this lane holds
+      u32x4 tb[2];
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const f32x4& t0 = t[2 * kb2];
+        const f32x4& t1 = t[2 * kb2 + 1];
+        tb[kb2] = u32x4{pack_f16(t0[0], t0[1]), pack_f16(t0[2], t0[3]), pack_f16(t1[0], t1[1]), pack_f16(t1[2], t1[3])};
+      }
+#pragma unroll
+      for (int ab2 = 0; ab2 < 4; ++ab2) {
+        f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          const uint32_t fa = ((ab2 >> 1) & kb2) ? FLIP : 0u, fb = fa ^ ((ab2 & 1) ? FLIP : 0u);
+          const u32x4 ha = u32x4{pa[0] ^ fa, pa[1] ^ fa, pa[2] ^ fb, pa[3] ^ fb};
+          z = qf::mma_f16(ha, tb[kb2], z);
+        }
+        // lane (q, r) holds Y[16 ab2 + 4 q + j][16 nb + r]: column k = 64 a + b
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int k = 64 * (16 * ab2 + 4 * q4 + j) + 16 * nb + r16;
+          zcol[8 * k] = (uint16_t)(pack_f16(z[j], 0.f) & 0xffffu);
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // per output token slot: undo the staging scale and normalise (wscale
+  // carries 64 / sqrt(d_in) for a zero-extended input)
+  const int slot = lane & 3;  // lane within the row's quad: tokens 4 slot .. 4 slot + 3
+  float osc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) osc[i] = ldexpf(wscale, texp[4 * slot + i]);
+
+  auto seg_of = [&](int beg, int end, int ns, int i, int& sb, int& se) {
+    const int b4 = beg & ~3;
+    sb = i == 0 ? beg : b4 + 16 * qf::SEG * i;
+    se = ns == 1 ? end : min(end, b4 + 16 * qf::SEG * (i + 1));
+  };
+  const uint64_t below = (1ull << lane) - 1ull;
+
+  for (int base = r_lo; base < r_hi;) {
+    const int avail = min(qf::CHUNK, r_hi - base);
+    // ---- 3. the chunk: its first rows whose split rows fit the partial
+    // slots.  A row of nst steps is cut into ceil(nst / SEG) segments (the
+    // row's steps 0..SEG-1, SEG..2 SEG-1, ...); a row of one segment writes
+    // its outputs directly, the segments of a longer row write fp32 partial
+    // sums that are added in segment order afterwards (deterministic).  The
+    // segments are ordered by step count, longest first, by a counting sort
+    // over (bucket, wave) with ballots.  One lane per row (waves 0..RW-1).
+    uint32_t* rowtag = reinterpret_cast<uint32_t*>(obuf);  // per row until the gather: bucket | rank | full start
+    constexpr int B8 = 1;                                 // the bucket of SEG-step segments
+    const int r = tid;
+    int st = 0, ns = 0, dem = 0, incl = 0;
+    if (wave < qf::RW) {
+      if (r < avail) {
+        st = qf::steps_of(rps[r], rps[r + 1]);
+        ns = st > qf::SEG ? (st + qf::SEG - 1) / qf::SEG : 1;
+        if (ns > qf::PSLOTS) ns = 1;  // longer than any row of distinct columns: kept whole
+        dem = ns > 1 ? ns : 0;
+      }
+      incl = qf::wave_incl_scan(dem);
+      if (lane == 63) wt[wave] = incl;
+    }
+    if (tid < 3) misc[2 + tid] = 0;
+    __syncthreads();
+    if (wave < qf::RW) {
+      int pre = 0;
+#pragma unroll
+      for (int w = 0; w < qf::RW; ++w) pre += w < wave ? wt[w] : 0;
+      const bool fits = r < avail && pre + incl <= qf::PSLOTS;  // a prefix of the rows (incl grows with r)
+      // bucket of the last segment: 0 for a row kept whole past SEG steps,
+      // else 1 + SEG - steps of the remainder
+      const int lst = ns > 1 ? st - qf::SEG * (ns - 1) : st;
+      const int lastb = lst > qf::SEG ? 0 : 1 + qf::SEG - lst;
+      const int nfull = fits ? ns - 1 : 0;
+      const int fincl = qf::wave_incl_scan(nfull);
+      const int full_tot = __builtin_amdgcn_readlane(fincl, 63);
+      uint32_t mine = 0, rank = 0;
+#pragma unroll
+      for (int bi = 0; bi < qf::NBKT; ++bi) {
+        const uint64_t m = __ballot(fits && lastb == bi);
+        uint32_t c = (uint32_t)__popcll(m);
+        if (bi == B8) c += (uint32_t)full_tot;  // the full segments come first in their bucket
+        mine = lane == bi ? c : mine;
+        if (lastb == bi) rank = (uint32_t)__popcll(m & below) + (bi == B8 ? (uint32_t)full_tot : 0u);
+      }
+      if (lane < qf::NBKT) cnt[lane * qf::RW + wave] = mine;
+      const int nfit = __popcll(__ballot(fits));
+      if (lane == 0) atomicAdd(&misc[2], nfit);
+      if (fits) {
+        rowps[r] = (uint16_t)(pre + incl - dem);
+        rnseg[r] = (uint8_t)ns;
+        rowtag[r] = (uint32_t)lastb | (rank << 4) | ((uint32_t)(fincl - nfull) << 18);
+        if (ns > 1) splitrows[atomicAdd(&misc[4], 1)] = (uint16_t)r;  // order free: at most PSLOTS / 2
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {  // exclusive scan over (bucket, wave), bucket-major
+      constexpr int NC = qf::NBKT * qf::RW;
+      int run = 0;
+      for (int i0 = 0; i0 < NC; i0 += 64) {
+        const int c = i0 + lane < NC ? (int)cnt[i0 + lane] : 0;
+        const int in = qf::wave_incl_scan(c);
+        if (i0 + lane < NC) cnt[i0 + lane] = (uint32_t)(run + in - c);
+        run += __builtin_amdgcn_readlane(in, 63);
+      }
+      if (lane == 0) misc[3] = run;  // every segment of the chunk
+    }
+    __syncthreads();
+    const int cn = misc[2];
+    // whole rows and the last segment of split rows: one thread per row
+    if (r < cn) {
+      const int beg = rps[r], end = rps[r + 1], ns1 = rnseg[r];
+      const uint32_t tag = rowtag[r];
+      const int lastb = (int)(tag & 15u), rank = (int)((tag >> 4) & 0x3fffu);
+      const int pl = (int)cnt[lastb * qf::RW + (r >> 6)] + rank;
+      int sb, se;
+      seg_of(beg, end, ns1, ns1 - 1, sb, se);
+      s_rid[pl] = (uint16_t)r;
+      s_beg[pl] = sb;
+      s_end[pl] = se;
+      s_ps[pl] = (int8_t)(ns1 > 1 ? rowps[r] + ns1 - 1 : -1);
+    }
+    // the full segments of split rows: eight threads per row
+    {
+      const int k = (tid - qf::CHUNK) >> 3, sub = tid & 7;
+      if (tid >= qf::CHUNK && k < misc[4]) {
+        const int rr = splitrows[k], beg = rps[rr], end = rps[rr + 1], ns1 = rnseg[rr];
+        const int p8 = (int)cnt[B8 * qf::RW + (rr >> 6)] + (int)(rowtag[rr] >> 18);
+        for (int i = sub; i < ns1 - 1; i += 8) {
+          int sb, se;
+          seg_of(beg, end, ns1, i, sb, se);
+          s_rid[p8 + i] = (uint16_t)rr;
+          s_beg[p8 + i] = sb;
+          s_end[p8 + i] = se;
+          s_ps[p8 + i] = (int8_t)(rowps[rr] + i);
+        }
+      }
+      static_assert(qf::CHUNK + qf::PSLOTS / 2 * 8 <= qf::THREADS, "eight threads per split row");
+    }
+    // the next chunk's row_ptr slice is requested now and written to LDS
+    // after the gather (its latency hides behind the gather)
+    const int nbase = base + cn, navail = min(qf::CHUNK, r_hi - nbase);
+    int nrp = 0;
+    if (tid <= navail && nbase < r_hi) nrp = row_ptr[nbase + tid];
+    __syncthreads();
+    const int nseg = misc[3];
+    // ---- 4. gather: group g = 16 sorted segments, a quad of lanes per
+    // segment; a wave takes groups rr NW + (wave, or NW - 1 - wave on odd rr)
+    // (snake order mixes long and short groups).  Index / value loads run one
+    // step ahead, across group boundaries.
+    const int ng = nnz > 0 ? (nseg + 15) >> 4 : 0;
+    if (nnz == 0)  // F = 0: every output is zero
+      for (int i = tid; i < TT * cn; i += qf::THREADS) obuf[(i / cn) * qf::CHUNK + i % cn] = 0;
+    struct Row {
+      int r, beg, end, nst, ps;
+    };
+    auto row_of = [&](int rr) {
+      const int g = rr * qf::NW + ((rr & 1) ? qf::NW - 1 - wave : wave);
+      const int p = 16 * g + (lane >> 2);
+      Row w{0, 0, 0, 0, -1};
+      if (g < ng && p < nseg) {
+        w.r = s_rid[p];
+        w.beg = s_beg[p];
+        w.end = s_end[p];
+        w.nst = qf::steps_of(w.beg, w.end);
+        w.ps = s_ps[p];
+      }
+      return w;
+    };
+    struct Buf {
+      u32x4 cw;
+      typename V::raw vw;
+    };
+    // this lane's entries of step s: [(beg & ~3) + 16 s + 4 slot, + 4).  The
+    // whole aligned 16-byte index block (8 or 16 bytes of values) is read even
+    // where the arrays end inside it (an aligned block never straddles a
+    // page); entries outside the row are masked.  Every step issues the same
+    // two loads (a step with nothing to do reads block 0), so the compiler's
+    // wait counts hold on every path.
+    auto load_step = [&](const Row& w, int s, Buf& b) {
+      int jj = (w.beg & ~3) + 16 * s + 4 * slot;
+      jj = (s < w.nst && jj < w.end) ? jj : 0;
+      b.cw = ldg<u32x4>(reinterpret_cast<const uint8_t*>(col_idx) + 4u * (uint32_t)jj);
+      b.vw = V::load(vals, jj);
+    };
+    auto run_step = [&](const Row& w, int s, const Buf& b, float* acc) {
+      const int jc = (w.beg & ~3) + 16 * s + 4 * slot;
+      if (s >= w.nst || jc >= w.end) return;
+      u32x4 cw = b.cw;
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = V::get(b.vw, q);
+      if (jc < w.beg || jc + 4 > w.end) {  // the row's first or last quad: drop other entries
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[q] = (jc + q >= w.beg && jc + q < w.end) ? v[q] : 0.f;
+          cw[q] &= (uint32_t)(qf::NZ - 1);  // past the arrays' end the index is arbitrary
+        }
+      }
+      // all eight column reads first, then each entry's 16 FMAs as its reads land
+      u32x4 z0[4], z1[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint8_t* zp = smem + (cw[q] << 4);
+        z0[q] = *reinterpret_cast<const u32x4*>(zp);
+        z1[q] = *reinterpret_cast<const u32x4*>(zp + qf::ZP);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t a[4], b2[4];
+        __builtin_memcpy(a, &z0[q], 16);
+        __builtin_memcpy(b2, &z1[q], 16);
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+          fma_mix_lo(acc[2 * w2], v[q], a[w2]);
+          fma_mix_hi(acc[2 * w2 + 1], v[q], a[w2]);
+          fma_mix_lo(acc[8 + 2 * w2], v[q], b2[w2]);
+          fma_mix_hi(acc[8 + 2 * w2 + 1], v[q], b2[w2]);
+        }
+      }
+    };
+    Buf A{}, B{};
+    Row cur = row_of(0);
+    load_step(cur, 0, A);
+    for (int rr = 0; rr * qf::NW < ng; ++rr) {
+      const Row nxt = row_of(rr + 1);
+      float acc[TT];
+#pragma unroll
+      for (int k = 0; k < TT; ++k) acc[k] = 0.f;
+      // steps in pairs (an odd count gets an empty last step); the group after
+      // this one starts in buffer A again
+      for (int s = 0; s < cur.nst || s == 0; s += 2) {
+        load_step(cur, s + 1, B);
+        run_step(cur, s, A, acc);
+        if (s + 2 < cur.nst) load_step(cur, s + 2, A);
+        else load_step(nxt, 0, A);
+        run_step(cur, s + 1, B, acc);
+      }
+      // quad all-reduce: every lane of the quad gets the row's 16 sums
+#pragma unroll
+      for (int k = 0; k < TT; ++k) {
+        acc[k] += as_f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u(acc[k]), 0xB1, 0xF, 0xF, true));  // ^1
+        acc[k] += as_f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u(acc[k]), 0x4E, 0xF, 0xF, true));  // ^2
+      }
+      const int g = rr * qf::NW + ((rr & 1) ? qf::NW - 1 - wave : wave);
+      if (g < ng && 16 * g + (lane >> 2) < nseg) {
+        if (cur.ps < 0) {  // a whole row: scaled bf16 outputs
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float a = acc[i];
+#pragma unroll
+            for (int k = 1; k < 4; ++k) a = slot == k ? acc[4 * k + i] : a;
+            obuf[(4 * slot + i) * qf::CHUNK + cur.r] = (uint16_t)(pack_bf16(a * osc[i], 0.f) & 0xffffu);
+          }
+        } else {  // one segment of a split row: raw fp32 partial sums
+          f32x4 pv;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float a = acc[i];
+#pragma unroll
+            for (int k = 1; k < 4; ++k) a = slot == k ? acc[4 * k + i] : a;
+            pv[i] = a;
+          }
+          *reinterpret_cast<f32x4*>(part + cur.ps * TT + 4 * slot) = pv;
+        }
+      }
+      cur = nxt;
+    }
+    __syncthreads();
+    // ---- 4b. split rows: partial sums added in segment order, one (row,
+    // token) per thread (at most PSLOTS / 2 split rows)
+    {
+      const int nsplit = misc[4];
+      const int k = tid >> 4, t = tid & 15;
+      if (k < nsplit) {
+        const int r = splitrows[k], ns = rnseg[r];
+        const float* pp = part + rowps[r] * TT + t;
+        float a = pp[0];
+        int j = 1;
+        for (; j + 4 <= ns; j += 4) {  // four independent reads, added in order
+          const float p0 = pp[j * TT], p1 = pp[(j + 1) * TT], p2 = pp[(j + 2) * TT], p3 = pp[(j + 3) * TT];
+          a = (((a + p0) + p1) + p2) + p3;
+        }
+        for (; j < ns; ++j) a += pp[j * TT];
+        obuf[t * qf::CHUNK + r] = (uint16_t)(pack_bf16(a * ldexpf(wscale, texp[t]), 0.f) & 0xffffu);
+      }
+      static_assert(qf::PSLOTS / 2 * qf::TT <= qf::THREADS, "one thread per split row and token");
+    }
+    __syncthreads();
+
+    // ---- 5. the chunk's outputs, row-contiguous: thread = (token, 8 rows)
+    {
+      static_assert(qf::TT * (qf::CHUNK / 8) == qf::THREADS, "one 16-byte piece per thread");
+      const int t = tid / (qf::CHUNK / 8), q = tid % (qf::CHUNK / 8);
+      if (t < ntok && 8 * q < cn) {
+        const uint16_t* src = obuf + t * qf::CHUNK + 8 * q;
+        uint16_t* dst = y + (tok0 + t) * ldy + base + 8 * q;
+        if (vec && 8 * q + 8 <= cn) {
+          stg(dst, *reinterpret_cast<const u32x4*>(src));
+        } else {
+          for (int e = 0; e < 8 && 8 * q + e < cn; ++e) dst[e] = src[e];
+        }
+      }
+    }
+    if (tid <= navail && nbase < r_hi) rps[tid] = nrp;  // the partial slots are read no more
+    base = nbase;
+    __syncthreads();  // the next chunk reuses the lists and the output buffer
+  }
+}
+
+template <int VALDT>
+static void launch_fwd(const void* x, int64_t tokens, int64_t ldx, int in_cols, const int32_t* row_ptr,
+                       const int32_t* col_idx, const void* vals, int d_out, int nnz, void* y, int64_t ldy, int vec,
+                       float wscale, int tiles, int splits, hipStream_t s) {
+  static const bool attr = hipFuncSetAttribute((const void*)k_qwha_fwd<VALDT>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, qf::BYTES) == hipSuccess;
+  (void)attr;
+  hipLaunchKernelGGL(k_qwha_fwd<VALDT>, dim3((unsigned)tiles * (unsigned)splits), dim3(qf::THREADS), qf::BYTES, s,
+                     (const uint16_t*)x, tokens, ldx, in_cols, row_ptr, col_idx, vals, d_out, nnz, (uint16_t*)y, ldy,
+                     vec, wscale, tiles, splits);
+}
+
+int device_cu_count(int dev);
+
+// d_in a power of two in [64, 4096]
+hipError_t launch_qwha_fwd(const void* x, int64_t tokens, int64_t d_in, int64_t ldx, const int32_t* row_ptr,
+                           const int32_t* col_idx, const void* vals, int val_dt, int64_t d_out, int64_t nnz, void* y,
+                           int64_t ldy, hipStream_t s) {
+  const int vec = ((reinterpret_cast<uintptr_t>(y) & 15u) == 0 && (ldy * 2) % 16 == 0) ? 1 : 0;
+  const int64_t tiles = (tokens + qf::TT - 1) / qf::TT;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  const int64_t cus = device_cu_count(dev);
+  // row splits: enough blocks for one per CU, at most 8, none past the rows
+  int64_t splits = std::min<int64_t>(8, std::max<int64_t>(1, (cus + tiles - 1) / tiles));
+  splits = std::max<int64_t>(1, std::min<int64_t>(splits, (d_out + 7) / 8));
+  if (tiles * splits > INT32_MAX) return hipErrorInvalidValue;
+  const float wscale = (float)(64.0 / std::sqrt((double)d_in));
+  if (val_dt == DT_BF16)
+    launch_fwd<DT_BF16>(x, tokens, ldx, (int)d_in, row_ptr, col_idx, vals, (int)d_out, (int)nnz, y, ldy, vec, wscale,
+                        (int)tiles, (int)splits, s);
+  else
+    launch_fwd<DT_F32>(x, tokens, ldx, (int)d_in, row_ptr, col_idx, vals, (int)d_out, (int)nnz, y, ldy, vec, wscale,
+                       (int)tiles, (int)splits, s);
+  return hipGetLastError();
+}
+
+}  // namespace whtq
