@@ -21,7 +21,9 @@
 //      d_in entries of the 4096-point transform of [x; 0] are H_d x (the
 //      factor 64 / sqrt(d_in) is applied to the outputs).
 //   2. Y goes to Z in LDS as two planes of 16-byte columns (tokens 0-7 and
-//      8-15): one column read gives a row entry's value for 8 tokens.
+//      8-15): one column read gives a row entry's value for 8 tokens (two
+//      planes rather than 32-byte columns: random 16-byte reads then spread
+//      over all 16 bank slots of a 256-byte LDS row, not 8).
 //   3. The block's rows are taken in chunks of 512 and bucketed by the
 //      number of 16-entry steps they need (longest first), so the 16 rows a
 //      wave runs together finish at about the same time.
@@ -157,22 +159,6 @@ __global__ __launch_bounds__(qf::THREADS) void k_qwha_fwd(const uint16_t* __rest
   int* texp = reinterpret_cast<int*>(smem + qf::EXP);
   int* misc = reinterpret_cast<int*>(smem + qf::MISC);
 
-  // ---- the token rows' loads go out first (one wave per token; each 16-byte
-  // load is the A operand of pass 1: lane (q, r) holds M[16 ab + r][32 kb + 8 q + 0..7])
-  const int r16 = lane & 15, q4 = lane >> 4;
-  u32x4 xa[4][2];
-  {
-    const int64_t tok = tok0 + wave;
-    const uint16_t* xr = x + (tok < tokens ? tok : 0) * ldx;
-#pragma unroll
-    for (int ab = 0; ab < 4; ++ab)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int c = 64 * (16 * ab + r16) + 32 * kb + 8 * q4;
-        xa[ab][kb] = (tok < tokens && c < in_cols) ? ldg<u32x4>(xr + c) : u32x4{0u, 0u, 0u, 0u};
-      }
-  }
-
   // ---- the block's rows: [lower_bound(row_ptr, nnz s / S)] rounded down to
   // a multiple of 8 (aligned output stores), for s = split and split + 1
   if (tid < 2) misc[tid] = (split + tid >= splits) ? d_out : d_out + 1;
@@ -201,11 +187,150 @@ __global__ __launch_bounds__(qf::THREADS) void k_qwha_fwd(const uint16_t* __rest
   __syncthreads();
   const int r_lo = split == 0 ? 0 : min(misc[0], d_out);
   const int r_hi = max(r_lo, min(misc[1], d_out));
-  // the first chunk's slice of row_ptr (the partial slots are free until the
-  // gather); its loads complete behind the transform
+  // the first chunk's slice of row_ptr is requested before the token rows,
+  // so that the first chunk is prepared while the rows arrive (the partial
+  // slots hold the slice until the gather)
   int* rps = reinterpret_cast<int*>(smem + qf::PART);
   static_assert((qf::CHUNK + 1) * 4 <= qf::PSLOTS * qf::TT * 4, "row_ptr slice in the partial slots");
-  for (int i = tid; i <= min(qf::CHUNK, r_hi - r_lo) && r_lo < r_hi; i += qf::THREADS) rps[i] = row_ptr[r_lo + i];
+  static_assert(qf::CHUNK + 1 <= qf::THREADS, "one row_ptr entry per thread");
+  const bool stage0 = r_lo < r_hi && tid <= min(qf::CHUNK, r_hi - r_lo);
+  const int rp0 = stage0 ? row_ptr[r_lo + tid] : 0;
+
+  // ---- the token rows (one wave per token; each 16-byte load is the A
+  // operand of pass 1: lane (q, r) holds M[16 ab + r][32 kb + 8 q + 0..7])
+  const int r16 = lane & 15, q4 = lane >> 4;
+  u32x4 xa[4][2];
+  {
+    const int64_t tok = tok0 + wave;
+    const uint16_t* xr = x + (tok < tokens ? tok : 0) * ldx;
+#pragma unroll
+    for (int ab = 0; ab < 4; ++ab)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int c = 64 * (16 * ab + r16) + 32 * kb + 8 * q4;
+        xa[ab][kb] = (tok < tokens && c < in_cols) ? ldg<u32x4>(xr + c) : u32x4{0u, 0u, 0u, 0u};
+      }
+  }
+
+  if (stage0) rps[tid] = rp0;
+  __syncthreads();
+
+  auto seg_of = [&](int beg, int end, int ns, int i, int& sb, int& se) {
+    const int b4 = beg & ~3;
+    sb = i == 0 ? beg : b4 + 16 * qf::SEG * i;
+    se = ns == 1 ? end : min(end, b4 + 16 * qf::SEG * (i + 1));
+  };
+  const uint64_t below = (1ull << lane) - 1ull;
+  int cn = 0, nseg = 0, nbase = r_lo, navail = 0, nrp = 0;
+  auto prep = [&](int base) {
+    const int avail = min(qf::CHUNK, r_hi - base);
+    // ---- 3. the chunk: its first rows whose split rows fit the partial
+    // slots.  A row of nst steps is cut into ceil(nst / SEG) segments (the
+    // row's steps 0..SEG-1, SEG..2 SEG-1, ...); a row of one segment writes
+    // its outputs directly, the segments of a longer row write fp32 partial
+    // sums that are added in segment order afterwards (deterministic).  The
+    // segments are ordered by step count, longest first, by a counting sort
+    // over (bucket, wave) with ballots.  One lane per row (waves 0..RW-1).
+    uint32_t* rowtag = reinterpret_cast<uint32_t*>(obuf);  // per row until the gather: bucket | rank | full start
+    constexpr int B8 = 1;                                 // the bucket of SEG-step segments
+    const int r = tid;
+    int st = 0, ns = 0, dem = 0, incl = 0;
+    if (wave < qf::RW) {
+      if (r < avail) {
+        st = qf::steps_of(rps[r], rps[r + 1]);
+        ns = st > qf::SEG ? (st + qf::SEG - 1) / qf::SEG : 1;
+        if (ns > qf::PSLOTS) ns = 1;  // longer than any row of distinct columns: kept whole
+        dem = ns > 1 ? ns : 0;
+      }
+      incl = qf::wave_incl_scan(dem);
+      if (lane == 63) wt[wave] = incl;
+    }
+    if (tid < 3) misc[2 + tid] = 0;
+    __syncthreads();
+    if (wave < qf::RW) {
+      int pre = 0;
+#pragma unroll
+      for (int w = 0; w < qf::RW; ++w) pre += w < wave ? wt[w] : 0;
+      const bool fits = r < avail && pre + incl <= qf::PSLOTS;  // a prefix of the rows (incl grows with r)
+      // bucket of the last segment: 0 for a row kept whole past SEG steps,
+      // else 1 + SEG - steps of the remainder
+      const int lst = ns > 1 ? st - qf::SEG * (ns - 1) : st;
+      const int lastb = lst > qf::SEG ? 0 : 1 + qf::SEG - lst;
+      const int nfull = fits ? ns - 1 : 0;
+      const int fincl = qf::wave_incl_scan(nfull);
+      const int full_tot = __builtin_amdgcn_readlane(fincl, 63);
+      uint32_t mine = 0, rank = 0;
+#pragma unroll
+      for (int bi = 0; bi < qf::NBKT; ++bi) {
+        const uint64_t m = __ballot(fits && lastb == bi);
+        uint32_t c = (uint32_t)__popcll(m);
+        if (bi == B8) c += (uint32_t)full_tot;  // the full segments come first in their bucket
+        mine = lane == bi ? c : mine;
+        if (lastb == bi) rank = (uint32_t)__popcll(m & below) + (bi == B8 ? (uint32_t)full_tot : 0u);
+      }
+      if (lane < qf::NBKT) cnt[lane * qf::RW + wave] = mine;
+      const int nfit = __popcll(__ballot(fits));
+      if (lane == 0) atomicAdd(&misc[2], nfit);
+      if (fits) {
+        rowps[r] = (uint16_t)(pre + incl - dem);
+        rnseg[r] = (uint8_t)ns;
+        rowtag[r] = (uint32_t)lastb | (rank << 4) | ((uint32_t)(fincl - nfull) << 18);
+        if (ns > 1) splitrows[atomicAdd(&misc[4], 1)] = (uint16_t)r;  // order free: at most PSLOTS / 2
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {  // exclusive scan over (bucket, wave), bucket-major
+      constexpr int NC = qf::NBKT * qf::RW;
+      int run = 0;
+      for (int i0 = 0; i0 < NC; i0 += 64) {
+        const int c = i0 + lane < NC ? (int)cnt[i0 + lane] : 0;
+        const int in = qf::wave_incl_scan(c);
+        if (i0 + lane < NC) cnt[i0 + lane] = (uint32_t)(run + in - c);
+        run += __builtin_amdgcn_readlane(in, 63);
+      }
+      if (lane == 0) misc[3] = run;  // every segment of the chunk
+    }
+    __syncthreads();
+    cn = misc[2];
+    // whole rows and the last segment of split rows: one thread per row
+    if (r < cn) {
+      const int beg = rps[r], end = rps[r + 1], ns1 = rnseg[r];
+      const uint32_t tag = rowtag[r];
+      const int lastb = (int)(tag & 15u), rank = (int)((tag >> 4) & 0x3fffu);
+      const int pl = (int)cnt[lastb * qf::RW + (r >> 6)] + rank;
+      int sb, se;
+      seg_of(beg, end, ns1, ns1 - 1, sb, se);
+      s_rid[pl] = (uint16_t)r;
+      s_beg[pl] = sb;
+      s_end[pl] = se;
+      s_ps[pl] = (int8_t)(ns1 > 1 ? rowps[r] + ns1 - 1 : -1);
+    }
+    // the full segments of split rows: eight threads per row
+    {
+      const int k = (tid - qf::CHUNK) >> 3, sub = tid & 7;
+      if (tid >= qf::CHUNK && k < misc[4]) {
+        const int rr = splitrows[k], beg = rps[rr], end = rps[rr + 1], ns1 = rnseg[rr];
+        const int p8 = (int)cnt[B8 * qf::RW + (rr >> 6)] + (int)(rowtag[rr] >> 18);
+        for (int i = sub; i < ns1 - 1; i += 8) {
+          int sb, se;
+          seg_of(beg, end, ns1, i, sb, se);
+          s_rid[p8 + i] = (uint16_t)rr;
+          s_beg[p8 + i] = sb;
+          s_end[p8 + i] = se;
+          s_ps[p8 + i] = (int8_t)(rowps[rr] + i);
+        }
+      }
+      static_assert(qf::CHUNK + qf::PSLOTS / 2 * 8 <= qf::THREADS, "eight threads per split row");
+    }
+    // the next chunk's row_ptr slice is requested now and written to LDS
+    // after the gather (its latency hides behind the gather)
+    nbase = base + cn;
+    navail = min(qf::CHUNK, r_hi - nbase);
+    nrp = (tid <= navail && nbase < r_hi) ? row_ptr[nbase + tid] : 0;
+    __syncthreads();
+    nseg = misc[3];
+  };
+  if (r_lo < r_hi) prep(r_lo);
 
   // ---- 1-2. the token's transform on the matrix cores, into the Z planes
   {
@@ -301,120 +426,8 @@ __global__ __launch_bounds__(qf::THREADS) void k_qwha_fwd(const uint16_t* __rest
 #pragma unroll
   for (int i = 0; i < 4; ++i) osc[i] = ldexpf(wscale, texp[4 * slot + i]);
 
-  auto seg_of = [&](int beg, int end, int ns, int i, int& sb, int& se) {
-    const int b4 = beg & ~3;
-    sb = i == 0 ? beg : b4 + 16 * qf::SEG * i;
-    se = ns == 1 ? end : min(end, b4 + 16 * qf::SEG * (i + 1));
-  };
-  const uint64_t below = (1ull << lane) - 1ull;
 
   for (int base = r_lo; base < r_hi;) {
-    const int avail = min(qf::CHUNK, r_hi - base);
-    // ---- 3. the chunk: its first rows whose split rows fit the partial
-    // slots.  A row of nst steps is cut into ceil(nst / SEG) segments (the
-    // row's steps 0..SEG-1, SEG..2 SEG-1, ...); a row of one segment writes
-    // its outputs directly, the segments of a longer row write fp32 partial
-    // sums that are added in segment order afterwards (deterministic).  The
-    // segments are ordered by step count, longest first, by a counting sort
-    // over (bucket, wave) with ballots.  One lane per row (waves 0..RW-1).
-    uint32_t* rowtag = reinterpret_cast<uint32_t*>(obuf);  // per row until the gather: bucket | rank | full start
-    constexpr int B8 = 1;                                 // the bucket of SEG-step segments
-    const int r = tid;
-    int st = 0, ns = 0, dem = 0, incl = 0;
-    if (wave < qf::RW) {
-      if (r < avail) {
-        st = qf::steps_of(rps[r], rps[r + 1]);
-        ns = st > qf::SEG ? (st + qf::SEG - 1) / qf::SEG : 1;
-        if (ns > qf::PSLOTS) ns = 1;  // longer than any row of distinct columns: kept whole
-        dem = ns > 1 ? ns : 0;
-      }
-      incl = qf::wave_incl_scan(dem);
-      if (lane == 63) wt[wave] = incl;
-    }
-    if (tid < 3) misc[2 + tid] = 0;
-    __syncthreads();
-    if (wave < qf::RW) {
-      int pre = 0;
-#pragma unroll
-      for (int w = 0; w < qf::RW; ++w) pre += w < wave ? wt[w] : 0;
-      const bool fits = r < avail && pre + incl <= qf::PSLOTS;  // a prefix of the rows (incl grows with r)
-      // bucket of the last segment: 0 for a row kept whole past SEG steps,
-      // else 1 + SEG - steps of the remainder
-      const int lst = ns > 1 ? st - qf::SEG * (ns - 1) : st;
-      const int lastb = lst > qf::SEG ? 0 : 1 + qf::SEG - lst;
-      const int nfull = fits ? ns - 1 : 0;
-      const int fincl = qf::wave_incl_scan(nfull);
-      const int full_tot = __builtin_amdgcn_readlane(fincl, 63);
-      uint32_t mine = 0, rank = 0;
-#pragma unroll
-      for (int bi = 0; bi < qf::NBKT; ++bi) {
-        const uint64_t m = __ballot(fits && lastb == bi);
-        uint32_t c = (uint32_t)__popcll(m);
-        if (bi == B8) c += (uint32_t)full_tot;  // the full segments come first in their bucket
-        mine = lane == bi ? c : mine;
-        if (lastb == bi) rank = (uint32_t)__popcll(m & below) + (bi == B8 ? (uint32_t)full_tot : 0u);
-      }
-      if (lane < qf::NBKT) cnt[lane * qf::RW + wave] = mine;
-      const int nfit = __popcll(__ballot(fits));
-      if (lane == 0) atomicAdd(&misc[2], nfit);
-      if (fits) {
-        rowps[r] = (uint16_t)(pre + incl - dem);
-        rnseg[r] = (uint8_t)ns;
-        rowtag[r] = (uint32_t)lastb | (rank << 4) | ((uint32_t)(fincl - nfull) << 18);
-        if (ns > 1) splitrows[atomicAdd(&misc[4], 1)] = (uint16_t)r;  // order free: at most PSLOTS / 2
-      }
-    }
-    __syncthreads();
-    if (wave == 0) {  // exclusive scan over (bucket, wave), bucket-major
-      constexpr int NC = qf::NBKT * qf::RW;
-      int run = 0;
-      for (int i0 = 0; i0 < NC; i0 += 64) {
-        const int c = i0 + lane < NC ? (int)cnt[i0 + lane] : 0;
-        const int in = qf::wave_incl_scan(c);
-        if (i0 + lane < NC) cnt[i0 + lane] = (uint32_t)(run + in - c);
-        run += __builtin_amdgcn_readlane(in, 63);
-      }
-      if (lane == 0) misc[3] = run;  // every segment of the chunk
-    }
-    __syncthreads();
-    const int cn = misc[2];
-    // whole rows and the last segment of split rows: one thread per row
-    if (r < cn) {
-      const int beg = rps[r], end = rps[r + 1], ns1 = rnseg[r];
-      const uint32_t tag = rowtag[r];
-      const int lastb = (int)(tag & 15u), rank = (int)((tag >> 4) & 0x3fffu);
-      const int pl = (int)cnt[lastb * qf::RW + (r >> 6)] + rank;
-      int sb, se;
-      seg_of(beg, end, ns1, ns1 - 1, sb, se);
-      s_rid[pl] = (uint16_t)r;
-      s_beg[pl] = sb;
-      s_end[pl] = se;
-      s_ps[pl] = (int8_t)(ns1 > 1 ? rowps[r] + ns1 - 1 : -1);
-    }
-    // the full segments of split rows: eight threads per row
-    {
-      const int k = (tid - qf::CHUNK) >> 3, sub = tid & 7;
-      if (tid >= qf::CHUNK && k < misc[4]) {
-        const int rr = splitrows[k], beg = rps[rr], end = rps[rr + 1], ns1 = rnseg[rr];
-        const int p8 = (int)cnt[B8 * qf::RW + (rr >> 6)] + (int)(rowtag[rr] >> 18);
-        for (int i = sub; i < ns1 - 1; i += 8) {
-          int sb, se;
-          seg_of(beg, end, ns1, i, sb, se);
-          s_rid[p8 + i] = (uint16_t)rr;
-          s_beg[p8 + i] = sb;
-          s_end[p8 + i] = se;
-          s_ps[p8 + i] = (int8_t)(rowps[rr] + i);
-        }
-      }
-      static_assert(qf::CHUNK + qf::PSLOTS / 2 * 8 <= qf::THREADS, "eight threads per split row");
-    }
-    // the next chunk's row_ptr slice is requested now and written to LDS
-    // after the gather (its latency hides behind the gather)
-    const int nbase = base + cn, navail = min(qf::CHUNK, r_hi - nbase);
-    int nrp = 0;
-    if (tid <= navail && nbase < r_hi) nrp = row_ptr[nbase + tid];
-    __syncthreads();
-    const int nseg = misc[3];
     // ---- 4. gather: group g = 16 sorted segments, a quad of lanes per
     // segment; a wave takes groups rr NW + (wave, or NW - 1 - wave on odd rr)
     // (snake order mixes long and short groups).  Index / value loads run one
@@ -450,13 +463,13 @@ __global__ __launch_bounds__(qf::THREADS) void k_qwha_fwd(const uint16_t* __rest
     // wait counts hold on every path.
     auto load_step = [&](const Row& w, int s, Buf& b) {
       int jj = (w.beg & ~3) + 16 * s + 4 * slot;
-      jj = (s < w.nst && jj < w.end) ? jj : 0;
+      jj = jj < w.end ? jj : 0;  // (jj < end implies s < nst)
       b.cw = ldg<u32x4>(reinterpret_cast<const uint8_t*>(col_idx) + 4u * (uint32_t)jj);
       b.vw = V::load(vals, jj);
     };
     auto run_step = [&](const Row& w, int s, const Buf& b, float* acc) {
       const int jc = (w.beg & ~3) + 16 * s + 4 * slot;
-      if (s >= w.nst || jc >= w.end) return;
+      if (jc >= w.end) return;
       u32x4 cw = b.cw;
       float v[4];
 #pragma unroll
@@ -472,6 +485,7 @@ __global__ __launch_bounds__(qf::THREADS) void k_qwha_fwd(const uint16_t* __rest
       u32x4 z0[4], z1[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
+        // two planes: 16 distinct 16-byte bank slots for random columns
         const uint8_t* zp = smem + (cw[q] << 4);
         z0[q] = *reinterpret_cast<const u32x4*>(zp);
         z1[q] = *reinterpret_cast<const u32x4*>(zp + qf::ZP);
@@ -576,6 +590,7 @@ __global__ __launch_bounds__(qf::THREADS) void k_qwha_fwd(const uint16_t* __rest
     if (tid <= navail && nbase < r_hi) rps[tid] = nrp;  // the partial slots are read no more
     base = nbase;
     __syncthreads();  // the next chunk reuses the lists and the output buffer
+    if (base < r_hi) prep(base);
   }
 }
 
