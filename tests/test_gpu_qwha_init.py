@@ -298,3 +298,45 @@ def test_initialize_on_a_side_stream():
     for a, b in zip(ref, got):
         assert torch.equal(a.cpu(), b.cpu())
 
+
+
+def test_select_and_refine_in_a_graph():
+    """Both calls captured in a HIP graph with caller-given outputs (the
+    bindings read nothing back from the device under capture), replayed
+    three times with eager work in between: every replay equals the eager
+    result bit for bit."""
+    rng = np.random.default_rng(77)
+    n, rows, tokens = 256, 24, 300
+    f = rng.standard_normal((rows, n)).astype(np.float32)
+    budgets = rng.integers(1, 33, rows)
+    row_ptr, _ = QI.select(f.astype(np.float64), budgets)
+    x = rng.standard_normal((tokens, n))
+    g64 = QI.calibration_gram(x)
+    g32, p32 = g64.astype(np.float32), (f.astype(np.float64) @ g64).astype(np.float32)
+    fd, rp, gd, pd = dev(f), i32(row_ptr), dev(g32), dev(p32)
+    col_e = W().qwha_init_select(fd, rp)
+    val_e = W().qwha_init_refine(gd, pd, rp, col_e)
+    col = torch.empty_like(col_e)
+    val = torch.empty_like(val_e)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # one call outside the capture on this stream
+        W().qwha_init_select(fd, rp, col_idx=col)
+        W().qwha_init_refine(gd, pd, rp, col, vals=val)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        graph.capture_begin()
+        W().qwha_init_select(fd, rp, col_idx=col)
+        W().qwha_init_refine(gd, pd, rp, col, vals=val)
+        graph.capture_end()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        col.fill_(-1)
+        val.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(col, col_e), rep
+        assert torch.equal(val, val_e), rep
+        W().qwha_init_select(fd, rp)  # eager work between replays

@@ -51,6 +51,36 @@ __device__ __forceinline__ float blk_at(const void* blocks, long long i) {
   else return (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(blocks)[i]);
 }
 
+// N consecutive block coefficients from element e0, widened to fp32: 16-byte
+// loads where the run is a whole number of aligned 16-byte pieces (blocks of
+// radix 2 to 16 in fp32, 4 to 16 in fp16, whose runs start on such
+// boundaries), element loads otherwise
+template <int BDT, int N>
+__device__ __forceinline__ void blk_run(const void* blocks, long long e0, float* co) {
+  constexpr int ESZ = BDT == DT_F32 ? 4 : 2;
+  const uint8_t* p = reinterpret_cast<const uint8_t*>(blocks) + e0 * ESZ;
+  if constexpr ((N * ESZ) % 16 == 0) {
+    if ((reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
+#pragma unroll
+      for (int v = 0; v < N * ESZ / 16; ++v) {
+        const u32x4 w = ldg<u32x4>(p + 16 * v);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if constexpr (ESZ == 4) {
+            co[4 * v + q] = as_f(w[q]);
+          } else {
+            co[8 * v + 2 * q] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[q] & 0xffffu));
+            co[8 * v + 2 * q + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[q] >> 16));
+          }
+        }
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < N; ++k) co[k] = blk_at<BDT>(blocks, e0 + k);
+}
+
 // in-register Sylvester FWHT of B values (B a power of two), scaled by 1/sqrt(B)
 template <int B>
 __device__ __forceinline__ void had_regs(float (&x)[B]) {
@@ -81,10 +111,15 @@ __device__ __forceinline__ void hg_stage(float* tile, int ldt, int nt, int d, in
     const int base = (c % s) + (c / s) * s * B;
     float co[RPL][B];
     const long long bo = off + (long long)c * B * B;
+    if constexpr (RPL * LPB == B) {
+      // the lane's rows r0 .. r0 + RPL - 1 are one contiguous run of the block
+      blk_run<BDT, RPL * B>(blocks, bo + (long long)r0 * B, &co[0][0]);
+    } else {
 #pragma unroll
-    for (int r = 0; r < RPL; ++r)
+      for (int r = 0; r < RPL; ++r)
 #pragma unroll
-      for (int k = 0; k < B; ++k) co[r][k] = r0 + r < B ? blk_at<BDT>(blocks, bo + (r0 + r) * B + k) : 0.f;
+        for (int k = 0; k < B; ++k) co[r][k] = r0 + r < B ? blk_at<BDT>(blocks, bo + (r0 + r) * B + k) : 0.f;
+    }
     // the item's LDS addresses, computed once for all its tokens (rows past
     // the block's end, in the last lane of a split block, write nowhere)
     int ia[B], oa[RPL];
@@ -144,41 +179,64 @@ __global__ __launch_bounds__(hg::THREADS) void k_harp_gen(const void* __restrict
   const int nch = (d + 7) >> 3;  // 8-value chunks per row
 
   // ---- load (signs flipped on the way when preconditioning); rows are bf16
-  // or fp32 (XDT), the tile fp32 either way
-  for (int f = threadIdx.x; f < nt * nch; f += hg::THREADS) {
-    const int j = f / nch, i0 = 8 * (f - j * nch);
-    uint32_t sb = sbits ? (sbits[i0 >> 5] >> (i0 & 31)) & 0xffu : 0u;
-    float v[8];
-    if constexpr (XDT == DT_F32) {
-      const float* xr = reinterpret_cast<const float*>(xv_) + (tok0 + j) * ldx;
-      if (vec && i0 + 8 <= d) {
-        const f32x4 a = ldg<f32x4>(xr + i0), b = ldg<f32x4>(xr + i0 + 4);
+  // or fp32 (XDT), the tile fp32 either way.  Every 8-value chunk of the
+  // tile goes to one thread; a thread's chunks are all requested before any
+  // is written,
+  // so the tile costs one memory latency rather than one per chunk (the
+  // tile's tt d values fit in LDS_FLOATS, so a thread has at most LDCH chunks).
+  constexpr int LDCH = (hg::LDS_FLOATS / 8 + hg::THREADS - 1) / hg::THREADS;
+  {
+    constexpr int W = XDT == DT_F32 ? 8 : 4;  // 32-bit words per chunk
+    uint32_t raw[LDCH][W];
+    const int nf = nt * nch;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          v[q] = a[q];
-          v[4 + q] = b[q];
+    for (int u = 0; u < LDCH; ++u) {
+      const int f = threadIdx.x + u * hg::THREADS;
+      if (f < nf) {
+        const int j = f / nch, i0 = 8 * (f - j * nch);
+        if (vec && i0 + 8 <= d) {
+          if constexpr (XDT == DT_F32) {
+            const float* xr = reinterpret_cast<const float*>(xv_) + (tok0 + j) * ldx;
+            const u32x4 a = ldg<u32x4>(xr + i0), b = ldg<u32x4>(xr + i0 + 4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              raw[u][q] = a[q];
+              raw[u][4 + q] = b[q];
+            }
+          } else {
+            const uint16_t* xr = reinterpret_cast<const uint16_t*>(xv_) + (tok0 + j) * ldx;
+            const u32x4 w = ldg<u32x4>(xr + i0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) raw[u][q] = w[q];
+          }
         }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = i0 + e < d ? xr[i0 + e] : 0.f;
-      }
-    } else {
-      const uint16_t* xr = reinterpret_cast<const uint16_t*>(xv_) + (tok0 + j) * ldx;
-      if (vec && i0 + 8 <= d) {
-        const u32x4 w = ldg<u32x4>(xr + i0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          v[2 * q] = bf16lo(w[q]);
-          v[2 * q + 1] = bf16hi(w[q]);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = i0 + e < d ? as_f((uint32_t)xr[i0 + e] << 16) : 0.f;
       }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (i0 + e < d) tile[j * ldt + hg::pos(i0 + e)] = as_f(as_u(v[e]) ^ (((sb >> e) & 1u) << 31));
+    for (int u = 0; u < LDCH; ++u) {
+      const int f = threadIdx.x + u * hg::THREADS;
+      if (f < nf) {
+        const int j = f / nch, i0 = 8 * (f - j * nch);
+        const uint32_t sb = sbits ? (sbits[i0 >> 5] >> (i0 & 31)) & 0xffu : 0u;
+        float v[8];
+        if (vec && i0 + 8 <= d) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            v[e] = XDT == DT_F32 ? as_f(raw[u][e]) : ((e & 1) ? bf16hi(raw[u][e >> 1]) : bf16lo(raw[u][e >> 1]));
+        } else if constexpr (XDT == DT_F32) {
+          const float* xr = reinterpret_cast<const float*>(xv_) + (tok0 + j) * ldx;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = i0 + e < d ? xr[i0 + e] : 0.f;
+        } else {
+          const uint16_t* xr = reinterpret_cast<const uint16_t*>(xv_) + (tok0 + j) * ldx;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = i0 + e < d ? as_f((uint32_t)xr[i0 + e] << 16) : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (i0 + e < d) tile[j * ldt + hg::pos(i0 + e)] = as_f(as_u(v[e]) ^ (((sb >> e) & 1u) << 31));
+      }
+    }
   }
   __syncthreads();
 

@@ -496,13 +496,15 @@ def qwha_init_select(f, row_ptr, col_idx=None):
     _need_cuda("row_ptr", row_ptr)
     if row_ptr.dtype != torch.int32 or row_ptr.shape != (rows + 1,) or not row_ptr.is_contiguous():
         raise ValueError("row_ptr must be contiguous int32 [rows + 1]")
-    total = int(row_ptr[-1].item())
+    # the size check reads row_ptr[-1] on the host, which a stream under
+    # graph capture does not allow: there the caller's col_idx is trusted
+    capturing = torch.cuda.is_current_stream_capturing()
     if col_idx is None:
-        col_idx = torch.empty(total, dtype=torch.int32, device=f.device)
+        col_idx = torch.empty(int(row_ptr[-1].item()), dtype=torch.int32, device=f.device)
     _need_cuda("col_idx", col_idx)
     if col_idx.dtype != torch.int32 or not col_idx.is_contiguous():
         raise ValueError("col_idx must be contiguous int32")
-    if col_idx.numel() < total:
+    if not capturing and col_idx.numel() < int(row_ptr[-1].item()):
         raise ValueError("col_idx must hold row_ptr[-1] entries")
     with torch.cuda.device(f.device):
         _check("qwha_init_select", _lib.qwha_init_select(
@@ -529,8 +531,8 @@ def qwha_init_refine(g, p, row_ptr, col_idx, vals=None):
     _need_cuda("vals", vals)
     if vals.dtype != torch.float32 or vals.numel() != col_idx.numel() or not vals.is_contiguous():
         raise ValueError("vals must be contiguous float32 with one entry per column index")
-    if col_idx.numel() < int(row_ptr[-1].item()):
-        raise ValueError("col_idx and vals must hold row_ptr[-1] entries")
+    if not torch.cuda.is_current_stream_capturing() and col_idx.numel() < int(row_ptr[-1].item()):
+        raise ValueError("col_idx and vals must hold row_ptr[-1] entries")  # (not checked under graph capture)
     with torch.cuda.device(g.device):
         _check("qwha_init_refine", _lib.qwha_init_refine(
             _ptr(g), n, _ptr(p), rows, _ptr(row_ptr), _ptr(col_idx), _ptr(vals), _stream(g)))
