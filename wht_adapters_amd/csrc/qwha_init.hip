@@ -31,30 +31,81 @@ constexpr int KS = 16;        // GEMM k-step staged in LDS
 constexpr int LDT = BT + 16;  // LDS row stride of a k-major tile (conflict-free MFMA operand reads)
 }  // namespace qi
 
-// f[r][i] = w[r][i] - f[r][i] (w bf16, f16 or f32; f fp32)
+// one weight element (bf16, fp16 or fp32) as fp32
 template <int WDT>
-__global__ void k_qi_sub(const void* __restrict__ w, int64_t ldw, float* __restrict__ f, int64_t ldf, int64_t rows,
-                         int64_t n) {
-  const int64_t total = rows * n;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = e / n, i = e - r * n;
-    float wv;
-    if constexpr (WDT == DT_F32) {
-      wv = reinterpret_cast<const float*>(w)[r * ldw + i];
-    } else {
-      const uint16_t b = reinterpret_cast<const uint16_t*>(w)[r * ldw + i];
-      wv = WDT == DT_BF16 ? as_f((uint32_t)b << 16) : (float)__builtin_bit_cast(_Float16, b);
+__device__ __forceinline__ float qi_w_at(const void* w, int64_t i) {
+  if constexpr (WDT == DT_F32) {
+    return reinterpret_cast<const float*>(w)[i];
+  } else {
+    const uint16_t b = reinterpret_cast<const uint16_t*>(w)[i];
+    return WDT == DT_BF16 ? as_f((uint32_t)b << 16) : (float)__builtin_bit_cast(_Float16, b);
+  }
+}
+
+// F = W - Q(W), in place over Q(W): a block per row (grid-stride over the
+// rows), eight consecutive values per thread and step with 16-byte accesses
+// (W with element loads where its rows are not 16-byte aligned).
+template <int WDT>
+__global__ __launch_bounds__(256) void k_qi_sub(const void* __restrict__ w, int64_t ldw, float* __restrict__ f,
+                                                int64_t ldf, int64_t rows, int n, int vec) {
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    float* fr = f + r * ldf;
+    const int64_t wr = r * ldw;
+    for (int c = 8 * (int)threadIdx.x; c < n; c += 8 * 256) {
+      if (c + 8 > n) {  // (n below 8)
+        for (int e = c; e < n; ++e) fr[e] = qi_w_at<WDT>(w, wr + e) - fr[e];
+        continue;
+      }
+      float wv[8];
+      if (vec) {
+        if constexpr (WDT == DT_F32) {
+          const f32x4 a = ldg<f32x4>(reinterpret_cast<const float*>(w) + wr + c);
+          const f32x4 b = ldg<f32x4>(reinterpret_cast<const float*>(w) + wr + c + 4);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            wv[q] = a[q];
+            wv[4 + q] = b[q];
+          }
+        } else {
+          const u32x4 v = ldg<u32x4>(reinterpret_cast<const uint16_t*>(w) + wr + c);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if constexpr (WDT == DT_BF16) {
+              wv[2 * q] = bf16lo(v[q]);
+              wv[2 * q + 1] = bf16hi(v[q]);
+            } else {
+              wv[2 * q] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[q] & 0xffffu));
+              wv[2 * q + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[q] >> 16));
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wv[e] = qi_w_at<WDT>(w, wr + c + e);
+      }
+      f32x4 a = *reinterpret_cast<const f32x4*>(fr + c), b = *reinterpret_cast<const f32x4*>(fr + c + 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a[q] = wv[q] - a[q];
+        b[q] = wv[4 + q] - b[q];
+      }
+      *reinterpret_cast<f32x4*>(fr + c) = a;
+      *reinterpret_cast<f32x4*>(fr + c + 4) = b;
     }
-    f[r * ldf + i] = wv - f[r * ldf + i];
   }
 }
 
 hipError_t launch_qi_sub(const void* w, int wdt, int64_t ldw, float* f, int64_t ldf, int64_t rows, int64_t n,
                          hipStream_t s) {
-  const unsigned grid = persistent_grid((rows * n + 255) / 256, 8);
-  if (wdt == DT_F32) hipLaunchKernelGGL(k_qi_sub<DT_F32>, dim3(grid), dim3(256), 0, s, w, ldw, f, ldf, rows, n);
-  else if (wdt == DT_F16) hipLaunchKernelGGL(k_qi_sub<DT_F16>, dim3(grid), dim3(256), 0, s, w, ldw, f, ldf, rows, n);
-  else hipLaunchKernelGGL(k_qi_sub<DT_BF16>, dim3(grid), dim3(256), 0, s, w, ldw, f, ldf, rows, n);
+  const unsigned grid = persistent_grid(rows, 8);
+  const int esz = wdt == DT_F32 ? 4 : 2;
+  const int vec = ((reinterpret_cast<uintptr_t>(w) & 15u) == 0 && (ldw * esz) % 16 == 0) ? 1 : 0;
+  if (wdt == DT_F32)
+    hipLaunchKernelGGL(k_qi_sub<DT_F32>, dim3(grid), dim3(256), 0, s, w, ldw, f, ldf, rows, (int)n, vec);
+  else if (wdt == DT_F16)
+    hipLaunchKernelGGL(k_qi_sub<DT_F16>, dim3(grid), dim3(256), 0, s, w, ldw, f, ldf, rows, (int)n, vec);
+  else
+    hipLaunchKernelGGL(k_qi_sub<DT_BF16>, dim3(grid), dim3(256), 0, s, w, ldw, f, ldf, rows, (int)n, vec);
   return hipGetLastError();
 }
 
