@@ -114,3 +114,33 @@ def test_full_config_8192x4096(bdt):
     write_report("parity_harp_8192x4096_" + str(bdt).split(".")[-1] + "_blocks",
                  {"tokens": 8192, "max_scaled_err": err, "max_row_rel_err": roww, "tol": TOL})
     assert err <= TOL
+
+
+def off_lead_rows(rng, n):
+    """Rows whose mass avoids elements 8m and 8m + 1 (the first 32-bit word
+    of every 16-byte chunk the kernel loads), at very different magnitudes:
+    the per-row power-of-two scale must come from every element."""
+    x = np.zeros((7, n))
+    x[0, 2] = 3.0e4
+    x[1, 5::8] = 1.0e3
+    keep = (np.arange(n) % 8) >= 2
+    x[2, keep] = rng.standard_normal(keep.sum()) * 1e20
+    x[3, keep] = rng.standard_normal(keep.sum()) * 1e-20
+    x[4, 7::8] = rng.standard_normal(n // 8) * 100.0
+    x[5, 3] = 1e-30
+    x[6] = rng.standard_normal(n)
+    return x
+
+
+@pytest.mark.parametrize("pre", [True, False])
+def test_row_scale_from_every_element(pre):
+    rng = np.random.default_rng(91)
+    x = synth.to_bf16(off_lead_rows(rng, 4096))
+    blocks = [synth.orthogonal_blocks(rng, 256, 16) for _ in range(3)]
+    mask = synth.sign_bits_to_mask(rng.integers(0, 2, 4096))
+    y = host64(run(x, blocks, mask=mask if pre else None, pre=pre, bdt=torch.float16))
+    assert np.isfinite(y).all()
+    want = harp.harp_rotate(synth.bf16_to_f64(x), RAD, blocks, s=H.signs_from_bits(mask, 4096) if pre else None,
+                            precondition=pre)
+    err = compare.float_err(y, want)[0]
+    assert err <= TOL, err

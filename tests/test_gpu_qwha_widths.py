@@ -132,3 +132,38 @@ def test_wide_2048x8192_nnz524288():
                  {"y_max_scaled_err": err_y, "dx_max_scaled_err": err_dx, "dc_max_scaled_err": err_dc,
                   "tol_bf16": TOL_BF16, "tol_f32": TOL_F32, "tokens": tokens, "entries": int(ci.size)})
     assert err_y <= TOL_BF16 and err_dx <= TOL_BF16 and err_dc <= TOL_F32
+
+
+def off_lead_rows(rng, n):
+    """Token rows whose mass avoids elements 8m and 8m + 1 (the first 32-bit
+    word of every 16-byte chunk the kernels load), at very different
+    magnitudes: the per-token staging scale must come from every element."""
+    x = np.zeros((7, n))
+    x[0, 2] = 3.0e4
+    x[1, 5::8] = 1.0e3
+    keep = (np.arange(n) % 8) >= 2
+    x[2, keep] = rng.standard_normal(keep.sum()) * 1e20
+    x[3, keep] = rng.standard_normal(keep.sum()) * 1e-20
+    x[4, 7::8] = rng.standard_normal(n // 8) * 100.0
+    x[5, 3] = 1e-30
+    x[6] = rng.standard_normal(n)
+    return x
+
+
+@pytest.mark.parametrize("d_in", [64, 1024, 4096, 8192])
+def test_token_scale_from_every_element(d_in):
+    rng = np.random.default_rng(17 + d_in)
+    d_out = 512
+    x = synth.to_bf16(off_lead_rows(rng, d_in))
+    rp, ci, v = random_csr(rng, d_out, d_in, 20 * d_out)
+    y = host64(W().qwha_adapter_forward(dev(x), dev(rp), dev(ci), dev(v), d_out))
+    assert np.isfinite(y).all()
+    want = qwha.qwha_forward(synth.bf16_to_f64(x), rp, ci, synth.bf16_to_f64(v), d_out)
+    err = compare.float_err(y, want)[0]
+    assert err <= TOL_BF16, err
+    dy = synth.to_bf16(off_lead_rows(rng, d_out))
+    dx = host64(dx_gpu(dy, rp, ci, v, d_in))
+    assert np.isfinite(dx).all()
+    want = qwha.qwha_backward_input(synth.bf16_to_f64(dy), rp, ci, synth.bf16_to_f64(v), d_in)
+    err = compare.float_err(dx, want)[0]
+    assert err <= TOL_BF16, err

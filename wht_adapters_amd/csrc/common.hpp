@@ -23,6 +23,40 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t as_u(float f) { return __builtin_bit_cast(uint32_t, f); }
 
+// Largest magnitude among 16-bit floats (bf16 or fp16), exactly and with no
+// floating-point arithmetic: for non-NaN values |a| <= |b| exactly when the
+// bit patterns with the sign cleared compare the same way as integers.  acc
+// holds two running maxima (one per 16-bit half of the words folded in).
+__device__ __forceinline__ u16x2 absmax16(u16x2 acc, uint32_t w) {
+  const uint32_t m = w & 0x7fff7fffu;
+  return __builtin_elementwise_max(acc, u16x2{(uint16_t)(m & 0xffffu), (uint16_t)(m >> 16)});
+}
+__device__ __forceinline__ uint32_t absmax16(u16x2 acc) { return acc.x > acc.y ? acc.x : acc.y; }
+
+// The maximum of a non-negative value over the 64 lanes, returned as a
+// wave-uniform value: an inclusive max-scan (row_shr 1, 2, 4, 8 within rows
+// of 16 lanes, row_bcast 15 / 31 across rows; lanes without a source read 0,
+// the identity), then lane 63's result.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_max_step(uint32_t x) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWS, 0xf, false);
+  return o > x ? o : x;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = dpp_max_step<0x111, 0xf>(x);
+  x = dpp_max_step<0x112, 0xf>(x);
+  x = dpp_max_step<0x114, 0xf>(x);
+  x = dpp_max_step<0x118, 0xf>(x);
+  x = dpp_max_step<0x142, 0xa>(x);
+  x = dpp_max_step<0x143, 0xc>(x);
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+// For the magnitude bits b of a bf16 value (sign cleared): an exponent E with
+// |value| < 2^E (E = biased exponent - 126; subnormals get the normal range's
+// bound, -126); 0 for b = 0.
+__device__ __forceinline__ int bf16_mag_exp(uint32_t b) { return b ? (int)(b >> 7) - 126 : 0; }
+
 constexpr int popc_c(unsigned x) { return x ? (int)(x & 1u) + popc_c(x >> 1) : 0; }
 
 // In-register radix-2 butterfly: (a, b) -> (a + b, a - b).

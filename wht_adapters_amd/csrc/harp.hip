@@ -20,8 +20,9 @@
 // One workgroup (8 waves) per CU, looping over tiles of 16 tokens kept in
 // LDS as fp16 (140 KB with padding):
 //   load   each wave takes two token rows: sign flips, and an exact power-of-
-//          two scale that puts the row's L2 norm in [2^13, 2^14) (every later
-//          value is bounded by that norm, all stages being orthogonal); the
+//          two scale that puts 64 max |x_i|, a bound on the row's L2 norm, in
+//          [2^13, 2^14) (every later value is bounded by that norm, all
+//          stages being orthogonal); the
 //          rows stay bf16 in the tile and the first G pass (bf16 MFMA) applies
 //          the scale to its fp32 result before rounding to fp16; the next
 //          tile's rows are fetched meanwhile;
@@ -52,17 +53,16 @@ static_assert(RS >= 4096 + 4 * 64 + 4 * 4 && (RS / 2) % 4 == 2, "row stride");
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 
-// power-of-two exponent of a row with squared norm `ss` (wave-uniform)
-__device__ __forceinline__ int row_exponent(float ss) {
-  int e = 0;
-  if (ss > 0.f) (void)frexpf(__builtin_sqrtf(ss), &e);  // ||z|| = m 2^e, m in [0.5, 1)
-  return e;
-}
-
-__device__ __forceinline__ float wave_sum(float a) {
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) a += __shfl_xor(a, s);
-  return a;
+// Power-of-two exponent e of a row whose largest magnitude has bf16 bits
+// `mb` (wave-uniform): ||x|| <= sqrt(4096) max |x_i| < 2^e, so every value of
+// every later stage (all stages are orthogonal) stays below 2^e.  The exact
+// maximum cannot overflow or underflow the way a sum of squares in fp32
+// would.  e >= -112 keeps the scale 2^(14-e) and its inverse normal fp32
+// numbers (a row with max |x_i| < 2^-118 is staged with a smaller scale
+// than this bound would allow).
+__device__ __forceinline__ int row_exponent(uint32_t mb) {
+  const int e = bf16_mag_exp(mb) + 6;
+  return mb ? (e > -112 ? e : -112) : 0;
 }
 
 // Tile layout (halfwords): row n at n * RS; element i at lay(i), which pads
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(hp::THREADS) void k_harp(const uint16_t* __restrict
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int row = 2 * w + s;
-      float ss = 0.f;
+      u16x2 am{0, 0};
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         u32x4 v = raw[s][r];
@@ -312,12 +312,9 @@ __global__ __launch_bounds__(hp::THREADS) void k_harp(const uint16_t* __restrict
         v.z ^= msk[r][2];
         v.w ^= msk[r][3];
         raw[s][r] = v;
-        ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v.x), __builtin_bit_cast(bf16x2_t, v.x), ss, false);
-        ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v.y), __builtin_bit_cast(bf16x2_t, v.y), ss, false);
-        ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v.z), __builtin_bit_cast(bf16x2_t, v.z), ss, false);
-        ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v.w), __builtin_bit_cast(bf16x2_t, v.w), ss, false);
+        am = absmax16(absmax16(absmax16(absmax16(am, v.x), v.y), v.z), v.w);
       }
-      const int e = row_exponent(wave_sum(ss));
+      const int e = row_exponent(wave_max_u32(absmax16(am)));
       if (lane == 0) texp[row] = e;
       if (pre) {
         // raw (sign-flipped) bf16: the first G pass reads it with a bf16 MFMA and scales its result

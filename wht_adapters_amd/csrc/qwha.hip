@@ -169,7 +169,7 @@ __global__ __launch_bounds__(qw::THREADS) void k_qwha(const uint16_t* __restrict
       const int64_t tok = tok0 + min(k, ntok - 1);  // tail tokens recompute the last one
       const uint16_t* xr = x + tok * ldx;
       float v[64];
-      float nrm = 0.f;  // split: 4 ||x||^2 (the widened values carry two butterflies)
+      u16x2 am{0, 0};  // split: the largest |x_i| of the token, from the bf16 bits
       if constexpr (BWD) {
         // lane t holds columns 64 t .. 64 t + 63 (layout B); columns past
         // in_cols are zero (16-byte loads where a chunk lies inside and the
@@ -197,14 +197,13 @@ __global__ __launch_bounds__(qw::THREADS) void k_qwha(const uint16_t* __restrict
             Raw8 rl, rh;
             fetch8<DT_BF16>(xr, col[c], rl);
             fetch8<DT_BF16>(xr, col[c] + 4096, rh);
+            am = absmax16(absmax16(absmax16(absmax16(am, rl.a.x), rl.a.y), rl.a.z), rl.a.w);
+            am = absmax16(absmax16(absmax16(absmax16(am, rh.a.x), rh.a.y), rh.a.z), rh.a.w);
             float vl[8], vh[8];
             widen8<DT_BF16, false>(rl, vl, nomask, 0u);
             widen8<DT_BF16, false>(rh, vh, nomask, 0u);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              nrm = __builtin_fmaf(vl[e], vl[e], __builtin_fmaf(vh[e], vh[e], nrm));
-              v[8 * c + e] = half ? vl[e] - vh[e] : vl[e] + vh[e];
-            }
+            for (int e = 0; e < 8; ++e) v[8 * c + e] = half ? vl[e] - vh[e] : vl[e] + vh[e];
           } else {
             // d_in < 4096: the row is zero-extended to 4096
             Raw8 raw{};
@@ -218,15 +217,13 @@ __global__ __launch_bounds__(qw::THREADS) void k_qwha(const uint16_t* __restrict
       }
       int e = 0;
       if constexpr (SPLIT) {
-        // every raw sum |(H_4096 (x_lo +- x_hi))_k| <= 64 ||x_lo +- x_hi|| <= 64 sqrt(2) ||x||;
-        // e is taken from 64 ||x|| (< 2^e), so staged values stay below
-        // sqrt(2) 2^14, inside fp16.  Both halves compute the same e (an
-        // xor-butterfly sum gives every lane the same value: IEEE addition
-        // commutes)
-#pragma unroll
-        for (int s = 1; s < 64; s <<= 1) nrm += __shfl_xor(nrm, s);
-        const float bound = 128.0f * __builtin_sqrtf(0.25f * nrm);
-        if (bound > 0.f) (void)frexpf(bound, &e);
+        // every raw sum |(H_4096 (x_lo +- x_hi))_k| <= 8192 max |x_i| <
+        // 2^(em+13) with max |x_i| < 2^em (the maximum is exact: no sum of
+        // squares that could overflow or underflow fp32); e = em + 12 keeps
+        // the staged values (times 2^(14-e)) below 2^15, inside fp16.  Both
+        // halves compute the same e.
+        const uint32_t mb = wave_max_u32(absmax16(am));
+        if (mb) e = bf16_mag_exp(mb) + 12;
       } else {
         // exact power-of-two scale putting max |z| in [2^13, 2^14)
         float a4[4] = {0.f, 0.f, 0.f, 0.f};
@@ -237,6 +234,9 @@ __global__ __launch_bounds__(qw::THREADS) void k_qwha(const uint16_t* __restrict
         for (int s = 1; s < 64; s <<= 1) a = fmaxf(a, __shfl_xor(a, s));
         if (a > 0.f) (void)frexpf(a, &e);       // a = m 2^e, m in [0.5, 1)
       }
+      // e >= -100 keeps 2^(14-e) and the output factor 2^(e-20) normal fp32
+      // numbers (tokens below about 2^-113 are staged with a smaller scale)
+      e = e > -100 ? e : -100;
       const float mult = ldexpf(rho ? -1.0f : 1.0f, 14 - e);
       if (lane == 0 && half == 0) texp[k] = e;
       uint16_t* zrow = zt + k * Q::ZW + half * 4096 + t * 64;
