@@ -125,6 +125,24 @@ def test_quant_subnormal_scales_clip(bits, g, logn):
     check_quant(w, mask, bits, g)
 
 
+@pytest.mark.parametrize("bits,g,logn", [(4, 128, 12), (2, 64, 13), (3, 32, 10)])
+def test_quant_extreme_magnitudes(bits, g, logn):
+    """bf16 rows whose fp16 scales overflow to inf (codes 0), a row whose
+    groups straddle that threshold (max |y| near 65520 qmax), a row near
+    1e4, a normal row, and rows of 1e-30 and 1e-38 (scales 0, codes 0):
+    codes and scales follow the oracle bit for bit like any other row."""
+    n = 1 << logn
+    rng = np.random.default_rng(7 + bits)
+    edge = 65520.0 * rtn.qmax_of(bits) / 3.0  # about 3 sigma of a group at the overflow threshold
+    sig = np.array([1e6, 3e5, edge, 1e4, 1.0, 1e-30, 1e-38])[:, None]
+    w = dev(sig * rng.standard_normal((7, n)), torch.bfloat16)
+    mask = synth.sign_bits_to_mask(rng.integers(0, 2, n))
+    codes, scales, _ = check_quant(w, mask, bits, g)
+    sc = scales_host(scales).astype(np.float32)
+    assert np.isinf(sc[0]).all() and (np.isinf(sc[2]).any() and np.isfinite(sc[2]).any())
+    assert (sc[5:] == 0).all()
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("logn,g", [(6, 64), (10, 32), (12, 64), (12, 128), (13, 64), (13, 256), (11, 8)])
 def test_dequant_arbitrary_codes(logn, g, bits):
