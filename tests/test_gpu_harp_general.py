@@ -222,3 +222,38 @@ def test_two_sided(dt):
         want = harp.harp_two_sided(host64(w_dev), _oracle_side(so), _oracle_side(si))
         err = compare.float_err(got, want)[0]
         assert err <= (TOL_F32 if dt == torch.float32 else TOL), (rout, rin, err)
+
+
+@pytest.mark.parametrize("radices,pre", [((16, 8, 8), False), ((8, 8, 8, 4), True), ((5, 5, 5, 8, 2), False),
+                                         ((2, 8, 2), False), ((8, 8, 8), True)])
+def test_small_tiles_matrix_cores(radices, pre):
+    """bf16 rows of small d with a mean radix of at least 4 run on the matrix
+    cores in 16-token tiles: token counts around the tile, fp16 blocks against
+    the oracle, fp32 blocks giving the same bits (rounded to fp16 the same
+    way), and rows of very different magnitudes."""
+    d = int(np.prod(radices))
+    rng = np.random.default_rng(d + len(radices))
+    blocks = rand_blocks(rng, radices)
+    b16 = [np.asarray(b, np.float16).astype(np.float32) for b in blocks]
+    mask = synth.sign_bits_to_mask(rng.integers(0, 2, d)) if pre else None
+    s = H.signs_from_bits(mask, d) if pre else None
+    for tokens in (1, 15, 16, 17, 40):
+        x = synth.to_bf16(rng.standard_normal((tokens, d)))
+        y16 = run(x, radices, blocks, mask=mask, pre=pre, bdt=torch.float16)
+        y32 = run(x, radices, blocks, mask=mask, pre=pre, bdt=torch.float32)
+        assert torch.equal(y16.cpu(), y32.cpu())
+        want = harp.harp_rotate(synth.bf16_to_f64(x), list(radices), b16, s=s, precondition=pre)
+        err = compare.float_err(host64(y16), want)[0]
+        assert err <= 1e-2, (tokens, err)
+    x = np.zeros((5, d))
+    x[0, 2] = 3.0e4
+    keep = (np.arange(d) % 8) >= 2
+    x[1, keep] = rng.standard_normal(keep.sum()) * 1e20
+    x[2, keep] = rng.standard_normal(keep.sum()) * 1e-20
+    x[3, 5::8] = 1e3
+    x[4] = rng.standard_normal(d)
+    x = synth.to_bf16(x)
+    y = host64(run(x, radices, blocks, mask=mask, pre=pre, bdt=torch.float16))
+    assert np.isfinite(y).all()
+    want = harp.harp_rotate(synth.bf16_to_f64(x), list(radices), b16, s=s, precondition=pre)
+    assert compare.float_err(y, want)[0] <= 1e-2

@@ -292,6 +292,383 @@ __global__ __launch_bounds__(hg::THREADS) void k_harp_gen(const void* __restrict
   }
 }
 
+// ------------------------------------------------- bf16 rows on the matrix cores
+//
+// bf16 rows (output tolerance 2e-2) of small d take fp16 MFMAs with fp32
+// accumulation, as the radix-16 kernel's stages do.  The tile holds TT tokens
+// token-fastest: element i of all TT tokens is one slot of 2 TT bytes, each
+// token scaled by an exact power of two from its largest |x_i|.  A stage of
+// radix b packs P = 16 / b blocks block-diagonally into one 16 x 16 operand
+// Bp and computes, per MFMA, D^T = X Bp^T for the 16 token lanes:
+//   A = X[token][j]: one transposing LDS read per lane.  ds_read_b64_tr_b16
+//       gives lane 4p + e of a 16-lane group halfword e of the 8 bytes
+//       addressed by lanes p, p + 4, p + 8 and p + 12; those lanes address
+//       token quad p of the inputs j = 4g .. 4g + 3, so lane 4p + e receives
+//       token 4p + e of all four;
+//   B = Bp^T: lane (k, g) holds row k of Bp at columns 4g .. 4g + 3 (zero
+//       outside the row's own block);
+//   D^T[token][k]: lane (k, g) holds tokens 4g .. 4g + 3 of output k, one
+//       8-byte write into the tile (in place: the same elements were read).
+// The P blocks of one MFMA are consecutive blocks c0 .. c0 + P - 1 of one
+// run of s blocks (s the digit's stride; a run's blocks share the digits
+// above) when s >= P, else P' = floor(P / s) s blocks making whole runs:
+// either way an element is a wave-uniform base plus a per-lane offset fixed
+// for the stage, so addressing costs a few VALU operations per MFMA.  Each
+// wave takes a contiguous range of MFMAs; their coefficients are loaded PD
+// MFMAs ahead (unconditional loads, combined when used) and the next MFMA's
+// inputs are read before the current one runs.  The MFMA count per token
+// grows with the number of stages, not with the radices, and the fixed cost
+// per MFMA is several times the VALU kernel's per coefficient, so this form
+// is used where it measured faster: d <= 3072 (at 4096 and above, with one
+// 8-wave block per CU, the VALU kernel was as fast or faster) and a mean
+// radix of at least 4 (radix-2 chains stay on the VALU kernel).
+namespace hm {
+constexpr int THREADS = 512;
+constexpr int PD = 8;  // coefficient loads run PD MFMAs ahead (L2 latency)
+constexpr int NW = THREADS / 64;
+constexpr int MAXR = 12;  // 16-byte chunks a lane loads per tile (16 tokens, d <= 3072)
+__host__ __device__ constexpr int slot(int i) { return i; }
+template <int TT>
+__host__ __device__ constexpr int tile_bytes(int d) { return (slot(d - 1) + 1) * 2 * TT; }
+}  // namespace hm
+
+typedef short hm_s16x4 __attribute__((ext_vector_type(4)));
+typedef float hm_f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 hm_f16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x2 hm_tr_read(const uint8_t* smem, int off) {
+  const hm_s16x4 v =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) hm_s16x4*)(smem + off));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// coefficient (row r, column col) of block c, rounded to fp16 bits
+template <int BDT>
+__device__ __forceinline__ uint32_t hm_coef(const void* blocks, long long i) {
+  if constexpr (BDT == DT_F32)
+    return __builtin_bit_cast(uint16_t, (_Float16)reinterpret_cast<const float*>(blocks)[i]);
+  else
+    return reinterpret_cast<const uint16_t*>(blocks)[i];
+}
+
+
+// WIDE: the digit's stride s >= P, P consecutive blocks of one run per MFMA;
+// HAD: a fixed Hadamard factor (coefficients computed, nothing loaded)
+template <int B, int BDT, int TT, bool WIDE, bool HAD>
+__device__ __forceinline__ void hm_stage_w(uint8_t* smem, int d, int st, const void* blocks, long long off, int w,
+                                           int lane) {
+  constexpr int S = 2 * TT;
+  constexpr int P = 16 / B;
+  constexpr int PD = hm::PD;
+  constexpr int ESZ = BDT == DT_F32 ? 4 : 2;
+  const int nblk = d / B;
+  const int PP = WIDE ? P : (P / st) * st;      // blocks per MFMA
+  const int mpr = WIDE ? (st + P - 1) / P : 1;  // MFMAs per run of st blocks
+  const int nmf = WIDE ? (nblk / st) * mpr : (nblk + PP - 1) / PP;
+  // the wave's MFMAs: a contiguous range [m0, m1)
+  const int per = (nmf + hm::NW - 1) / hm::NW;
+  const int m0 = min(nmf, w * per), m1 = min(nmf, m0 + per);
+  if (m0 >= m1) return;
+  const int g = lane >> 4, l16 = lane & 15;
+  // this lane as a source of the transposing read: contraction index ja, token quad qa
+  const int ja = 4 * g + (l16 >> 2), qa = l16 & 3;
+  const int pa = ja / B, ra = ja - pa * B;
+  const bool ina = pa < PP;
+  const int da = !ina ? 0 : WIDE ? pa + ra * st : (pa % st) + (pa / st) * st * B + ra * st;
+  const int qoff = 8 * ((4 * qa < TT) ? qa : 0);  // token quads past TT read quad 0 (outputs unused)
+  const int aoff = da * S + qoff;                 // LDS bytes from the MFMA's base element
+  const int pa_s = ina ? pa : 1 << 20;            // block of the input slot (never below nv when unused)
+  // this lane as output k = l16 (row rk of block pk), tokens 4g .. 4g + 3
+  const int pk = l16 / B, rk = l16 - pk * B;
+  const bool ink = pk < PP;
+  const int dk = !ink ? 0 : WIDE ? pk + rk * st : (pk % st) + (pk / st) * st * B + rk * st;
+  const int ooff = dk * S + 8 * g;
+  // row k's coefficients at columns 4g + jj: in block pk for column 4g + jj - pk B in [0, B)
+  unsigned cm = 0;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int col = 4 * g + jj - pk * B;
+    if (ink && col >= 0 && col < B) cm |= 1u << jj;
+  }
+  // the lane writes output k for tokens 4g .. 4g + 3 when its block is present
+  // (as an operand lane it holds columns 4g .. 4g + 3 of row k: a separate role)
+  const int pk_s = (ink && 4 * g < TT) ? pk : 1 << 20;
+  const int pk_c = cm != 0u ? pk : 1 << 20;
+  const int h2 = (cm & 1u) ? 0 : 1;  // radix 2: the row's two columns are the first or second pair
+  // byte offset of the lane's first coefficient within its MFMA's block group
+  const uint32_t cboff = cm ? (uint32_t)(pk * B * B + rk * B - pk * B + 4 * g + (B == 2 ? 2 * h2 : 0)) * ESZ : 0u;
+  uint32_t hw[2] = {0u, 0u};
+  if constexpr (HAD) {
+    const float hs = B == 2 ? 0.70710678118654752f : B == 4 ? 0.5f : B == 8 ? 0.35355339059327376f : 0.25f;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      if (cm & (1u << jj)) {
+        const int col = 4 * g + jj - pk * B;
+        const float v = (__builtin_popcount(rk & col) & 1) ? -hs : hs;
+        hw[jj >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v) << (16 * (jj & 1));
+      }
+  }
+  // wave-uniform MFMA state: base element e0, valid blocks nv, first block c0
+  int run = WIDE ? m0 / mpr : 0;
+  int idx = WIDE ? m0 - run * mpr : m0 * PP;
+  auto cur = [&](int& pe0, int& pnv, int& pc0) {
+    if constexpr (WIDE) {
+      pc0 = run * st + idx * P;
+      pnv = min(P, st - idx * P);
+      pe0 = idx * P + run * st * B;
+    } else {
+      pc0 = idx;
+      pnv = min(PP, nblk - idx);
+      pe0 = idx * B;
+    }
+  };
+  auto step = [&]() {
+    if constexpr (WIDE) {
+      ++idx;
+      run += idx == mpr ? 1 : 0;
+      idx = idx == mpr ? 0 : idx;
+    } else {
+      idx += PP;
+    }
+  };
+  const uint8_t* bbase = reinterpret_cast<const uint8_t*>(blocks) + off * ESZ;
+  // one MFMA's coefficients as loaded (unconditional loads: rows without
+  // coefficients in the MFMA read its first coefficient)
+  struct Raw {
+    uint32_t v[4];  // fp16 words or halfwords, or fp32 bits
+  };
+  auto cload = [&](int pnv, int pc0) {
+    Raw r{};
+    if constexpr (!HAD) {
+      const uint8_t* bp = bbase + (size_t)pc0 * (B * B * ESZ) + (pk_c < pnv ? cboff : 0u);
+      if constexpr (BDT == DT_F16) {
+        if constexpr (B % 4 == 0) {
+          const u32x2 v = ldg<u32x2>(bp);
+          r.v[0] = v.x;
+          r.v[1] = v.y;
+        } else if constexpr (B == 2) {
+          r.v[0] = ldg<uint32_t>(bp);
+        } else {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) r.v[jj] = ldg<uint16_t>(bp + ((cm >> jj) & 1u) * 2 * jj);
+        }
+      } else {
+        if constexpr (B % 4 == 0) {
+          const u32x4 v = ldg<u32x4>(bp);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) r.v[q] = v[q];
+        } else if constexpr (B == 2) {
+          const u32x2 v = ldg<u32x2>(bp);
+          r.v[0] = v.x;
+          r.v[1] = v.y;
+        } else {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) r.v[jj] = ldg<uint32_t>(bp + ((cm >> jj) & 1u) * 4 * jj);
+        }
+      }
+    }
+    return r;
+  };
+  auto cword = [&](const Raw& r, int pnv) -> u32x2 {
+    const bool ok = pk_c < pnv;
+    u32x2 c;
+    if constexpr (HAD) {
+      c = u32x2{hw[0], hw[1]};
+    } else if constexpr (BDT == DT_F16) {
+      if constexpr (B % 4 == 0) c = u32x2{r.v[0], r.v[1]};
+      else if constexpr (B == 2) c = h2 ? u32x2{0u, r.v[0]} : u32x2{r.v[0], 0u};
+      else {
+        uint32_t hv[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) hv[jj] = (cm & (1u << jj)) ? (r.v[jj] & 0xffffu) : 0u;
+        c = u32x2{hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};
+      }
+    } else {
+      if constexpr (B % 4 == 0) c = u32x2{pack_f16(as_f(r.v[0]), as_f(r.v[1])), pack_f16(as_f(r.v[2]), as_f(r.v[3]))};
+      else if constexpr (B == 2) {
+        const uint32_t pw = pack_f16(as_f(r.v[0]), as_f(r.v[1]));
+        c = h2 ? u32x2{0u, pw} : u32x2{pw, 0u};
+      } else {
+        float fv[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) fv[jj] = (cm & (1u << jj)) ? as_f(r.v[jj]) : 0.f;
+        c = u32x2{pack_f16(fv[0], fv[1]), pack_f16(fv[2], fv[3])};
+      }
+    }
+    return ok ? c : u32x2{0u, 0u};
+  };
+  // an MFMA's inputs; slots of blocks missing from a partial MFMA (and MFMAs
+  // past the range, nv = 0) read its base element, times zero weights
+  auto xread = [&](int pe0, int pnv) { return hm_tr_read(smem, pe0 * S + (pa_s < pnv ? aoff : qoff)); };
+  int re0[PD], rnv[PD];
+  Raw cq[PD];
+#pragma unroll
+  for (int u = 0; u < PD; ++u) {
+    int c0 = 0;
+    re0[u] = 0;
+    rnv[u] = 0;
+    if (m0 + u < m1) {
+      cur(re0[u], rnv[u], c0);
+      step();
+    }
+    cq[u] = cload(rnv[u], c0);
+  }
+  u32x2 xn = xread(re0[0], rnv[0]);
+  for (int base = m0; base < m1; base += PD) {
+#pragma unroll
+    for (int u = 0; u < PD; ++u) {
+      if (base + u < m1) {
+        const int e0 = re0[u], nv = rnv[u];
+        const u32x2 xa = xn;
+        xn = xread(re0[(u + 1) % PD], rnv[(u + 1) % PD]);  // the next MFMA's inputs: other blocks, other elements
+        const u32x2 cw = cword(cq[u], nv);
+        int c0 = 0;
+        re0[u] = 0;
+        rnv[u] = 0;
+        if (base + u + PD < m1) {
+          cur(re0[u], rnv[u], c0);
+          step();
+        }
+        cq[u] = cload(rnv[u], c0);  // the MFMA PD ahead
+        const f32x4 dv = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(hm_f16x4, xa),
+                                                               __builtin_bit_cast(hm_f16x4, cw),
+                                                               f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        if (pk_s < nv)
+          *reinterpret_cast<u32x2*>(smem + e0 * S + ooff) = u32x2{pack_f16(dv[0], dv[1]), pack_f16(dv[2], dv[3])};
+      }
+    }
+  }
+}
+
+template <int B, int BDT, int TT>
+__device__ __forceinline__ void hm_stage(uint8_t* smem, int d, int st, bool had, const void* blocks, long long off,
+                                         int w, int lane) {
+  constexpr bool H = B == 2 || B == 4 || B == 8 || B == 16;
+  // a fresh copy of the lane index per stage: the per-lane constants of every
+  // radix would otherwise be hoisted out of the stage loop and stay live
+  asm volatile("" : "+v"(lane));
+  if (st >= 16 / B) {
+    if (H && had) hm_stage_w<B, BDT, TT, true, H>(smem, d, st, blocks, off, w, lane);
+    else hm_stage_w<B, BDT, TT, true, false>(smem, d, st, blocks, off, w, lane);
+  } else {
+    if (H && had) hm_stage_w<B, BDT, TT, false, H>(smem, d, st, blocks, off, w, lane);
+    else hm_stage_w<B, BDT, TT, false, false>(smem, d, st, blocks, off, w, lane);
+  }
+}
+
+template <int BDT, int TT>
+__global__ __launch_bounds__(hm::THREADS) void k_harp_mx(const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
+                                                        int64_t tokens, int64_t ldx, int64_t ldy, int d, int lgd,
+                                                        const uint32_t* __restrict__ sbits,
+                                                        const void* __restrict__ blocks, HgSched sc) {
+  constexpr int S = 2 * TT;
+  constexpr int GPW = 64 / TT;  // token groups of a wave in the row phases
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint32_t* tmax = reinterpret_cast<uint32_t*>(smem + ((hm::tile_bytes<TT>(d) + 15) & ~15));
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int64_t tok0 = (int64_t)blockIdx.x * TT;
+  if (threadIdx.x < 16) tmax[threadIdx.x] = 0u;
+  __syncthreads();
+
+  // ---- load: lane (token jt, group gq) takes 16-byte chunks cc = (u NW + w) GPW + gq
+  // of its token's row (signs flipped on the way when preconditioning)
+  const int jt = lane % TT, gq = lane / TT;
+  const int nch = d >> 3;
+  const bool lact = gq < GPW && tok0 + jt < tokens;
+  const uint16_t* xr = x + (tok0 + jt) * ldx;
+  u32x4 raw[hm::MAXR];
+  uint32_t mb = 0u;
+#pragma unroll
+  for (int u = 0; u < hm::MAXR; ++u) {
+    const int cc = (u * hm::NW + w) * GPW + gq;
+    raw[u] = u32x4{0u, 0u, 0u, 0u};
+    if (lact && cc < nch) {
+      u32x4 v = ldg<u32x4>(xr + 8 * cc);
+      if (sbits) {
+        const int i0 = 8 * cc;
+        const uint32_t sb = (sbits[i0 >> 5] >> (i0 & 31)) & 0xffu;
+        v ^= u32x4{pair_mask16(sb), pair_mask16(sb >> 2), pair_mask16(sb >> 4), pair_mask16(sb >> 6)};
+      }
+      raw[u] = v;
+    }
+  }
+  {
+    u16x2 am{0, 0};
+#pragma unroll
+    for (int u = 0; u < hm::MAXR; ++u) {
+      const u32x4 v = raw[u];
+      am = absmax16(absmax16(absmax16(absmax16(am, v.x), v.y), v.z), v.w);
+    }
+    mb = absmax16(am);
+  }
+  if (lact) atomicMax(&tmax[jt], mb);
+  __syncthreads();
+  // power-of-two scale per token: ||x|| <= sqrt(d) max |x_i| < 2^e with
+  // e = exp(max) + ceil(log2 sqrt(d)), so every stage's values (the stages
+  // being orthogonal) stay below 2^14 after multiplying by 2^(14 - e);
+  // e >= -112 keeps both factors normal fp32 numbers
+  auto tok_exp = [&](int j) {
+    const uint32_t m = tmax[j];
+    const int e = bf16_mag_exp(m) + lgd;
+    return m ? (e > -112 ? e : -112) : 0;
+  };
+  {
+    const float scl = ldexpf(1.0f, 14 - tok_exp(jt));
+#pragma unroll
+    for (int u = 0; u < hm::MAXR; ++u) {
+      const int cc = (u * hm::NW + w) * GPW + gq;
+      if (gq < GPW && cc < nch) {
+        const u32x4 v = raw[u];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int i = 8 * cc + 2 * q;
+          *reinterpret_cast<_Float16*>(smem + hm::slot(i) * S + 2 * jt) = (_Float16)(bf16lo(v[q]) * scl);
+          *reinterpret_cast<_Float16*>(smem + hm::slot(i + 1) * S + 2 * jt) = (_Float16)(bf16hi(v[q]) * scl);
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- stages
+  for (int t = 0; t < sc.n; ++t) {
+    switch (sc.b[t]) {
+#define HM_CASE(BB) \
+  case BB: hm_stage<BB, BDT, TT>(smem, d, sc.s[t], sc.had[t] != 0, blocks, sc.off[t], w, lane); break;
+      HM_CASE(2) HM_CASE(3) HM_CASE(4) HM_CASE(5) HM_CASE(6) HM_CASE(7) HM_CASE(8) HM_CASE(9)
+      HM_CASE(10) HM_CASE(11) HM_CASE(12) HM_CASE(13) HM_CASE(14) HM_CASE(15) HM_CASE(16)
+#undef HM_CASE
+      default: break;
+    }
+    __syncthreads();
+  }
+
+  // ---- store: transposing reads give lane t of group g token t's elements
+  // E + 4g .. E + 4g + 3 (source lane s addresses element E + 4g + s / 4,
+  // token quad s % 4); unscale, round to bf16
+  {
+    const int g = lane >> 4, l16 = lane & 15;
+    const int qs = l16 & 3;
+    const int qoff = 8 * ((4 * qs < TT) ? qs : 0);
+    const bool act = l16 < TT && tok0 + l16 < tokens;
+    const float us = ldexpf(1.0f, tok_exp(l16 < TT ? l16 : 0) - 14);
+    uint16_t* yr = y + (tok0 + l16) * ldy;
+    for (int e0 = 16 * w; e0 < d; e0 += 16 * hm::NW) {
+      // d is a multiple of 8: a group past the row's end reads element 0 and stores nothing
+      const int ei = e0 + 4 * g;
+      const bool in = ei < d;
+      const u32x2 hv = hm_tr_read(smem, hm::slot(in ? ei + (l16 >> 2) : 0) * S + qoff);
+      if (act && in) {
+        // (vector elements copied to scalars first: this compiler's bit_cast
+        // of an element of a vector value reads element 0)
+        const uint32_t w0 = hv.x, w1 = hv.y;
+        const f16x2_t a = __builtin_bit_cast(f16x2_t, w0), b = __builtin_bit_cast(f16x2_t, w1);
+        stg<u32x2>(yr + ei, u32x2{pack_bf16((float)a.x * us, (float)a.y * us), pack_bf16((float)b.x * us, (float)b.y * us)});
+      }
+    }
+  }
+}
+
 // Entry from the C ABI (arguments validated there): radices each in [2, 16],
 // product d <= 8192, precondition only for d a power of two.
 template <int BDT, int XDT>
@@ -304,6 +681,17 @@ static void launch_hg(const void* x, void* y, int64_t tokens, int64_t ldx, int64
   (void)a;
   hipLaunchKernelGGL((k_harp_gen<BDT, XDT>), dim3(grid), dim3(hg::THREADS), lds, s, x, y, tokens, ldx, ldy, d, ldt,
                      tt, sbits, blocks, sc, vec);
+}
+
+template <int BDT, int TT>
+static void launch_hm(const void* x, void* y, int64_t tokens, int64_t ldx, int64_t ldy, int d, int lgd,
+                      const uint32_t* sbits, const void* blocks, const HgSched& sc, unsigned grid, size_t lds,
+                      hipStream_t s) {
+  static const bool a = hipFuncSetAttribute((const void*)k_harp_mx<BDT, TT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                            160 * 1024) == hipSuccess;
+  (void)a;
+  hipLaunchKernelGGL((k_harp_mx<BDT, TT>), dim3(grid), dim3(hm::THREADS), lds, s, (const uint16_t*)x, (uint16_t*)y,
+                     tokens, ldx, ldy, d, lgd, sbits, blocks, sc);
 }
 
 hipError_t launch_harp_gen(const void* x, void* y, int xdt, int64_t tokens, int d, int64_t ldx, int64_t ldy,
@@ -348,6 +736,25 @@ hipError_t launch_harp_gen(const void* x, void* y, int xdt, int64_t tokens, int 
                       ? 1 : 0;
   const unsigned grid = (unsigned)((tokens + tt - 1) / tt);
   const uint32_t* sb = precondition ? sbits : nullptr;
+  // bf16 rows whose length is a multiple of 8 (16-byte chunks), with 16-byte
+  // aligned rows and blocks, d <= 3072 and a mean radix of at least 4: the
+  // matrix-core form (16-token tiles), where it measured faster
+  int rsum = 0;
+  for (int t = 0; t < n; ++t) rsum += sc.b[t];
+  const bool mx_fits = hm::tile_bytes<16>(d) <= 96 * 1024;  // d <= 3072
+  if (xdt == DT_BF16 && vec && d % 8 == 0 && (reinterpret_cast<uintptr_t>(blocks) & 15u) == 0 && mx_fits &&
+      rsum >= 4 * n) {
+    int lgd = 0;
+    while ((1LL << (2 * lgd)) < d) ++lgd;  // sqrt(d) <= 2^lgd
+    const int nch = d / 8, per_round = hm::NW * (64 / 16);
+    if ((nch + per_round - 1) / per_round <= hm::MAXR) {
+      const size_t lds = (size_t)((hm::tile_bytes<16>(d) + 15) & ~15) + 64;
+      const unsigned gm = (unsigned)((tokens + 15) / 16);
+      if (bdt == DT_F16) launch_hm<DT_F16, 16>(x, y, tokens, ldx, ldy, d, lgd, sb, blocks, sc, gm, lds, s);
+      else launch_hm<DT_F32, 16>(x, y, tokens, ldx, ldy, d, lgd, sb, blocks, sc, gm, lds, s);
+      return hipGetLastError();
+    }
+  }
   if (bdt == DT_F16 && xdt == DT_F32) launch_hg<DT_F16, DT_F32>(x, y, tokens, ldx, ldy, d, ldt, tt, sb, blocks, sc, vec, grid, lds, s);
   else if (bdt == DT_F16) launch_hg<DT_F16, DT_BF16>(x, y, tokens, ldx, ldy, d, ldt, tt, sb, blocks, sc, vec, grid, lds, s);
   else if (xdt == DT_F32) launch_hg<DT_F32, DT_F32>(x, y, tokens, ldx, ldy, d, ldt, tt, sb, blocks, sc, vec, grid, lds, s);
