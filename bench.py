@@ -6,8 +6,9 @@ quantisation, bf16 weight matrix 4096 x 4096, group 128 along d_in, fp16
 scales, signed int4 codes -- one `rht_quantize_rtn` launch per step.  The
 other workloads (orthonormal FWHT 256 x 4096 fp32 and its row sweep, the
 inverse of the INT4 path, QWHA adapter forward and backward, HARP rotation
-with the radix-16 schedule and with the mixed-radix 8*8*8*5*2 schedule at
-d = 5120, 28672 x 8192 RHT + INT2 and its inverse, the online-RHT INT2
+with the radix-16 schedule, with the mixed-radix 8*8*8*5*2 schedule at
+d = 5120 and with 16*8*8 at d = 1024 (the matrix-core path of the general
+schedules), 28672 x 8192 RHT + INT2 and its inverse, the online-RHT INT2
 product, the QWHA initialisation) are timed the same way and reported under
 "workloads".
 
@@ -58,6 +59,7 @@ ALGO_BYTES = {
     # gradient of the values: x and dy in, F's row_ptr and col_idx, fp32 dc out
     "qwha_bwd_dc_2048x4096_nnz262144": 2 * 2048 * 4096 * 2 + 4097 * 4 + 262144 * 4 + 262144 * 4,
     "harp_8192x5120_r88852": 2 * 8192 * 5120 * 2 + 5120 * (8 + 8 + 8 + 5 + 2) * 2,  # fp16 blocks
+    "harp_8192x1024_r1688": 2 * 8192 * 1024 * 2 + 1024 * (16 + 8 + 8) * 2,  # fp16 blocks
     "rht_int2_g64_28672x8192": 28672 * 8192 * 2 + 1024 + 28672 * 2048 + 28672 * 128 * 2,
     "rht_int2_g64_28672x8192_inverse": 28672 * 8192 * 2 + 1024 + 28672 * 2048 + 28672 * 128 * 2,
     # decode through the INT2 layer: codes + fp16 scales + sign vector + one bf16 token in, bf16 y out
@@ -68,7 +70,7 @@ ROWS = {
     "rht_int4_g128_4096x4096_inverse": 4096, "qwha_2048x4096_nnz262144": 2048,
     "harp_8192x4096_r16x3": 8192, "rht_int2_g64_28672x8192": 28672,
     "qwha_bwd_dx_2048x4096_nnz262144": 2048, "qwha_bwd_dc_2048x4096_nnz262144": 2048,
-    "harp_8192x5120_r88852": 8192,
+    "harp_8192x5120_r88852": 8192, "harp_8192x1024_r1688": 8192,
     "rht_int2_g64_28672x8192_inverse": 28672,
     "gemv_int2_g64_28672x8192_t1": 28672,
 }
@@ -91,6 +93,7 @@ KERNELS = {  # kernel (as rocprofv3 names it) and the sources it is built from, 
                                          "launch.hpp"]),
     "harp_8192x4096_r16x3": ("k_harp<true>", ["harp.hip", "common.hpp", "launch.hpp"]),
     "qwha_2048x4096_nnz262144": ("k_qwha_fwd<1>", ["qwha_fwd.hip", "io.hpp", "engine.hpp", "common.hpp"]),
+    "harp_8192x1024_r1688": ("k_harp_mx<2, 16>", ["harp_gen.hip", "io.hpp", "common.hpp", "launch.hpp"]),
 }
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
@@ -320,7 +323,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workloads", default="all",
-                    help="all | main | comma list of fwht, qwha, qwha_bwd, harp, harp_gen, int2, gemv, qinit "
+                    help="all | main | comma list of fwht, qwha, qwha_bwd, harp, harp_gen, harp_mx, int2, gemv, qinit "
                          "(the main workload always runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -356,7 +359,7 @@ def main():
         del a, b
         log("[bench] copy probe: 3 x 256 MiB device copy done")
 
-    sel = {"all": {"main", "fwht", "qwha", "qwha_bwd", "harp", "harp_gen", "int2", "gemv", "qinit"},
+    sel = {"all": {"main", "fwht", "qwha", "qwha_bwd", "harp", "harp_gen", "harp_mx", "int2", "gemv", "qinit"},
            "main": {"main"}}.get(
         args.workloads, set(args.workloads.split(",")))
     sel.add("main")  # `value` is always quoted on the main workload
@@ -367,7 +370,7 @@ def main():
         res.update(bench_fwht(torch, W, synth, K, Wm))
         log(f"[bench] fwht_f32_256x4096: {res['fwht_f32_256x4096']}")
     for fn, nm in (("qwha", "qwha_2048x4096_nnz262144"), ("harp", "harp_8192x4096_r16x3"),
-                   ("harp_gen", "harp_8192x5120_r88852")):
+                   ("harp_gen", "harp_8192x5120_r88852"), ("harp_mx", "harp_8192x1024_r1688")):
         if fn in sel:
             res[nm] = bench_other(torch, W, mask_dev, synth, fn, nm, K, Wm)
             log(f"[bench] {nm}: {res[nm]}")
@@ -569,8 +572,8 @@ def bench_other(torch, W, mask_dev, synth, fn, name, K, Wm):
         ys = [torch.empty((x0.shape[0], d["d_out"]), dtype=torch.bfloat16, device="cuda:0") for _ in xs]
         t = Timed(torch, lambda i: W.qwha_adapter_forward(xs[i % len(xs)], rp, ci, v, d["d_out"],
                                                           out=ys[i % len(xs)]), n_launch(K, len(xs)), Wm)
-    elif fn == "harp_gen":
-        d = synth.harp_general()
+    elif fn in ("harp_gen", "harp_mx"):
+        d = synth.harp_general() if fn == "harp_gen" else synth.harp_general(radices=(16, 8, 8))
         x0 = d["x"].to("cuda:0")
         blocks = torch.from_numpy(np.concatenate([b.reshape(-1) for b in d["blocks"]])).to("cuda:0").half()
         xs = copies(torch, x0)
