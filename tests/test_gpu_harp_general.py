@@ -55,6 +55,8 @@ SCHED = [
     ((12, 10, 11, 6), 6, False),      # d = 7920, radices 9..16 split over lanes
     ((13, 9, 14, 2, 2), 4, False),
     ((16, 16, 4), 30, True),
+    ((16, 16, 2, 9), 11, False),      # d = 4608: two 512-thread blocks per CU, 4-token tiles
+    ((16, 15, 5, 4), 9, False),       # d = 4800: one 1024-thread block per CU
 ]
 
 

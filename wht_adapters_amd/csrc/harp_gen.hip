@@ -12,8 +12,11 @@
 // the row is loaded and Hn = (x) H_{2^a} / 2^(a/2) over a split of the index
 // bits into digits of at most 16 values, each an in-register Hadamard stage.
 //
-// One block per tile of tt tokens (as many as fit in LDS, at most 16): the
-// tile stays in LDS in fp32 across every stage, one stage per barrier.  A
+// One block per tile of tt tokens (as many as fit in its share of LDS, at
+// most 16): 1024 threads and the whole LDS per block, or for d <= 4717 two
+// 512-thread blocks per CU with half of it each, so that one block's row
+// loads overlap the other's stages.  The tile stays in LDS in fp32 across
+// every stage, one stage per barrier.  A
 // stage's work items are (block c, row chunk): a lane holds its chunk of
 // the block's coefficients in registers (the whole block when b <= 8, a
 // quarter when b > 8; the four lanes of one block sit in one wave, so all
@@ -32,6 +35,9 @@ constexpr int THREADS = 1024;
 constexpr int MAXST = 20;          // stages, preconditioning factors included
 constexpr int MAXTT = 16;
 constexpr int LDS_FLOATS = 38912;  // 152 KB of tile
+// tile floats per block of nt threads: 1024 threads, one block per CU; 512
+// threads, two blocks per CU (half the tile each)
+__host__ __device__ constexpr int lds_floats(int nt) { return nt == THREADS ? LDS_FLOATS : LDS_FLOATS / 2; }
 // one float of padding per 32: strided digit accesses spread over the banks
 __device__ __forceinline__ int pos(int i) { return i + (i >> 5); }
 inline int pos_h(int i) { return i + (i >> 5); }
@@ -94,7 +100,7 @@ __device__ __forceinline__ void had_regs(float (&x)[B]) {
   for (int k = 0; k < B; ++k) x[k] *= sc;
 }
 
-template <int B, int BDT>
+template <int B, int BDT, int NT>
 __device__ __forceinline__ void hg_stage(float* tile, int ldt, int nt, int d, int s, const void* blocks,
                                          long long off) {
   constexpr int LPB = B <= 8 ? 1 : 4;            // lanes per block
@@ -102,9 +108,9 @@ __device__ __forceinline__ void hg_stage(float* tile, int ldt, int nt, int d, in
   const int items = (d / B) * LPB;
   // token loop inside the item (coefficients loaded once per tile) when the
   // items fill the block; otherwise items and tokens are spread together
-  const bool spread = items < hg::THREADS / 2;
+  const bool spread = items < NT / 2;
   const int total = spread ? items * nt : items;
-  for (int f = threadIdx.x; f < total; f += hg::THREADS) {
+  for (int f = threadIdx.x; f < total; f += NT) {
     const int it = spread ? f % items : f;
     const int j0 = spread ? f / items : 0, j1 = spread ? j0 + 1 : nt;
     const int c = it / LPB, r0 = (it - c * LPB) * RPL;
@@ -149,10 +155,10 @@ __device__ __forceinline__ void hg_stage(float* tile, int ldt, int nt, int d, in
 
 // A fixed Hadamard factor H_B / sqrt(B) along a digit: one lane per group
 // and token, the group's B values through in-register butterflies.
-template <int B>
+template <int B, int NT>
 __device__ __forceinline__ void hg_had(float* tile, int ldt, int nt, int d, int s) {
   const int groups = d / B;
-  for (int f = threadIdx.x; f < groups * nt; f += hg::THREADS) {
+  for (int f = threadIdx.x; f < groups * nt; f += NT) {
     const int j = f / groups, c = f - j * groups;
     const int base = (c % s) + (c / s) * s * B;
     float* row = tile + j * ldt;
@@ -168,8 +174,8 @@ __device__ __forceinline__ void hg_had(float* tile, int ldt, int nt, int d, int 
   }
 }
 
-template <int BDT, int XDT>
-__global__ __launch_bounds__(hg::THREADS) void k_harp_gen(const void* __restrict__ xv_, void* __restrict__ yv_,
+template <int BDT, int XDT, int NT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_harp_gen(const void* __restrict__ xv_, void* __restrict__ yv_,
                                                          int64_t tokens, int64_t ldx, int64_t ldy, int d, int ldt,
                                                          int tt, const uint32_t* __restrict__ sbits,
                                                          const void* __restrict__ blocks, HgSched sc, int vec) {
@@ -183,15 +189,15 @@ __global__ __launch_bounds__(hg::THREADS) void k_harp_gen(const void* __restrict
   // tile goes to one thread; a thread's chunks are all requested before any
   // is written,
   // so the tile costs one memory latency rather than one per chunk (the
-  // tile's tt d values fit in LDS_FLOATS, so a thread has at most LDCH chunks).
-  constexpr int LDCH = (hg::LDS_FLOATS / 8 + hg::THREADS - 1) / hg::THREADS;
+  // tile's tt d values fit in lds_floats(NT), so a thread has at most LDCH chunks).
+  constexpr int LDCH = (hg::lds_floats(NT) / 8 + NT - 1) / NT;
   {
     constexpr int W = XDT == DT_F32 ? 8 : 4;  // 32-bit words per chunk
     uint32_t raw[LDCH][W];
     const int nf = nt * nch;
 #pragma unroll
     for (int u = 0; u < LDCH; ++u) {
-      const int f = threadIdx.x + u * hg::THREADS;
+      const int f = threadIdx.x + u * NT;
       if (f < nf) {
         const int j = f / nch, i0 = 8 * (f - j * nch);
         if (vec && i0 + 8 <= d) {
@@ -214,7 +220,7 @@ __global__ __launch_bounds__(hg::THREADS) void k_harp_gen(const void* __restrict
     }
 #pragma unroll
     for (int u = 0; u < LDCH; ++u) {
-      const int f = threadIdx.x + u * hg::THREADS;
+      const int f = threadIdx.x + u * NT;
       if (f < nf) {
         const int j = f / nch, i0 = 8 * (f - j * nch);
         const uint32_t sb = sbits ? (sbits[i0 >> 5] >> (i0 & 31)) & 0xffu : 0u;
@@ -244,10 +250,10 @@ __global__ __launch_bounds__(hg::THREADS) void k_harp_gen(const void* __restrict
   for (int t = 0; t < sc.n; ++t) {
     if (sc.had[t]) {
       switch (sc.b[t]) {
-        case 2: hg_had<2>(tile, ldt, nt, d, sc.s[t]); break;
-        case 4: hg_had<4>(tile, ldt, nt, d, sc.s[t]); break;
-        case 8: hg_had<8>(tile, ldt, nt, d, sc.s[t]); break;
-        case 16: hg_had<16>(tile, ldt, nt, d, sc.s[t]); break;
+        case 2: hg_had<2, NT>(tile, ldt, nt, d, sc.s[t]); break;
+        case 4: hg_had<4, NT>(tile, ldt, nt, d, sc.s[t]); break;
+        case 8: hg_had<8, NT>(tile, ldt, nt, d, sc.s[t]); break;
+        case 16: hg_had<16, NT>(tile, ldt, nt, d, sc.s[t]); break;
         default: break;
       }
       __syncthreads();
@@ -255,7 +261,7 @@ __global__ __launch_bounds__(hg::THREADS) void k_harp_gen(const void* __restrict
     }
     switch (sc.b[t]) {
 #define HG_CASE(B) \
-  case B: hg_stage<B, BDT>(tile, ldt, nt, d, sc.s[t], blocks, sc.off[t]); break;
+  case B: hg_stage<B, BDT, NT>(tile, ldt, nt, d, sc.s[t], blocks, sc.off[t]); break;
       HG_CASE(2) HG_CASE(3) HG_CASE(4) HG_CASE(5) HG_CASE(6) HG_CASE(7) HG_CASE(8) HG_CASE(9)
       HG_CASE(10) HG_CASE(11) HG_CASE(12) HG_CASE(13) HG_CASE(14) HG_CASE(15) HG_CASE(16)
 #undef HG_CASE
@@ -265,7 +271,7 @@ __global__ __launch_bounds__(hg::THREADS) void k_harp_gen(const void* __restrict
   }
 
   // ---- store: fp32 as is, or rounded once to bf16
-  for (int f = threadIdx.x; f < nt * nch; f += hg::THREADS) {
+  for (int f = threadIdx.x; f < nt * nch; f += NT) {
     const int j = f / nch, i0 = 8 * (f - j * nch);
     const float* row = tile + j * ldt;
     if constexpr (XDT == DT_F32) {
@@ -671,16 +677,26 @@ __global__ __launch_bounds__(hm::THREADS) void k_harp_mx(const uint16_t* __restr
 
 // Entry from the C ABI (arguments validated there): radices each in [2, 16],
 // product d <= 8192, precondition only for d a power of two.
-template <int BDT, int XDT>
-static void launch_hg(const void* x, void* y, int64_t tokens, int64_t ldx, int64_t ldy, int d, int ldt, int tt,
-                      const uint32_t* sbits, const void* blocks, const HgSched& sc, int vec, unsigned grid,
-                      size_t lds, hipStream_t s) {
-  static const bool a = hipFuncSetAttribute((const void*)k_harp_gen<BDT, XDT>,
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, hg::LDS_FLOATS * 4) ==
+template <int BDT, int XDT, int NT>
+static void launch_hg(const void* x, void* y, int64_t tokens, int64_t ldx, int64_t ldy, int d, int ldt,
+                      const uint32_t* sbits, const void* blocks, const HgSched& sc, int vec, hipStream_t s) {
+  static const bool a = hipFuncSetAttribute((const void*)k_harp_gen<BDT, XDT, NT>,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, hg::lds_floats(NT) * 4) ==
                         hipSuccess;
   (void)a;
-  hipLaunchKernelGGL((k_harp_gen<BDT, XDT>), dim3(grid), dim3(hg::THREADS), lds, s, x, y, tokens, ldx, ldy, d, ldt,
-                     tt, sbits, blocks, sc, vec);
+  const int tt = std::max(1, std::min(hg::MAXTT, hg::lds_floats(NT) / ldt));
+  const size_t lds = (size_t)tt * ldt * sizeof(float);
+  const unsigned grid = (unsigned)((tokens + tt - 1) / tt);
+  hipLaunchKernelGGL((k_harp_gen<BDT, XDT, NT>), dim3(grid), dim3(NT), lds, s, x, y, tokens, ldx, ldy, d, ldt, tt,
+                     sbits, blocks, sc, vec);
+}
+template <int NT>
+static void launch_hg_dt(const void* x, void* y, int xdt, int bdt, int64_t tokens, int64_t ldx, int64_t ldy, int d,
+                         int ldt, const uint32_t* sb, const void* blocks, const HgSched& sc, int vec, hipStream_t s) {
+  if (bdt == DT_F16 && xdt == DT_F32) launch_hg<DT_F16, DT_F32, NT>(x, y, tokens, ldx, ldy, d, ldt, sb, blocks, sc, vec, s);
+  else if (bdt == DT_F16) launch_hg<DT_F16, DT_BF16, NT>(x, y, tokens, ldx, ldy, d, ldt, sb, blocks, sc, vec, s);
+  else if (xdt == DT_F32) launch_hg<DT_F32, DT_F32, NT>(x, y, tokens, ldx, ldy, d, ldt, sb, blocks, sc, vec, s);
+  else launch_hg<DT_F32, DT_BF16, NT>(x, y, tokens, ldx, ldy, d, ldt, sb, blocks, sc, vec, s);
 }
 
 template <int BDT, int TT>
@@ -727,14 +743,11 @@ hipError_t launch_harp_gen(const void* x, void* y, int xdt, int64_t tokens, int 
   }
   sc.n = n;
   const int ldt = (hg::pos_h(d - 1) + 4) & ~3;
-  const int tt = std::max(1, std::min(hg::MAXTT, hg::LDS_FLOATS / ldt));
-  const size_t lds = (size_t)tt * ldt * sizeof(float);
   // 16-byte row accesses need a 16-byte aligned base and row stride on both sides
   const int esz = xdt == DT_F32 ? 4 : 2;
   const int vec = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15u) == 0 &&
                           (ldx * esz) % 16 == 0 && (ldy * esz) % 16 == 0
                       ? 1 : 0;
-  const unsigned grid = (unsigned)((tokens + tt - 1) / tt);
   const uint32_t* sb = precondition ? sbits : nullptr;
   // bf16 rows whose length is a multiple of 8 (16-byte chunks), with 16-byte
   // aligned rows and blocks, d <= 3072 and a mean radix of at least 4: the
@@ -755,10 +768,12 @@ hipError_t launch_harp_gen(const void* x, void* y, int xdt, int64_t tokens, int 
       return hipGetLastError();
     }
   }
-  if (bdt == DT_F16 && xdt == DT_F32) launch_hg<DT_F16, DT_F32>(x, y, tokens, ldx, ldy, d, ldt, tt, sb, blocks, sc, vec, grid, lds, s);
-  else if (bdt == DT_F16) launch_hg<DT_F16, DT_BF16>(x, y, tokens, ldx, ldy, d, ldt, tt, sb, blocks, sc, vec, grid, lds, s);
-  else if (xdt == DT_F32) launch_hg<DT_F32, DT_F32>(x, y, tokens, ldx, ldy, d, ldt, tt, sb, blocks, sc, vec, grid, lds, s);
-  else launch_hg<DT_F32, DT_BF16>(x, y, tokens, ldx, ldy, d, ldt, tt, sb, blocks, sc, vec, grid, lds, s);
+  // two 512-thread blocks per CU where half the tile still holds 4 tokens
+  // (d <= 4717): one block's row loads and stage-start coefficient waits
+  // overlap the other's stages; else one 1024-thread block with the whole
+  // tile (fewer tokens per tile would multiply the coefficient loads)
+  if (hg::lds_floats(512) / ldt >= 4) launch_hg_dt<512>(x, y, xdt, bdt, tokens, ldx, ldy, d, ldt, sb, blocks, sc, vec, s);
+  else launch_hg_dt<hg::THREADS>(x, y, xdt, bdt, tokens, ldx, ldy, d, ldt, sb, blocks, sc, vec, s);
   return hipGetLastError();
 }
 
