@@ -99,6 +99,9 @@ struct MxGeo {
       return ((y & 3) << 4) | (y >> 2);
     }
   }
+  // n = 4096: slot of chunk c minus slot of chunk 0, the same for every lane
+  // (chunk bits c0, c1 land on slot bits 4, 5 and c2 on bit 7)
+  static constexpr int slot_step(int c) { return ((c & 1) << 4) | (((c >> 1) & 1) << 5) | (((c >> 2) & 1) << 7); }
   // in-lane position of output register j' of out-block ob of tile group g
   static constexpr int out_off(int g, int ob, int jp) {
     return ((ob >> 1) & 1) | (((ob >> 2) & 1) << 1) | ((g & 1) << 2) | ((ob & 1) << 3) | (jp << 4) |
@@ -161,46 +164,6 @@ __global__ __launch_bounds__(MxGeo<LOGN>::THREADS) void k_rht_quant_mx(
   // each wave's next row, fetched straight into LDS while the current row is
   // transformed: [chunk][lane] x 16 bytes, the image of the register layout
   __shared__ u32x4 rowbuf[G::WPB][NC * 64];
-  {
-    const uint32_t* sp = sbits != nullptr ? sbits : kNoSigns;
-    for (int i = threadIdx.x; i < NC * 64; i += blockDim.x) {
-      const int c = i / 64, ll = i % 64;
-      const int p = G::chunk_pos(ll, c);
-      const uint32_t sbyte = (sp[p >> 5] >> (p & 31)) & 0xffu;
-      smask[i] = u32x4{pair_mask16(sbyte), pair_mask16(sbyte >> 2), pair_mask16(sbyte >> 4),
-                       pair_mask16(sbyte >> 6)};
-    }
-  }
-  __syncthreads();
-
-  // the four distinct 16x32 slices of H_128 (A operands): lane l holds
-  // row i = l % 16, columns k = 8 (l / 16) + j; T[o0][s] has entries
-  // (-1)^(s + popcount(i & k & 15) + o0 * (k >> 4))
-  u32x4 T[2][2];
-#pragma unroll
-  for (int o0 = 0; o0 < 2; ++o0)
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int k = 8 * (l >> 4) + 2 * d + h, i = l & 15;
-          const int par = (s + __builtin_popcount(i & k & 15) + o0 * (k >> 4)) & 1;
-          word |= (uint32_t)(par ? OP::NEG : OP::ONE) << (16 * h);
-        }
-        T[o0][s][d] = word;
-      }
-
-  // DPP coefficients and the accumulated sign rho of the lane
-  const int tw = G::twist(l);
-  float cf[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) cf[b] = ((tw >> b) & 1) ? -1.0f : 1.0f;
-  const bool rho = __builtin_popcount(tw) & 1;
-  const int ob_lane = G::out_block(l);
-
   const int64_t wave0 = (int64_t)blockIdx.x * G::WPB + wv;
   const int64_t wstride = (int64_t)gridDim.x * G::WPB;
   u32x4* buf = rowbuf[wv];
@@ -219,12 +182,75 @@ __global__ __launch_bounds__(MxGeo<LOGN>::THREADS) void k_rht_quant_mx(
           (const __attribute__((address_space(1))) void*)(wr + b * 1024 + src_off[b % NV]),
           (__attribute__((address_space(3))) void*)(buf + b * 64), 16, 0, 2 /* nt */);
   };
-  // LDS slot of chunk c of lane l
+  // LDS slot of chunk c of lane l; at n = 4096 the chunk bits enter the slot
+  // additively (a lane base plus a per-chunk constant), so the reads share
+  // one address register
   auto slot_of = [&](int c) {
-    const int m = G::chunk_pos(l, c) >> 3;
-    return (m >> 6) * 64 + G::sig(m >> 6, m & 63);
+    if constexpr (LOGN == 12) {
+      const int m0 = G::chunk_pos(l, 0) >> 3;
+      return (m0 >> 6) * 64 + G::sig(m0 >> 6, m0 & 63) + G::slot_step(c);
+    } else {
+      const int m = G::chunk_pos(l, c) >> 3;
+      return (m >> 6) * 64 + G::sig(m >> 6, m & 63);
+    }
   };
+  // the first row's copy is in flight while the block builds its sign masks
   if (wave0 < rows) fetch_row(wave0);
+  {
+    // every sign word is requested before any is used, so the block waits
+    // for one round trip (overlapping the row copy's), not one per pass
+    constexpr int NIT = NC * 64 / G::THREADS;
+    static_assert(NIT * G::THREADS == NC * 64, "sign-mask setup: whole passes");
+    const uint32_t* sp = sbits != nullptr ? sbits : kNoSigns;
+    uint32_t wd[NIT];
+    int pos[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int i = threadIdx.x + it * G::THREADS;
+      pos[it] = G::chunk_pos(i % 64, i / 64);
+      wd[it] = sp[pos[it] >> 5];
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const uint32_t sbyte = (wd[it] >> (pos[it] & 31)) & 0xffu;
+      smask[threadIdx.x + it * G::THREADS] = u32x4{pair_mask16(sbyte), pair_mask16(sbyte >> 2),
+                                                   pair_mask16(sbyte >> 4), pair_mask16(sbyte >> 6)};
+    }
+  }
+  // a barrier on the LDS writes only: the row copies stay in flight
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  // the four distinct 16x32 slices of H_128 (A operands): lane l holds
+  // row i = l % 16, columns k = 8 (l / 16) + j; T[o0][s] has entries
+  // (-1)^(s + popcount(i & k & 15) + o0 * (k >> 4)).  With q = l / 16 and
+  // j = 2d + h that exponent is s + o0 q1 + i3 q0 + i1 d0 + i2 d1 + i0 h
+  // (bits of q, d, i), so each word is a lane constant with both halves'
+  // sign bits (M) flipped by the terms in o0, s and d.
+  u32x4 T[2][2];
+  {
+    constexpr uint32_t M = 0x80008000u;
+    const int i = l & 15, q = l >> 4;
+    const uint32_t w0 = (uint32_t)OP::ONE * 0x10001u ^ ((i & 1) ? 0x80000000u : 0u);
+    const uint32_t e1 = ((i >> 1) & 1) ? M : 0u, e2 = ((i >> 2) & 1) ? M : 0u;
+    const uint32_t ed[4] = {0u, e1, e2, e1 ^ e2};
+#pragma unroll
+    for (int o0 = 0; o0 < 2; ++o0) {
+      const uint32_t x = w0 ^ ((((o0 & (q >> 1)) ^ ((i >> 3) & q)) & 1) ? M : 0u);
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) T[o0][s][d] = x ^ ed[d] ^ (s ? M : 0u);
+    }
+  }
+
+  // DPP coefficients and the accumulated sign rho of the lane
+  const int tw = G::twist(l);
+  float cf[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) cf[b] = ((tw >> b) & 1) ? -1.0f : 1.0f;
+  const bool rho = __builtin_popcount(tw) & 1;
+  const int ob_lane = G::out_block(l);
+
   for (int64_t row = wave0; row < rows; row += wstride) {
     u32x4 raw[NC];
     // The copies must have landed before any read of buf.  The compiler sees
