@@ -194,8 +194,12 @@ __global__ __launch_bounds__(MxGeo<LOGN>::THREADS) void k_rht_quant_mx(
       return (m >> 6) * 64 + G::sig(m >> 6, m & 63);
     }
   };
-  // the first row's copy is in flight while the block builds its sign masks
-  if (wave0 < rows) fetch_row(wave0);
+  // n = 4096 (a row or two per wave, latency-bound): the first row's copy is
+  // in flight while the block builds its sign masks.  n = 8192 (fourteen rows
+  // per wave at the benchmark size) measured about 1 % slower that way and
+  // copies after the set-up.
+  if constexpr (LOGN == 12)
+    if (wave0 < rows) fetch_row(wave0);
   {
     // every sign word is requested before any is used, so the block waits
     // for one round trip (overlapping the row copy's), not one per pass
@@ -217,8 +221,10 @@ __global__ __launch_bounds__(MxGeo<LOGN>::THREADS) void k_rht_quant_mx(
                                                    pair_mask16(sbyte >> 4), pair_mask16(sbyte >> 6)};
     }
   }
-  // a barrier on the LDS writes only: the row copies stay in flight
+  // a barrier on the LDS writes only (an n = 4096 row copy stays in flight)
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if constexpr (LOGN == 13)
+    if (wave0 < rows) fetch_row(wave0);
 
   // the four distinct 16x32 slices of H_128 (A operands): lane l holds
   // row i = l % 16, columns k = 8 (l / 16) + j; T[o0][s] has entries
