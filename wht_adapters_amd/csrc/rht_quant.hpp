@@ -337,14 +337,11 @@ __global__ __launch_bounds__(Geo<LOGN>::THREADS) void k_rht_dequant(
 #pragma unroll
     for (int k = 0; k < NG; ++k) in.hb[k] = SPAN == 1 ? sr[t * NG + k] : sr[t / SPAN];
   };
-  // rows of at most one wave: the first row's codes are in flight while the
-  // sign masks are built
-  constexpr bool ONE_WAVE = T <= 64;
+  // the first row's codes are in flight while the sign masks are built
   In ia;
-  if constexpr (ONE_WAVE)
-    if (blockIdx.x < ngroups) fetch_row(ia, blockIdx.x);
+  if (blockIdx.x < ngroups) fetch_row(ia, blockIdx.x);
   // output sign masks (S and the rho of the DPP butterflies) for the store layout
-  uint32_t sw[8], sb[8], m[8][4];
+  uint32_t sw[8], sb[8], m[8];
   int obase[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) obase[c] = G::TWO ? G::idxA(t, c * 8) : t * 64 + c * 8;
@@ -361,19 +358,14 @@ __global__ __launch_bounds__(Geo<LOGN>::THREADS) void k_rht_dequant(
     } else {
       if (rho_B<LOGN>(t)) sb[c] ^= 0xffu;
     }
-    if constexpr (ONE_WAVE) {
-      // one word per chunk: the signs of elements 2q and 2q + 1 on bits
-      // 15 - q and 31 - q, so (x << q) & 0x80008000 is pair q's mask (8
-      // registers instead of 32 keep four waves per SIMD with the prefetch)
-      uint32_t x = 0;
+    // one word per chunk: the signs of elements 2q and 2q + 1 on bits
+    // 15 - q and 31 - q, so (x << q) & 0x80008000 is pair q's mask (8
+    // registers instead of 32, room for the next row's codes)
+    uint32_t x = 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        x |= ((sb[c] >> (2 * q)) & 1u) << (15 - q) | ((sb[c] >> (2 * q + 1)) & 1u) << (31 - q);
-      m[c][0] = x;
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) m[c][q] = pair_mask16(sb[c] >> (2 * q));
-    }
+    for (int q = 0; q < 4; ++q)
+      x |= ((sb[c] >> (2 * q)) & 1u) << (15 - q) | ((sb[c] >> (2 * q + 1)) & 1u) << (31 - q);
+    m[c] = x;
   }
 
   auto do_row = [&](const In& in, int64_t g) {
@@ -411,27 +403,20 @@ __global__ __launch_bounds__(Geo<LOGN>::THREADS) void k_rht_dequant(
         for (int q = 0; q < 4; ++q) {
           const uint32_t p = DOUT == DT_BF16 ? pack_bf16(v[c * 8 + 2 * q], v[c * 8 + 2 * q + 1])
                                              : pack_f16(v[c * 8 + 2 * q], v[c * 8 + 2 * q + 1]);
-          wv[q] = p ^ (ONE_WAVE ? (m[c][0] << q) & 0x80008000u : m[c][q]);
+          wv[q] = p ^ ((m[c] << q) & 0x80008000u);
         }
         stg_dq<u32x4>(reinterpret_cast<uint16_t*>(orow) + i, wv);
       }
     }
   };
-  if constexpr (ONE_WAVE) {
-    // the next row's codes are requested before this row's arithmetic (a few
-    // registers; the two-wave rows of n = 8192 would lose a wave per SIMD to
-    // them)
-    for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
-      In ib;
-      if (g + gridDim.x < ngroups) fetch_row(ib, g + gridDim.x);
-      do_row(ia, g);
-      ia = ib;
-    }
-  } else {
-    for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
-      fetch_row(ia, g);
-      do_row(ia, g);
-    }
+  // the next row's codes are requested before this row's arithmetic (at
+  // n = 8192 they cost the fourth wave per SIMD, and still measured 4 %
+  // faster at 28672 rows: the code loads' latency was exposed every row)
+  for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
+    In ib;
+    if (g + gridDim.x < ngroups) fetch_row(ib, g + gridDim.x);
+    do_row(ia, g);
+    ia = ib;
   }
 }
 
