@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define WHTQ_ABI_VERSION 3
+#define WHTQ_ABI_VERSION 4
 
 typedef enum {
   WHTQ_OK = 0,
@@ -169,6 +169,52 @@ whtq_status qwha_adapter_forward(const void* x, whtq_dtype x_dtype, int64_t toke
                                  int64_t ldx, const int32_t* row_ptr, const int32_t* col_idx,
                                  const void* vals, whtq_dtype val_dtype, int64_t d_out, int64_t nnz,
                                  void* y, whtq_dtype y_dtype, int64_t ldy, void* stream);
+
+/*
+ * ---- Forward plans.  In [QWHA] 2.1 the support of F (its row_ptr and
+ * col_idx) is chosen once and then fixed while only the values train, so the
+ * forward's per-chunk bookkeeping, which depends on row_ptr alone (rows cut
+ * into segments of at most 128 entries and ordered by length for the
+ * gather), can be computed once and reused by every call and every token
+ * tile.  A plan holds it for one (tokens, d_out, nnz, row_ptr) on one device;
+ * it is an opaque device buffer the caller allocates.
+ *
+ * qwha_forward_plan_bytes -- bytes a plan needs for these sizes on the
+ *   current device (the split of F's rows across blocks follows the token
+ *   count and the device's CU count); 0 for d_in = 8192 (that kernel needs
+ *   no plan); -1 for invalid sizes (as in qwha_adapter_forward, tokens >= 1)
+ *   or when no device is present.
+ */
+int64_t qwha_forward_plan_bytes(int64_t tokens, int64_t d_in, int64_t d_out, int64_t nnz);
+
+/*
+ * qwha_forward_plan -- builds the plan into `plan` (device, 16-byte aligned,
+ *   plan_bytes >= qwha_forward_plan_bytes(...), caller-owned) from row_ptr
+ *   (device int32[d_out + 1], the CSR rules of qwha_adapter_forward) on
+ *   `stream`.  Reads nothing but row_ptr; asynchronous like the other device
+ *   calls.  d_in = 8192: returns WHTQ_OK and writes nothing.
+ *   Errors: WHTQ_EINVAL (sizes, null pointers, plan_bytes too small),
+ *   WHTQ_EALIGN, WHTQ_EUNSUPPORTED (d_in, d_out > 4096), WHTQ_EHIP.
+ */
+whtq_status qwha_forward_plan(int64_t tokens, int64_t d_in, const int32_t* row_ptr, int64_t d_out, int64_t nnz,
+                              void* plan, int64_t plan_bytes, void* stream);
+
+/*
+ * qwha_adapter_forward_planned -- qwha_adapter_forward with a plan (or
+ *   plan = NULL, the same as qwha_adapter_forward).  Arguments, layouts and
+ *   errors as qwha_adapter_forward, plus: plan 16-byte aligned, plan_bytes
+ *   its size (>= 256 when plan is not NULL).  Results are bit-identical with
+ *   and without a plan.  A plan whose header does not match (another d_out,
+ *   nnz or split of the rows, one that ran out of room, or one larger than
+ *   plan_bytes) is ignored and the call prepares its chunks itself; a plan
+ *   built from a different row_ptr with the same sizes gives undefined
+ *   results, so rebuild it whenever the support changes.
+ */
+whtq_status qwha_adapter_forward_planned(const void* x, whtq_dtype x_dtype, int64_t tokens, int64_t d_in,
+                                         int64_t ldx, const int32_t* row_ptr, const int32_t* col_idx,
+                                         const void* vals, whtq_dtype val_dtype, int64_t d_out, int64_t nnz,
+                                         const void* plan, int64_t plan_bytes, void* y, whtq_dtype y_dtype,
+                                         int64_t ldy, void* stream);
 
 /*
  * ---- QWHA adapter backward (training).  [QWHA] 2.1 makes the adapter linear

@@ -39,13 +39,14 @@ def test_exports_every_declared_symbol(lib):
                           "harp_build_blocks", "rht_lowbit_gemv", "qwha_init_error_coeffs",
                           "qwha_init_gram", "qwha_init_channel_errors", "qwha_init_allocate",
                           "qwha_init_select", "qwha_init_refine", "qwha_adapter_grad_values_noalloc",
-                          "whtq_stream_probe"}
+                          "whtq_stream_probe", "qwha_forward_plan_bytes", "qwha_forward_plan",
+                          "qwha_adapter_forward_planned"}
     for nm in names:
         assert hasattr(lib, nm), nm
 
 
 def test_version_and_strings(lib):
-    assert lib.whtq_abi_version() == 3
+    assert lib.whtq_abi_version() == 4
     for s in range(6):
         assert lib.whtq_status_string(s)
     assert b"unknown" in lib.whtq_status_string(99)
@@ -179,11 +180,51 @@ def test_harp_validation(lib):
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="needs a host without a GPU")
+def qwp(lib, x=P, tokens=8, d_in=4096, ldx=4096, rp=P, d_out=4096, nnz=100, plan=P, plan_bytes=1 << 20):
+    return lib.qwha_adapter_forward_planned(x, 1, tokens, d_in, ldx, rp, P, P, 1, d_out, nnz, plan, plan_bytes,
+                                            P, 1, 4096, NULL)
+
+
+def plan(lib, tokens=8, d_in=4096, rp=P, d_out=4096, nnz=100, out=P, nbytes=1 << 20):
+    return lib.qwha_forward_plan(tokens, d_in, rp, d_out, nnz, out, nbytes, NULL)
+
+
+def test_qwha_forward_plan_validation(lib):
+    """Forward plans: sizes, pointers and alignment are checked before the
+    device; d_in = 8192 needs no plan (size 0, building is a no-op)."""
+    nb = lib.qwha_forward_plan_bytes
+    assert nb(0, 4096, 4096, 100) == -1           # tokens >= 1
+    assert nb(8, 3000, 4096, 100) == -1           # d_in a power of two
+    assert nb(8, 4096, 5000, 100) == -1           # d_out <= 4096
+    assert nb(8, 64, 4, 257) == -1                # nnz > d_in d_out
+    assert nb(8, 8192, 4096, 100) == 0
+    assert plan(lib, tokens=0) == EINVAL
+    assert plan(lib, rp=NULL) == EINVAL
+    assert plan(lib, rp=ctypes.c_void_p(0x10002)) == EALIGN
+    assert plan(lib, d_in=3000) == EUNSUP
+    assert plan(lib, d_out=5000) == EUNSUP
+    assert plan(lib, nbytes=-1) == EINVAL
+    assert plan(lib, d_in=8192) == OK             # nothing to plan
+    assert plan(lib, out=NULL) == EINVAL
+    assert plan(lib, out=P_MIS) == EALIGN
+    # the planned forward: the forward's rules, then the plan's
+    assert qwp(lib, ldx=100) == EINVAL
+    assert qwp(lib, d_in=3000, ldx=3000) == EUNSUP
+    assert qwp(lib, x=P_MIS) == EALIGN
+    assert qwp(lib, plan_bytes=100) == EINVAL     # a plan holds at least its 256-byte header
+    assert qwp(lib, plan_bytes=-1) == EINVAL
+    assert qwp(lib, plan=P_MIS) == EALIGN
+    assert qwp(lib, tokens=0) == OK
+    assert qwp(lib, tokens=0, plan=NULL, plan_bytes=0) == OK
+
+
 def test_valid_call_without_device_is_ehip(lib):
     assert wht(lib) == EHIP
     assert lib.whtq_last_hip_error() != 0
     assert q(lib) == EHIP and dq(lib) == EHIP
     assert qw(lib) == EHIP and hp(lib) == EHIP
+    assert qwp(lib) == EHIP and plan(lib) == EHIP
+    assert lib.qwha_forward_plan_bytes(8, 4096, 4096, 100) == -1  # the split follows the device's CUs
 
 
 # ---- QWHA backward entry points

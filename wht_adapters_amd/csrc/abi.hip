@@ -28,7 +28,10 @@ hipError_t launch_rht_gemv(int logn, int bits, int logg, const void* x, int64_t 
                            void* y, int64_t ldy, hipStream_t s);
 hipError_t launch_qwha(const void* x, int64_t tokens, int64_t d_in, int64_t ldx, const int32_t* row_ptr,
                        const int32_t* col_idx, const void* vals, int val_dt, int64_t d_out, int64_t nnz,
-                       void* y, int64_t ldy, hipStream_t s);
+                       void* y, int64_t ldy, const void* plan, int64_t plan_bytes, hipStream_t s);
+int64_t qwha_fwd_plan_bytes(int64_t tokens, int64_t d_out, int64_t nnz);
+hipError_t launch_qwha_fwd_plan(int64_t tokens, const int32_t* row_ptr, int64_t d_out, int64_t nnz, void* plan,
+                                int64_t plan_bytes, hipStream_t s);
 hipError_t launch_qwha_bwd_input(const void* dy, int64_t tokens, int64_t lddy, int64_t d_out,
                                  const int32_t* t_row_ptr, const int32_t* t_col_idx, const void* t_vals,
                                  int val_dt, int64_t d_in, int64_t nnz, void* dx, int64_t lddx, hipStream_t s);
@@ -238,10 +241,11 @@ whtq_status rht_lowbit_gemv(const void* x, int64_t tokens, int64_t ldx, const ui
                                     (hipStream_t)stream));
 }
 
-whtq_status qwha_adapter_forward(const void* x, whtq_dtype x_dtype, int64_t tokens, int64_t d_in,
-                                 int64_t ldx, const int32_t* row_ptr, const int32_t* col_idx,
-                                 const void* vals, whtq_dtype val_dtype, int64_t d_out, int64_t nnz,
-                                 void* y, whtq_dtype y_dtype, int64_t ldy, void* stream) {
+// the argument rules of qwha_adapter_forward (shared with the planned form)
+static whtq_status qwha_fwd_check(const void* x, whtq_dtype x_dtype, int64_t tokens, int64_t d_in, int64_t ldx,
+                                  const int32_t* row_ptr, const int32_t* col_idx, const void* vals,
+                                  whtq_dtype val_dtype, int64_t d_out, int64_t nnz, void* y, whtq_dtype y_dtype,
+                                  int64_t ldy) {
   if (!dt_valid(x_dtype) || !dt_valid(val_dtype) || !dt_valid(y_dtype)) return WHTQ_EINVAL;
   if (tokens < 0 || d_in < 1 || d_out < 1 || nnz < 0 || ldx < d_in || ldy < d_out) return WHTQ_EINVAL;
   if (nnz > d_in * d_out) return WHTQ_EINVAL;
@@ -252,11 +256,54 @@ whtq_status qwha_adapter_forward(const void* x, whtq_dtype x_dtype, int64_t toke
   if (val_dtype != WHTQ_BF16 && val_dtype != WHTQ_F32) return WHTQ_EUNSUPPORTED;
   if (!rows_aligned(x, d_in, ldx, 2) || !rows_aligned(y, d_out, ldy, 2)) return WHTQ_EALIGN;
   if ((reinterpret_cast<uintptr_t>(row_ptr) & 3u) || !aligned16(col_idx) || !aligned16(vals)) return WHTQ_EALIGN;
-  if (tokens == 0) return WHTQ_OK;
+  return WHTQ_OK;
+}
+
+whtq_status qwha_adapter_forward(const void* x, whtq_dtype x_dtype, int64_t tokens, int64_t d_in,
+                                 int64_t ldx, const int32_t* row_ptr, const int32_t* col_idx,
+                                 const void* vals, whtq_dtype val_dtype, int64_t d_out, int64_t nnz,
+                                 void* y, whtq_dtype y_dtype, int64_t ldy, void* stream) {
+  return qwha_adapter_forward_planned(x, x_dtype, tokens, d_in, ldx, row_ptr, col_idx, vals, val_dtype, d_out, nnz,
+                                      nullptr, 0, y, y_dtype, ldy, stream);
+}
+
+int64_t qwha_forward_plan_bytes(int64_t tokens, int64_t d_in, int64_t d_out, int64_t nnz) {
+  if (tokens < 1 || d_out < 1 || d_out > 4096 || nnz < 0 || nnz > d_in * d_out) return -1;
+  if (ilog2_pow2(d_in) < 6 || ilog2_pow2(d_in) > 13) return -1;
+  if (d_in > 4096) return 0;  // the d_in = 8192 kernel prepares nothing per chunk
+  if (need_device() != WHTQ_OK) return -1;
+  return qwha_fwd_plan_bytes(tokens, d_out, nnz);
+}
+
+whtq_status qwha_forward_plan(int64_t tokens, int64_t d_in, const int32_t* row_ptr, int64_t d_out, int64_t nnz,
+                              void* plan, int64_t plan_bytes, void* stream) {
+  if (tokens < 1 || d_out < 1 || nnz < 0 || nnz > d_in * d_out || plan_bytes < 0) return WHTQ_EINVAL;
+  if (!row_ptr || (reinterpret_cast<uintptr_t>(row_ptr) & 3u)) return row_ptr ? WHTQ_EALIGN : WHTQ_EINVAL;
+  if (ilog2_pow2(d_in) < 6 || ilog2_pow2(d_in) > 13 || d_out > 4096) return WHTQ_EUNSUPPORTED;
+  if (d_in > 4096) return WHTQ_OK;  // nothing to plan
+  if (!plan) return WHTQ_EINVAL;
+  if (!aligned16(plan)) return WHTQ_EALIGN;
   whtq_status st = need_device();
   if (st != WHTQ_OK) return st;
+  if (plan_bytes < qwha_fwd_plan_bytes(tokens, d_out, nnz)) return WHTQ_EINVAL;
+  return hip_status(launch_qwha_fwd_plan(tokens, row_ptr, d_out, nnz, plan, plan_bytes, (hipStream_t)stream));
+}
+
+whtq_status qwha_adapter_forward_planned(const void* x, whtq_dtype x_dtype, int64_t tokens, int64_t d_in,
+                                         int64_t ldx, const int32_t* row_ptr, const int32_t* col_idx,
+                                         const void* vals, whtq_dtype val_dtype, int64_t d_out, int64_t nnz,
+                                         const void* plan, int64_t plan_bytes, void* y, whtq_dtype y_dtype,
+                                         int64_t ldy, void* stream) {
+  whtq_status st = qwha_fwd_check(x, x_dtype, tokens, d_in, ldx, row_ptr, col_idx, vals, val_dtype, d_out, nnz, y,
+                                  y_dtype, ldy);
+  if (st != WHTQ_OK) return st;
+  if (plan_bytes < 0 || (plan && plan_bytes < 256)) return WHTQ_EINVAL;
+  if (plan && !aligned16(plan)) return WHTQ_EALIGN;
+  if (tokens == 0) return WHTQ_OK;
+  st = need_device();
+  if (st != WHTQ_OK) return st;
   return hip_status(launch_qwha(x, tokens, d_in, ldx, row_ptr, col_idx, vals, val_dtype, d_out, nnz, y, ldy,
-                                (hipStream_t)stream));
+                                plan, plan ? plan_bytes : 0, (hipStream_t)stream));
 }
 
 whtq_status qwha_csr_transpose(const int32_t* row_ptr, const int32_t* col_idx, int64_t d_out, int64_t d_in,

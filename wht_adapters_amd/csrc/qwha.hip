@@ -532,15 +532,16 @@ static float qw_width_scale(int64_t d_in) {
 
 hipError_t launch_qwha_fwd(const void* x, int64_t tokens, int64_t d_in, int64_t ldx, const int32_t* row_ptr,
                            const int32_t* col_idx, const void* vals, int val_dt, int64_t d_out, int64_t nnz, void* y,
-                           int64_t ldy, hipStream_t s);
+                           int64_t ldy, const void* plan, int64_t plan_bytes, hipStream_t s);
 
 // d_in <= 4096 runs the 16-token matrix-core kernel (qwha_fwd.hip); d_in =
 // 8192 the split-transform kernel above
 hipError_t launch_qwha(const void* x, int64_t tokens, int64_t d_in, int64_t ldx, const int32_t* row_ptr,
                        const int32_t* col_idx, const void* vals, int val_dt, int64_t d_out, int64_t nnz,
-                       void* y, int64_t ldy, hipStream_t s) {
+                       void* y, int64_t ldy, const void* plan, int64_t plan_bytes, hipStream_t s) {
   if (d_in <= 4096)
-    return launch_qwha_fwd(x, tokens, d_in, ldx, row_ptr, col_idx, vals, val_dt, d_out, nnz, y, ldy, s);
+    return launch_qwha_fwd(x, tokens, d_in, ldx, row_ptr, col_idx, vals, val_dt, d_out, nnz, y, ldy, plan,
+                           plan_bytes, s);
   // 16-byte output stores need a 16-byte aligned base and row stride
   const int vec_out = ((reinterpret_cast<uintptr_t>(y) & 15u) == 0 && (ldy * 2) % 16 == 0) ? 1 : 0;
   launch_w<false>(d_in == 8192, val_dt, x, tokens, ldx, (int)d_in, row_ptr, col_idx, vals, (int)d_out, (int)nnz,

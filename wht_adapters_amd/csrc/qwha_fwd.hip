@@ -69,6 +69,23 @@ constexpr int EXP = SPLIT + PSLOTS;             // int [TT]: per-token exponents
 constexpr int MISC = EXP + TT * 4;              // int [8]: row range, chunk size, segments, split rows
 constexpr int BYTES = MISC + 32;
 static_assert(BYTES <= 160 * 1024, "LDS map");
+
+// Forward plans (qwha_forward_plan): a chunk's segment lists depend only on
+// row_ptr and the row range, so they can be built once for a fixed support
+// and reused by every token tile.  A record is the LDS image [SBEG, EXP) of
+// the chunk's lists followed by {chunk rows, segments, split rows, 0}; a
+// plan is a header of PLAN_HDR bytes (int32 fields below) and then, per
+// split, `cap` records of REC_BYTES.
+constexpr int REC_IMG = EXP - SBEG;
+constexpr int REC_BYTES = (REC_IMG + 16 + 255) / 256 * 256;
+constexpr int REC_THREADS = REC_IMG / 16 + 1;  // one 16-byte piece per thread, the counts last
+constexpr int PLAN_HDR = 256;
+constexpr int PLAN_MAGIC = 0x4c505751;  // "QWPL"
+// header fields: magic, d_out, nnz, splits, cap, bytes used; per split s:
+// status (0 complete, 1 more chunks than cap) and records written
+enum { H_MAGIC = 0, H_DOUT, H_NNZ, H_SPLITS, H_CAP, H_USED, H_STATUS = 16, H_NREC = 32 };
+static_assert(REC_IMG % 16 == 0 && SBEG % 16 == 0 && REC_THREADS <= THREADS, "plan record pieces");
+static_assert(H_NREC + 8 <= PLAN_HDR / 4, "plan header");
 static_assert(NZ / (16 * SEG) + 1 <= PSLOTS && PSLOTS < 128, "a row of NZ entries fits the partial slots");
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -119,13 +136,19 @@ template <> struct FVal<DT_F32> {
   static __device__ __forceinline__ float get(const raw& r, int q) { return r[q]; }
 };
 
-template <int VALDT>
+// BUILD: one block per split writes the chunks' segment lists to plan_out
+// (no tokens).  Otherwise a valid plan for this split (header matching d_out,
+// nnz, splits, complete, within plan_bytes) replaces the per-chunk
+// preparation; without one the block prepares each chunk itself.
+template <int VALDT, bool BUILD>
 __global__ __launch_bounds__(qf::THREADS) void k_qwha_fwd(const uint16_t* __restrict__ x, int64_t tokens, int64_t ldx,
                                                           int in_cols, const int32_t* __restrict__ row_ptr,
                                                           const int32_t* __restrict__ col_idx,
                                                           const void* __restrict__ vals, int d_out, int nnz,
                                                           uint16_t* __restrict__ y, int64_t ldy, int vec,
-                                                          float wscale, int tiles, int splits) {
+                                                          float wscale, int tiles, int splits,
+                                                          const uint8_t* __restrict__ plan, int64_t plan_bytes,
+                                                          uint8_t* __restrict__ plan_out, int plan_cap) {
   using V = FVal<VALDT>;
   constexpr int TT = qf::TT;
   extern __shared__ __align__(16) uint8_t smem[];
@@ -149,6 +172,24 @@ __global__ __launch_bounds__(qf::THREADS) void k_qwha_fwd(const uint16_t* __rest
   uint16_t* splitrows = reinterpret_cast<uint16_t*>(smem + qf::SPLIT);
   int* texp = reinterpret_cast<int*>(smem + qf::EXP);
   int* misc = reinterpret_cast<int*>(smem + qf::MISC);
+
+  // ---- this split's records, if a plan is given and matches (the header
+  // is the same for every thread: scalar loads)
+  const uint8_t* prec = nullptr;
+  int nrec = 0;  // records of this split
+  if constexpr (!BUILD) {
+    if (plan != nullptr) {
+      const int* h = reinterpret_cast<const int*>(plan);
+      const int cap = h[qf::H_CAP];
+      if (h[qf::H_MAGIC] == qf::PLAN_MAGIC && h[qf::H_DOUT] == d_out && h[qf::H_NNZ] == nnz &&
+          h[qf::H_SPLITS] == splits && split < 8 && h[qf::H_STATUS + split] == 0 && cap >= 0 &&
+          h[qf::H_NREC + split] >= 0 && h[qf::H_NREC + split] <= cap && (int64_t)h[qf::H_USED] <= plan_bytes) {
+        prec = plan + qf::PLAN_HDR + (size_t)split * (size_t)cap * qf::REC_BYTES;
+        nrec = h[qf::H_NREC + split];
+      }
+    }
+  }
+  const bool planned = prec != nullptr;
 
   // ---- the block's rows: [lower_bound(row_ptr, nnz s / S)] rounded down to
   // a multiple of 8 (aligned output stores), for s = split and split + 1
@@ -184,14 +225,18 @@ __global__ __launch_bounds__(qf::THREADS) void k_qwha_fwd(const uint16_t* __rest
   int* rps = reinterpret_cast<int*>(smem + qf::PART);
   static_assert((qf::CHUNK + 1) * 4 <= qf::PSLOTS * qf::TT * 4, "row_ptr slice in the partial slots");
   static_assert(qf::CHUNK + 1 <= qf::THREADS, "one row_ptr entry per thread");
-  const bool stage0 = r_lo < r_hi && tid <= min(qf::CHUNK, r_hi - r_lo);
+  const bool stage0 = !planned && r_lo < r_hi && tid <= min(qf::CHUNK, r_hi - r_lo);
   const int rp0 = stage0 ? row_ptr[r_lo + tid] : 0;
+  // with a plan: the first chunk's record instead (one 16-byte piece per thread)
+  u32x4 rec{0u, 0u, 0u, 0u};
+  int ci = 0;
+  if (planned && r_lo < r_hi && nrec > 0 && tid < qf::REC_THREADS) rec = ldg<u32x4>(prec + 16 * tid);
 
   // ---- the token rows (one wave per token; each 16-byte load is the A
   // operand of pass 1: lane (q, r) holds M[16 ab + r][32 kb + 8 q + 0..7])
   const int r16 = lane & 15, q4 = lane >> 4;
   u32x4 xa[4][2];
-  {
+  if constexpr (!BUILD) {
     const int64_t tok = tok0 + wave;
     const uint16_t* xr = x + (tok < tokens ? tok : 0) * ldx;
 #pragma unroll
@@ -321,7 +366,67 @@ __global__ __launch_bounds__(qf::THREADS) void k_qwha_fwd(const uint16_t* __rest
     __syncthreads();
     nseg = misc[3];
   };
-  if (r_lo < r_hi) prep(r_lo);
+  // a chunk from its plan record: the lists into LDS, the counts from the
+  // record's last piece; the next record is requested now and written after
+  // the gather
+  auto use_rec = [&](int base) {
+    if (tid < qf::REC_THREADS - 1) {
+      *reinterpret_cast<u32x4*>(smem + qf::SBEG + 16 * tid) = rec;
+    } else if (tid == qf::REC_THREADS - 1) {
+      misc[2] = (int)rec[0];
+      misc[3] = (int)rec[1];
+      misc[4] = (int)rec[2];
+    }
+    __syncthreads();
+    // a plan built from another row_ptr of the same sizes is documented as
+    // undefined results; the clamp and the record count keep even that in
+    // bounds (at least one row per chunk, the stores inside the split)
+    cn = max(1, min(misc[2], r_hi - base));
+    nseg = misc[3];
+    nbase = base + cn;
+    ++ci;
+    if (nbase < r_hi && ci < nrec && tid < qf::REC_THREADS)
+      rec = ldg<u32x4>(prec + (size_t)ci * qf::REC_BYTES + 16 * tid);
+  };
+  if (r_lo < r_hi) {
+    if (planned) use_rec(r_lo);
+    else prep(r_lo);
+  }
+
+  if constexpr (BUILD) {
+    // ---- the plan: each prepared chunk's LDS image and counts, in order
+    int nw = 0, status = 0;
+    for (int base = r_lo; base < r_hi;) {
+      if (nw == plan_cap) {
+        status = 1;
+        break;
+      }
+      uint8_t* dst = plan_out + qf::PLAN_HDR + ((size_t)split * (size_t)plan_cap + nw) * qf::REC_BYTES;
+      if (tid < qf::REC_THREADS - 1)
+        *reinterpret_cast<u32x4*>(dst + 16 * tid) = *reinterpret_cast<const u32x4*>(smem + qf::SBEG + 16 * tid);
+      else if (tid == qf::REC_THREADS - 1)
+        *reinterpret_cast<u32x4*>(dst + 16 * tid) = u32x4{(uint32_t)cn, (uint32_t)nseg, (uint32_t)misc[4], 0u};
+      ++nw;
+      if (tid <= navail && nbase < r_hi) rps[tid] = nrp;
+      base = nbase;
+      __syncthreads();  // every piece read before the next chunk's lists overwrite them
+      if (base < r_hi) prep(base);
+    }
+    if (tid == 0) {
+      int* h = reinterpret_cast<int*>(plan_out);
+      h[qf::H_STATUS + split] = status;
+      h[qf::H_NREC + split] = nw;
+      if (split == 0) {
+        h[qf::H_MAGIC] = qf::PLAN_MAGIC;
+        h[qf::H_DOUT] = d_out;
+        h[qf::H_NNZ] = nnz;
+        h[qf::H_SPLITS] = splits;
+        h[qf::H_CAP] = plan_cap;
+        h[qf::H_USED] = (int)(qf::PLAN_HDR + (int64_t)splits * plan_cap * qf::REC_BYTES);
+      }
+    }
+    return;
+  }
 
   // ---- 1-2. the token's transform on the matrix cores, into the Z planes
   {
@@ -576,47 +681,79 @@ __global__ __launch_bounds__(qf::THREADS) void k_qwha_fwd(const uint16_t* __rest
         }
       }
     }
-    if (tid <= navail && nbase < r_hi) rps[tid] = nrp;  // the partial slots are read no more
+    if (!planned && tid <= navail && nbase < r_hi) rps[tid] = nrp;  // the partial slots are read no more
     base = nbase;
     __syncthreads();  // the next chunk reuses the lists and the output buffer
-    if (base < r_hi) prep(base);
+    if (base < r_hi) {
+      if (planned) use_rec(base);
+      else prep(base);
+    }
   }
 }
 
-template <int VALDT>
+template <int VALDT, bool BUILD>
 static void launch_fwd(const void* x, int64_t tokens, int64_t ldx, int in_cols, const int32_t* row_ptr,
                        const int32_t* col_idx, const void* vals, int d_out, int nnz, void* y, int64_t ldy, int vec,
-                       float wscale, int tiles, int splits, hipStream_t s) {
-  static const bool attr = hipFuncSetAttribute((const void*)k_qwha_fwd<VALDT>,
+                       float wscale, int tiles, int splits, const void* plan, int64_t plan_bytes, void* plan_out,
+                       int plan_cap, hipStream_t s) {
+  static const bool attr = hipFuncSetAttribute((const void*)k_qwha_fwd<VALDT, BUILD>,
                                                hipFuncAttributeMaxDynamicSharedMemorySize, qf::BYTES) == hipSuccess;
   (void)attr;
-  hipLaunchKernelGGL(k_qwha_fwd<VALDT>, dim3((unsigned)tiles * (unsigned)splits), dim3(qf::THREADS), qf::BYTES, s,
-                     (const uint16_t*)x, tokens, ldx, in_cols, row_ptr, col_idx, vals, d_out, nnz, (uint16_t*)y, ldy,
-                     vec, wscale, tiles, splits);
+  hipLaunchKernelGGL((k_qwha_fwd<VALDT, BUILD>), dim3((unsigned)tiles * (unsigned)splits), dim3(qf::THREADS),
+                     qf::BYTES, s, (const uint16_t*)x, tokens, ldx, in_cols, row_ptr, col_idx, vals, d_out, nnz,
+                     (uint16_t*)y, ldy, vec, wscale, tiles, splits, (const uint8_t*)plan, plan_bytes,
+                     (uint8_t*)plan_out, plan_cap);
 }
 
 int device_cu_count(int dev);
 
-// d_in a power of two in [64, 4096]
-hipError_t launch_qwha_fwd(const void* x, int64_t tokens, int64_t d_in, int64_t ldx, const int32_t* row_ptr,
-                           const int32_t* col_idx, const void* vals, int val_dt, int64_t d_out, int64_t nnz, void* y,
-                           int64_t ldy, hipStream_t s) {
-  const int vec = ((reinterpret_cast<uintptr_t>(y) & 15u) == 0 && (ldy * 2) % 16 == 0) ? 1 : 0;
+// row splits: enough blocks for one per CU, at most 8, none past the rows
+static int64_t fwd_splits(int64_t tokens, int64_t d_out) {
   const int64_t tiles = (tokens + qf::TT - 1) / qf::TT;
   int dev = 0;
   (void)hipGetDevice(&dev);
   const int64_t cus = device_cu_count(dev);
-  // row splits: enough blocks for one per CU, at most 8, none past the rows
   int64_t splits = std::min<int64_t>(8, std::max<int64_t>(1, (cus + tiles - 1) / tiles));
-  splits = std::max<int64_t>(1, std::min<int64_t>(splits, (d_out + 7) / 8));
+  return std::max<int64_t>(1, std::min<int64_t>(splits, (d_out + 7) / 8));
+}
+
+// Records per split a plan holds: a chunk ends at CHUNK rows or where the
+// next row's segments would overflow the PSLOTS partial slots.  Split rows
+// have more than 125 entries and at most one segment per 42 of them, and two
+// consecutive chunks that end early hold more than PSLOTS segments together,
+// so nnz / 2352 + 1 early ends cover any support; the rest is slack.
+static int64_t fwd_plan_cap(int64_t d_out, int64_t nnz) { return (d_out + qf::CHUNK - 1) / qf::CHUNK + nnz / 2048 + 4; }
+
+// bytes of a plan for these sizes on the current device (d_in <= 4096 only)
+int64_t qwha_fwd_plan_bytes(int64_t tokens, int64_t d_out, int64_t nnz) {
+  return qf::PLAN_HDR + fwd_splits(tokens, d_out) * fwd_plan_cap(d_out, nnz) * qf::REC_BYTES;
+}
+
+hipError_t launch_qwha_fwd_plan(int64_t tokens, const int32_t* row_ptr, int64_t d_out, int64_t nnz, void* plan,
+                                int64_t plan_bytes, hipStream_t s) {
+  const int64_t splits = fwd_splits(tokens, d_out);
+  const int64_t cap = std::min<int64_t>(fwd_plan_cap(d_out, nnz), (plan_bytes - qf::PLAN_HDR) / (splits * qf::REC_BYTES));
+  if (cap < 0 || qf::PLAN_HDR + splits * cap * qf::REC_BYTES > INT32_MAX) return hipErrorInvalidValue;
+  launch_fwd<DT_F32, true>(nullptr, 0, 0, 0, row_ptr, nullptr, nullptr, (int)d_out, (int)nnz, nullptr, 0, 0, 1.0f, 1,
+                           (int)splits, nullptr, 0, plan, (int)cap, s);
+  return hipGetLastError();
+}
+
+// d_in a power of two in [64, 4096]; plan may be null
+hipError_t launch_qwha_fwd(const void* x, int64_t tokens, int64_t d_in, int64_t ldx, const int32_t* row_ptr,
+                           const int32_t* col_idx, const void* vals, int val_dt, int64_t d_out, int64_t nnz, void* y,
+                           int64_t ldy, const void* plan, int64_t plan_bytes, hipStream_t s) {
+  const int vec = ((reinterpret_cast<uintptr_t>(y) & 15u) == 0 && (ldy * 2) % 16 == 0) ? 1 : 0;
+  const int64_t tiles = (tokens + qf::TT - 1) / qf::TT;
+  const int64_t splits = fwd_splits(tokens, d_out);
   if (tiles * splits > INT32_MAX) return hipErrorInvalidValue;
   const float wscale = (float)(64.0 / std::sqrt((double)d_in));
   if (val_dt == DT_BF16)
-    launch_fwd<DT_BF16>(x, tokens, ldx, (int)d_in, row_ptr, col_idx, vals, (int)d_out, (int)nnz, y, ldy, vec, wscale,
-                        (int)tiles, (int)splits, s);
+    launch_fwd<DT_BF16, false>(x, tokens, ldx, (int)d_in, row_ptr, col_idx, vals, (int)d_out, (int)nnz, y, ldy, vec,
+                               wscale, (int)tiles, (int)splits, plan, plan_bytes, nullptr, 0, s);
   else
-    launch_fwd<DT_F32>(x, tokens, ldx, (int)d_in, row_ptr, col_idx, vals, (int)d_out, (int)nnz, y, ldy, vec, wscale,
-                       (int)tiles, (int)splits, s);
+    launch_fwd<DT_F32, false>(x, tokens, ldx, (int)d_in, row_ptr, col_idx, vals, (int)d_out, (int)nnz, y, ldy, vec,
+                              wscale, (int)tiles, (int)splits, plan, plan_bytes, nullptr, 0, s);
   return hipGetLastError();
 }
 

@@ -44,6 +44,9 @@ _SIG = {
     "whtq_stream_probe": [_vp, _i64, _vp, _i64, _vp],
     "qwha_adapter_grad_values_noalloc": [_vp, _vp, _int, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp,
                                          _vp],
+    "qwha_forward_plan": [_i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp],
+    "qwha_adapter_forward_planned": [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _int, _i64, _i64, _vp, _i64,
+                                     _vp, _int, _i64, _vp],
 }
 for _name, _args in _SIG.items():
     _f = getattr(_lib, _name)
@@ -51,6 +54,8 @@ for _name, _args in _SIG.items():
     _f.restype = _int
 _lib.qwha_grad_values_workspace_bytes.argtypes = [_i64, _i64, _i64]
 _lib.qwha_grad_values_workspace_bytes.restype = _i64
+_lib.qwha_forward_plan_bytes.argtypes = [_i64, _i64, _i64, _i64]
+_lib.qwha_forward_plan_bytes.restype = _i64
 _lib.whtq_status_string.argtypes = [_int]
 _lib.whtq_status_string.restype = ctypes.c_char_p
 _lib.whtq_last_hip_error.restype = _int
@@ -202,8 +207,33 @@ def rht_lowbit_gemv(x, codes, scales, signs, bits, group, out=None):
     return out
 
 
-def qwha_adapter_forward(x, row_ptr, col_idx, vals, d_out, out=None):
-    """y = (x Hn) F^T with F [d_out x d_in] in CSR (int32 row_ptr / col_idx)."""
+def qwha_forward_plan(tokens, d_in, row_ptr, d_out, nnz, out=None):
+    """The forward's per-chunk bookkeeping for a fixed support (row_ptr), as
+    a uint8 device tensor to pass as `plan` to qwha_adapter_forward (built on
+    row_ptr's stream; valid for this token count and device).  `out`: a
+    contiguous uint8 buffer of at least qwha_forward_plan_bytes to reuse."""
+    _need_cuda("row_ptr", row_ptr)
+    if row_ptr.dtype != torch.int32 or not row_ptr.is_contiguous() or row_ptr.numel() != d_out + 1:
+        raise ValueError("row_ptr must be contiguous int32 with d_out + 1 entries")
+    with torch.cuda.device(row_ptr.device):
+        nb = _lib.qwha_forward_plan_bytes(tokens, d_in, d_out, nnz)
+        if nb < 0:
+            raise ValueError("invalid sizes for a forward plan")
+        if out is None:
+            plan = torch.empty(max(int(nb), 256), dtype=torch.uint8, device=row_ptr.device)
+        else:
+            _need_cuda("out", out)
+            if out.dtype != torch.uint8 or not out.is_contiguous() or out.numel() < nb:
+                raise ValueError("out must be a contiguous uint8 buffer of qwha_forward_plan_bytes or more")
+            plan = out
+        _check("qwha_forward_plan", _lib.qwha_forward_plan(
+            tokens, d_in, _ptr(row_ptr), d_out, nnz, _ptr(plan), plan.numel(), _stream(row_ptr)))
+    return plan
+
+
+def qwha_adapter_forward(x, row_ptr, col_idx, vals, d_out, out=None, plan=None):
+    """y = (x Hn) F^T with F [d_out x d_in] in CSR (int32 row_ptr / col_idx);
+    `plan` from qwha_forward_plan skips the per-chunk bookkeeping."""
     _need_cuda("x", x)
     tokens, d_in, ldx = _rows_ld("x", x)
     for nm, t in (("row_ptr", row_ptr), ("col_idx", col_idx), ("vals", vals)):
@@ -225,9 +255,18 @@ def qwha_adapter_forward(x, row_ptr, col_idx, vals, d_out, out=None):
     if (r2, n2) != (tokens, d_out):
         raise ValueError("out shape mismatch")
     with torch.cuda.device(x.device):
-        _check("qwha_adapter_forward", _lib.qwha_adapter_forward(
-            _ptr(x), _DT[x.dtype], tokens, d_in, ldx, _ptr(row_ptr), _ptr(col_idx), _ptr(vals),
-            _DT[vals.dtype], d_out, nnz, _ptr(out), _DT[out.dtype], ldy, _stream(x)))
+        if plan is None:
+            _check("qwha_adapter_forward", _lib.qwha_adapter_forward(
+                _ptr(x), _DT[x.dtype], tokens, d_in, ldx, _ptr(row_ptr), _ptr(col_idx), _ptr(vals),
+                _DT[vals.dtype], d_out, nnz, _ptr(out), _DT[out.dtype], ldy, _stream(x)))
+        else:
+            _need_cuda("plan", plan)
+            if plan.dtype != torch.uint8 or not plan.is_contiguous():
+                raise ValueError("plan must be a contiguous uint8 tensor from qwha_forward_plan")
+            _check("qwha_adapter_forward_planned", _lib.qwha_adapter_forward_planned(
+                _ptr(x), _DT[x.dtype], tokens, d_in, ldx, _ptr(row_ptr), _ptr(col_idx), _ptr(vals),
+                _DT[vals.dtype], d_out, nnz, _ptr(plan), plan.numel(), _ptr(out), _DT[out.dtype], ldy,
+                _stream(x)))
     return out
 
 
