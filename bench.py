@@ -92,7 +92,7 @@ KERNELS = {  # kernel (as rocprofv3 names it) and the sources it is built from, 
                                         ["rht_quant.hpp", "rq_inv_b2.hip", "engine.hpp", "io.hpp", "common.hpp",
                                          "launch.hpp"]),
     "harp_8192x4096_r16x3": ("k_harp<true>", ["harp.hip", "common.hpp", "launch.hpp"]),
-    "qwha_2048x4096_nnz262144": ("k_qwha_fwd<1>", ["qwha_fwd.hip", "io.hpp", "engine.hpp", "common.hpp"]),
+    "qwha_2048x4096_nnz262144": ("k_qwha_fwd<1, false>", ["qwha_fwd.hip", "io.hpp", "engine.hpp", "common.hpp"]),
     "harp_8192x1024_r1688": ("k_harp_mx<2, 16>", ["harp_gen.hip", "io.hpp", "common.hpp", "launch.hpp"]),
 }
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
