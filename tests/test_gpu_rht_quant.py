@@ -45,6 +45,19 @@ def test_quant_all_sizes(logn, bits):
         check_quant(w, mask, bits, g)
 
 
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+def test_quant_4096_int4_strided_rows(dt):
+    """n = 4096 with 4-bit codes and groups of 64..256 on the matrix-core
+    kernel: bf16 and fp16 rows read through a row stride wider than the row,
+    and a row count that is not a multiple of anything the launch uses."""
+    rng = np.random.default_rng(4096 + (dt == torch.float16))
+    base = dev(0.02 * rng.standard_t(3, size=(517, 4096 + 72)), dt)
+    w = base[:, 8:4096 + 8]
+    mask = synth.sign_bits_to_mask(rng.integers(0, 2, 4096))
+    for g in (64, 128, 256):
+        check_quant(w, mask, 4, g)
+
+
 @pytest.mark.parametrize("dt", [torch.float32, torch.float16])
 def test_quant_other_input_dtypes(dt):
     rng = np.random.default_rng(5)
