@@ -168,3 +168,22 @@ def test_d_in_8192_needs_no_plan():
     assert W().raw().qwha_forward_plan_bytes(12, 8192, d_out, cols.size) == 0
     y0, y1, _ = both(x, rp, cols, v, d_out)
     assert torch.equal(y0, y1)
+
+
+@pytest.mark.parametrize("tokens,d_out,nnz", [(1, 5, 40), (17, 8, 200), (3, 9, 0)])
+def test_small_shapes_planned(tokens, d_out, nnz):
+    """One token, outputs narrower than a 16-byte store, one or two row
+    splits (at most one per 8 rows) and an empty support: the planned
+    forward gives the unplanned bytes."""
+    rng = np.random.default_rng(tokens * 100 + d_out)
+    rows = np.sort(rng.integers(0, d_out, nnz))
+    cols = rng.integers(0, 4096, nnz)
+    key = np.unique(rows * 4096 + cols)
+    rows, cols = key // 4096, (key % 4096).astype(np.int32)
+    rp = np.r_[0, np.cumsum(np.bincount(rows, minlength=d_out))].astype(np.int32)
+    x = synth.to_bf16(rng.standard_normal((tokens, 4096)))
+    v = synth.to_bf16(0.1 * rng.standard_normal(cols.size))
+    y0, y1, plan = both(x, rp, cols, v, d_out)
+    splits, _ = check_plan(plan, d_out, cols.size)
+    assert splits == (d_out + 7) // 8
+    assert torch.equal(y0, y1)
